@@ -1,0 +1,241 @@
+"""fp64 oracle: exact attention by its plain definition, and its gradient.
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.  Nothing here is
+tuned; every function forms the quantities the pages define explicitly.
+
+Tensor layout: Q and O are ``[B, Hq, L, d]``; K and V are ``[B, Hkv, L, d]``;
+the per-row log-sum-exp is ``[B, Hq, L]``.  Any float input is first
+converted to float64 (bf16 values are exactly representable in float64).
+
+Readings of the pages that this file encodes:
+
+* Attention is ``softmax(s * Q K^T) V`` with the softmax over keys (mdooai.com
+  "Ch.04 注意力优化", core formula); ``s`` is passed in (default 1/sqrt(d)).
+* A masked logit is minus infinity, so a masked key carries exactly zero
+  weight (same page, the sparse-attention formula in "公式速览").
+* Causal: key j is allowed for query i iff j <= i, the diagonal included
+  (claspmoon.cn "14 · 缩放定律与高效注意力" §3.5, ``is_causal=True``).
+* Sliding window of width w >= 1 (only together with causal): key j is
+  allowed iff i - w + 1 <= j <= i, i.e. the w most recent keys including
+  the query's own (book.anysome.cn "高效注意力" §4; window width as in the
+  Mistral-style configuration key of kler.cn §3.2.1).
+* GQA: query head h reads key/value head h // (Hq // Hkv) (book.anysome.cn
+  "高效注意力" §3: groups of query heads share one K/V head).
+* The log-sum-exp saved for the backward is the natural log over the scaled,
+  masked scores (claspmoon.cn §3.3: keep O and the per-row logsumexp).
+* A row with no allowed key (impossible for w >= 1 with causal masking, or
+  without masking) is defined as O = 0, LSE = -inf.
+"""
+
+import numpy as np
+
+
+def kv_head_of(h, hq, hkv):
+    """K/V head read by query head ``h``: contiguous groups of G = Hq/Hkv heads.
+
+    book.anysome.cn "高效注意力" §3 (MQA/GQA: several query heads share one
+    K/V head).  Requires Hq % Hkv == 0.
+    """
+    if hq % hkv != 0:
+        raise ValueError("Hq must be a multiple of Hkv")
+    return h // (hq // hkv)
+
+
+def allowed_mask(rows, L, causal, window):
+    """Boolean ``[len(rows), L]``: may query ``rows[r]`` attend to key ``j``?
+
+    Causal per claspmoon.cn §3.5 (``is_causal``); window per book.anysome.cn
+    §4 (each token attends only to the w nearby, here preceding, tokens).
+    """
+    i = np.asarray(rows, dtype=np.int64)[:, None]
+    j = np.arange(L, dtype=np.int64)[None, :]
+    ok = np.ones((i.shape[0], L), dtype=bool)
+    if causal:
+        ok &= j <= i
+    if window > 0:
+        if not causal:
+            raise ValueError("a sliding window is defined only with causal masking")
+        ok &= j >= i - window + 1
+    return ok
+
+
+def _masked_softmax_rows(S, ok):
+    """Row softmax of S with masked logits set to -inf (mdooai.com core formula).
+
+    Returns (A, lse) where A is row-stochastic over the allowed keys and
+    lse = log sum_j exp(S_ij) over allowed j.  The row maximum is subtracted
+    before exponentiating (safe softmax, kler.cn §3.1.1); in exact arithmetic
+    this changes nothing.
+    """
+    S = np.where(ok, S, -np.inf)
+    m = S.max(axis=-1, keepdims=True)
+    empty = ~ok.any(axis=-1, keepdims=True)
+    m_safe = np.where(empty, 0.0, m)
+    E = np.exp(S - m_safe)                       # exp(-inf) == 0 exactly
+    ell = E.sum(axis=-1, keepdims=True)
+    A = np.where(empty, 0.0, E / np.where(empty, 1.0, ell))
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, ell)))
+    return A, lse[..., 0]
+
+
+def _as64(x):
+    x = np.asarray(x)
+    return x.astype(np.float64, copy=False)
+
+
+def probabilities(q, k, scale, causal=False, window=0):
+    """The full attention matrix A = softmax(s Q K^T) per (b, hq): ``[B,Hq,L,L]``.
+
+    mdooai.com "Ch.04" core formula (A = softmax(S), rows sum to 1).  Only for
+    small L: it materialises L x L per head on purpose.
+    """
+    q, k = _as64(q), _as64(k)
+    B, Hq, L, _ = q.shape
+    Hkv = k.shape[1]
+    ok = allowed_mask(np.arange(L), L, causal, window)
+    A = np.empty((B, Hq, L, L))
+    for b in range(B):
+        for h in range(Hq):
+            S = scale * (q[b, h] @ k[b, kv_head_of(h, Hq, Hkv)].T)
+            A[b, h], _ = _masked_softmax_rows(S, ok)
+    return A
+
+
+def forward_rows(q, k, v, rows, scale, causal=False, window=0):
+    """O and LSE for the query rows ``rows`` only (exact for those rows).
+
+    For each row i: S_i = s * q_i K^T over all keys, masked logits -> -inf,
+    A_i = softmax(S_i), O_i = A_i V, LSE_i = log sum_j exp(S_ij)
+    (mdooai.com "Ch.04" core formula; claspmoon.cn §3.3 for the saved LSE).
+    Rows are independent in the definition, so any subset is exact.
+    Returns float64 ``O [B,Hq,len(rows),d]`` and ``LSE [B,Hq,len(rows)]``.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    rows = np.asarray(rows, dtype=np.int64)
+    ok = allowed_mask(rows, L, causal, window)
+    O = np.empty((B, Hq, rows.size, d))
+    lse = np.empty((B, Hq, rows.size))
+    for b in range(B):
+        for h in range(Hq):
+            kh = kv_head_of(h, Hq, Hkv)
+            S = scale * (q[b, h, rows] @ k[b, kh].T)
+            A, lse[b, h] = _masked_softmax_rows(S, ok)
+            O[b, h] = A @ v[b, kh]
+    return O, lse
+
+
+def forward(q, k, v, scale, causal=False, window=0, rows_per_chunk=4096):
+    """Exact attention forward: float64 ``(O [B,Hq,L,d], LSE [B,Hq,L])``.
+
+    The definition of ``forward_rows`` applied to every query row; rows are
+    visited in chunks only to bound the memory of the explicit S (each row's
+    arithmetic is unchanged by the chunking).
+    """
+    L = np.asarray(q).shape[2]
+    Os, ls = [], []
+    for r0 in range(0, L, rows_per_chunk):
+        O, lse = forward_rows(q, k, v, np.arange(r0, min(L, r0 + rows_per_chunk)),
+                              scale, causal, window)
+        Os.append(O)
+        ls.append(lse)
+    return np.concatenate(Os, axis=2), np.concatenate(ls, axis=2)
+
+
+def backward(q, k, v, dout, scale, causal=False, window=0):
+    """Analytic gradient of sum(O * dO) w.r.t. Q, K, V, in float64.
+
+    The pages only say that the backward recomputes the attention matrix from
+    Q, K, V instead of storing it (claspmoon.cn §3.3;
+    transformer.xph.ink "原理与机制").  The gradient itself is the softmax
+    Jacobian applied row by row, with A formed explicitly from its definition:
+        dV  = A^T dO
+        dA  = dO V^T
+        D_i = sum_j A_ij dA_ij
+        dS  = A * (dA - D)            (softmax Jacobian)
+        dQ  = s dS K,   dK = s dS^T Q
+    For GQA the K/V gradients of a group's query heads are summed into the
+    shared head.  Returns float64 ``(dQ, dK, dV)``.
+    """
+    q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    ok = allowed_mask(np.arange(L), L, causal, window)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            kh = kv_head_of(h, Hq, Hkv)
+            S = scale * (q[b, h] @ k[b, kh].T)
+            A, _ = _masked_softmax_rows(S, ok)
+            dv[b, kh] += A.T @ dout[b, h]
+            dA = dout[b, h] @ v[b, kh].T
+            dS = _softmax_backward(A, dA)
+            dq[b, h] = scale * (dS @ k[b, kh])
+            dk[b, kh] += scale * (dS.T @ q[b, h])
+    return dq, dk, dv
+
+
+def _softmax_backward(A, dA):
+    """dS = A * (dA - rowsum(A * dA)): the Jacobian of a row softmax."""
+    D = (A * dA).sum(axis=-1, keepdims=True)
+    return A * (dA - D)
+
+
+def tiled_online_forward(q, k, v, scale, causal=False, window=0,
+                         row_edges=None, col_edges=None):
+    """The pages' tiled algorithm with the online-softmax recurrence, in fp64.
+
+    claspmoon.cn §3.2 (loop over query tiles Q_i, then key tiles K_j; only
+    the final O is written) with the running statistics of
+    transformer.xph.ink "原理与机制": per row a running max m and running sum
+    l; for each key tile
+        m_new = max(m, rowmax(S_tile))
+        P     = exp(S_tile - m_new)
+        l     = exp(m - m_new) * l + rowsum(P)
+        O     = exp(m - m_new) * O + P V_tile
+    and at the end O / l, LSE = m + log l.  (The printed recurrence on
+    claspmoon.cn swaps the names of the max and the sum; the reading used
+    here is the one the other pages state.)  ``row_edges``/``col_edges`` are
+    increasing tile boundaries from 0 to L; tiles may have any sizes.
+    This is an independent second path, used only to pin that the recurrence
+    equals the direct definition.
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    row_edges = list(row_edges) if row_edges is not None else [0, L]
+    col_edges = list(col_edges) if col_edges is not None else [0, L]
+    O = np.zeros((B, Hq, L, d))
+    lse = np.zeros((B, Hq, L))
+    for b in range(B):
+        for h in range(Hq):
+            kh = kv_head_of(h, Hq, Hkv)
+            for r0, r1 in zip(row_edges[:-1], row_edges[1:]):
+                rows = np.arange(r0, r1)
+                m = np.full(rows.size, -np.inf)
+                ell = np.zeros(rows.size)
+                acc = np.zeros((rows.size, d))
+                for c0, c1 in zip(col_edges[:-1], col_edges[1:]):
+                    ok = allowed_mask(rows, L, causal, window)[:, c0:c1]
+                    S = scale * (q[b, h, rows] @ k[b, kh, c0:c1].T)
+                    S = np.where(ok, S, -np.inf)
+                    m_new = np.maximum(m, S.max(axis=1))
+                    # rows with nothing allowed so far keep m = -inf; use 0 as
+                    # the shift there so that exp(-inf - 0) = 0 and no NaN arises
+                    shift = np.where(np.isneginf(m_new), 0.0, m_new)
+                    P = np.exp(S - shift[:, None])
+                    alpha = np.exp(np.where(np.isneginf(m), -np.inf, m - shift))
+                    ell = alpha * ell + P.sum(axis=1)
+                    acc = alpha[:, None] * acc + P @ v[b, kh, c0:c1]
+                    m = m_new
+                empty = ell == 0.0
+                O[b, h, rows] = np.where(empty[:, None], 0.0,
+                                         acc / np.where(empty, 1.0, ell)[:, None])
+                with np.errstate(divide="ignore"):
+                    lse[b, h, rows] = np.where(empty, -np.inf,
+                                               m + np.log(np.where(empty, 1.0, ell)))
+    return O, lse

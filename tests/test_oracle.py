@@ -1,0 +1,349 @@
+"""Pins for the fp64 CPU oracle (no GPU).
+
+The oracle must be anchored to something other than itself before GPU results
+are compared with it.  Each pin below is a fact fixed by the pages or by the
+mathematics: closed forms, invariants, exact zeros, a library routine
+(PyTorch's float64 CPU ``scaled_dot_product_attention`` and autograd,
+``scipy.special.logsumexp``), central finite differences, and the equivalence
+of the tiled online-softmax recurrence with the direct definition.  The
+``test_planted_*`` cases plant plausible mistakes in the oracle (on the CPU)
+and check that at least one pin catches each of them.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+import torch.nn.functional as F
+
+import oracle
+import oracle.attention as oa
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+def rnd(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def allowed_range(i, L, causal, window):
+    """Allowed keys of query i as a Python range (written independently of the mask code)."""
+    hi = i if causal else L - 1
+    lo = max(0, i - window + 1) if window > 0 else 0
+    return range(lo, hi + 1)
+
+
+MASKS = [(False, 0), (True, 0), (True, 1), (True, 3), (True, 7)]
+
+
+# ----------------------------------------------------------------------------- pins
+
+def pin_rows_stochastic(o):
+    for causal, window in MASKS:
+        q, k = rnd((2, 3, 9, 4), 1), rnd((2, 3, 9, 4), 2)
+        A = o.probabilities(q, k, 0.5, causal, window)
+        assert np.allclose(A.sum(-1), 1.0, atol=1e-14, rtol=0), "rows of A must sum to 1"
+        for i in range(9):
+            allowed = set(allowed_range(i, 9, causal, window))
+            for j in range(9):
+                if j in allowed:
+                    assert (A[:, :, i, j] > 0).all()
+                else:
+                    assert (A[:, :, i, j] == 0.0).all(), "masked keys carry exactly zero weight"
+
+
+def pin_two_key_worked_example(o):
+    # scores 0 and ln 3 -> weights 1/4 and 3/4 -> O = 1/4*1 + 3/4*5 = 4, LSE = ln 4
+    q = np.array([1.0, 1.0]).reshape(1, 1, 2, 1)
+    k = np.array([0.0, math.log(3.0)]).reshape(1, 1, 2, 1)
+    v = np.array([1.0, 5.0]).reshape(1, 1, 2, 1)
+    O, lse = o.forward(q, k, v, 1.0, causal=False)
+    assert abs(O[0, 0, 0, 0] - 4.0) < 1e-14 and abs(O[0, 0, 1, 0] - 4.0) < 1e-14
+    assert abs(lse[0, 0, 0] - math.log(4.0)) < 1e-14
+    # causal: query 0 sees only key 0 -> O = 1, LSE = 0
+    O, lse = o.forward(q, k, v, 1.0, causal=True)
+    assert O[0, 0, 0, 0] == 1.0 and lse[0, 0, 0] == 0.0
+    assert abs(O[0, 0, 1, 0] - 4.0) < 1e-14
+
+
+def pin_length_one(o):
+    q, k, v = rnd((2, 4, 1, 8), 3), rnd((2, 2, 1, 8), 4), rnd((2, 2, 1, 8), 5)
+    for causal, window in [(False, 0), (True, 0), (True, 1)]:
+        O, lse = o.forward(q, k, v, 0.3, causal, window)
+        for h in range(4):
+            assert np.allclose(O[:, h], v[:, h // 2], atol=1e-15, rtol=0)
+            assert np.allclose(lse[:, h, 0], 0.3 * (q[:, h, 0] * k[:, h // 2, 0]).sum(-1), atol=1e-14, rtol=0)
+
+
+def pin_zero_query_is_mean(o):
+    L = 11
+    for causal, window in MASKS:
+        q = np.zeros((1, 2, L, 5))
+        k, v = rnd((1, 2, L, 5), 6), rnd((1, 2, L, 5), 7)
+        O, lse = o.forward(q, k, v, 0.7, causal, window)
+        for h in range(2):
+            for i in range(L):
+                r = allowed_range(i, L, causal, window)
+                assert np.allclose(O[0, h, i], v[0, h, r.start:r.stop].mean(0), atol=1e-14, rtol=0)
+                assert abs(lse[0, h, i] - math.log(len(r))) < 1e-14
+
+
+def pin_identical_keys(o):
+    L = 10
+    for causal, window in MASKS:
+        q, v = rnd((1, 2, L, 4), 8), rnd((1, 1, L, 4), 9)
+        k0 = rnd((4,), 10)
+        k = np.broadcast_to(k0, (1, 1, L, 4)).copy()
+        O, lse = o.forward(q, k, v, 0.9, causal, window)
+        for h in range(2):
+            for i in range(L):
+                r = allowed_range(i, L, causal, window)
+                assert np.allclose(O[0, h, i], v[0, 0, r.start:r.stop].mean(0), atol=1e-13, rtol=0)
+                expect = 0.9 * float(q[0, h, i] @ k0) + math.log(len(r))
+                assert abs(lse[0, h, i] - expect) < 1e-13
+
+
+def pin_convexity(o):
+    L = 13
+    for causal, window in MASKS:
+        q, k, v = rnd((2, 2, L, 6), 11, 3.0), rnd((2, 2, L, 6), 12, 3.0), rnd((2, 2, L, 6), 13)
+        O, _ = o.forward(q, k, v, 1.0, causal, window)
+        for i in range(L):
+            r = allowed_range(i, L, causal, window)
+            lo = v[:, :, r.start:r.stop].min(2)
+            hi = v[:, :, r.start:r.stop].max(2)
+            assert (O[:, :, i] >= lo - 1e-14).all() and (O[:, :, i] <= hi + 1e-14).all()
+
+
+def pin_shift_invariance(o):
+    L = 12
+    q, k, v = rnd((1, 3, L, 5), 14), rnd((1, 3, L, 5), 15), rnd((1, 3, L, 5), 16)
+    c = rnd((5,), 17)
+    for causal, window in MASKS:
+        O1, l1 = o.forward(q, k, v, 0.6, causal, window)
+        O2, l2 = o.forward(q, k + c, v, 0.6, causal, window)
+        assert np.allclose(O1, O2, atol=1e-13, rtol=0)
+        assert np.allclose(l2 - l1, 0.6 * (q @ c), atol=1e-12, rtol=0)
+
+
+def pin_permutation_noncausal(o):
+    L = 9
+    q, k, v = rnd((2, 2, L, 4), 18), rnd((2, 2, L, 4), 19), rnd((2, 2, L, 4), 20)
+    perm = np.random.default_rng(21).permutation(L)
+    O1, l1 = o.forward(q, k, v, 0.5)
+    O2, l2 = o.forward(q, k[:, :, perm], v[:, :, perm], 0.5)
+    assert np.allclose(O1, O2, atol=1e-14, rtol=0) and np.allclose(l1, l2, atol=1e-14, rtol=0)
+
+
+def pin_gqa_is_repeated_mha(o):
+    B, Hq, Hkv, L, d = 2, 6, 2, 10, 4
+    q, k, v, do = rnd((B, Hq, L, d), 22), rnd((B, Hkv, L, d), 23), rnd((B, Hkv, L, d), 24), rnd((B, Hq, L, d), 25)
+    G = Hq // Hkv
+    kr, vr = np.repeat(k, G, axis=1), np.repeat(v, G, axis=1)
+    for causal, window in MASKS:
+        O1, l1 = o.forward(q, k, v, 0.5, causal, window)
+        O2, l2 = o.forward(q, kr, vr, 0.5, causal, window)
+        assert np.allclose(O1, O2, atol=1e-14, rtol=0) and np.allclose(l1, l2, atol=1e-14, rtol=0)
+        dq1, dk1, dv1 = o.backward(q, k, v, do, 0.5, causal, window)
+        dq2, dk2, dv2 = o.backward(q, kr, vr, do, 0.5, causal, window)
+        assert np.allclose(dq1, dq2, atol=1e-13, rtol=0)
+        assert np.allclose(dk1, dk2.reshape(B, Hkv, G, L, d).sum(2), atol=1e-13, rtol=0)
+        assert np.allclose(dv1, dv2.reshape(B, Hkv, G, L, d).sum(2), atol=1e-13, rtol=0)
+
+
+def pin_window_at_least_L_is_causal(o):
+    L = 8
+    q, k, v = rnd((1, 2, L, 3), 26), rnd((1, 2, L, 3), 27), rnd((1, 2, L, 3), 28)
+    O1, l1 = o.forward(q, k, v, 1.0, True, 0)
+    for w in (L, L + 5):
+        O2, l2 = o.forward(q, k, v, 1.0, True, w)
+        assert np.array_equal(O1, O2) and np.array_equal(l1, l2)
+
+
+def _torch_mask(L, causal, window):
+    m = torch.zeros(L, L, dtype=torch.bool)
+    for i in range(L):
+        for j in allowed_range(i, L, causal, window):
+            m[i, j] = True
+    return m
+
+
+def pin_torch_sdpa_and_logsumexp(o):
+    B, Hq, Hkv, L, d = 2, 4, 2, 17, 8
+    q, k, v = rnd((B, Hq, L, d), 29), rnd((B, Hkv, L, d), 30), rnd((B, Hkv, L, d), 31)
+    scale = 1.0 / math.sqrt(d)
+    tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
+    for causal, window in MASKS:
+        mask = _torch_mask(L, causal, window)
+        ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale, enable_gqa=True).numpy()
+        O, lse = o.forward(q, k, v, scale, causal, window)
+        assert np.allclose(O, ref, atol=1e-13, rtol=0), "oracle O disagrees with torch float64 SDPA"
+        kr = torch.repeat_interleave(tk, Hq // Hkv, dim=1)
+        S = (tq @ kr.transpose(-1, -2)).numpy() * scale
+        S = np.where(mask.numpy(), S, -np.inf)
+        assert np.allclose(lse, scipy.special.logsumexp(S, axis=-1), atol=1e-13, rtol=0)
+
+
+def pin_backward_vs_torch_autograd(o):
+    B, Hq, Hkv, L, d = 1, 4, 2, 13, 6
+    q, k, v, do = rnd((B, Hq, L, d), 32), rnd((B, Hkv, L, d), 33), rnd((B, Hkv, L, d), 34), rnd((B, Hq, L, d), 35)
+    for causal, window in MASKS:
+        tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_(True) for x in (q, k, v))
+        out = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=_torch_mask(L, causal, window),
+                                             scale=0.4, enable_gqa=True)
+        out.backward(torch.from_numpy(do))
+        dq, dk, dv = o.backward(q, k, v, do, 0.4, causal, window)
+        assert np.allclose(dq, tq.grad.numpy(), atol=1e-12, rtol=0)
+        assert np.allclose(dk, tk.grad.numpy(), atol=1e-12, rtol=0)
+        assert np.allclose(dv, tv.grad.numpy(), atol=1e-12, rtol=0)
+
+
+def pin_backward_finite_differences(o):
+    B, Hq, Hkv, L, d = 1, 2, 1, 5, 3
+    q, k, v, do = rnd((B, Hq, L, d), 36), rnd((B, Hkv, L, d), 37), rnd((B, Hkv, L, d), 38), rnd((B, Hq, L, d), 39)
+    h = 1e-6
+    for causal, window in [(False, 0), (True, 0), (True, 2)]:
+        grads = o.backward(q, k, v, do, 0.8, causal, window)
+
+        def f(q_, k_, v_):
+            return float((o.forward(q_, k_, v_, 0.8, causal, window)[0] * do).sum())
+
+        for which, x in enumerate((q, k, v)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                args_p[which], args_m[which] = xp, xm
+                num[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+            g = grads[which]
+            rel = np.linalg.norm(num - g) / np.linalg.norm(num)
+            assert rel <= 1e-6, f"finite-difference mismatch on input {which}: rel {rel:.2e}"
+
+
+def pin_backward_identities(o):
+    B, Hq, Hkv, L, d = 2, 4, 2, 15, 5
+    q, k, v, do = rnd((B, Hq, L, d), 40), rnd((B, Hkv, L, d), 41), rnd((B, Hkv, L, d), 42), rnd((B, Hq, L, d), 43)
+    for causal, window in MASKS:
+        dq, dk, dv = o.backward(q, k, v, do, 0.5, causal, window)
+        assert np.allclose(dk.sum(2), 0.0, atol=1e-12), "sum_j dK_j must vanish"
+        assert np.allclose(dv.sum(2), do.reshape(B, Hkv, Hq // Hkv, L, d).sum((2, 3)), atol=1e-12)
+
+
+def pin_tiled_recurrence_equals_direct(o):
+    B, Hq, Hkv, L, d = 1, 4, 2, 37, 6
+    q, k, v = rnd((B, Hq, L, d), 44, 2.0), rnd((B, Hkv, L, d), 45, 2.0), rnd((B, Hkv, L, d), 46)
+    rng = np.random.default_rng(47)
+    for causal, window in MASKS:
+        for _ in range(3):
+            re = [0] + sorted(rng.choice(np.arange(1, L), size=4, replace=False).tolist()) + [L]
+            ce = [0] + sorted(rng.choice(np.arange(1, L), size=5, replace=False).tolist()) + [L]
+            O1, l1 = o.forward(q, k, v, 0.45, causal, window)
+            O2, l2 = o.tiled_online_forward(q, k, v, 0.45, causal, window, re, ce)
+            assert np.allclose(O1, O2, atol=1e-12, rtol=0) and np.allclose(l1, l2, atol=1e-12, rtol=0)
+
+
+def pin_rows_subset(o):
+    L = 20
+    q, k, v = rnd((1, 2, L, 4), 48), rnd((1, 2, L, 4), 49), rnd((1, 2, L, 4), 50)
+    rows = np.array([0, 3, 7, 19])
+    for causal, window in MASKS:
+        O, l = o.forward(q, k, v, 0.5, causal, window)
+        Or, lr = o.forward_rows(q, k, v, rows, 0.5, causal, window)
+        assert np.array_equal(O[:, :, rows], Or) and np.array_equal(l[:, :, rows], lr)
+
+
+PINS = [pin_rows_stochastic, pin_two_key_worked_example, pin_length_one, pin_zero_query_is_mean,
+        pin_identical_keys, pin_convexity, pin_shift_invariance, pin_permutation_noncausal,
+        pin_gqa_is_repeated_mha, pin_window_at_least_L_is_causal, pin_torch_sdpa_and_logsumexp,
+        pin_backward_vs_torch_autograd, pin_backward_finite_differences, pin_backward_identities,
+        pin_tiled_recurrence_equals_direct, pin_rows_subset]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_pin(pin):
+    pin(oracle)
+
+
+# ----------------------------------------------------------------- planted mistakes
+
+def _some_pin_fails(pins):
+    for p in pins:
+        try:
+            p(oracle)
+        except AssertionError:
+            return True
+    return False
+
+
+FWD_PINS = [pin_zero_query_is_mean, pin_torch_sdpa_and_logsumexp, pin_length_one,
+            pin_shift_invariance, pin_gqa_is_repeated_mha, pin_rows_stochastic]
+BWD_PINS = [pin_backward_finite_differences, pin_backward_vs_torch_autograd, pin_backward_identities]
+
+
+def test_planted_causal_off_by_one(monkeypatch):
+    good = oa.allowed_mask
+
+    def bad(rows, L, causal, window):
+        ok = good(rows, L, False, 0)
+        i = np.asarray(rows)[:, None]
+        j = np.arange(L)[None, :]
+        if causal:
+            ok &= j < i                      # diagonal wrongly excluded
+        if window > 0:
+            ok &= j >= i - window + 1
+        return ok
+
+    monkeypatch.setattr(oa, "allowed_mask", bad)
+    assert _some_pin_fails(FWD_PINS)
+
+
+def test_planted_window_off_by_one(monkeypatch):
+    good = oa.allowed_mask
+
+    def bad(rows, L, causal, window):
+        ok = good(rows, L, causal, 0)
+        if window > 0:
+            ok &= np.arange(L)[None, :] >= np.asarray(rows)[:, None] - window   # one key too many
+        return ok
+
+    monkeypatch.setattr(oa, "allowed_mask", bad)
+    assert _some_pin_fails(FWD_PINS)
+
+
+def test_planted_gqa_head_mapping(monkeypatch):
+    monkeypatch.setattr(oa, "kv_head_of", lambda h, hq, hkv: h % hkv)   # interleaved instead of grouped
+    assert _some_pin_fails(FWD_PINS)
+
+
+def test_planted_lse_without_max(monkeypatch):
+    good = oa._masked_softmax_rows
+
+    def bad(S, ok):
+        A, lse = good(S, ok)
+        Sm = np.where(ok, S, -np.inf)
+        return A, lse - Sm.max(axis=-1)       # drops the max term from the log-sum-exp
+    monkeypatch.setattr(oa, "_masked_softmax_rows", bad)
+    assert _some_pin_fails(FWD_PINS)
+
+
+def test_planted_softmax_backward_without_D(monkeypatch):
+    monkeypatch.setattr(oa, "_softmax_backward", lambda A, dA: A * dA)
+    assert _some_pin_fails(BWD_PINS)
+
+
+def test_planted_softmax_backward_sign(monkeypatch):
+    monkeypatch.setattr(oa, "_softmax_backward",
+                        lambda A, dA: A * ((A * dA).sum(-1, keepdims=True) - dA))
+    assert _some_pin_fails(BWD_PINS)
+
+
+def test_unallowed_window_without_causal_is_rejected():
+    with pytest.raises(ValueError):
+        oracle.allowed_mask(np.arange(4), 4, False, 2)
+    with pytest.raises(ValueError):
+        oracle.kv_head_of(0, 6, 4)
