@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Throughput of exact tiled attention on one MI355X, as one JSON line.
+
+A step is one pass of the whole hot path over one batch of synthetic input: the
+forward (O and the per-row log-sum-exp) followed by the recomputing backward
+(dQ, dK, dV) of a LLaMA-7B-shaped causal attention layer, B=2, H=32, L=4096,
+d=128, bf16 inputs with fp32 accumulation.  Inputs are seeded Gaussians already
+resident in HBM when the timed region starts.
+
+FLOPs are counted algorithmically: forward 4*B*Hq*L^2*d, halved for causal
+(the allowed band for a sliding window); backward 2.5x the forward (five
+matrix products, the recomputation of Q K^T included).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0              # MI355X HBM3E, published
+METRIC = "attention fwd/bwd TFLOP/s + % bf16 MFMA peak, B2 H32 L4096 d128 causal"
+
+
+def fwd_flops(B, Hq, L, d, causal, window):
+    if window and window > 0:
+        w = min(window, L)
+        return 4.0 * B * Hq * d * (w * L - w * (w - 1) / 2)
+    full = 4.0 * B * Hq * L * L * d
+    return full / 2 if causal else full
+
+
+def bwd_flops(B, Hq, L, d, causal, window):
+    return 2.5 * fwd_flops(B, Hq, L, d, causal, window)
+
+
+def fwd_bytes(B, Hq, Hkv, L, d, elt=2):
+    """Algorithmic HBM bytes of one forward: Q, K, V read once; O and LSE written."""
+    return (B * Hq * L * d + 2 * B * Hkv * L * d) * elt + B * Hq * L * d * elt + B * Hq * L * 4
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "exact_tiled_attention_flash_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".hpp", ".h")):
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key):
+    """HBM traffic per launch from committed rocprofv3 counter runs, or None if stale/absent."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        data = json.load(open(p))
+        ent = data.get(kernel_key)
+        if not ent or ent.get("source_digest") != kernel_source_digest():
+            return None
+        return float(ent["bytes_per_launch"])
+    except Exception:
+        return None
+
+
+def cpu_baseline(budget_s=20.0):
+    """Time the fp64 oracle on a bounded sample of the same workload (rank 0 only)."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    w = W.LLAMA7B_CAUSAL
+    q, k, v, do = W.make_inputs(w, with_dout=True)
+    qn, kn, vn, don = (t.float().numpy() for t in (q, k, v, do))
+    flops = 0.0
+    heads = 0
+    t0 = time.perf_counter()
+    # forward, one (batch, head) at a time, until about half the budget is spent
+    for h in range(w.Hq):
+        oracle.forward(qn[:1, h:h + 1], kn[:1, h:h + 1], vn[:1, h:h + 1], w.scale, True, 0)
+        flops += fwd_flops(1, 1, w.L, w.d, True, 0)
+        heads += 1
+        if time.perf_counter() - t0 > budget_s / 2:
+            break
+    t_f = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    bheads = 0
+    for h in range(w.Hq):
+        oracle.backward(qn[:1, h:h + 1], kn[:1, h:h + 1], vn[:1, h:h + 1], don[:1, h:h + 1], w.scale, True, 0)
+        flops += bwd_flops(1, 1, w.L, w.d, True, 0)
+        bheads += 1
+        if time.perf_counter() - t1 > budget_s / 2:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 NumPy oracle on {heads} head(s) forward + {bheads} head(s) backward "
+                      f"of B2 H32 L4096 d128 causal (each one full 4096x4096 head); "
+                      f"{dt:.1f} s wall, {t_f:.1f} s of it forward; host os.cpu_count()={os.cpu_count()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(heads and batches would shard with no communication; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import exact_tiled_attention_flash_amd as fa
+    import workloads as W
+
+    fa.library()
+    dev = torch.device("cuda:0")
+    w = W.LLAMA7B_CAUSAL
+    q, k, v, do = W.make_inputs(w, with_dout=True)
+    q, k, v, do = (t.to(dev) for t in (q, k, v, do))
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.Hq, w.L, dtype=torch.float32, device=dev)
+    have_bwd = True
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.L, w.d), dtype=torch.uint8, device=dev)
+
+    def run_fwd():
+        fa.fwd(q, k, v, causal=True, scale=w.scale, out=o, lse=lse)
+
+    def run_bwd():
+        fa.bwd(q, k, v, o, lse, do, causal=True, scale=w.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+
+    run_fwd()
+    try:
+        run_bwd()
+    except RuntimeError as e:
+        print("backward unavailable, timing forward only:", e, file=sys.stderr)
+        have_bwd = False
+    torch.cuda.synchronize()
+
+    for _ in range(args.warmup):
+        run_fwd()
+        if have_bwd:
+            run_bwd()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        ev[i][0].record()
+        run_fwd()
+        ev[i][1].record()
+        if have_bwd:
+            run_bwd()
+        ev[i][2].record()
+    t_end.record()
+    torch.cuda.synchronize()
+
+    total_ms = t_start.elapsed_time(t_end)
+    f_ms = [e[0].elapsed_time(e[1]) for e in ev]
+    b_ms = [e[1].elapsed_time(e[2]) for e in ev] if have_bwd else []
+    ms_step = total_ms / args.steps
+    ff = fwd_flops(w.B, w.Hq, w.L, w.d, True, 0)
+    bf = bwd_flops(w.B, w.Hq, w.L, w.d, True, 0) if have_bwd else 0.0
+    f_avg = sum(f_ms) / len(f_ms)
+    b_avg = sum(b_ms) / len(b_ms) if b_ms else None
+    f_med = sorted(f_ms)[len(f_ms) // 2]
+    value = (ff + bf) / (ms_step * 1e-3) / 1e12
+
+    fwd_tf = ff / (f_avg * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "llama7b-shaped attention layer fwd+bwd" if have_bwd else
+                   "llama7b-shaped attention layer fwd only",
+                   "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "d": w.d, "causal": True,
+                   "window": 0, "inputs": "seeded N(0,1) bf16, resident in HBM"},
+        "fwd": {"ms_mean": round(f_avg, 4), "ms_median": round(f_med, 4),
+                "tflops": round(fwd_tf, 2), "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
+    }
+    if have_bwd:
+        bwd_tf = bf / (b_avg * 1e-3) / 1e12
+        out["bwd"] = {"ms_mean": round(b_avg, 4), "ms_median": round(sorted(b_ms)[len(b_ms) // 2], 4),
+                      "tflops": round(bwd_tf, 2), "frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)}
+    # the forward kernel: one launch per fwd call, timed on the stream it runs on
+    traffic = load_traffic("fwd_bf16_d128_causal")
+    out["roofline"] = {"kernel": "fwd_bf16_kernel<128,causal>", "bound": "mfma",
+                       "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                       "algorithmic_bytes": fwd_bytes(w.B, w.Hq, w.Hkv, w.L, w.d)}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

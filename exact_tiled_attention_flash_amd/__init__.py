@@ -1,0 +1,146 @@
+"""Exact tiled attention for AMD MI355X (gfx950): thin Python binding.
+
+The work is done entirely by the HIP kernels in ``libflashattn.so`` behind the
+C ABI declared in ``include/flash_attn.h``; this module only marshals torch
+tensors into device pointers, sizes and the current HIP stream.  There is no
+fallback: if the library is missing or a call fails, a RuntimeError is raised.
+
+    o, lse = fwd(q, k, v, causal=True)                 # q [B,Hq,L,d], k/v [B,Hkv,L,d]
+    dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
+
+The interface mirrors the pages' ``scaled_dot_product_attention(q, k, v,
+is_causal=...)`` usage (claspmoon.cn "14 · 缩放定律与高效注意力" §3.5) plus the
+grouped-query and sliding-window options (kler.cn, §3.2.1 configuration keys).
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "strerror", "library", "library_path",
+           "FA_DTYPE_F32", "FA_DTYPE_BF16", "EXPORTED_SYMBOLS"]
+
+FA_DTYPE_F32 = 0
+FA_DTYPE_BF16 = 1
+_DTYPES = {torch.float32: FA_DTYPE_F32, torch.bfloat16: FA_DTYPE_BF16}
+
+EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_bytes",
+                    "flash_attn_strerror", "flash_attn_version")
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB = None
+
+
+def library_path():
+    return os.path.join(_HERE, "libflashattn.so")
+
+
+def library():
+    """Load ``libflashattn.so`` (once).  Raises RuntimeError if it is not built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(
+            "libflashattn.so is not built (expected at %s); run "
+            "`python -m exact_tiled_attention_flash_amd.build`" % path)
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.flash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    lib.flash_attn_fwd.restype = i
+    lib.flash_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                   i, i, i, i, i, f, i, i, i, vp]
+    lib.flash_attn_bwd.restype = i
+    lib.flash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.flash_attn_bwd_workspace_bytes.restype = sz
+    lib.flash_attn_strerror.argtypes = [i]
+    lib.flash_attn_strerror.restype = ctypes.c_char_p
+    lib.flash_attn_version.argtypes = []
+    lib.flash_attn_version.restype = i
+    _LIB = lib
+    return lib
+
+
+def strerror(code):
+    return library().flash_attn_strerror(int(code)).decode()
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError("%s failed: %s (code %d)" % (what, strerror(rc), rc))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _shapes(q, k, v):
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, L, d]")
+    B, Hq, L, d = q.shape
+    if k.shape != v.shape or k.shape[0] != B or k.shape[2] != L or k.shape[3] != d:
+        raise ValueError("k and v must be [B, Hkv, L, d] matching q")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous CUDA tensors of one dtype")
+    if q.dtype not in _DTYPES:
+        raise ValueError("dtype must be float32 or bfloat16")
+    return B, Hq, k.shape[1], L, d
+
+
+def fwd(q, k, v, causal=False, window=0, scale=None, out=None, lse=None):
+    """Exact attention forward.  Returns ``(o, lse)``; ``lse`` is float32 ``[B,Hq,L]``.
+
+    ``window`` (>= 1, with ``causal``) limits query i to keys i-window+1..i.
+    ``scale`` defaults to 1/sqrt(d).
+    """
+    B, Hq, Hkv, L, d = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    rc = library().flash_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                  B, Hq, Hkv, L, d, scale, int(bool(causal)), int(window),
+                                  _DTYPES[q.dtype], _stream(q))
+    _check(rc, "flash_attn_fwd")
+    return out, lse
+
+
+def bwd_workspace_bytes(B, Hq, Hkv, L, d, dtype=torch.bfloat16):
+    return int(library().flash_attn_bwd_workspace_bytes(B, Hq, Hkv, L, d, _DTYPES[dtype]))
+
+
+def bwd(q, k, v, o, lse, dout, causal=False, window=0, scale=None, workspace=None,
+        dq=None, dk=None, dv=None):
+    """Gradient of sum(o * dout) w.r.t. q, k, v, recomputing P from ``lse``.
+
+    Returns ``(dq, dk, dv)`` in the input dtype.  ``workspace`` (optional) is a
+    device uint8 tensor of at least ``bwd_workspace_bytes(...)`` bytes.
+    """
+    B, Hq, Hkv, L, d = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    for t in (o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError("o and dout must match q")
+    if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be contiguous float32 [B, Hq, L]")
+    nbytes = bwd_workspace_bytes(B, Hq, Hkv, L, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    rc = library().flash_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                  _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                                  B, Hq, Hkv, L, d, scale, int(bool(causal)), int(window),
+                                  _DTYPES[q.dtype], _stream(q))
+    _check(rc, "flash_attn_bwd")
+    return dq, dk, dv

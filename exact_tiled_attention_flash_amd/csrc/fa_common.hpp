@@ -1,0 +1,112 @@
+// fa_common.hpp -- device-side building blocks shared by the gfx950 kernels.
+//
+// MFMA register layouts used throughout (v_mfma_f32_32x32x16_bf16, one wave):
+//   A operand (32 x 16, M x K): lane l holds row m = l % 32 and 8 consecutive
+//     K slots of slice g = l / 32.
+//   B operand (16 x 32, K x N): lane l holds column n = l % 32, same K slots.
+//   C/D (32 x 32 fp32):         lane l, register i holds
+//     row m = 8*(i/4) + 4*(l/32) + (i%4), column n = l % 32.
+// A and B label their K slots identically, so any bijection between
+// (slice, slot) and the contraction index gives the same product; the kernels
+// choose the bijection that lets one MFMA's C registers feed the next MFMA's
+// B operand directly.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define FA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+// Running-max sentinel: finite, so that exp2(m_old - m_new) never sees
+// (-inf) - (-inf).  Any real scaled score is far above it.
+constexpr float kNegBig = -1.0e30f;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte LDS load at a byte offset.
+__device__ __forceinline__ bf16x8 lds_load16(const char* base, int byte_off) {
+  return *(const FA_LDS bf16x8*)((const FA_LDS char*)(base) + byte_off);
+}
+
+// gfx950 transposing LDS read.  Within each group of 16 lanes, result lane i,
+// element r is element (i % 4) of the 8 bytes addressed by lane 4*r + i/4.
+__device__ __forceinline__ bf16x4 lds_load_tr(const char* base, int byte_off) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA_LDS i16x4*)((FA_LDS char*)(base) + byte_off));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+// Direct 16-byte global -> LDS copy for a whole wave: lane l's 16 bytes from
+// `src` land at lds_wave_base + 16*l.  `lds_wave_base` must be wave-uniform.
+__device__ __forceinline__ void g2lds16(const void* src, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (FA_LDS void*)(lds_wave_base), 16, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 concat4(const bf16x4& lo, const bf16x4& hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Round-to-nearest-even fp32 -> bf16 of 8 values (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float a3,
+                                            float a4, float a5, float a6, float a7) {
+  bf16x8 r;
+  r[0] = (bf16)a0; r[1] = (bf16)a1; r[2] = (bf16)a2; r[3] = (bf16)a3;
+  r[4] = (bf16)a4; r[5] = (bf16)a5; r[6] = (bf16)a6; r[7] = (bf16)a7;
+  return r;
+}
+
+__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// LDS row swizzle (XOR on the 16-byte chunk index of row r) that keeps two read
+// patterns free of bank conflicts: 16 consecutive rows read at one chunk
+// (16-byte reads), and 4 consecutive rows x 4 chunks (the transposing read).
+template <int D>
+__device__ __forceinline__ int swz_dual(int r) {
+  return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// Byte offset, inside a [rows x D] bf16 tile stored with swz_dual, of the 8
+// bytes lane `lane` supplies to the transposing read for MFMA K-step t (16
+// rows) and 32-wide column block db.  Slots 0..3 come from this offset,
+// slots 4..7 from the same offset plus 8 rows.  The rows then line up with
+// the C-layout rows 16t + 8*(slot/4) + 4*(lane/32) + slot%4 of an MFMA result.
+template <int D>
+__device__ __forceinline__ int tr_offset_dual(int t, int db, int lane) {
+  const int s16 = lane & 15, jg = lane >> 4;
+  const int row = 16 * t + 4 * (lane >> 5) + (s16 >> 2);
+  const int col = 32 * db + 16 * (jg & 1) + 4 * (s16 & 3);
+  return row * (2 * D) + (((col >> 3) ^ swz_dual<D>(row)) << 4) + ((col & 4) << 1);
+}
+
+// Byte offset of the 16 bytes (head dims 16k + 8g .. +7) of row r in a tile
+// stored with swz_dual.
+template <int D>
+__device__ __forceinline__ int row_offset_dual(int r, int k, int g) {
+  return r * (2 * D) + (((2 * k + g) ^ swz_dual<D>(r)) << 4);
+}
+
+// Work-group -> (head, query-tile) remap.  Work-groups are dealt round-robin to
+// the 8 XCDs (each with its own L2), so when the grid is a multiple of 8 the
+// index is permuted such that consecutive logical indices run on one XCD:
+// the query tiles of one (batch, K/V head) then share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int id, int n) {
+  constexpr int kXcds = 8;
+  if (n % kXcds != 0) return id;
+  return (id % kXcds) * (n / kXcds) + id / kXcds;
+}
+
+}  // namespace fa

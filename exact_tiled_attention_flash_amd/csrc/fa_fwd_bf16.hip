@@ -1,0 +1,265 @@
+// fa_fwd_bf16.hip -- tiled exact attention forward, bf16 in, fp32 accumulate (gfx950).
+//
+// One work-group of 4 waves owns 128 query rows of one (batch, query head);
+// each wave owns 32 of them.  The work-group streams the allowed 64-key tiles
+// of K and V through LDS (double-buffered, filled by direct global->LDS copies
+// while the previous tile is being used), and for every tile each wave
+//   1. S^T = K Q^T on MFMA (keys as rows, the wave's 32 queries as columns:
+//      every lane then holds 32 scores of ONE query),
+//   2. masks the scores (only on tiles that straddle the causal diagonal, the
+//      window's left edge or the end of the sequence),
+//   3. runs the online-softmax update in registers -- running maximum m and
+//      running sum l per query, rescale of the partial output by
+//      exp(m_old - m_new) (transformer.xph.ink "高效注意力：FlashAttention 与
+//      线性注意力", 原理与机制; claspmoon.cn "14 · 缩放定律与高效注意力" §3.2),
+//   4. O^T += V^T P^T on MFMA, with P^T fed straight from step 1's result
+//      registers and V^T read with the gfx950 transposing LDS read.
+// The work is done in base 2: scores are multiplied by s*log2(e) and exp2 is
+// the hardware v_exp_f32; the saved log-sum-exp is converted back to ln.
+// Only O and the per-row log-sum-exp are written (claspmoon.cn §3.3).
+#include "fa_common.hpp"
+#include "fa_kernels.h"
+
+namespace fa {
+
+namespace {
+
+template <int D>
+struct FwdCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int BR = 32 * kWaves;     // query rows per work-group
+  static constexpr int BC = 64;              // keys per K/V tile
+  static constexpr int CH = D / 8;           // 16-byte chunks per row
+  static constexpr int TILE = BC * D * 2;    // bytes of one K (or V) tile
+  static constexpr int NSTEP = D / 16;       // MFMA K-steps over the head dim
+  static constexpr int NDB = D / 32;         // 32-wide blocks of the head dim
+};
+
+// LDS swizzles (XOR on the 16-byte chunk index of a row).
+// K is read 16 rows at a time at one chunk: spread those rows over all banks.
+template <int D> __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+// V is read by the transposing read: 4 rows x 4 chunks per half-wave.
+template <int D> __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+// Issue the direct copies of K/V rows [k0, k0+64) into one LDS stage.  Rows past
+// the end of the sequence are clamped to the last row (finite data whose
+// scores are masked to -inf, so they add exactly zero).
+template <int D>
+__device__ __forceinline__ void issue_kv_tile(const bf16* __restrict__ Kh, const bf16* __restrict__ Vh,
+                                              int k0, int L, char* kbuf, char* vbuf, int wave, int lane) {
+  using C = FwdCfg<D>;
+  constexpr int kPerWave = C::TILE / C::kWaves;
+  constexpr int kInstr = kPerWave / 1024;
+#pragma unroll
+  for (int n = 0; n < kInstr; ++n) {
+    const int base = wave * kPerWave + n * 1024;
+    const int p = base / 16 + lane;
+    const int r = p / C::CH, slot = p % C::CH;
+    const int row = min(k0 + r, L - 1);
+    g2lds16(Kh + (size_t)row * D + (slot ^ swz_k<D>(r)) * 8, kbuf + base);
+    g2lds16(Vh + (size_t)row * D + (slot ^ swz_v<D>(r)) * 8, vbuf + base);
+  }
+}
+
+__device__ __forceinline__ void wait_copies_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// Per-wave state carried across key tiles.
+template <int D>
+struct FwdState {
+  bf16x8 qr[FwdCfg<D>::NSTEP];   // the wave's 32 queries (B operand of S^T = K Q^T)
+  f32x16 o[FwdCfg<D>::NDB];      // O^T accumulator: lane = query, registers = head dims
+  float m_run, l_run;            // running max (log2 units) and this lane's partial sum
+};
+
+// One key tile for one wave: S^T, mask, online softmax, O^T += V^T P^T.
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, const char* vbuf, int k0,
+                                         int L, int window, int my_q, int q_w0, int wq_hi, float c,
+                                         int lane) {
+  using C = FwdCfg<D>;
+  const int g = lane >> 5, ln = lane & 31;
+  // 1. S^T (64 keys x 32 queries) as two 32x32 blocks
+  f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+  for (int k = 0; k < C::NSTEP; ++k) {
+    const int ch = 2 * k + g;
+    const bf16x8 a0 = lds_load16(kbuf, ln * (2 * D) + ((ch ^ swz_k<D>(ln)) << 4));
+    const bf16x8 a1 = lds_load16(kbuf, (32 + ln) * (2 * D) + ((ch ^ swz_k<D>(32 + ln)) << 4));
+    s0 = mfma32(a0, st.qr[k], s0);
+    s1 = mfma32(a1, st.qr[k], s1);
+  }
+
+  // 2. mask, only on tiles that straddle a boundary (wave-uniform decision)
+  const bool need_mask = (k0 + C::BC > L) || (CAUSAL && k0 + C::BC - 1 > q_w0) ||
+                         (window > 0 && k0 < wq_hi - window + 1);
+  if (need_mask) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int kk0 = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
+      const int kk1 = kk0 + 32;
+      const bool ok0 = kk0 < L && (!CAUSAL || kk0 <= my_q) && (window <= 0 || kk0 > my_q - window);
+      const bool ok1 = kk1 < L && (!CAUSAL || kk1 <= my_q) && (window <= 0 || kk1 > my_q - window);
+      if (!ok0) s0[i] = -INFINITY;
+      if (!ok1) s1[i] = -INFINITY;
+    }
+  }
+
+  // 3. online softmax: the two lanes holding one query share the tile maximum
+  float mx = fmaxf(s0[0], s1[0]);
+#pragma unroll
+  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
+  mx = fmaxf(mx, wave_xor32(mx));
+  const float m_new = fmaxf(st.m_run, mx * c);
+  const float alpha = fast_exp2(st.m_run - m_new);
+  float rs = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s0[i] = fast_exp2(fmaf(s0[i], c, -m_new));
+    s1[i] = fast_exp2(fmaf(s1[i], c, -m_new));
+    rs += s0[i] + s1[i];
+  }
+  st.l_run = st.l_run * alpha + rs;
+  st.m_run = m_new;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) st.o[db] *= alpha;
+
+  // 4. O^T += V^T P^T, 16 keys per MFMA step.  P^T's K slots (from the C
+  // layout of step 1) are keys 16t + 8*(slot/4) + 4g + slot%4; the transposing
+  // read gives V^T the same keys: lane supplies row 16t + 4g + (lane%16)/4
+  // (+8 for slots 4..7) and 4 head-dim values of its 16-wide half.
+  bf16x8 pb[4];
+  pb[0] = to_bf16x8(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
+  pb[1] = to_bf16x8(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
+  pb[2] = to_bf16x8(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
+  pb[3] = to_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
+  const int s16 = lane & 15, jg = lane >> 4;
+  const int vrow = 4 * g + (s16 >> 2);
+  const int vcol = 16 * (jg & 1) + 4 * (s16 & 3);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int row = 16 * t + vrow;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const int col = 32 * db + vcol;
+      const int off = row * (2 * D) + (((col >> 3) ^ swz_v<D>(row)) << 4) + ((col & 4) << 1);
+      const bf16x4 lo = lds_load_tr(vbuf, off);
+      const bf16x4 hi = lds_load_tr(vbuf, off + 8 * (2 * D));
+      st.o[db] = mfma32(concat4(lo, hi), pb[t], st.o[db]);
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
+  using C = FwdCfg<D>;
+  // Four distinct LDS objects (K and V of two stages): distinct objects carry
+  // distinct alias scopes, which lets the compiler see that reading one stage
+  // does not have to wait for the direct copies into the other.
+  __shared__ __attribute__((aligned(1024))) char k_st0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_st0[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char k_st1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char v_st1[C::TILE];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, ln = lane & 31;
+
+  // ---- work decomposition: (batch, query head) major, heaviest query tile first
+  const int r = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = r / a.n_qtiles;
+  const int qt_rank = r % a.n_qtiles;
+  const int qt = CAUSAL ? a.n_qtiles - 1 - qt_rank : qt_rank;
+  const int b = bh / a.Hq, h = bh % a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int L = a.L;
+
+  const bf16* __restrict__ Qh = reinterpret_cast<const bf16*>(a.q) + ((size_t)(b * a.Hq + h) * L) * D;
+  const bf16* __restrict__ Kh = reinterpret_cast<const bf16*>(a.k) + ((size_t)(b * a.Hkv + hk) * L) * D;
+  const bf16* __restrict__ Vh = reinterpret_cast<const bf16*>(a.v) + ((size_t)(b * a.Hkv + hk) * L) * D;
+
+  const int q_wg0 = qt * C::BR;
+  const int q_w0 = q_wg0 + 32 * wave;
+  const int my_q = q_w0 + ln;
+  const int wq_hi = min(q_w0 + 31, L - 1);
+  const int window = a.window;
+
+  // ---- key-tile range of the work-group
+  const int kv_end = CAUSAL ? min(L, q_wg0 + C::BR) : L;
+  const int kv_begin = (window > 0) ? max(0, q_wg0 - window + 1) : 0;
+  const int j_lo = kv_begin / C::BC, j_hi = (kv_end - 1) / C::BC;
+
+  issue_kv_tile<D>(Kh, Vh, j_lo * C::BC, L, k_st0, v_st0, wave, lane);
+
+  FwdState<D> st;
+#pragma unroll
+  for (int k = 0; k < C::NSTEP; ++k) {
+    if (my_q < L) st.qr[k] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)my_q * D + 16 * k + 8 * g);
+    else st.qr[k] = bf16x8{};
+  }
+  st.m_run = kNegBig;
+  st.l_run = 0.f;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) st.o[db] = f32x16{};
+  const float c = a.scale_log2;
+
+  auto wave_needs = [&](int k0) {
+    return (q_w0 < L) && (!CAUSAL || k0 <= wq_hi) && (window <= 0 || k0 + C::BC - 1 >= q_w0 - window + 1);
+  };
+
+  wait_copies_and_barrier();
+  // Tiles alternate between the two stages; the loop is unrolled by two so
+  // that every LDS access names its stage statically.
+  for (int j = j_lo; j <= j_hi; j += 2) {
+    if (j < j_hi) issue_kv_tile<D>(Kh, Vh, (j + 1) * C::BC, L, k_st1, v_st1, wave, lane);
+    if (wave_needs(j * C::BC))
+      fwd_tile<D, CAUSAL>(st, k_st0, v_st0, j * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+    wait_copies_and_barrier();
+    if (j + 1 > j_hi) break;
+    if (j + 1 < j_hi) issue_kv_tile<D>(Kh, Vh, (j + 2) * C::BC, L, k_st0, v_st0, wave, lane);
+    if (wave_needs((j + 1) * C::BC))
+      fwd_tile<D, CAUSAL>(st, k_st1, v_st1, (j + 1) * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+    wait_copies_and_barrier();
+  }
+
+  // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2
+  const float l_tot = st.l_run + wave_xor32(st.l_run);
+  if (my_q < L) {
+    const float inv = 1.f / l_tot;
+    bf16* Oq = reinterpret_cast<bf16*>(a.o) + ((size_t)(b * a.Hq + h) * L + my_q) * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 w;
+        w[0] = (bf16)(st.o[db][4 * i4 + 0] * inv);
+        w[1] = (bf16)(st.o[db][4 * i4 + 1] * inv);
+        w[2] = (bf16)(st.o[db][4 * i4 + 2] * inv);
+        w[3] = (bf16)(st.o[db][4 * i4 + 3] * inv);
+        *reinterpret_cast<bf16x4*>(Oq + 32 * db + 8 * i4 + 4 * g) = w;
+      }
+    }
+    if (a.lse != nullptr && g == 0)
+      a.lse[(size_t)(b * a.Hq + h) * L + my_q] = (st.m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const FwdArgs& args, hipStream_t stream) {
+  using C = FwdCfg<D>;
+  FwdArgs a = args;
+  a.n_qtiles = (a.L + C::BR - 1) / C::BR;
+  const long long nblk = (long long)a.B * a.Hq * a.n_qtiles;
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, hipStream_t stream) {
+  if (a.d == 128) return causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
+  return causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,42 @@
+// fa_kernels.h -- internal launcher interface between the C ABI and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;        // may be null
+  int B, Hq, Hkv, L, d;
+  int window;        // 0 = none
+  float scale_log2;  // softmax scale * log2(e)
+  int n_qtiles;      // filled in by the launcher
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;      // workspace: D_i = sum_c dO_ic * O_ic, [B, Hq, L]
+  int B, Hq, Hkv, L, d;
+  int window;
+  float scale;       // softmax scale
+  float scale_log2;  // softmax scale * log2(e)
+  int n_tiles;       // filled in by the launchers
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, hipStream_t stream);
+hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,105 @@
+// flash_attn_api.hip -- the extern "C" boundary: validation, then dispatch.
+//
+// Every argument is checked on the host before any HIP call, so a rejected
+// call has no side effect.  The library allocates nothing; all buffers and the
+// stream belong to the caller.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/flash_attn.h"
+#include "fa_kernels.h"
+
+namespace {
+
+constexpr int kMaxL = 1 << 24;  // keeps row * d in 32 bits inside the kernels
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_common(int B, int Hq, int Hkv, int L, int d, float scale, int causal, int window, int dtype) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || L < 1 || L > kMaxL) return FA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (window < 0) return FA_ERR_INVALID_ARG;
+  if (window > 0 && !causal) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (Hq % Hkv != 0) return FA_ERR_GQA;
+  // grid size: one work-group per (batch, head, 64-row tile) at most
+  const long long tiles = ((long long)L + 63) / 64;
+  if ((long long)B * Hq * tiles > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  return FA_OK;
+}
+
+size_t delta_bytes(int B, int Hq, int L) {
+  const size_t raw = (size_t)B * (size_t)Hq * (size_t)L * sizeof(float);
+  return (raw + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int L, int d,
+                              float softmax_scale, int causal, int window, int dtype, void* stream) {
+  int rc = check_common(B, Hq, Hkv, L, d, softmax_scale, causal, window, dtype);
+  if (rc != FA_OK) return rc;
+  if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return FA_ERR_INVALID_ARG;
+
+  fa::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.d = d;
+  a.window = window;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = (dtype == FA_DTYPE_BF16) ? fa::launch_fwd_bf16(a, causal != 0, s)
+                                          : fa::launch_fwd_f32(a, causal != 0, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int dtype) {
+  if (check_common(B, Hq, Hkv, L, d, 1.f, 0, 0, dtype) != FA_OK) return 0;
+  return delta_bytes(B, Hq, L);
+}
+
+extern "C" int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, void* dq, void* dk, void* dv,
+                              void* workspace, size_t workspace_bytes,
+                              int B, int Hq, int Hkv, int L, int d,
+                              float softmax_scale, int causal, int window, int dtype, void* stream) {
+  int rc = check_common(B, Hq, Hkv, L, d, softmax_scale, causal, window, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
+  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      workspace_bytes < delta_bytes(B, Hq, L))
+    return FA_ERR_WORKSPACE;
+
+  fa::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.delta = static_cast<float*>(workspace);
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.d = d;
+  a.window = window;
+  a.scale = softmax_scale;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  hipError_t e = fa::launch_bwd_bf16(a, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" const char* flash_attn_strerror(int code) {
+  switch (code) {
+    case FA_OK: return "ok";
+    case FA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, non-positive size, or bad scale)";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dim, dtype, or window without causal)";
+    case FA_ERR_GQA: return "number of query heads is not a multiple of the number of key/value heads";
+    case FA_ERR_WORKSPACE: return "backward workspace missing, misaligned or too small";
+    case FA_ERR_HIP: return "HIP launch or runtime error";
+    default: return "unknown error code";
+  }
+}
+
+extern "C" int flash_attn_version(void) { return 100; }

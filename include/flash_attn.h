@@ -1,0 +1,122 @@
+/*
+ * flash_attn.h -- C ABI of the MI355X (gfx950) exact tiled attention library.
+ *
+ * What is computed (forward): for every batch b and query head h,
+ *     O = softmax(s * Q K^T) V
+ * with the softmax taken over keys (mdooai.com, "Ch.04 注意力优化：
+ * FlashAttention 与稀疏注意力", core formula), computed tile by tile with the
+ * online-softmax recurrence -- a running row maximum and running row sum,
+ * and a rescale of the partial output whenever the maximum grows
+ * (claspmoon.cn, "14 · 缩放定律与高效注意力", §3.2 Tiling;
+ * transformer.xph.ink, "高效注意力：FlashAttention 与线性注意力", 原理与机制).
+ * The L x L score matrix is never stored.  The forward also returns the
+ * per-row natural log-sum-exp of the scaled, masked scores, which is all the
+ * backward needs besides O (claspmoon.cn §3.3, backward recomputation).
+ *
+ * Backward: given dO, returns dQ, dK, dV of sum(O * dO), recomputing the
+ * attention probabilities from Q, K and the saved log-sum-exp instead of
+ * reading a stored matrix (claspmoon.cn §3.3).
+ *
+ * Masks (a masked score is -inf and carries exactly zero weight,
+ * mdooai.com "Ch.04", sparse-attention formula):
+ *   causal  -- key j is allowed for query i iff j <= i (claspmoon.cn §3.5,
+ *              is_causal);
+ *   window  -- w >= 1 together with causal: allowed iff i-w+1 <= j <= i, the
+ *              w most recent keys including the query itself
+ *              (book.anysome.cn, "高效注意力", §4 sliding window).
+ * Grouped-query attention (book.anysome.cn "高效注意力" §3): Hkv divides Hq
+ * and query head h reads K/V head h / (Hq / Hkv).
+ *
+ * Layout (all tensors dense, row-major, the head dimension fastest):
+ *   Q, O, dO, dQ : [B, Hq,  L, d]
+ *   K, V, dK, dV : [B, Hkv, L, d]
+ *   LSE          : [B, Hq,  L]     float32, natural logarithm
+ * Element type of Q/K/V/O/dO/dQ/dK/dV is given by `dtype` (FA_DTYPE_*).
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers are device pointers (hipMalloc'd or equivalent), 16-byte
+ *     aligned.  The caller allocates and owns every buffer; the library
+ *     allocates nothing and keeps no per-call state.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *     asynchronous on that stream and never synchronise the host.
+ *   - Every argument is validated on the host before any HIP call; a
+ *     rejected call launches nothing and returns a negative FA_ERR_* code.
+ *     A HIP launch failure returns FA_ERR_HIP.  flash_attn_strerror() names
+ *     every code.
+ *   - Outputs must not alias inputs.
+ */
+#ifndef FLASH_ATTN_MI355_H
+#define FLASH_ATTN_MI355_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define FA_DTYPE_F32  0
+#define FA_DTYPE_BF16 1
+
+/* return codes */
+#define FA_OK                0
+#define FA_ERR_INVALID_ARG  (-1)  /* null/misaligned pointer, non-positive size, bad scale */
+#define FA_ERR_UNSUPPORTED  (-2)  /* head dim, dtype, or window without causal */
+#define FA_ERR_GQA          (-3)  /* Hq is not a multiple of Hkv */
+#define FA_ERR_WORKSPACE    (-4)  /* backward workspace missing or too small */
+#define FA_ERR_HIP          (-5)  /* a HIP launch or runtime call failed */
+
+/*
+ * Forward pass.
+ *   q [B,Hq,L,d], k/v [B,Hkv,L,d]  : inputs (dtype)
+ *   o [B,Hq,L,d]                    : output (dtype, rounded to nearest even)
+ *   lse [B,Hq,L] float32            : output log-sum-exp; may be NULL if not wanted
+ *   softmax_scale                   : s > 0 and finite (usually 1/sqrt(d))
+ *   causal                          : 0 or 1
+ *   window                          : 0 = none; w >= 1 requires causal = 1
+ *   dtype                           : FA_DTYPE_BF16 (d in {64,128}) or
+ *                                     FA_DTYPE_F32  (d in {64,128})
+ * Extra device memory: none.  Returns FA_OK or a negative FA_ERR_* code.
+ */
+int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int L, int d,
+                   float softmax_scale, int causal, int window, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace flash_attn_bwd needs for these sizes: one
+ * float32 per query row (the row dot product D_i = sum_c dO_ic * O_ic),
+ * rounded up to 256 bytes.  Returns 0 for invalid sizes.
+ */
+size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int dtype);
+
+/*
+ * Backward pass (recomputation from Q, K, V, O and the forward's LSE).
+ *   q, k, v, o, lse                 : exactly the forward's inputs and outputs
+ *   dout [B,Hq,L,d]                 : upstream gradient dO (dtype)
+ *   dq [B,Hq,L,d], dk/dv [B,Hkv,L,d]: outputs (dtype); for GQA the K/V
+ *                                     gradients of a group's query heads are
+ *                                     summed into the shared head
+ *   workspace, workspace_bytes      : caller-owned device scratch of at least
+ *                                     flash_attn_bwd_workspace_bytes() bytes,
+ *                                     256-byte aligned; its contents on entry
+ *                                     are ignored
+ *   dtype                           : FA_DTYPE_BF16 with d in {64,128}
+ * Returns FA_OK or a negative FA_ERR_* code.
+ */
+int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int Hq, int Hkv, int L, int d,
+                   float softmax_scale, int causal, int window, int dtype, void* stream);
+
+/* Static, never-NULL description of a return code. */
+const char* flash_attn_strerror(int code);
+
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int flash_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASH_ATTN_MI355_H */

@@ -1,0 +1,120 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+public header declares, and rejects invalid arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_tiled_attention_flash_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flash_attn.h")
+
+FAKE = 0x10000      # 16-byte aligned, never dereferenced: validation must fail first
+MISALIGNED = 0x10008
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flash_attn_\w+)\s*\(", text)))
+
+
+def header_constants():
+    text = open(HEADER).read()
+    return {m.group(1): int(m.group(2)) for m in re.finditer(r"#define\s+(FA_\w+)\s+\(?(-?\d+)\)?", text)}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.library_path()):
+        pytest.skip("libflashattn.so not built")
+    return fa.library()
+
+
+def test_header_declares_the_boundary():
+    assert header_functions() == sorted(fa.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_binding_constants_match_header():
+    c = header_constants()
+    assert c["FA_DTYPE_F32"] == fa.FA_DTYPE_F32 and c["FA_DTYPE_BF16"] == fa.FA_DTYPE_BF16
+    assert c["FA_OK"] == 0
+
+
+def test_strerror_and_version(lib):
+    c = header_constants()
+    for name in ("FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_GQA",
+                 "FA_ERR_WORKSPACE", "FA_ERR_HIP"):
+        s = fa.strerror(c[name])
+        assert s and s != "unknown error code"
+    assert fa.strerror(12345) == "unknown error code"
+    assert lib.flash_attn_version() >= 100
+
+
+def call_fwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=1, Hq=2, Hkv=2, L=16, d=64,
+             scale=0.125, causal=1, window=0, dtype=fa.FA_DTYPE_BF16):
+    return lib.flash_attn_fwd(q, k, v, o, lse, B, Hq, Hkv, L, d, scale, causal, window, dtype, None)
+
+
+def call_bwd(lib, ws=FAKE * 16, ws_bytes=1 << 20, B=1, Hq=2, Hkv=2, L=16, d=64, scale=0.125,
+             causal=1, window=0, dtype=fa.FA_DTYPE_BF16, **ptrs):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, do=FAKE, dq=FAKE, dk=FAKE, dv=FAKE)
+    p.update(ptrs)
+    return lib.flash_attn_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"],
+                              ws, ws_bytes, B, Hq, Hkv, L, d, scale, causal, window, dtype, None)
+
+
+def test_fwd_rejects_invalid_arguments(lib):
+    c = header_constants()
+    INV, UNS, GQA = c["FA_ERR_INVALID_ARG"], c["FA_ERR_UNSUPPORTED"], c["FA_ERR_GQA"]
+    assert call_fwd(lib, q=None) == INV
+    assert call_fwd(lib, o=None) == INV
+    assert call_fwd(lib, k=MISALIGNED) == INV
+    assert call_fwd(lib, lse=MISALIGNED) == INV
+    for bad in (dict(B=0), dict(Hq=0), dict(Hkv=0), dict(L=0), dict(L=-3), dict(L=(1 << 24) + 1),
+                dict(scale=0.0), dict(scale=-1.0), dict(scale=float("inf")), dict(scale=float("nan")),
+                dict(causal=2), dict(window=-1)):
+        assert call_fwd(lib, **bad) == INV, bad
+    assert call_fwd(lib, d=96) == UNS
+    assert call_fwd(lib, d=256) == UNS
+    assert call_fwd(lib, dtype=7) == UNS
+    assert call_fwd(lib, causal=0, window=4) == UNS
+    assert call_fwd(lib, Hq=6, Hkv=4) == GQA
+
+
+def test_bwd_rejects_invalid_arguments(lib):
+    c = header_constants()
+    INV, UNS, WS = c["FA_ERR_INVALID_ARG"], c["FA_ERR_UNSUPPORTED"], c["FA_ERR_WORKSPACE"]
+    need = lib.flash_attn_bwd_workspace_bytes(1, 2, 2, 16, 64, fa.FA_DTYPE_BF16)
+    assert need == 256                                   # 2*16 floats rounded up to 256 bytes
+    assert call_bwd(lib, ws=None) == WS
+    assert call_bwd(lib, ws_bytes=need - 1) == WS
+    assert call_bwd(lib, ws=FAKE * 16 + 16) == WS        # must be 256-byte aligned
+    assert call_bwd(lib, dq=None) == INV
+    assert call_bwd(lib, lse=MISALIGNED) == INV
+    assert call_bwd(lib, dtype=fa.FA_DTYPE_F32) == UNS
+    assert call_bwd(lib, causal=0, window=3) == UNS
+    assert call_bwd(lib, Hq=3, Hkv=2) == c["FA_ERR_GQA"]
+
+
+def test_workspace_size_formula(lib):
+    f = lib.flash_attn_bwd_workspace_bytes
+    assert f(2, 32, 32, 4096, 128, fa.FA_DTYPE_BF16) == 2 * 32 * 4096 * 4
+    assert f(1, 3, 1, 5, 64, fa.FA_DTYPE_BF16) == 256
+    assert f(1, 3, 2, 5, 64, fa.FA_DTYPE_BF16) == 0       # invalid sizes -> 0
+    assert f(1, 2, 2, 5, 80, fa.FA_DTYPE_BF16) == 0
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fa, "_LIB", None)
+    monkeypatch.setattr(fa, "library_path", lambda: str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError):
+        fa.library()
