@@ -111,7 +111,6 @@ def forward_rows(q, k, v, rows, scale, causal=False, window=0):
     Rows are independent in the definition, so any subset is exact.
     Returns float64 ``O [B,Hq,len(rows),d]`` and ``LSE [B,Hq,len(rows)]``.
     """
-    q, k, v = _as64(q), _as64(k), _as64(v)
     B, Hq, L, d = q.shape
     Hkv = k.shape[1]
     rows = np.asarray(rows, dtype=np.int64)
@@ -121,9 +120,11 @@ def forward_rows(q, k, v, rows, scale, causal=False, window=0):
     for b in range(B):
         for h in range(Hq):
             kh = kv_head_of(h, Hq, Hkv)
-            S = scale * (q[b, h, rows] @ k[b, kh].T)
+            # float64 copies are made one head at a time (memory only)
+            qh, kk, vv = _as64(q[b, h])[rows], _as64(k[b, kh]), _as64(v[b, kh])
+            S = scale * (qh @ kk.T)
             A, lse[b, h] = _masked_softmax_rows(S, ok)
-            O[b, h] = A @ v[b, kh]
+            O[b, h] = A @ vv
     return O, lse
 
 
