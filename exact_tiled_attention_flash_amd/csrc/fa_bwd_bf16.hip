@@ -1,5 +1,488 @@
-// fa_bwd_bf16.hip -- placeholder until the backward kernels land.
+// fa_bwd_bf16.hip -- recomputing attention backward, bf16 in, fp32 accumulate (gfx950).
+//
+// Only O and the per-row log-sum-exp survive the forward; the probabilities
+// are recomputed here as P = exp(s*Q K^T - LSE) from Q, K and that statistic
+// (claspmoon.cn "14 · 缩放定律与高效注意力" §3.3, backward by recomputation;
+// transformer.xph.ink "高效注意力：FlashAttention 与线性注意力", 原理与机制).
+// The gradient is the softmax Jacobian applied row by row:
+//     dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,  dS = P * (dP - D),
+//     dQ = s dS K,  dK = s dS^T Q.
+// Three kernels, all on the caller's stream, none using atomics:
+//   1. delta:  D_i and LSE_i*log2(e) per query row into the workspace;
+//   2. dK/dV:  one work-group per (batch, K/V head, 128 keys), each wave
+//              holding 32 keys' K and V rows in registers, streams the
+//              allowed 64-query tiles of Q and dO (every query head of the
+//              GQA group) through LDS and accumulates dK and dV in registers;
+//   3. dQ:     one work-group per (batch, query head, 128 queries), each wave
+//              holding 32 queries' Q and dO rows in registers, streams the
+//              allowed 64-key tiles of K and V through LDS and accumulates dQ.
+// The two tile kernels reuse the forward's MFMA layouts: a product whose C
+// registers hold one column per lane feeds the next product's A or B operand
+// directly, and the operand that needs the other orientation comes from the
+// gfx950 transposing LDS read.
+#include "fa_common.hpp"
 #include "fa_kernels.h"
+
 namespace fa {
-hipError_t launch_bwd_bf16(const BwdArgs&, bool, hipStream_t) { return hipErrorNotSupported; }
+
+namespace {
+
+__device__ __forceinline__ void wait_copies_and_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// Direct 4-byte global -> LDS copy for a whole wave (lane l -> base + 4*l).
+__device__ __forceinline__ void g2lds4(const void* src, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(src, (FA_LDS void*)(lds_wave_base), 4, 0, 0);
+}
+
+// Copy rows [r0, r0 + rows) of a [L x D] bf16 tensor into an LDS tile stored
+// with swz_dual; rows past the end are clamped to the last row.  The 4 waves
+// split the tile evenly.
+template <int D, int ROWS>
+__device__ __forceinline__ void issue_rows(const bf16* __restrict__ src, int r0, int L, char* dst, int wave, int lane) {
+  constexpr int CH = D / 8;
+  constexpr int kBytes = ROWS * D * 2;
+  constexpr int kPerWave = kBytes / 4;
+  static_assert(kPerWave % 1024 == 0, "tile must split into whole wave copies");
+#pragma unroll
+  for (int n = 0; n < kPerWave / 1024; ++n) {
+    const int base = wave * kPerWave + n * 1024;
+    const int p = base / 16 + lane;
+    const int r = p / CH, slot = p % CH;
+    const int row = min(r0 + r, L - 1);
+    g2lds16(src + (size_t)row * D + (slot ^ swz_dual<D>(r)) * 8, dst + base);
+  }
+}
+
+// ------------------------------------------------------------ 1. delta
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
+                                                        const float* __restrict__ lse, float* __restrict__ delta,
+                                                        float* __restrict__ lse2, long long rows) {
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
+  const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
+  const int part = threadIdx.x % kLanesPerRow;
+  float acc = 0.f;
+  if (row < rows) {
+    const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + row * D + part * 8);
+    const bf16x8 y = *reinterpret_cast<const bf16x8*>(dout + row * D + part * 8);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc = fmaf((float)x[i], (float)y[i], acc);
+  }
+#pragma unroll
+  for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (row < rows && part == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
+}
+
+// ------------------------------------------------------------ 2. dK / dV
+
+template <int D>
+struct KVCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int BK = 32 * kWaves;   // keys per work-group
+  static constexpr int BQ = 64;            // queries per streamed tile
+  static constexpr int QT = BQ * D * 2;    // bytes of a Q (or dO) tile
+  static constexpr int NSTEP = D / 16;
+  static constexpr int NDB = D / 32;
+};
+
+template <int D>
+struct KVState {
+  bf16x8 kr[KVCfg<D>::NSTEP];   // this wave's 32 K rows (B operand of S = Q K^T)
+  bf16x8 vr[KVCfg<D>::NSTEP];   // this wave's 32 V rows (B operand of dP = dO V^T)
+  f32x16 dv[KVCfg<D>::NDB];     // dV accumulator: lane = head dim column, registers = keys
+  f32x16 dk[KVCfg<D>::NDB];     // dK accumulator (scale applied at the end)
+};
+
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void kv_tile(KVState<D>& st, const char* qbuf, const char* dobuf, const float* stats,
+                                        int q0, int L, int window, int key_w0, float c, int lane) {
+  using C = KVCfg<D>;
+  const int g = lane >> 5, ln = lane & 31;
+  const int my_key = key_w0 + ln;
+
+  // S = Q K^T for two 32-query blocks: lane = key, registers = queries
+  f32x16 p[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int k = 0; k < C::NSTEP; ++k)
+      s = mfma32(lds_load16(qbuf, row_offset_dual<D>(32 * qb + ln, k, g)), st.kr[k], s);
+    p[qb] = s;
+  }
+  // P = exp2(S*s*log2e - LSE*log2e), zero where masked
+  const bool need_mask = (q0 + C::BQ > L) || (CAUSAL && q0 < key_w0 + 31) ||
+                         (window > 0 && q0 + C::BQ - 1 > key_w0 + window - 1);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 l4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (32 * qb + 8 * i4 + 4 * g));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int i = 4 * i4 + j;
+        float pv = fast_exp2(fmaf(p[qb][i], c, -l4[j]));
+        if (need_mask) {
+          const int q = q0 + 32 * qb + 8 * i4 + 4 * g + j;
+          const bool ok = q < L && (!CAUSAL || my_key <= q) && (window <= 0 || q - my_key < window);
+          pv = ok ? pv : 0.f;
+        }
+        p[qb][i] = pv;
+      }
+    }
+  }
+  // dV += P^T dO: A = P (lane = key, K slots = queries), B = dO via the transposing read
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const f32x16& pp = p[t >> 1];
+    const int o8 = 8 * (t & 1);
+    const bf16x8 pa = to_bf16x8(pp[o8 + 0], pp[o8 + 1], pp[o8 + 2], pp[o8 + 3], pp[o8 + 4], pp[o8 + 5],
+                                pp[o8 + 6], pp[o8 + 7]);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const bf16x8 bo = concat4(lds_load_tr(dobuf, tr_offset_dual<D>(t, db, 0, lane)),
+                                lds_load_tr(dobuf, tr_offset_dual<D>(t, db, 1, lane)));
+      st.dv[db] = mfma32(pa, bo, st.dv[db]);
+    }
+  }
+  // dP = dO V^T, then dS = P * (dP - D) in place
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    f32x16 dp = f32x16{};
+#pragma unroll
+    for (int k = 0; k < C::NSTEP; ++k)
+      dp = mfma32(lds_load16(dobuf, row_offset_dual<D>(32 * qb + ln, k, g)), st.vr[k], dp);
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const f32x4 d4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (C::BQ + 32 * qb + 8 * i4 + 4 * g));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[qb][4 * i4 + j] *= dp[4 * i4 + j] - d4[j];
+    }
+  }
+  // dK += dS^T Q: A = dS (lane = key), B = Q via the transposing read
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const f32x16& pp = p[t >> 1];
+    const int o8 = 8 * (t & 1);
+    const bf16x8 da = to_bf16x8(pp[o8 + 0], pp[o8 + 1], pp[o8 + 2], pp[o8 + 3], pp[o8 + 4], pp[o8 + 5],
+                                pp[o8 + 6], pp[o8 + 7]);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const bf16x8 bq = concat4(lds_load_tr(qbuf, tr_offset_dual<D>(t, db, 0, lane)),
+                                lds_load_tr(qbuf, tr_offset_dual<D>(t, db, 1, lane)));
+      st.dk[db] = mfma32(da, bq, st.dk[db]);
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+  using C = KVCfg<D>;
+  // distinct LDS objects per stage so reads of one stage need not wait for the
+  // direct copies into the other (alias scopes)
+  __shared__ __attribute__((aligned(1024))) char q_st0[C::QT];
+  __shared__ __attribute__((aligned(1024))) char do_st0[C::QT];
+  __shared__ __attribute__((aligned(1024))) char q_st1[C::QT];
+  __shared__ __attribute__((aligned(1024))) char do_st1[C::QT];
+  __shared__ __attribute__((aligned(16))) float stat_st0[2 * C::BQ];   // LSE*log2e, then D
+  __shared__ __attribute__((aligned(16))) float stat_st1[2 * C::BQ];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, ln = lane & 31;
+  const int L = a.L, window = a.window;
+  const int G = a.Hq / a.Hkv;
+
+  // (batch, K/V head) major; the key tile with the most queries first
+  const int r = xcd_remap(blockIdx.x, gridDim.x);
+  const int bhk = r / a.n_tiles;
+  const int kt = r % a.n_tiles;
+  const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const int key_wg0 = kt * C::BK;
+  const int key_w0 = key_wg0 + 32 * wave;
+  const int my_key = key_w0 + ln;
+
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
+  const bf16* __restrict__ Kh = reinterpret_cast<const bf16*>(a.k) + kv_off;
+  const bf16* __restrict__ Vh = reinterpret_cast<const bf16*>(a.v) + kv_off;
+
+  // queries that can see this work-group's keys
+  const int q_begin = CAUSAL ? key_wg0 : 0;
+  const int q_end = (window > 0) ? min(L, key_wg0 + C::BK - 1 + window) : L;
+  const int qt_lo = q_begin / C::BQ, qt_hi = (q_end - 1) / C::BQ;
+  const int nq = qt_hi - qt_lo + 1;
+  const int n_it = G * nq;
+
+  auto head_of = [&](int it) { return hk * G + it / nq; };
+  auto q0_of = [&](int it) { return (qt_lo + it % nq) * C::BQ; };
+  auto issue = [&](int it, char* qs, char* dos, float* ss) {
+    const int hq = head_of(it), q0 = q0_of(it);
+    const size_t qoff = ((size_t)(b * a.Hq + hq) * L) * D;
+    issue_rows<D, C::BQ>(reinterpret_cast<const bf16*>(a.q) + qoff, q0, L, qs, wave, lane);
+    issue_rows<D, C::BQ>(reinterpret_cast<const bf16*>(a.dout) + qoff, q0, L, dos, wave, lane);
+    if (wave == 0) {
+      const size_t srow = (size_t)(b * a.Hq + hq) * L + min(q0 + lane, L - 1);
+      g2lds4(a.lse2 + srow, reinterpret_cast<char*>(ss));
+      g2lds4(a.delta + srow, reinterpret_cast<char*>(ss) + 4 * C::BQ);
+    }
+  };
+
+  issue(0, q_st0, do_st0, stat_st0);
+
+  KVState<D> st;
+  {
+    const int kr = min(my_key, L - 1);
+#pragma unroll
+    for (int k = 0; k < C::NSTEP; ++k) {
+      st.kr[k] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)kr * D + 16 * k + 8 * g);
+      st.vr[k] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)kr * D + 16 * k + 8 * g);
+    }
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      st.dv[db] = f32x16{};
+      st.dk[db] = f32x16{};
+    }
+  }
+  const float c = a.scale_log2;
+  auto wave_needs = [&](int q0) {
+    return key_w0 < L && (!CAUSAL || q0 + C::BQ - 1 >= key_w0) && (window <= 0 || q0 <= key_w0 + 31 + window - 1);
+  };
+
+  wait_copies_and_barrier();
+  for (int it = 0; it < n_it; it += 2) {
+    if (it + 1 < n_it) issue(it + 1, q_st1, do_st1, stat_st1);
+    if (wave_needs(q0_of(it))) kv_tile<D, CAUSAL>(st, q_st0, do_st0, stat_st0, q0_of(it), L, window, key_w0, c, lane);
+    wait_copies_and_barrier();
+    if (it + 1 >= n_it) break;
+    if (it + 2 < n_it) issue(it + 2, q_st0, do_st0, stat_st0);
+    if (wave_needs(q0_of(it + 1)))
+      kv_tile<D, CAUSAL>(st, q_st1, do_st1, stat_st1, q0_of(it + 1), L, window, key_w0, c, lane);
+    wait_copies_and_barrier();
+  }
+
+  // epilogue: lane holds head-dim column 32*db + ln of keys key_w0 + 8*(i/4) + 4g + i%4
+  bf16* dKh = reinterpret_cast<bf16*>(a.dk) + kv_off;
+  bf16* dVh = reinterpret_cast<bf16*>(a.dv) + kv_off;
+  const float s = a.scale;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int key = key_w0 + 8 * (i >> 2) + 4 * g + (i & 3);
+    if (key < L) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        dKh[(size_t)key * D + 32 * db + ln] = (bf16)(st.dk[db][i] * s);
+        dVh[(size_t)key * D + 32 * db + ln] = (bf16)(st.dv[db][i]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------ 3. dQ
+
+template <int D>
+struct QCfg {
+  static constexpr int kWaves = 4;
+  static constexpr int BQ = 32 * kWaves;   // queries per work-group
+  static constexpr int BC = 64;            // keys per streamed tile
+  static constexpr int KT = BC * D * 2;    // bytes of a K (or V) tile
+  static constexpr int NSTEP = D / 16;
+  static constexpr int NDB = D / 32;
+};
+
+template <int D>
+struct QState {
+  bf16x8 qr[QCfg<D>::NSTEP];    // this wave's 32 Q rows (B operand of S^T = K Q^T)
+  bf16x8 dor[QCfg<D>::NSTEP];   // this wave's 32 dO rows (B operand of dP^T = V dO^T)
+  f32x16 dq[QCfg<D>::NDB];      // dQ^T accumulator: lane = query, registers = head dims
+  float lse2, dlt;              // this lane's query statistics
+};
+
+template <int D, bool CAUSAL>
+__device__ __forceinline__ void q_tile(QState<D>& st, const char* kbuf, const char* vbuf, int k0, int L, int window,
+                                       int my_q, int q_w0, int wq_hi, float c, int lane) {
+  using C = QCfg<D>;
+  const int g = lane >> 5, ln = lane & 31;
+  // S^T = K Q^T: lane = query, registers = keys
+  f32x16 p[2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int k = 0; k < C::NSTEP; ++k)
+      s = mfma32(lds_load16(kbuf, row_offset_dual<D>(32 * kb + ln, k, g)), st.qr[k], s);
+    p[kb] = s;
+  }
+  const bool need_mask = (k0 + C::BC > L) || (CAUSAL && k0 + C::BC - 1 > q_w0) ||
+                         (window > 0 && k0 < wq_hi - window + 1);
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float pv = fast_exp2(fmaf(p[kb][i], c, -st.lse2));
+      if (need_mask) {
+        const int kk = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
+        const bool ok = kk < L && (!CAUSAL || kk <= my_q) && (window <= 0 || kk > my_q - window);
+        pv = ok ? pv : 0.f;
+      }
+      p[kb][i] = pv;
+    }
+  }
+  // dP^T = V dO^T, dS^T = P^T * (dP^T - D)
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    f32x16 dp = f32x16{};
+#pragma unroll
+    for (int k = 0; k < C::NSTEP; ++k)
+      dp = mfma32(lds_load16(vbuf, row_offset_dual<D>(32 * kb + ln, k, g)), st.dor[k], dp);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[kb][i] *= dp[i] - st.dlt;
+  }
+  // dQ^T += K^T dS^T: A = K^T via the transposing read, B = dS^T (lane = query)
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const f32x16& pp = p[t >> 1];
+    const int o8 = 8 * (t & 1);
+    const bf16x8 db8 = to_bf16x8(pp[o8 + 0], pp[o8 + 1], pp[o8 + 2], pp[o8 + 3], pp[o8 + 4], pp[o8 + 5],
+                                 pp[o8 + 6], pp[o8 + 7]);
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+      const bf16x8 ka = concat4(lds_load_tr(kbuf, tr_offset_dual<D>(t, db, 0, lane)),
+                                lds_load_tr(kbuf, tr_offset_dual<D>(t, db, 1, lane)));
+      st.dq[db] = mfma32(ka, db8, st.dq[db]);
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  using C = QCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char k_st0[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st0[C::KT];
+  __shared__ __attribute__((aligned(1024))) char k_st1[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st1[C::KT];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 5, ln = lane & 31;
+  const int L = a.L, window = a.window;
+
+  const int r = xcd_remap(blockIdx.x, gridDim.x);
+  const int bh = r / a.n_tiles;
+  const int qt_rank = r % a.n_tiles;
+  const int qt = CAUSAL ? a.n_tiles - 1 - qt_rank : qt_rank;
+  const int b = bh / a.Hq, h = bh % a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+
+  const size_t q_off = ((size_t)(b * a.Hq + h) * L) * D;
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
+  const bf16* __restrict__ Kh = reinterpret_cast<const bf16*>(a.k) + kv_off;
+  const bf16* __restrict__ Vh = reinterpret_cast<const bf16*>(a.v) + kv_off;
+
+  const int q_wg0 = qt * C::BQ;
+  const int q_w0 = q_wg0 + 32 * wave;
+  const int my_q = q_w0 + ln;
+  const int wq_hi = min(q_w0 + 31, L - 1);
+
+  const int kv_end = CAUSAL ? min(L, q_wg0 + C::BQ) : L;
+  const int kv_begin = (window > 0) ? max(0, q_wg0 - window + 1) : 0;
+  const int j_lo = kv_begin / C::BC, j_hi = (kv_end - 1) / C::BC;
+
+  issue_rows<D, C::BC>(Kh, j_lo * C::BC, L, k_st0, wave, lane);
+  issue_rows<D, C::BC>(Vh, j_lo * C::BC, L, v_st0, wave, lane);
+
+  QState<D> st;
+  {
+    const int qr = min(my_q, L - 1);
+    const bf16* Qr = reinterpret_cast<const bf16*>(a.q) + q_off + (size_t)qr * D;
+    const bf16* dOr = reinterpret_cast<const bf16*>(a.dout) + q_off + (size_t)qr * D;
+#pragma unroll
+    for (int k = 0; k < C::NSTEP; ++k) {
+      st.qr[k] = *reinterpret_cast<const bf16x8*>(Qr + 16 * k + 8 * g);
+      st.dor[k] = *reinterpret_cast<const bf16x8*>(dOr + 16 * k + 8 * g);
+    }
+    const size_t srow = (size_t)(b * a.Hq + h) * L + qr;
+    st.lse2 = a.lse2[srow];
+    st.dlt = a.delta[srow];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) st.dq[db] = f32x16{};
+  }
+  const float c = a.scale_log2;
+  auto wave_needs = [&](int k0) {
+    return (q_w0 < L) && (!CAUSAL || k0 <= wq_hi) && (window <= 0 || k0 + C::BC - 1 >= q_w0 - window + 1);
+  };
+
+  wait_copies_and_barrier();
+  for (int j = j_lo; j <= j_hi; j += 2) {
+    if (j < j_hi) {
+      issue_rows<D, C::BC>(Kh, (j + 1) * C::BC, L, k_st1, wave, lane);
+      issue_rows<D, C::BC>(Vh, (j + 1) * C::BC, L, v_st1, wave, lane);
+    }
+    if (wave_needs(j * C::BC))
+      q_tile<D, CAUSAL>(st, k_st0, v_st0, j * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+    wait_copies_and_barrier();
+    if (j + 1 > j_hi) break;
+    if (j + 1 < j_hi) {
+      issue_rows<D, C::BC>(Kh, (j + 2) * C::BC, L, k_st0, wave, lane);
+      issue_rows<D, C::BC>(Vh, (j + 2) * C::BC, L, v_st0, wave, lane);
+    }
+    if (wave_needs((j + 1) * C::BC))
+      q_tile<D, CAUSAL>(st, k_st1, v_st1, (j + 1) * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+    wait_copies_and_barrier();
+  }
+
+  // epilogue: dQ = s * dQ^T; lane = query, registers = head dims 32db + 8*(i/4) + 4g + i%4
+  if (my_q < L) {
+    bf16* dQr = reinterpret_cast<bf16*>(a.dq) + q_off + (size_t)my_q * D;
+    const float s = a.scale;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 w;
+        w[0] = (bf16)(st.dq[db][4 * i4 + 0] * s);
+        w[1] = (bf16)(st.dq[db][4 * i4 + 1] * s);
+        w[2] = (bf16)(st.dq[db][4 * i4 + 2] * s);
+        w[3] = (bf16)(st.dq[db][4 * i4 + 3] * s);
+        *reinterpret_cast<bf16x4*>(dQr + 32 * db + 8 * i4 + 4 * g) = w;
+      }
+    }
+  }
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch(const BwdArgs& args, hipStream_t stream) {
+  BwdArgs a = args;
+  const long long rows = (long long)a.B * a.Hq * a.L;
+  constexpr int kRowsPerBlock = 256 / (D / 8);
+  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                     dim3(256), 0, stream, reinterpret_cast<const bf16*>(a.o),
+                     reinterpret_cast<const bf16*>(a.dout), a.lse, a.delta, a.lse2, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  a.n_tiles = (a.L + KVCfg<D>::BK - 1) / KVCfg<D>::BK;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((long long)a.B * a.Hkv * a.n_tiles)),
+                     dim3(256), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+
+  a.n_tiles = (a.L + QCfg<D>::BQ - 1) / QCfg<D>::BQ;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)a.B * a.Hq * a.n_tiles)),
+                     dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream) {
+  if (a.d == 128) return causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
+  return causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+}
+
 }  // namespace fa

@@ -71,23 +71,45 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Forward LDS swizzles (XOR on the 16-byte chunk index of row r of a tile).
+// K is only read 16 rows at a time at one chunk: spread those rows over all
+// banks.  V is only read by the transposing read (4 rows x 4 chunks per
+// half-wave), and rows r and r+8 share a swizzle.
+template <int D> __host__ __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D> __host__ __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
+
+// Offsets into the forward's K tile (16-byte row read) and V tile (8 bytes
+// supplied to the transposing read; h selects K slots 0..3 or 4..7).
+template <int D>
+__host__ __device__ __forceinline__ int row_offset_k(int r, int k, int g) {
+  return r * (2 * D) + (((2 * k + g) ^ swz_k<D>(r)) << 4);
+}
+template <int D>
+__host__ __device__ __forceinline__ int tr_offset_v(int t, int db, int h, int lane) {
+  const int s16 = lane & 15, jg = lane >> 4;
+  const int row = 16 * t + 8 * h + 4 * (lane >> 5) + (s16 >> 2);
+  const int col = 32 * db + 16 * (jg & 1) + 4 * (s16 & 3);
+  return row * (2 * D) + (((col >> 3) ^ swz_v<D>(row)) << 4) + ((col & 4) << 1);
+}
+
 // LDS row swizzle (XOR on the 16-byte chunk index of row r) that keeps two read
 // patterns free of bank conflicts: 16 consecutive rows read at one chunk
 // (16-byte reads), and 4 consecutive rows x 4 chunks (the transposing read).
 template <int D>
-__device__ __forceinline__ int swz_dual(int r) {
+__host__ __device__ __forceinline__ int swz_dual(int r) {
   return D == 128 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
 // Byte offset, inside a [rows x D] bf16 tile stored with swz_dual, of the 8
 // bytes lane `lane` supplies to the transposing read for MFMA K-step t (16
-// rows) and 32-wide column block db.  Slots 0..3 come from this offset,
-// slots 4..7 from the same offset plus 8 rows.  The rows then line up with
-// the C-layout rows 16t + 8*(slot/4) + 4*(lane/32) + slot%4 of an MFMA result.
+// rows), 32-wide column block db and half h: h = 0 gives K slots 0..3, h = 1
+// slots 4..7 (8 rows further down, with that row's own swizzle).  The rows
+// then line up with the C-layout rows 16t + 8*(slot/4) + 4*(lane/32) + slot%4
+// of an MFMA result.
 template <int D>
-__device__ __forceinline__ int tr_offset_dual(int t, int db, int lane) {
+__host__ __device__ __forceinline__ int tr_offset_dual(int t, int db, int h, int lane) {
   const int s16 = lane & 15, jg = lane >> 4;
-  const int row = 16 * t + 4 * (lane >> 5) + (s16 >> 2);
+  const int row = 16 * t + 8 * h + 4 * (lane >> 5) + (s16 >> 2);
   const int col = 32 * db + 16 * (jg & 1) + 4 * (s16 & 3);
   return row * (2 * D) + (((col >> 3) ^ swz_dual<D>(row)) << 4) + ((col & 4) << 1);
 }
@@ -95,7 +117,7 @@ __device__ __forceinline__ int tr_offset_dual(int t, int db, int lane) {
 // Byte offset of the 16 bytes (head dims 16k + 8g .. +7) of row r in a tile
 // stored with swz_dual.
 template <int D>
-__device__ __forceinline__ int row_offset_dual(int r, int k, int g) {
+__host__ __device__ __forceinline__ int row_offset_dual(int r, int k, int g) {
   return r * (2 * D) + (((2 * k + g) ^ swz_dual<D>(r)) << 4);
 }
 

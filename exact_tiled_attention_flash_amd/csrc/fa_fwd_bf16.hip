@@ -35,12 +35,6 @@ struct FwdCfg {
   static constexpr int NDB = D / 32;         // 32-wide blocks of the head dim
 };
 
-// LDS swizzles (XOR on the 16-byte chunk index of a row).
-// K is read 16 rows at a time at one chunk: spread those rows over all banks.
-template <int D> __device__ __forceinline__ int swz_k(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
-// V is read by the transposing read: 4 rows x 4 chunks per half-wave.
-template <int D> __device__ __forceinline__ int swz_v(int r) { return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
-
 // Issue the direct copies of K/V rows [k0, k0+64) into one LDS stage.  Rows past
 // the end of the sequence are clamped to the last row (finite data whose
 // scores are masked to -inf, so they add exactly zero).
@@ -85,9 +79,8 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
   f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
   for (int k = 0; k < C::NSTEP; ++k) {
-    const int ch = 2 * k + g;
-    const bf16x8 a0 = lds_load16(kbuf, ln * (2 * D) + ((ch ^ swz_k<D>(ln)) << 4));
-    const bf16x8 a1 = lds_load16(kbuf, (32 + ln) * (2 * D) + ((ch ^ swz_k<D>(32 + ln)) << 4));
+    const bf16x8 a0 = lds_load16(kbuf, row_offset_k<D>(ln, k, g));
+    const bf16x8 a1 = lds_load16(kbuf, row_offset_k<D>(32 + ln, k, g));
     s0 = mfma32(a0, st.qr[k], s0);
     s1 = mfma32(a1, st.qr[k], s1);
   }
@@ -135,18 +128,12 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
   pb[1] = to_bf16x8(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
   pb[2] = to_bf16x8(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
   pb[3] = to_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
-  const int s16 = lane & 15, jg = lane >> 4;
-  const int vrow = 4 * g + (s16 >> 2);
-  const int vcol = 16 * (jg & 1) + 4 * (s16 & 3);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int row = 16 * t + vrow;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const int col = 32 * db + vcol;
-      const int off = row * (2 * D) + (((col >> 3) ^ swz_v<D>(row)) << 4) + ((col & 4) << 1);
-      const bf16x4 lo = lds_load_tr(vbuf, off);
-      const bf16x4 hi = lds_load_tr(vbuf, off + 8 * (2 * D));
+      const bf16x4 lo = lds_load_tr(vbuf, tr_offset_v<D>(t, db, 0, lane));
+      const bf16x4 hi = lds_load_tr(vbuf, tr_offset_v<D>(t, db, 1, lane));
       st.o[db] = mfma32(concat4(lo, hi), pb[t], st.o[db]);
     }
   }

@@ -28,6 +28,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;      // workspace: D_i = sum_c dO_ic * O_ic, [B, Hq, L]
+  float* lse2;       // workspace: LSE_i * log2(e), [B, Hq, L]
   int B, Hq, Hkv, L, d;
   int window;
   float scale;       // softmax scale

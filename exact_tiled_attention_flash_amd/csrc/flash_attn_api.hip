@@ -30,8 +30,9 @@ int check_common(int B, int Hq, int Hkv, int L, int d, float scale, int causal, 
   return FA_OK;
 }
 
-size_t delta_bytes(int B, int Hq, int L) {
-  const size_t raw = (size_t)B * (size_t)Hq * (size_t)L * sizeof(float);
+// Backward workspace: two float32 per query row -- D_i and LSE_i*log2(e).
+size_t workspace_bytes(int B, int Hq, int L) {
+  const size_t raw = 2 * (size_t)B * (size_t)Hq * (size_t)L * sizeof(float);
   return (raw + 255) & ~(size_t)255;
 }
 
@@ -59,7 +60,7 @@ extern "C" int flash_attn_fwd(const void* q, const void* k, const void* v, void*
 
 extern "C" size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int dtype) {
   if (check_common(B, Hq, Hkv, L, d, 1.f, 0, 0, dtype) != FA_OK) return 0;
-  return delta_bytes(B, Hq, L);
+  return workspace_bytes(B, Hq, L);
 }
 
 extern "C" int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -75,13 +76,14 @@ extern "C" int flash_attn_bwd(const void* q, const void* k, const void* v, const
   for (const void* p : ptrs)
     if (!aligned16(p)) return FA_ERR_INVALID_ARG;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
-      workspace_bytes < delta_bytes(B, Hq, L))
+      workspace_bytes < ::workspace_bytes(B, Hq, L))
     return FA_ERR_WORKSPACE;
 
   fa::BwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
   a.delta = static_cast<float*>(workspace);
+  a.lse2 = a.delta + (size_t)B * Hq * L;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.d = d;
   a.window = window;
   a.scale = softmax_scale;

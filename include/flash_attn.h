@@ -83,9 +83,10 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    float softmax_scale, int causal, int window, int dtype, void* stream);
 
 /*
- * Bytes of device workspace flash_attn_bwd needs for these sizes: one
- * float32 per query row (the row dot product D_i = sum_c dO_ic * O_ic),
- * rounded up to 256 bytes.  Returns 0 for invalid sizes.
+ * Bytes of device workspace flash_attn_bwd needs for these sizes: two
+ * float32 per query row (the row dot product D_i = sum_c dO_ic * O_ic and
+ * the log-sum-exp in base 2), i.e. 8*B*Hq*L rounded up to 256 bytes.
+ * Returns 0 for invalid sizes.
  */
 size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int dtype);
 

@@ -94,7 +94,7 @@ def test_bwd_rejects_invalid_arguments(lib):
     c = header_constants()
     INV, UNS, WS = c["FA_ERR_INVALID_ARG"], c["FA_ERR_UNSUPPORTED"], c["FA_ERR_WORKSPACE"]
     need = lib.flash_attn_bwd_workspace_bytes(1, 2, 2, 16, 64, fa.FA_DTYPE_BF16)
-    assert need == 256                                   # 2*16 floats rounded up to 256 bytes
+    assert need == 256                                   # 2*2*16 floats rounded up to 256 bytes
     assert call_bwd(lib, ws=None) == WS
     assert call_bwd(lib, ws_bytes=need - 1) == WS
     assert call_bwd(lib, ws=FAKE * 16 + 16) == WS        # must be 256-byte aligned
@@ -107,8 +107,9 @@ def test_bwd_rejects_invalid_arguments(lib):
 
 def test_workspace_size_formula(lib):
     f = lib.flash_attn_bwd_workspace_bytes
-    assert f(2, 32, 32, 4096, 128, fa.FA_DTYPE_BF16) == 2 * 32 * 4096 * 4
+    assert f(2, 32, 32, 4096, 128, fa.FA_DTYPE_BF16) == 2 * 32 * 4096 * 8
     assert f(1, 3, 1, 5, 64, fa.FA_DTYPE_BF16) == 256
+    assert f(1, 1, 1, 40, 64, fa.FA_DTYPE_BF16) == 512
     assert f(1, 3, 2, 5, 64, fa.FA_DTYPE_BF16) == 0       # invalid sizes -> 0
     assert f(1, 2, 2, 5, 80, fa.FA_DTYPE_BF16) == 0
 
