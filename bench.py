@@ -116,6 +116,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (3x), so that HBM counters "
+                         "(FETCH_SIZE/WRITE_SIZE) can be scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -128,6 +131,13 @@ def main():
 
     fa.library()
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        src = torch.ones(64 * 2**20, dtype=torch.float32, device=dev)    # 256 MiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     w = W.LLAMA7B_CAUSAL
     q, k, v, do = W.make_inputs(w, with_dout=True)
     q, k, v, do = (t.to(dev) for t in (q, k, v, do))
