@@ -83,111 +83,142 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__
 
 // ------------------------------------------------------------ 2. dK / dV
 
+// One work-group of 8 waves per (batch, K/V head, 128 keys).  Wave w owns the
+// 32 keys of block w % 4 and the 32-query half w / 4 of every streamed 64-query
+// tile, so two waves share each SIMD; the halves' partial dK and dV are summed
+// through LDS at the end.  K and V of the work-group's keys sit in LDS for the
+// whole kernel.
 template <int D>
 struct KVCfg {
-  static constexpr int kWaves = 4;
-  static constexpr int BK = 32 * kWaves;   // keys per work-group
+  static constexpr int kWaves = 8;
+  static constexpr int BK = 128;           // keys per work-group
   static constexpr int BQ = 64;            // queries per streamed tile
   static constexpr int QT = BQ * D * 2;    // bytes of a Q (or dO) tile
+  static constexpr int KT = BK * D * 2;    // bytes of the K (or V) block
   static constexpr int NSTEP = D / 16;
   static constexpr int NDB = D / 32;
 };
 
 template <int D>
 struct KVState {
-  bf16x8 kr[KVCfg<D>::NSTEP];   // this wave's 32 K rows (B operand of S = Q K^T)
-  bf16x8 vr[KVCfg<D>::NSTEP];   // this wave's 32 V rows (B operand of dP = dO V^T)
-  f32x16 dv[KVCfg<D>::NDB];     // dV accumulator: lane = head dim column, registers = keys
+  f32x16 dv[KVCfg<D>::NDB];     // dV accumulator: lane = head-dim column, registers = keys
   f32x16 dk[KVCfg<D>::NDB];     // dK accumulator (scale applied at the end)
 };
 
+// Copy rows [r0, r0 + ROWS) of a [L x D] tensor into LDS with the swz_k layout
+// (rows are only read 16 at a time at one chunk).  8 waves split the block.
+template <int D, int ROWS>
+__device__ __forceinline__ void issue_rows_k(const bf16* __restrict__ src, int r0, int L, char* dst, int wave, int lane) {
+  constexpr int CH = D / 8;
+  constexpr int kPerWave = ROWS * D * 2 / 8;
+  static_assert(kPerWave % 1024 == 0, "block must split into whole wave copies");
+#pragma unroll
+  for (int n = 0; n < kPerWave / 1024; ++n) {
+    const int base = wave * kPerWave + n * 1024;
+    const int p = base / 16 + lane;
+    const int r = p / CH, slot = p % CH;
+    const int row = min(r0 + r, L - 1);
+    g2lds16(src + (size_t)row * D + (slot ^ swz_k<D>(r)) * 8, dst + base);
+  }
+}
+
+// 8-wave variant of issue_rows for the streamed Q / dO tiles (swz_dual layout).
+template <int D, int ROWS>
+__device__ __forceinline__ void issue_rows8(const bf16* __restrict__ src, int r0, int L, char* dst, int wave, int lane) {
+  constexpr int CH = D / 8;
+  constexpr int kBytes = ROWS * D * 2;
+  constexpr int kWaves = (kBytes / 1024) < 8 ? (kBytes / 1024) : 8;   // D=64: 8 copies for 8 waves
+  constexpr int kPerWave = kBytes / kWaves;
+  if (wave >= kWaves) return;
+#pragma unroll
+  for (int n = 0; n < kPerWave / 1024; ++n) {
+    const int base = wave * kPerWave + n * 1024;
+    const int p = base / 16 + lane;
+    const int r = p / CH, slot = p % CH;
+    const int row = min(r0 + r, L - 1);
+    g2lds16(src + (size_t)row * D + (slot ^ swz_dual<D>(r)) * 8, dst + base);
+  }
+}
+
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void kv_tile(KVState<D>& st, const char* qbuf, const char* dobuf, const float* stats,
-                                        int q0, int L, int window, int key_w0, float c, int lane) {
+__device__ __forceinline__ void kv_tile(KVState<D>& st, const char* kblk, const char* vblk, const char* qbuf,
+                                        const char* dobuf, const float* stats, int q0, int L, int window,
+                                        int kb, int qh, int key_w0, float c, int lane) {
   using C = KVCfg<D>;
   const int g = lane >> 5, ln = lane & 31;
   const int my_key = key_w0 + ln;
+  const int qr = 32 * qh + ln;            // this lane's query row of the tile, as an A-operand row
+  const int kr = 32 * kb + ln;            // this lane's key row of the K/V block, as a B-operand row
 
-  // S = Q K^T for two 32-query blocks: lane = key, registers = queries
-  f32x16 p[2];
+  // S = Q K^T (32 queries x 32 keys): lane = key, registers = queries
+  f32x16 p = f32x16{};
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    f32x16 s = f32x16{};
-#pragma unroll
-    for (int k = 0; k < C::NSTEP; ++k)
-      s = mfma32(lds_load16(qbuf, row_offset_dual<D>(32 * qb + ln, k, g)), st.kr[k], s);
-    p[qb] = s;
-  }
+  for (int k = 0; k < C::NSTEP; ++k)
+    p = mfma32(lds_load16(qbuf, row_offset_dual<D>(qr, k, g)), lds_load16(kblk, row_offset_k<D>(kr, k, g)), p);
+
   // P = exp2(S*s*log2e - LSE*log2e), zero where masked
-  const bool need_mask = (q0 + C::BQ > L) || (CAUSAL && q0 < key_w0 + 31) ||
-                         (window > 0 && q0 + C::BQ - 1 > key_w0 + window - 1);
+  const int qw0 = q0 + 32 * qh;           // first query of this wave's half
+  const bool need_mask = (qw0 + 32 > L) || (CAUSAL && qw0 < key_w0 + 31) ||
+                         (window > 0 && qw0 + 31 > key_w0 + window - 1);
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int i4 = 0; i4 < 4; ++i4) {
+    const f32x4 l4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (32 * qh + 8 * i4 + 4 * g));
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 l4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (32 * qb + 8 * i4 + 4 * g));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int i = 4 * i4 + j;
-        float pv = fast_exp2(fmaf(p[qb][i], c, -l4[j]));
-        if (need_mask) {
-          const int q = q0 + 32 * qb + 8 * i4 + 4 * g + j;
-          const bool ok = q < L && (!CAUSAL || my_key <= q) && (window <= 0 || q - my_key < window);
-          pv = ok ? pv : 0.f;
-        }
-        p[qb][i] = pv;
+    for (int j = 0; j < 4; ++j) {
+      const int i = 4 * i4 + j;
+      float pv = fast_exp2(fmaf(p[i], c, -l4[j]));
+      if (need_mask) {
+        const int q = qw0 + 8 * i4 + 4 * g + j;
+        const bool ok = q < L && (!CAUSAL || my_key <= q) && (window <= 0 || q - my_key < window);
+        pv = ok ? pv : 0.f;
       }
+      p[i] = pv;
     }
   }
   // dV += P^T dO: A = P (lane = key, K slots = queries), B = dO via the transposing read
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const f32x16& pp = p[t >> 1];
-    const int o8 = 8 * (t & 1);
-    const bf16x8 pa = to_bf16x8(pp[o8 + 0], pp[o8 + 1], pp[o8 + 2], pp[o8 + 3], pp[o8 + 4], pp[o8 + 5],
-                                pp[o8 + 6], pp[o8 + 7]);
+  for (int u = 0; u < 2; ++u) {
+    const int o8 = 8 * u;
+    const bf16x8 pa = to_bf16x8(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5], p[o8 + 6], p[o8 + 7]);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const bf16x8 bo = concat4(lds_load_tr(dobuf, tr_offset_dual<D>(t, db, 0, lane)),
-                                lds_load_tr(dobuf, tr_offset_dual<D>(t, db, 1, lane)));
+      const bf16x8 bo = concat4(lds_load_tr(dobuf, tr_offset_dual<D>(2 * qh + u, db, 0, lane)),
+                                lds_load_tr(dobuf, tr_offset_dual<D>(2 * qh + u, db, 1, lane)));
       st.dv[db] = mfma32(pa, bo, st.dv[db]);
     }
   }
   // dP = dO V^T, then dS = P * (dP - D) in place
+  f32x16 dp = f32x16{};
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    f32x16 dp = f32x16{};
+  for (int k = 0; k < C::NSTEP; ++k)
+    dp = mfma32(lds_load16(dobuf, row_offset_dual<D>(qr, k, g)), lds_load16(vblk, row_offset_k<D>(kr, k, g)), dp);
 #pragma unroll
-    for (int k = 0; k < C::NSTEP; ++k)
-      dp = mfma32(lds_load16(dobuf, row_offset_dual<D>(32 * qb + ln, k, g)), st.vr[k], dp);
+  for (int i4 = 0; i4 < 4; ++i4) {
+    const f32x4 d4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (C::BQ + 32 * qh + 8 * i4 + 4 * g));
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const f32x4 d4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (C::BQ + 32 * qb + 8 * i4 + 4 * g));
-#pragma unroll
-      for (int j = 0; j < 4; ++j) p[qb][4 * i4 + j] *= dp[4 * i4 + j] - d4[j];
-    }
+    for (int j = 0; j < 4; ++j) p[4 * i4 + j] *= dp[4 * i4 + j] - d4[j];
   }
   // dK += dS^T Q: A = dS (lane = key), B = Q via the transposing read
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const f32x16& pp = p[t >> 1];
-    const int o8 = 8 * (t & 1);
-    const bf16x8 da = to_bf16x8(pp[o8 + 0], pp[o8 + 1], pp[o8 + 2], pp[o8 + 3], pp[o8 + 4], pp[o8 + 5],
-                                pp[o8 + 6], pp[o8 + 7]);
+  for (int u = 0; u < 2; ++u) {
+    const int o8 = 8 * u;
+    const bf16x8 da = to_bf16x8(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5], p[o8 + 6], p[o8 + 7]);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const bf16x8 bq = concat4(lds_load_tr(qbuf, tr_offset_dual<D>(t, db, 0, lane)),
-                                lds_load_tr(qbuf, tr_offset_dual<D>(t, db, 1, lane)));
+      const bf16x8 bq = concat4(lds_load_tr(qbuf, tr_offset_dual<D>(2 * qh + u, db, 0, lane)),
+                                lds_load_tr(qbuf, tr_offset_dual<D>(2 * qh + u, db, 1, lane)));
       st.dk[db] = mfma32(da, bq, st.dk[db]);
     }
   }
 }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = KVCfg<D>;
   // distinct LDS objects per stage so reads of one stage need not wait for the
   // direct copies into the other (alias scopes)
+  __shared__ __attribute__((aligned(1024))) char k_blk[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_blk[C::KT];
   __shared__ __attribute__((aligned(1024))) char q_st0[C::QT];
   __shared__ __attribute__((aligned(1024))) char do_st0[C::QT];
   __shared__ __attribute__((aligned(1024))) char q_st1[C::QT];
@@ -197,6 +228,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, ln = lane & 31;
+  const int kb = wave & 3, qh = wave >> 2;
   const int L = a.L, window = a.window;
   const int G = a.Hq / a.Hkv;
 
@@ -206,8 +238,7 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int kt = r % a.n_tiles;
   const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
   const int key_wg0 = kt * C::BK;
-  const int key_w0 = key_wg0 + 32 * wave;
-  const int my_key = key_w0 + ln;
+  const int key_w0 = key_wg0 + 32 * kb;
 
   const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
   const bf16* __restrict__ Kh = reinterpret_cast<const bf16*>(a.k) + kv_off;
@@ -220,13 +251,12 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int nq = qt_hi - qt_lo + 1;
   const int n_it = G * nq;
 
-  auto head_of = [&](int it) { return hk * G + it / nq; };
   auto q0_of = [&](int it) { return (qt_lo + it % nq) * C::BQ; };
   auto issue = [&](int it, char* qs, char* dos, float* ss) {
-    const int hq = head_of(it), q0 = q0_of(it);
+    const int hq = hk * G + it / nq, q0 = q0_of(it);
     const size_t qoff = ((size_t)(b * a.Hq + hq) * L) * D;
-    issue_rows<D, C::BQ>(reinterpret_cast<const bf16*>(a.q) + qoff, q0, L, qs, wave, lane);
-    issue_rows<D, C::BQ>(reinterpret_cast<const bf16*>(a.dout) + qoff, q0, L, dos, wave, lane);
+    issue_rows8<D, C::BQ>(reinterpret_cast<const bf16*>(a.q) + qoff, q0, L, qs, wave, lane);
+    issue_rows8<D, C::BQ>(reinterpret_cast<const bf16*>(a.dout) + qoff, q0, L, dos, wave, lane);
     if (wave == 0) {
       const size_t srow = (size_t)(b * a.Hq + hq) * L + min(q0 + lane, L - 1);
       g2lds4(a.lse2 + srow, reinterpret_cast<char*>(ss));
@@ -234,51 +264,76 @@ __global__ __launch_bounds__(256, 1) void bwd_dkdv_kernel(BwdArgs a) {
     }
   };
 
+  issue_rows_k<D, C::BK>(Kh, key_wg0, L, k_blk, wave, lane);
+  issue_rows_k<D, C::BK>(Vh, key_wg0, L, v_blk, wave, lane);
   issue(0, q_st0, do_st0, stat_st0);
 
   KVState<D> st;
-  {
-    const int kr = min(my_key, L - 1);
 #pragma unroll
-    for (int k = 0; k < C::NSTEP; ++k) {
-      st.kr[k] = *reinterpret_cast<const bf16x8*>(Kh + (size_t)kr * D + 16 * k + 8 * g);
-      st.vr[k] = *reinterpret_cast<const bf16x8*>(Vh + (size_t)kr * D + 16 * k + 8 * g);
-    }
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      st.dv[db] = f32x16{};
-      st.dk[db] = f32x16{};
-    }
+  for (int db = 0; db < C::NDB; ++db) {
+    st.dv[db] = f32x16{};
+    st.dk[db] = f32x16{};
   }
   const float c = a.scale_log2;
   auto wave_needs = [&](int q0) {
-    return key_w0 < L && (!CAUSAL || q0 + C::BQ - 1 >= key_w0) && (window <= 0 || q0 <= key_w0 + 31 + window - 1);
+    const int qw0 = q0 + 32 * qh;
+    return key_w0 < L && qw0 < L && (!CAUSAL || qw0 + 31 >= key_w0) && (window <= 0 || qw0 <= key_w0 + 31 + window - 1);
   };
 
   wait_copies_and_barrier();
   for (int it = 0; it < n_it; it += 2) {
     if (it + 1 < n_it) issue(it + 1, q_st1, do_st1, stat_st1);
-    if (wave_needs(q0_of(it))) kv_tile<D, CAUSAL>(st, q_st0, do_st0, stat_st0, q0_of(it), L, window, key_w0, c, lane);
+    if (wave_needs(q0_of(it)))
+      kv_tile<D, CAUSAL>(st, k_blk, v_blk, q_st0, do_st0, stat_st0, q0_of(it), L, window, kb, qh, key_w0, c, lane);
     wait_copies_and_barrier();
     if (it + 1 >= n_it) break;
     if (it + 2 < n_it) issue(it + 2, q_st0, do_st0, stat_st0);
     if (wave_needs(q0_of(it + 1)))
-      kv_tile<D, CAUSAL>(st, q_st1, do_st1, stat_st1, q0_of(it + 1), L, window, key_w0, c, lane);
+      kv_tile<D, CAUSAL>(st, k_blk, v_blk, q_st1, do_st1, stat_st1, q0_of(it + 1), L, window, kb, qh, key_w0, c, lane);
     wait_copies_and_barrier();
   }
 
-  // epilogue: lane holds head-dim column 32*db + ln of keys key_w0 + 8*(i/4) + 4g + i%4
+  // Sum the two query halves through LDS (the stage buffers are free now):
+  // waves 4..7 deposit their partials, waves 0..3 add them.  Each key block
+  // uses one stage buffer, float [db][i][lane]; dV first, then dK.
+  constexpr int kPart = C::NDB * 16 * 64 * 4;     // bytes per wave per tensor
+  static_assert(kPart <= C::QT, "a partial must fit in one stage buffer");
   bf16* dKh = reinterpret_cast<bf16*>(a.dk) + kv_off;
   bf16* dVh = reinterpret_cast<bf16*>(a.dv) + kv_off;
   const float s = a.scale;
+  float* part = reinterpret_cast<float*>(kb == 0 ? q_st0 : kb == 1 ? do_st0 : kb == 2 ? q_st1 : do_st1);
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int key = key_w0 + 8 * (i >> 2) + 4 * g + (i & 3);
-    if (key < L) {
+  for (int pass = 0; pass < 2; ++pass) {
+    if (qh == 1) {
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        dKh[(size_t)key * D + 32 * db + ln] = (bf16)(st.dk[db][i] * s);
-        dVh[(size_t)key * D + 32 * db + ln] = (bf16)(st.dv[db][i]);
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          part[(db * 16 + i) * 64 + lane] = pass == 0 ? st.dv[db][i] : st.dk[db][i];
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (pass == 0) st.dv[db][i] += part[(db * 16 + i) * 64 + lane];
+          else st.dk[db][i] += part[(db * 16 + i) * 64 + lane];
+        }
+    }
+    __syncthreads();
+  }
+  if (qh == 0) {
+    // lane holds head-dim column 32*db + ln of keys key_w0 + 8*(i/4) + 4g + i%4
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = key_w0 + 8 * (i >> 2) + 4 * g + (i & 3);
+      if (key < L) {
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          dKh[(size_t)key * D + 32 * db + ln] = (bf16)(st.dk[db][i] * s);
+          dVh[(size_t)key * D + 32 * db + ln] = (bf16)(st.dv[db][i]);
+        }
       }
     }
   }
@@ -468,7 +523,7 @@ hipError_t launch(const BwdArgs& args, hipStream_t stream) {
 
   a.n_tiles = (a.L + KVCfg<D>::BK - 1) / KVCfg<D>::BK;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((long long)a.B * a.Hkv * a.n_tiles)),
-                     dim3(256), 0, stream, a);
+                     dim3(64 * KVCfg<D>::kWaves), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 

@@ -24,6 +24,10 @@ namespace fa {
 
 namespace {
 
+// Slack (log2 units) before the running maximum is raised: tile terms stay
+// below 2^8 = 256, far from fp32 (and bf16) overflow.
+constexpr float kRescaleSlack = 8.0f;
+
 template <int D>
 struct FwdCfg {
   static constexpr int kWaves = 4;
@@ -100,13 +104,26 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
     }
   }
 
-  // 3. online softmax: the two lanes holding one query share the tile maximum
+  // 3. online softmax: the two lanes holding one query share the tile maximum.
+  // The running maximum m is only raised when the tile's maximum exceeds it by
+  // more than kRescaleSlack (log2 units); otherwise the tile is exponentiated
+  // against the old m, so its terms are at most 2^kRescaleSlack.  O and l share
+  // that m, which cancels in O / l and is folded into the log-sum-exp, so the
+  // result is the same softmax; the rescale of O (and l) by exp2(m_old - m_new)
+  // then runs only when some lane raised its maximum.
   float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
   for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
   mx = fmaxf(mx, wave_xor32(mx));
-  const float m_new = fmaxf(st.m_run, mx * c);
-  const float alpha = fast_exp2(st.m_run - m_new);
+  const bool raise = mx * c > st.m_run + kRescaleSlack;
+  const float m_new = raise ? mx * c : st.m_run;
+  if (__ballot(raise) != 0) {
+    const float alpha = fast_exp2(st.m_run - m_new);
+    st.l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) st.o[db] *= alpha;
+    st.m_run = m_new;
+  }
   float rs = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
@@ -114,10 +131,7 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
     s1[i] = fast_exp2(fmaf(s1[i], c, -m_new));
     rs += s0[i] + s1[i];
   }
-  st.l_run = st.l_run * alpha + rs;
-  st.m_run = m_new;
-#pragma unroll
-  for (int db = 0; db < C::NDB; ++db) st.o[db] *= alpha;
+  st.l_run += rs;
 
   // 4. O^T += V^T P^T, 16 keys per MFMA step.  P^T's K slots (from the C
   // layout of step 1) are keys 16t + 8*(slot/4) + 4g + slot%4; the transposing

@@ -110,6 +110,9 @@ void check_all() {
   check_row_reads<D>("fwd K", kimg, 64, [](int r, int k, int g) { return row_offset_k<D>(r, k, g); });
   auto vimg = tile_image<D>(64, [](int r) { return swz_v<D>(r); });
   check_tr_reads<D>("fwd V", vimg, [](int t, int db, int h, int l) { return tr_offset_v<D>(t, db, h, l); });
+  // backward dK/dV: the work-group's 128-row K and V blocks (row reads)
+  auto kblk = tile_image<D>(128, [](int r) { return swz_k<D>(r); });
+  check_row_reads<D>("bwd K/V block", kblk, 128, [](int r, int k, int g) { return row_offset_k<D>(r, k, g); });
   // backward: tiles read both ways
   auto dimg = tile_image<D>(64, [](int r) { return swz_dual<D>(r); });
   check_row_reads<D>("bwd dual", dimg, 64, [](int r, int k, int g) { return row_offset_dual<D>(r, k, g); });
