@@ -50,6 +50,38 @@ __device__ __forceinline__ bf16x4 lds_load_tr(const char* base, int byte_off) {
   return __builtin_bit_cast(bf16x4, r);
 }
 
+// Buffer resource over `bytes` bytes at `base` (raw, no stride): loads past
+// the end return zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Direct 16-byte buffer -> LDS copy for a whole wave: lane l's 16 bytes from
+// byte voff + soff of the resource land at lds_wave_base + 16*l.
+// `lds_wave_base` and `soff` must be wave-uniform.
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, int voff, int soff, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)(lds_wave_base), 16, voff, soff, 0, 0);
+}
+
+// Value of x in lane l XOR 32 combined with x by op -- both halves of the wave
+// end up with op(x[l % 32], x[l % 32 + 32]).  One v_permlane32_swap.
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// acc + a + b for two bf16 values (v_dot2 with (1, 1)), exact products.
+__device__ __forceinline__ float dot2_ones(bf16 a, bf16 b, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {a, b};
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(v, one, acc, false);
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Direct 16-byte global -> LDS copy for a whole wave: lane l's 16 bytes from
 // `src` land at lds_wave_base + 16*l.  `lds_wave_base` must be wave-uniform.
 __device__ __forceinline__ void g2lds16(const void* src, char* lds_wave_base) {
@@ -90,6 +122,45 @@ __host__ __device__ __forceinline__ int tr_offset_v(int t, int db, int h, int la
   const int row = 16 * t + 8 * h + 4 * (lane >> 5) + (s16 >> 2);
   const int col = 32 * db + 16 * (jg & 1) + 4 * (s16 & 3);
   return row * (2 * D) + (((col >> 3) ^ swz_v<D>(row)) << 4) + ((col & 4) << 1);
+}
+
+// Padded LDS tiles.  A row of D bf16 values (2D bytes) is stored with a stride
+// of KSTR = 2D + 16 bytes in a tile read only by 16-byte row reads, and of
+// VSTR = 2D + 64 bytes in a tile read only by the transposing read.  Either
+// stride spreads the rows a read touches over all 64 banks, and, unlike an
+// XOR swizzle, keeps every operand address "one per-lane base + an immediate",
+// so the loop needs no address arithmetic.
+template <int D> struct Pad {
+  static constexpr int KSTR = 2 * D + 16;
+  static constexpr int VSTR = 2 * D + 64;
+};
+
+// Byte offset in a K-padded tile of head dims 16k + 8g .. +7 of row r.
+template <int D>
+__host__ __device__ __forceinline__ int row_offset_kpad(int r, int k, int g) {
+  return r * Pad<D>::KSTR + (2 * k + g) * 16;
+}
+
+// Byte offset in a V-padded tile of the 8 bytes lane `lane` supplies to the
+// transposing read for MFMA K-step t (16 rows), 32-wide column block db and
+// half h (K slots 0..3 or 4..7, 8 rows further down); the slots then hold rows
+// 16t + 8*(slot/4) + 4*(lane/32) + slot%4 and column 32db + lane%32.
+template <int D>
+__host__ __device__ __forceinline__ int tr_offset_vpad(int t, int db, int h, int lane) {
+  const int s16 = lane & 15, jg = lane >> 4;
+  const int row = 16 * t + 8 * h + 4 * (lane >> 5) + (s16 >> 2);
+  const int col = 32 * db + 16 * (jg & 1) + 4 * (s16 & 3);
+  return row * Pad<D>::VSTR + col * 2;
+}
+
+// Source of 16-byte slot p of a padded tile with STRIDE-byte rows: byte offset,
+// relative to the tile's first row in the [rows x D] bf16 tensor, of the data
+// that belongs there.  Padding slots repeat the row's first chunk.
+template <int D, int STRIDE>
+__host__ __device__ __forceinline__ int pad_slot_src(int p) {
+  constexpr int kSlots = STRIDE / 16, kChunks = D / 8;
+  const int r = p / kSlots, slot = p % kSlots;
+  return r * (2 * D) + (slot < kChunks ? slot : 0) * 16;
 }
 
 // LDS row swizzle (XOR on the 16-byte chunk index of row r) that keeps two read

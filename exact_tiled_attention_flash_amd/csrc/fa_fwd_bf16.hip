@@ -2,7 +2,7 @@
 //
 // One work-group of 4 waves owns 128 query rows of one (batch, query head);
 // each wave owns 32 of them.  The work-group streams the allowed 64-key tiles
-// of K and V through LDS (double-buffered, filled by direct global->LDS copies
+// of K and V through LDS (double-buffered, filled by direct buffer->LDS copies
 // while the previous tile is being used), and for every tile each wave
 //   1. S^T = K Q^T on MFMA (keys as rows, the wave's 32 queries as columns:
 //      every lane then holds 32 scores of ONE query),
@@ -17,6 +17,17 @@
 // The work is done in base 2: scores are multiplied by s*log2(e) and exp2 is
 // the hardware v_exp_f32; the saved log-sum-exp is converted back to ln.
 // Only O and the per-row log-sum-exp are written (claspmoon.cn §3.3).
+//
+// On gfx950 the vector ALU work of a wave does not hide behind its matrix-core
+// work, so the kernel keeps the per-tile VALU instruction count close to the
+// softmax itself: padded LDS rows make every operand address a per-lane base
+// plus an immediate, the copies use buffer loads with loop-invariant lane
+// offsets (past-the-end rows read as zeros, no clamping), the pair of lanes
+// holding one query exchange values with v_permlane32_swap, and the running
+// maximum is only raised (and O rescaled) when a tile's maximum exceeds it by
+// a wide margin.  (Summing the bf16-rounded probabilities with v_dot2 would
+// halve the row-sum instructions, but moves the log-sum-exp of short rows by
+// up to 2^-9 relative, beyond its tolerance; the sum stays fp32.)
 #include "fa_common.hpp"
 #include "fa_kernels.h"
 
@@ -31,32 +42,49 @@ constexpr float kRescaleSlack = 8.0f;
 template <int D>
 struct FwdCfg {
   static constexpr int kWaves = 4;
-  static constexpr int BR = 32 * kWaves;     // query rows per work-group
-  static constexpr int BC = 64;              // keys per K/V tile
-  static constexpr int CH = D / 8;           // 16-byte chunks per row
-  static constexpr int TILE = BC * D * 2;    // bytes of one K (or V) tile
-  static constexpr int NSTEP = D / 16;       // MFMA K-steps over the head dim
-  static constexpr int NDB = D / 32;         // 32-wide blocks of the head dim
+  static constexpr int BR = 32 * kWaves;          // query rows per work-group
+  static constexpr int BC = 64;                   // keys per K/V tile
+  static constexpr int KT = BC * Pad<D>::KSTR;    // bytes of a padded K tile
+  static constexpr int VT = BC * Pad<D>::VSTR;    // bytes of a padded V tile
+  static constexpr int KCOPIES = KT / 1024;       // wave-wide 1 KiB copies per K tile
+  static constexpr int VCOPIES = VT / 1024;
+  static constexpr int KPER = (KCOPIES + kWaves - 1) / kWaves;   // copies per wave (at most)
+  static constexpr int VPER = (VCOPIES + kWaves - 1) / kWaves;
+  static constexpr int NSTEP = D / 16;            // MFMA K-steps over the head dim
+  static constexpr int NDB = D / 32;              // 32-wide blocks of the head dim
+  static_assert(KT % 1024 == 0 && VT % 1024 == 0, "padded tiles must split into 1 KiB copies");
 };
 
-// Issue the direct copies of K/V rows [k0, k0+64) into one LDS stage.  Rows past
-// the end of the sequence are clamped to the last row (finite data whose
-// scores are masked to -inf, so they add exactly zero).
+// Loop-invariant per-lane source offsets of this wave's share of a tile copy.
+// Copy n (0 <= n < COPIES) belongs to wave n % 4 and fills tile bytes
+// [1024n, 1024n + 1024).
 template <int D>
-__device__ __forceinline__ void issue_kv_tile(const bf16* __restrict__ Kh, const bf16* __restrict__ Vh,
-                                              int k0, int L, char* kbuf, char* vbuf, int wave, int lane) {
+struct CopyPlan {
+  int koff[FwdCfg<D>::KPER];
+  int voff[FwdCfg<D>::VPER];
+};
+
+template <int D>
+__device__ __forceinline__ void make_copy_plan(CopyPlan<D>& cp, int wave, int lane) {
   using C = FwdCfg<D>;
-  constexpr int kPerWave = C::TILE / C::kWaves;
-  constexpr int kInstr = kPerWave / 1024;
 #pragma unroll
-  for (int n = 0; n < kInstr; ++n) {
-    const int base = wave * kPerWave + n * 1024;
-    const int p = base / 16 + lane;
-    const int r = p / C::CH, slot = p % C::CH;
-    const int row = min(k0 + r, L - 1);
-    g2lds16(Kh + (size_t)row * D + (slot ^ swz_k<D>(r)) * 8, kbuf + base);
-    g2lds16(Vh + (size_t)row * D + (slot ^ swz_v<D>(r)) * 8, vbuf + base);
-  }
+  for (int i = 0; i < C::KPER; ++i) cp.koff[i] = pad_slot_src<D, Pad<D>::KSTR>((wave + 4 * i) * 64 + lane);
+#pragma unroll
+  for (int i = 0; i < C::VPER; ++i) cp.voff[i] = pad_slot_src<D, Pad<D>::VSTR>((wave + 4 * i) * 64 + lane);
+}
+
+// Copy K and V rows [k0, k0 + 64) into one LDS stage (rows past L read zeros).
+template <int D>
+__device__ __forceinline__ void issue_kv(const CopyPlan<D>& cp, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                         int k0, char* kbuf, char* vbuf, int wave) {
+  using C = FwdCfg<D>;
+  const int soff = k0 * (2 * D);
+#pragma unroll
+  for (int i = 0; i < C::KPER; ++i)
+    if (wave + 4 * i < C::KCOPIES) buf2lds16(kr, cp.koff[i], soff, kbuf + (wave + 4 * i) * 1024);
+#pragma unroll
+  for (int i = 0; i < C::VPER; ++i)
+    if (wave + 4 * i < C::VCOPIES) buf2lds16(vr, cp.voff[i], soff, vbuf + (wave + 4 * i) * 1024);
 }
 
 __device__ __forceinline__ void wait_copies_and_barrier() {
@@ -72,6 +100,8 @@ struct FwdState {
   float m_run, l_run;            // running max (log2 units) and this lane's partial sum
 };
 
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
+
 // One key tile for one wave: S^T, mask, online softmax, O^T += V^T P^T.
 template <int D, bool CAUSAL>
 __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, const char* vbuf, int k0,
@@ -80,11 +110,17 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
   using C = FwdCfg<D>;
   const int g = lane >> 5, ln = lane & 31;
   // 1. S^T (64 keys x 32 queries) as two 32x32 blocks
-  f32x16 s0 = f32x16{}, s1 = f32x16{};
+  f32x16 s0, s1;
+  {
+    const bf16x8 a0 = lds_load16(kbuf, row_offset_kpad<D>(ln, 0, g));
+    const bf16x8 a1 = lds_load16(kbuf, row_offset_kpad<D>(32 + ln, 0, g));
+    s0 = mfma32(a0, st.qr[0], f32x16{});
+    s1 = mfma32(a1, st.qr[0], f32x16{});
+  }
 #pragma unroll
-  for (int k = 0; k < C::NSTEP; ++k) {
-    const bf16x8 a0 = lds_load16(kbuf, row_offset_k<D>(ln, k, g));
-    const bf16x8 a1 = lds_load16(kbuf, row_offset_k<D>(32 + ln, k, g));
+  for (int k = 1; k < C::NSTEP; ++k) {
+    const bf16x8 a0 = lds_load16(kbuf, row_offset_kpad<D>(ln, k, g));
+    const bf16x8 a1 = lds_load16(kbuf, row_offset_kpad<D>(32 + ln, k, g));
     s0 = mfma32(a0, st.qr[k], s0);
     s1 = mfma32(a1, st.qr[k], s1);
   }
@@ -111,10 +147,13 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
   // that m, which cancels in O / l and is folded into the log-sum-exp, so the
   // result is the same softmax; the rescale of O (and l) by exp2(m_old - m_new)
   // then runs only when some lane raised its maximum.
-  float mx = fmaxf(s0[0], s1[0]);
+  float mA = max3(s0[0], s1[0], s0[1]), mB = max3(s1[1], s0[2], s1[2]);
 #pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, fmaxf(s0[i], s1[i]));
-  mx = fmaxf(mx, wave_xor32(mx));
+  for (int i = 3; i < 15; i += 2) {
+    mA = max3(mA, s0[i], s1[i]);
+    mB = max3(mB, s0[i + 1], s1[i + 1]);
+  }
+  const float mx = pair_max(max3(mA, mB, fmaxf(s0[15], s1[15])));
   const bool raise = mx * c > st.m_run + kRescaleSlack;
   const float m_new = raise ? mx * c : st.m_run;
   if (__ballot(raise) != 0) {
@@ -124,30 +163,32 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
     for (int db = 0; db < C::NDB; ++db) st.o[db] *= alpha;
     st.m_run = m_new;
   }
-  float rs = 0.f;
+  // P = exp2(s*c - m); the row sum is accumulated in fp32 from the unrounded
+  // values (two chains), and P is rounded to bf16 for the P.V product.
+  float rA = 0.f, rB = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     s0[i] = fast_exp2(fmaf(s0[i], c, -m_new));
     s1[i] = fast_exp2(fmaf(s1[i], c, -m_new));
-    rs += s0[i] + s1[i];
+    rA += s0[i];
+    rB += s1[i];
   }
-  st.l_run += rs;
-
-  // 4. O^T += V^T P^T, 16 keys per MFMA step.  P^T's K slots (from the C
-  // layout of step 1) are keys 16t + 8*(slot/4) + 4g + slot%4; the transposing
-  // read gives V^T the same keys: lane supplies row 16t + 4g + (lane%16)/4
-  // (+8 for slots 4..7) and 4 head-dim values of its 16-wide half.
+  st.l_run += rA + rB;
   bf16x8 pb[4];
   pb[0] = to_bf16x8(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
   pb[1] = to_bf16x8(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
   pb[2] = to_bf16x8(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
   pb[3] = to_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
+
+  // 4. O^T += V^T P^T, 16 keys per MFMA step.  P^T's K slots (from the C
+  // layout of step 1) are keys 16t + 8*(slot/4) + 4g + slot%4; the transposing
+  // read gives V^T the same keys.
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const bf16x4 lo = lds_load_tr(vbuf, tr_offset_v<D>(t, db, 0, lane));
-      const bf16x4 hi = lds_load_tr(vbuf, tr_offset_v<D>(t, db, 1, lane));
+      const bf16x4 lo = lds_load_tr(vbuf, tr_offset_vpad<D>(t, db, 0, lane));
+      const bf16x4 hi = lds_load_tr(vbuf, tr_offset_vpad<D>(t, db, 1, lane));
       st.o[db] = mfma32(concat4(lo, hi), pb[t], st.o[db]);
     }
   }
@@ -159,10 +200,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   // Four distinct LDS objects (K and V of two stages): distinct objects carry
   // distinct alias scopes, which lets the compiler see that reading one stage
   // does not have to wait for the direct copies into the other.
-  __shared__ __attribute__((aligned(1024))) char k_st0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char v_st0[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char k_st1[C::TILE];
-  __shared__ __attribute__((aligned(1024))) char v_st1[C::TILE];
+  __shared__ __attribute__((aligned(1024))) char k_st0[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st0[C::VT];
+  __shared__ __attribute__((aligned(1024))) char k_st1[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st1[C::VT];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, ln = lane & 31;
@@ -177,8 +218,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int L = a.L;
 
   const bf16* __restrict__ Qh = reinterpret_cast<const bf16*>(a.q) + ((size_t)(b * a.Hq + h) * L) * D;
-  const bf16* __restrict__ Kh = reinterpret_cast<const bf16*>(a.k) + ((size_t)(b * a.Hkv + hk) * L) * D;
-  const bf16* __restrict__ Vh = reinterpret_cast<const bf16*>(a.v) + ((size_t)(b * a.Hkv + hk) * L) * D;
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
+  const unsigned head_bytes = (unsigned)L * (2 * D);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16*>(a.v) + kv_off, head_bytes);
 
   const int q_wg0 = qt * C::BR;
   const int q_w0 = q_wg0 + 32 * wave;
@@ -191,7 +234,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int kv_begin = (window > 0) ? max(0, q_wg0 - window + 1) : 0;
   const int j_lo = kv_begin / C::BC, j_hi = (kv_end - 1) / C::BC;
 
-  issue_kv_tile<D>(Kh, Vh, j_lo * C::BC, L, k_st0, v_st0, wave, lane);
+  CopyPlan<D> cp;
+  make_copy_plan<D>(cp, wave, lane);
+  issue_kv<D>(cp, krs, vrs, j_lo * C::BC, k_st0, v_st0, wave);
 
   FwdState<D> st;
 #pragma unroll
@@ -213,19 +258,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   // Tiles alternate between the two stages; the loop is unrolled by two so
   // that every LDS access names its stage statically.
   for (int j = j_lo; j <= j_hi; j += 2) {
-    if (j < j_hi) issue_kv_tile<D>(Kh, Vh, (j + 1) * C::BC, L, k_st1, v_st1, wave, lane);
+    if (j < j_hi) issue_kv<D>(cp, krs, vrs, (j + 1) * C::BC, k_st1, v_st1, wave);
     if (wave_needs(j * C::BC))
       fwd_tile<D, CAUSAL>(st, k_st0, v_st0, j * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
     wait_copies_and_barrier();
     if (j + 1 > j_hi) break;
-    if (j + 1 < j_hi) issue_kv_tile<D>(Kh, Vh, (j + 2) * C::BC, L, k_st0, v_st0, wave, lane);
+    if (j + 1 < j_hi) issue_kv<D>(cp, krs, vrs, (j + 2) * C::BC, k_st0, v_st0, wave);
     if (wave_needs((j + 1) * C::BC))
       fwd_tile<D, CAUSAL>(st, k_st1, v_st1, (j + 1) * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
     wait_copies_and_barrier();
   }
 
   // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2
-  const float l_tot = st.l_run + wave_xor32(st.l_run);
+  const float l_tot = pair_sum(st.l_run);
   if (my_q < L) {
     const float inv = 1.f / l_tot;
     bf16* Oq = reinterpret_cast<bf16*>(a.o) + ((size_t)(b * a.Hq + h) * L + my_q) * D;

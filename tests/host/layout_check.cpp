@@ -103,8 +103,28 @@ void check_tr_reads(const char* name, const std::vector<int>& img,
       }
 }
 
+// padded tile filled by the direct copies: 16-byte slot p holds the 16 bytes
+// at byte pad_slot_src(p) of the row-major [rows x D] source
+template <int D, int STRIDE>
+std::vector<int> padded_image(int rows) {
+  std::vector<int> img(rows * STRIDE / 2, -1);
+  for (int p = 0; p < rows * STRIDE / 16; ++p) {
+    const int src = pad_slot_src<D, STRIDE>(p);
+    for (int e = 0; e < 8; ++e) img[p * 8 + e] = src / 2 + e;   // element id = row * D + col
+  }
+  return img;
+}
+
 template <int D>
 void check_all() {
+  // forward (padded): K tile (row reads) and V tile (transposing reads), 64 rows each
+  {
+    auto kp = padded_image<D, Pad<D>::KSTR>(64);
+    check_row_reads<D>("fwd K padded", kp, 64, [](int r, int k, int g) { return row_offset_kpad<D>(r, k, g); });
+    auto vp = padded_image<D, Pad<D>::VSTR>(64);
+    check_tr_reads<D>("fwd V padded", vp, [](int t, int db, int h, int l) { return tr_offset_vpad<D>(t, db, h, l); });
+    CHECK(64 * Pad<D>::KSTR % 1024 == 0 && 64 * Pad<D>::VSTR % 1024 == 0, "padded tiles must be whole 1 KiB copies");
+  }
   // forward: K tile (row reads) and V tile (transposing reads), 64 rows each
   auto kimg = tile_image<D>(64, [](int r) { return swz_k<D>(r); });
   check_row_reads<D>("fwd K", kimg, 64, [](int r, int k, int g) { return row_offset_k<D>(r, k, g); });
