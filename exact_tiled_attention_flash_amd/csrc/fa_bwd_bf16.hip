@@ -19,7 +19,9 @@
 // The two tile kernels reuse the forward's MFMA layouts: a product whose C
 // registers hold one column per lane feeds the next product's A or B operand
 // directly, and the operand that needs the other orientation comes from the
-// gfx950 transposing LDS read.
+// gfx950 transposing LDS read.  As in the forward, every LDS address is a
+// loop-invariant per-lane offset plus an immediate and all tile copies are
+// buffer->LDS loads, which keeps the VALU work per tile small.
 #include "fa_common.hpp"
 #include "fa_kernels.h"
 
@@ -30,30 +32,6 @@ namespace {
 __device__ __forceinline__ void wait_copies_and_barrier() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-}
-
-// Direct 4-byte global -> LDS copy for a whole wave (lane l -> base + 4*l).
-__device__ __forceinline__ void g2lds4(const void* src, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(src, (FA_LDS void*)(lds_wave_base), 4, 0, 0);
-}
-
-// Copy rows [r0, r0 + rows) of a [L x D] bf16 tensor into an LDS tile stored
-// with swz_dual; rows past the end are clamped to the last row.  The 4 waves
-// split the tile evenly.
-template <int D, int ROWS>
-__device__ __forceinline__ void issue_rows(const bf16* __restrict__ src, int r0, int L, char* dst, int wave, int lane) {
-  constexpr int CH = D / 8;
-  constexpr int kBytes = ROWS * D * 2;
-  constexpr int kPerWave = kBytes / 4;
-  static_assert(kPerWave % 1024 == 0, "tile must split into whole wave copies");
-#pragma unroll
-  for (int n = 0; n < kPerWave / 1024; ++n) {
-    const int base = wave * kPerWave + n * 1024;
-    const int p = base / 16 + lane;
-    const int r = p / CH, slot = p % CH;
-    const int row = min(r0 + r, L - 1);
-    g2lds16(src + (size_t)row * D + (slot ^ swz_dual<D>(r)) * 8, dst + base);
-  }
 }
 
 // ------------------------------------------------------------ 1. delta
@@ -87,16 +65,24 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__
 // 32 keys of block w % 4 and the 32-query half w / 4 of every streamed 64-query
 // tile, so two waves share each SIMD; the halves' partial dK and dV are summed
 // through LDS at the end.  K and V of the work-group's keys sit in LDS for the
-// whole kernel.
+// whole kernel, in padded rows (they are only read row-wise); the streamed Q
+// and dO tiles are read both row-wise and by the transposing read, so they use
+// the swz_dual layout.  Every LDS address is a loop-invariant per-lane offset
+// plus an immediate, and all copies are buffer->LDS loads (rows past the end
+// of the sequence read as zeros).
 template <int D>
 struct KVCfg {
   static constexpr int kWaves = 8;
-  static constexpr int BK = 128;           // keys per work-group
-  static constexpr int BQ = 64;            // queries per streamed tile
-  static constexpr int QT = BQ * D * 2;    // bytes of a Q (or dO) tile
-  static constexpr int KT = BK * D * 2;    // bytes of the K (or V) block
+  static constexpr int BK = 128;                 // keys per work-group
+  static constexpr int BQ = 64;                  // queries per streamed tile
+  static constexpr int QT = BQ * D * 2;          // bytes of a Q (or dO) tile (swz_dual)
+  static constexpr int KB = BK * Pad<D>::KSTR;   // bytes of the padded K (or V) block
+  static constexpr int QCOPIES = QT / 1024;
+  static constexpr int QPER = QCOPIES / kWaves;  // copies per wave per tensor
+  static constexpr int KBCOPIES = KB / 1024;
   static constexpr int NSTEP = D / 16;
   static constexpr int NDB = D / 32;
+  static_assert(QCOPIES % kWaves == 0 && KB % 1024 == 0, "tiles must split into whole wave copies");
 };
 
 template <int D>
@@ -105,56 +91,28 @@ struct KVState {
   f32x16 dk[KVCfg<D>::NDB];     // dK accumulator (scale applied at the end)
 };
 
-// Copy rows [r0, r0 + ROWS) of a [L x D] tensor into LDS with the swz_k layout
-// (rows are only read 16 at a time at one chunk).  8 waves split the block.
-template <int D, int ROWS>
-__device__ __forceinline__ void issue_rows_k(const bf16* __restrict__ src, int r0, int L, char* dst, int wave, int lane) {
-  constexpr int CH = D / 8;
-  constexpr int kPerWave = ROWS * D * 2 / 8;
-  static_assert(kPerWave % 1024 == 0, "block must split into whole wave copies");
-#pragma unroll
-  for (int n = 0; n < kPerWave / 1024; ++n) {
-    const int base = wave * kPerWave + n * 1024;
-    const int p = base / 16 + lane;
-    const int r = p / CH, slot = p % CH;
-    const int row = min(r0 + r, L - 1);
-    g2lds16(src + (size_t)row * D + (slot ^ swz_k<D>(r)) * 8, dst + base);
-  }
-}
-
-// 8-wave variant of issue_rows for the streamed Q / dO tiles (swz_dual layout).
-template <int D, int ROWS>
-__device__ __forceinline__ void issue_rows8(const bf16* __restrict__ src, int r0, int L, char* dst, int wave, int lane) {
-  constexpr int CH = D / 8;
-  constexpr int kBytes = ROWS * D * 2;
-  constexpr int kWaves = (kBytes / 1024) < 8 ? (kBytes / 1024) : 8;   // D=64: 8 copies for 8 waves
-  constexpr int kPerWave = kBytes / kWaves;
-  if (wave >= kWaves) return;
-#pragma unroll
-  for (int n = 0; n < kPerWave / 1024; ++n) {
-    const int base = wave * kPerWave + n * 1024;
-    const int p = base / 16 + lane;
-    const int r = p / CH, slot = p % CH;
-    const int row = min(r0 + r, L - 1);
-    g2lds16(src + (size_t)row * D + (slot ^ swz_dual<D>(r)) * 8, dst + base);
-  }
-}
+// Loop-invariant per-lane offsets of one wave.
+template <int D>
+struct KVAddr {
+  int qcopy[KVCfg<D>::QPER];           // source offsets of this wave's Q / dO tile copies
+  int row[KVCfg<D>::NSTEP];            // row reads of the wave's 32 queries, per K-step
+  int tr[KVCfg<D>::NDB][2];            // transposing reads (t = 2*qh), per column block and half
+  int kv;                              // row reads of the wave's 32 keys in the padded K/V block
+};
 
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void kv_tile(KVState<D>& st, const char* kblk, const char* vblk, const char* qbuf,
-                                        const char* dobuf, const float* stats, int q0, int L, int window,
-                                        int kb, int qh, int key_w0, float c, int lane) {
+__device__ __forceinline__ void kv_tile(KVState<D>& st, const KVAddr<D>& ad, const char* kblk, const char* vblk,
+                                        const char* qbuf, const char* dobuf, const float* stats, int q0, int L,
+                                        int window, int qh, int key_w0, float c, int lane) {
   using C = KVCfg<D>;
-  const int g = lane >> 5, ln = lane & 31;
-  const int my_key = key_w0 + ln;
-  const int qr = 32 * qh + ln;            // this lane's query row of the tile, as an A-operand row
-  const int kr = 32 * kb + ln;            // this lane's key row of the K/V block, as a B-operand row
+  const int g = lane >> 5;
+  const int my_key = key_w0 + (lane & 31);
 
   // S = Q K^T (32 queries x 32 keys): lane = key, registers = queries
-  f32x16 p = f32x16{};
+  f32x16 p = mfma32(lds_load16(qbuf, ad.row[0]), lds_load16(kblk, ad.kv), f32x16{});
 #pragma unroll
-  for (int k = 0; k < C::NSTEP; ++k)
-    p = mfma32(lds_load16(qbuf, row_offset_dual<D>(qr, k, g)), lds_load16(kblk, row_offset_k<D>(kr, k, g)), p);
+  for (int k = 1; k < C::NSTEP; ++k)
+    p = mfma32(lds_load16(qbuf, ad.row[k]), lds_load16(kblk, ad.kv + 32 * k), p);
 
   // P = exp2(S*s*log2e - LSE*log2e), zero where masked
   const int qw0 = q0 + 32 * qh;           // first query of this wave's half
@@ -182,16 +140,16 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const char* kblk, const 
     const bf16x8 pa = to_bf16x8(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5], p[o8 + 6], p[o8 + 7]);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const bf16x8 bo = concat4(lds_load_tr(dobuf, tr_offset_dual<D>(2 * qh + u, db, 0, lane)),
-                                lds_load_tr(dobuf, tr_offset_dual<D>(2 * qh + u, db, 1, lane)));
+      const bf16x8 bo = concat4(lds_load_tr(dobuf, ad.tr[db][0] + u * 16 * (2 * D)),
+                                lds_load_tr(dobuf, ad.tr[db][1] + u * 16 * (2 * D)));
       st.dv[db] = mfma32(pa, bo, st.dv[db]);
     }
   }
   // dP = dO V^T, then dS = P * (dP - D) in place
-  f32x16 dp = f32x16{};
+  f32x16 dp = mfma32(lds_load16(dobuf, ad.row[0]), lds_load16(vblk, ad.kv), f32x16{});
 #pragma unroll
-  for (int k = 0; k < C::NSTEP; ++k)
-    dp = mfma32(lds_load16(dobuf, row_offset_dual<D>(qr, k, g)), lds_load16(vblk, row_offset_k<D>(kr, k, g)), dp);
+  for (int k = 1; k < C::NSTEP; ++k)
+    dp = mfma32(lds_load16(dobuf, ad.row[k]), lds_load16(vblk, ad.kv + 32 * k), dp);
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
     const f32x4 d4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (C::BQ + 32 * qh + 8 * i4 + 4 * g));
@@ -205,8 +163,8 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const char* kblk, const 
     const bf16x8 da = to_bf16x8(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5], p[o8 + 6], p[o8 + 7]);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const bf16x8 bq = concat4(lds_load_tr(qbuf, tr_offset_dual<D>(2 * qh + u, db, 0, lane)),
-                                lds_load_tr(qbuf, tr_offset_dual<D>(2 * qh + u, db, 1, lane)));
+      const bf16x8 bq = concat4(lds_load_tr(qbuf, ad.tr[db][0] + u * 16 * (2 * D)),
+                                lds_load_tr(qbuf, ad.tr[db][1] + u * 16 * (2 * D)));
       st.dk[db] = mfma32(da, bq, st.dk[db]);
     }
   }
@@ -217,8 +175,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = KVCfg<D>;
   // distinct LDS objects per stage so reads of one stage need not wait for the
   // direct copies into the other (alias scopes)
-  __shared__ __attribute__((aligned(1024))) char k_blk[C::KT];
-  __shared__ __attribute__((aligned(1024))) char v_blk[C::KT];
+  __shared__ __attribute__((aligned(1024))) char k_blk[C::KB];
+  __shared__ __attribute__((aligned(1024))) char v_blk[C::KB];
   __shared__ __attribute__((aligned(1024))) char q_st0[C::QT];
   __shared__ __attribute__((aligned(1024))) char do_st0[C::QT];
   __shared__ __attribute__((aligned(1024))) char q_st1[C::QT];
@@ -241,8 +199,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int key_w0 = key_wg0 + 32 * kb;
 
   const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
-  const bf16* __restrict__ Kh = reinterpret_cast<const bf16*>(a.k) + kv_off;
-  const bf16* __restrict__ Vh = reinterpret_cast<const bf16*>(a.v) + kv_off;
+  const unsigned head_bytes = (unsigned)L * (2 * D);
 
   // queries that can see this work-group's keys
   const int q_begin = CAUSAL ? key_wg0 : 0;
@@ -251,21 +208,51 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int nq = qt_hi - qt_lo + 1;
   const int n_it = G * nq;
 
+  KVAddr<D> ad;
+#pragma unroll
+  for (int i = 0; i < C::QPER; ++i) ad.qcopy[i] = dual_slot_src<D>((wave + C::kWaves * i) * 64 + lane);
+#pragma unroll
+  for (int k = 0; k < C::NSTEP; ++k) ad.row[k] = row_offset_dual<D>(32 * qh + ln, k, g);
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    ad.tr[db][0] = tr_offset_dual<D>(2 * qh, db, 0, lane);
+    ad.tr[db][1] = tr_offset_dual<D>(2 * qh, db, 1, lane);
+  }
+  ad.kv = row_offset_kpad<D>(32 * kb + ln, 0, g);
+
   auto q0_of = [&](int it) { return (qt_lo + it % nq) * C::BQ; };
   auto issue = [&](int it, char* qs, char* dos, float* ss) {
     const int hq = hk * G + it / nq, q0 = q0_of(it);
     const size_t qoff = ((size_t)(b * a.Hq + hq) * L) * D;
-    issue_rows8<D, C::BQ>(reinterpret_cast<const bf16*>(a.q) + qoff, q0, L, qs, wave, lane);
-    issue_rows8<D, C::BQ>(reinterpret_cast<const bf16*>(a.dout) + qoff, q0, L, dos, wave, lane);
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(reinterpret_cast<const bf16*>(a.q) + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(reinterpret_cast<const bf16*>(a.dout) + qoff, head_bytes);
+    const int soff = q0 * (2 * D);
+#pragma unroll
+    for (int i = 0; i < C::QPER; ++i) {
+      buf2lds16(qrs, ad.qcopy[i], soff, qs + (wave + C::kWaves * i) * 1024);
+      buf2lds16(drs, ad.qcopy[i], soff, dos + (wave + C::kWaves * i) * 1024);
+    }
     if (wave == 0) {
-      const size_t srow = (size_t)(b * a.Hq + hq) * L + min(q0 + lane, L - 1);
-      g2lds4(a.lse2 + srow, reinterpret_cast<char*>(ss));
-      g2lds4(a.delta + srow, reinterpret_cast<char*>(ss) + 4 * C::BQ);
+      const size_t srow = (size_t)(b * a.Hq + hq) * L;
+      const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.lse2 + srow, (unsigned)L * 4);
+      const __amdgpu_buffer_rsrc_t ers = make_rsrc(a.delta + srow, (unsigned)L * 4);
+      buf2lds4(lrs, 4 * lane, 4 * q0, reinterpret_cast<char*>(ss));
+      buf2lds4(ers, 4 * lane, 4 * q0, reinterpret_cast<char*>(ss) + 4 * C::BQ);
     }
   };
 
-  issue_rows_k<D, C::BK>(Kh, key_wg0, L, k_blk, wave, lane);
-  issue_rows_k<D, C::BK>(Vh, key_wg0, L, v_blk, wave, lane);
+  // the work-group's K and V rows, once (padded layout; rows past L read zeros)
+  {
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kv_off, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16*>(a.v) + kv_off, head_bytes);
+    const int soff = key_wg0 * (2 * D);
+#pragma unroll
+    for (int n = wave; n < C::KBCOPIES; n += C::kWaves) {
+      const int src = pad_slot_src<D, Pad<D>::KSTR>(n * 64 + lane);
+      buf2lds16(krs, src, soff, k_blk + n * 1024);
+      buf2lds16(vrs, src, soff, v_blk + n * 1024);
+    }
+  }
   issue(0, q_st0, do_st0, stat_st0);
 
   KVState<D> st;
@@ -284,12 +271,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   for (int it = 0; it < n_it; it += 2) {
     if (it + 1 < n_it) issue(it + 1, q_st1, do_st1, stat_st1);
     if (wave_needs(q0_of(it)))
-      kv_tile<D, CAUSAL>(st, k_blk, v_blk, q_st0, do_st0, stat_st0, q0_of(it), L, window, kb, qh, key_w0, c, lane);
+      kv_tile<D, CAUSAL>(st, ad, k_blk, v_blk, q_st0, do_st0, stat_st0, q0_of(it), L, window, qh, key_w0, c, lane);
     wait_copies_and_barrier();
     if (it + 1 >= n_it) break;
     if (it + 2 < n_it) issue(it + 2, q_st0, do_st0, stat_st0);
     if (wave_needs(q0_of(it + 1)))
-      kv_tile<D, CAUSAL>(st, k_blk, v_blk, q_st1, do_st1, stat_st1, q0_of(it + 1), L, window, kb, qh, key_w0, c, lane);
+      kv_tile<D, CAUSAL>(st, ad, k_blk, v_blk, q_st1, do_st1, stat_st1, q0_of(it + 1), L, window, qh, key_w0, c, lane);
     wait_copies_and_barrier();
   }
 
@@ -341,14 +328,25 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------ 3. dQ
 
+// One work-group of 4 waves per (batch, query head, 128 queries), mirroring the
+// forward.  The streamed K tile is read row-wise (S^T = K Q^T) and by the
+// transposing read (dQ^T = K^T dS^T), so it uses the swz_dual layout; the V
+// tile is only read row-wise (dP^T = V dO^T) and is padded.  The two 32-key
+// halves of a tile are processed one after the other to keep registers low.
 template <int D>
 struct QCfg {
   static constexpr int kWaves = 4;
-  static constexpr int BQ = 32 * kWaves;   // queries per work-group
-  static constexpr int BC = 64;            // keys per streamed tile
-  static constexpr int KT = BC * D * 2;    // bytes of a K (or V) tile
+  static constexpr int BQ = 32 * kWaves;         // queries per work-group
+  static constexpr int BC = 64;                  // keys per streamed tile
+  static constexpr int KT = BC * D * 2;          // bytes of a K tile (swz_dual)
+  static constexpr int VT = BC * Pad<D>::KSTR;   // bytes of a padded V tile
+  static constexpr int KCOPIES = KT / 1024;
+  static constexpr int VCOPIES = VT / 1024;
+  static constexpr int KPER = KCOPIES / kWaves;
+  static constexpr int VPER = (VCOPIES + kWaves - 1) / kWaves;
   static constexpr int NSTEP = D / 16;
   static constexpr int NDB = D / 32;
+  static_assert(KCOPIES % kWaves == 0 && VT % 1024 == 0, "tiles must split into whole wave copies");
 };
 
 template <int D>
@@ -359,58 +357,59 @@ struct QState {
   float lse2, dlt;              // this lane's query statistics
 };
 
+template <int D>
+struct QAddr {
+  int kcopy[QCfg<D>::KPER];     // source offsets of this wave's K tile copies (swz_dual)
+  int vcopy[QCfg<D>::VPER];     // source offsets of this wave's V tile copies (padded)
+  int krow[QCfg<D>::NSTEP];     // row reads of K rows ln (+32 per key half), per K-step
+  int ktr[QCfg<D>::NDB][2];     // transposing reads of K (t = 0), per column block and half
+  int vrow;                     // row reads of padded V rows ln (+32 per key half)
+};
+
 template <int D, bool CAUSAL>
-__device__ __forceinline__ void q_tile(QState<D>& st, const char* kbuf, const char* vbuf, int k0, int L, int window,
-                                       int my_q, int q_w0, int wq_hi, float c, int lane) {
+__device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const char* kbuf, const char* vbuf, int k0,
+                                       int L, int window, int my_q, int q_w0, int wq_hi, float c, int lane) {
   using C = QCfg<D>;
-  const int g = lane >> 5, ln = lane & 31;
-  // S^T = K Q^T: lane = query, registers = keys
-  f32x16 p[2];
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    f32x16 s = f32x16{};
-#pragma unroll
-    for (int k = 0; k < C::NSTEP; ++k)
-      s = mfma32(lds_load16(kbuf, row_offset_dual<D>(32 * kb + ln, k, g)), st.qr[k], s);
-    p[kb] = s;
-  }
+  const int g = lane >> 5;
   const bool need_mask = (k0 + C::BC > L) || (CAUSAL && k0 + C::BC - 1 > q_w0) ||
                          (window > 0 && k0 < wq_hi - window + 1);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
+    // S^T = K Q^T for keys 32kb..32kb+31: lane = query, registers = keys
+    f32x16 p = mfma32(lds_load16(kbuf, ad.krow[0] + kb * 32 * (2 * D)), st.qr[0], f32x16{});
+#pragma unroll
+    for (int k = 1; k < C::NSTEP; ++k)
+      p = mfma32(lds_load16(kbuf, ad.krow[k] + kb * 32 * (2 * D)), st.qr[k], p);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float pv = fast_exp2(fmaf(p[kb][i], c, -st.lse2));
+      float pv = fast_exp2(fmaf(p[i], c, -st.lse2));
       if (need_mask) {
         const int kk = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
         const bool ok = kk < L && (!CAUSAL || kk <= my_q) && (window <= 0 || kk > my_q - window);
         pv = ok ? pv : 0.f;
       }
-      p[kb][i] = pv;
+      p[i] = pv;
     }
-  }
-  // dP^T = V dO^T, dS^T = P^T * (dP^T - D)
+    // dP^T = V dO^T, dS^T = P^T * (dP^T - D)
+    f32x16 dp = mfma32(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR), st.dor[0], f32x16{});
 #pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    f32x16 dp = f32x16{};
+    for (int k = 1; k < C::NSTEP; ++k)
+      dp = mfma32(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR + 32 * k), st.dor[k], dp);
 #pragma unroll
-    for (int k = 0; k < C::NSTEP; ++k)
-      dp = mfma32(lds_load16(vbuf, row_offset_dual<D>(32 * kb + ln, k, g)), st.dor[k], dp);
+    for (int i = 0; i < 16; ++i) p[i] *= dp[i] - st.dlt;
+    // dQ^T += K^T dS^T: A = K^T via the transposing read, B = dS^T (lane = query)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[kb][i] *= dp[i] - st.dlt;
-  }
-  // dQ^T += K^T dS^T: A = K^T via the transposing read, B = dS^T (lane = query)
+    for (int u = 0; u < 2; ++u) {
+      const int o8 = 8 * u;
+      const int t = 2 * kb + u;
+      const bf16x8 db8 = to_bf16x8(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5],
+                                   p[o8 + 6], p[o8 + 7]);
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const f32x16& pp = p[t >> 1];
-    const int o8 = 8 * (t & 1);
-    const bf16x8 db8 = to_bf16x8(pp[o8 + 0], pp[o8 + 1], pp[o8 + 2], pp[o8 + 3], pp[o8 + 4], pp[o8 + 5],
-                                 pp[o8 + 6], pp[o8 + 7]);
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      const bf16x8 ka = concat4(lds_load_tr(kbuf, tr_offset_dual<D>(t, db, 0, lane)),
-                                lds_load_tr(kbuf, tr_offset_dual<D>(t, db, 1, lane)));
-      st.dq[db] = mfma32(ka, db8, st.dq[db]);
+      for (int db = 0; db < C::NDB; ++db) {
+        const bf16x8 ka = concat4(lds_load_tr(kbuf, ad.ktr[db][0] + t * 16 * (2 * D)),
+                                  lds_load_tr(kbuf, ad.ktr[db][1] + t * 16 * (2 * D)));
+        st.dq[db] = mfma32(ka, db8, st.dq[db]);
+      }
     }
   }
 }
@@ -419,9 +418,9 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   using C = QCfg<D>;
   __shared__ __attribute__((aligned(1024))) char k_st0[C::KT];
-  __shared__ __attribute__((aligned(1024))) char v_st0[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st0[C::VT];
   __shared__ __attribute__((aligned(1024))) char k_st1[C::KT];
-  __shared__ __attribute__((aligned(1024))) char v_st1[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st1[C::VT];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 5, ln = lane & 31;
@@ -436,8 +435,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const size_t q_off = ((size_t)(b * a.Hq + h) * L) * D;
   const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
-  const bf16* __restrict__ Kh = reinterpret_cast<const bf16*>(a.k) + kv_off;
-  const bf16* __restrict__ Vh = reinterpret_cast<const bf16*>(a.v) + kv_off;
+  const unsigned head_bytes = (unsigned)L * (2 * D);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16*>(a.v) + kv_off, head_bytes);
 
   const int q_wg0 = qt * C::BQ;
   const int q_w0 = q_wg0 + 32 * wave;
@@ -448,8 +448,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int kv_begin = (window > 0) ? max(0, q_wg0 - window + 1) : 0;
   const int j_lo = kv_begin / C::BC, j_hi = (kv_end - 1) / C::BC;
 
-  issue_rows<D, C::BC>(Kh, j_lo * C::BC, L, k_st0, wave, lane);
-  issue_rows<D, C::BC>(Vh, j_lo * C::BC, L, v_st0, wave, lane);
+  QAddr<D> ad;
+#pragma unroll
+  for (int i = 0; i < C::KPER; ++i) ad.kcopy[i] = dual_slot_src<D>((wave + C::kWaves * i) * 64 + lane);
+#pragma unroll
+  for (int i = 0; i < C::VPER; ++i) ad.vcopy[i] = pad_slot_src<D, Pad<D>::KSTR>((wave + C::kWaves * i) * 64 + lane);
+#pragma unroll
+  for (int k = 0; k < C::NSTEP; ++k) ad.krow[k] = row_offset_dual<D>(ln, k, g);
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    ad.ktr[db][0] = tr_offset_dual<D>(0, db, 0, lane);
+    ad.ktr[db][1] = tr_offset_dual<D>(0, db, 1, lane);
+  }
+  ad.vrow = row_offset_kpad<D>(ln, 0, g);
+
+  auto issue = [&](int j, char* kb, char* vb) {
+    const int soff = j * C::BC * (2 * D);
+#pragma unroll
+    for (int i = 0; i < C::KPER; ++i) buf2lds16(krs, ad.kcopy[i], soff, kb + (wave + C::kWaves * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < C::VPER; ++i)
+      if (wave + C::kWaves * i < C::VCOPIES) buf2lds16(vrs, ad.vcopy[i], soff, vb + (wave + C::kWaves * i) * 1024);
+  };
+  issue(j_lo, k_st0, v_st0);
 
   QState<D> st;
   {
@@ -474,20 +495,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   wait_copies_and_barrier();
   for (int j = j_lo; j <= j_hi; j += 2) {
-    if (j < j_hi) {
-      issue_rows<D, C::BC>(Kh, (j + 1) * C::BC, L, k_st1, wave, lane);
-      issue_rows<D, C::BC>(Vh, (j + 1) * C::BC, L, v_st1, wave, lane);
-    }
+    if (j < j_hi) issue(j + 1, k_st1, v_st1);
     if (wave_needs(j * C::BC))
-      q_tile<D, CAUSAL>(st, k_st0, v_st0, j * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+      q_tile<D, CAUSAL>(st, ad, k_st0, v_st0, j * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
     wait_copies_and_barrier();
     if (j + 1 > j_hi) break;
-    if (j + 1 < j_hi) {
-      issue_rows<D, C::BC>(Kh, (j + 2) * C::BC, L, k_st0, wave, lane);
-      issue_rows<D, C::BC>(Vh, (j + 2) * C::BC, L, v_st0, wave, lane);
-    }
+    if (j + 1 < j_hi) issue(j + 2, k_st0, v_st0);
     if (wave_needs((j + 1) * C::BC))
-      q_tile<D, CAUSAL>(st, k_st1, v_st1, (j + 1) * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+      q_tile<D, CAUSAL>(st, ad, k_st1, v_st1, (j + 1) * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
     wait_copies_and_barrier();
   }
 

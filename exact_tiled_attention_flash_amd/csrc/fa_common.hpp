@@ -63,6 +63,11 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, int voff, in
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)(lds_wave_base), 16, voff, soff, 0, 0);
 }
 
+// Same with 4 bytes per lane: lane l's dword lands at lds_wave_base + 4*l.
+__device__ __forceinline__ void buf2lds4(__amdgpu_buffer_rsrc_t r, int voff, int soff, char* lds_wave_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA_LDS void*)(lds_wave_base), 4, voff, soff, 0, 0);
+}
+
 // Value of x in lane l XOR 32 combined with x by op -- both halves of the wave
 // end up with op(x[l % 32], x[l % 32 + 32]).  One v_permlane32_swap.
 __device__ __forceinline__ float pair_max(float x) {
@@ -183,6 +188,15 @@ __host__ __device__ __forceinline__ int tr_offset_dual(int t, int db, int h, int
   const int row = 16 * t + 8 * h + 4 * (lane >> 5) + (s16 >> 2);
   const int col = 32 * db + 16 * (jg & 1) + 4 * (s16 & 3);
   return row * (2 * D) + (((col >> 3) ^ swz_dual<D>(row)) << 4) + ((col & 4) << 1);
+}
+
+// Source of 16-byte slot p of a [rows x D] tile stored with swz_dual: byte
+// offset, relative to the tile's first row, of the chunk that belongs there.
+template <int D>
+__host__ __device__ __forceinline__ int dual_slot_src(int p) {
+  constexpr int kChunks = D / 8;
+  const int r = p / kChunks, slot = p % kChunks;
+  return r * (2 * D) + (slot ^ swz_dual<D>(r)) * 16;
 }
 
 // Byte offset of the 16 bytes (head dims 16k + 8g .. +7) of row r in a tile

@@ -11,7 +11,9 @@
 
 namespace {
 
-constexpr int kMaxL = 1 << 24;  // keeps row * d in 32 bits inside the kernels
+// keeps the byte size of one head (L * 2d, d <= 128) in 32 bits: the kernels
+// address each head through a buffer resource with a 32-bit range
+constexpr int kMaxL = 1 << 23;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 

@@ -76,6 +76,7 @@ extern "C" {
  *   window                          : 0 = none; w >= 1 requires causal = 1
  *   dtype                           : FA_DTYPE_BF16 (d in {64,128}) or
  *                                     FA_DTYPE_F32  (d in {64,128})
+ * Sizes: 1 <= L <= 2^23 (one head must stay below 4 GiB), B, Hq, Hkv >= 1.
  * Extra device memory: none.  Returns FA_OK or a negative FA_ERR_* code.
  */
 int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -133,6 +133,18 @@ void check_all() {
   // backward dK/dV: the work-group's 128-row K and V blocks (row reads)
   auto kblk = tile_image<D>(128, [](int r) { return swz_k<D>(r); });
   check_row_reads<D>("bwd K/V block", kblk, 128, [](int r, int k, int g) { return row_offset_k<D>(r, k, g); });
+  // backward: the copy mapping of swz_dual tiles matches the modelled layout
+  {
+    auto dimg2 = tile_image<D>(64, [](int r) { return swz_dual<D>(r); });
+    for (int p = 0; p < 64 * D / 8; ++p)
+      for (int e = 0; e < 8; ++e)
+        CHECK(dimg2[p * 8 + e] == dual_slot_src<D>(p) / 2 + e, "dual_slot_src D=%d slot %d", D, p);
+  }
+  // backward: padded 128-row K/V block of the dK/dV kernel and padded V tile of the dQ kernel
+  {
+    auto kb = padded_image<D, Pad<D>::KSTR>(128);
+    check_row_reads<D>("bwd K/V block padded", kb, 128, [](int r, int k, int g) { return row_offset_kpad<D>(r, k, g); });
+  }
   // backward: tiles read both ways
   auto dimg = tile_image<D>(64, [](int r) { return swz_dual<D>(r); });
   check_row_reads<D>("bwd dual", dimg, 64, [](int r, int k, int g) { return row_offset_dual<D>(r, k, g); });

@@ -79,7 +79,7 @@ def test_fwd_rejects_invalid_arguments(lib):
     assert call_fwd(lib, o=None) == INV
     assert call_fwd(lib, k=MISALIGNED) == INV
     assert call_fwd(lib, lse=MISALIGNED) == INV
-    for bad in (dict(B=0), dict(Hq=0), dict(Hkv=0), dict(L=0), dict(L=-3), dict(L=(1 << 24) + 1),
+    for bad in (dict(B=0), dict(Hq=0), dict(Hkv=0), dict(L=0), dict(L=-3), dict(L=(1 << 23) + 1),
                 dict(scale=0.0), dict(scale=-1.0), dict(scale=float("inf")), dict(scale=float("nan")),
                 dict(causal=2), dict(window=-1)):
         assert call_fwd(lib, **bad) == INV, bad
