@@ -143,57 +143,70 @@ def main():
     q, k, v, do = (t.to(dev) for t in (q, k, v, do))
     o = torch.empty_like(q)
     lse = torch.empty(w.B, w.Hq, w.L, dtype=torch.float32, device=dev)
-    have_bwd = True
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(fa.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.L, w.d), dtype=torch.uint8, device=dev)
 
     def run_fwd():
         fa.fwd(q, k, v, causal=True, scale=w.scale, out=o, lse=lse)
 
-    def run_bwd():
-        fa.bwd(q, k, v, o, lse, do, causal=True, scale=w.scale, workspace=ws, dq=dq, dk=dk, dv=dv)
+    def run_bwd(between=None):
+        fa.bwd_stages(q, k, v, o, lse, do, causal=True, scale=w.scale, workspace=ws, dq=dq, dk=dk, dv=dv,
+                      between=between)
 
     run_fwd()
-    try:
-        run_bwd()
-    except RuntimeError as e:
-        print("backward unavailable, timing forward only:", e, file=sys.stderr)
-        have_bwd = False
+    run_bwd()
     torch.cuda.synchronize()
-
     for _ in range(args.warmup):
         run_fwd()
-        if have_bwd:
-            run_bwd()
+        run_bwd()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # One step = forward + the three backward stages, each launch bracketed by
+    # HIP events on the stream it runs on (torch's current stream).
+    names = ("fwd", "preprocess", "dkdv", "dq")
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record()
     for i in range(args.steps):
-        ev[i][0].record()
+        e = ev[i]
+        e[0].record()
         run_fwd()
-        ev[i][1].record()
-        if have_bwd:
-            run_bwd()
-        ev[i][2].record()
+        e[1].record()
+        marks = iter(e[2:])
+        run_bwd(between=lambda _name: next(marks).record())
     t_end.record()
     torch.cuda.synchronize()
 
     total_ms = t_start.elapsed_time(t_end)
-    f_ms = [e[0].elapsed_time(e[1]) for e in ev]
-    b_ms = [e[1].elapsed_time(e[2]) for e in ev] if have_bwd else []
+    per = {n: [e[j].elapsed_time(e[j + 1]) for e in ev] for j, n in enumerate(names)}
+    avg = {n: sum(x) / len(x) for n, x in per.items()}
+    med = {n: sorted(x)[len(x) // 2] for n, x in per.items()}
     ms_step = total_ms / args.steps
     ff = fwd_flops(w.B, w.Hq, w.L, w.d, True, 0)
-    bf = bwd_flops(w.B, w.Hq, w.L, w.d, True, 0) if have_bwd else 0.0
-    f_avg = sum(f_ms) / len(f_ms)
-    b_avg = sum(b_ms) / len(b_ms) if b_ms else None
-    f_med = sorted(f_ms)[len(f_ms) // 2]
+    bf = bwd_flops(w.B, w.Hq, w.L, w.d, True, 0)
     value = (ff + bf) / (ms_step * 1e-3) / 1e12
-
-    fwd_tf = ff / (f_avg * 1e-3) / 1e12
+    f_ms = avg["fwd"]
+    b_ms = avg["preprocess"] + avg["dkdv"] + avg["dq"]
+    fwd_tf = ff / (f_ms * 1e-3) / 1e12
+    bwd_tf = bf / (b_ms * 1e-3) / 1e12
+    # Algorithmic work per launch.  The backward's five L x L x d products
+    # (2.5x the forward) split as: dK/dV kernel -- S recomputation, dV, dP, dK
+    # (4 products); dQ kernel -- dQ (1 product; it also recomputes S and dP,
+    # which are not counted again).  The preprocess is HBM-bound: it reads O
+    # and dO and writes two floats per row.
+    one = ff / 2
+    alg = {"fwd": ("mfma", 2 * one), "dkdv": ("mfma", 4 * one), "dq": ("mfma", 1 * one),
+           "preprocess": ("hbm", 2 * w.B * w.Hq * w.L * w.d * 2 + 3 * w.B * w.Hq * w.L * 4)}
+    dom = max(avg, key=avg.get)
+    kernel_names = {"fwd": "fwd_bf16_kernel<128,causal>", "preprocess": "bwd_delta_kernel<128>",
+                    "dkdv": "bwd_dkdv_kernel<128,causal>", "dq": "bwd_dq_kernel<128,causal>"}
+    bound, work = alg[dom]
+    if bound == "mfma":
+        achieved, peak, unit = work / (avg[dom] * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = work / (avg[dom] * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -207,23 +220,19 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "llama7b-shaped attention layer fwd+bwd" if have_bwd else
-                   "llama7b-shaped attention layer fwd only",
+        "config": {"workload": "llama7b-shaped attention layer fwd+bwd",
                    "B": w.B, "Hq": w.Hq, "Hkv": w.Hkv, "L": w.L, "d": w.d, "causal": True,
                    "window": 0, "inputs": "seeded N(0,1) bf16, resident in HBM"},
-        "fwd": {"ms_mean": round(f_avg, 4), "ms_median": round(f_med, 4),
+        "fwd": {"ms_mean": round(f_ms, 4), "ms_median": round(med["fwd"], 4),
                 "tflops": round(fwd_tf, 2), "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms_mean": round(b_ms, 4), "tflops": round(bwd_tf, 2),
+                "frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "kernels_ms_mean": {n: round(avg[n], 4) for n in names},
+        "roofline": {"kernel": kernel_names[dom], "bound": bound, "achieved": round(achieved, 2),
+                     "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": load_traffic(kernel_names[dom]),
+                     "algorithmic_per_launch": work},
     }
-    if have_bwd:
-        bwd_tf = bf / (b_avg * 1e-3) / 1e12
-        out["bwd"] = {"ms_mean": round(b_avg, 4), "ms_median": round(sorted(b_ms)[len(b_ms) // 2], 4),
-                      "tflops": round(bwd_tf, 2), "frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4)}
-    # the forward kernel: one launch per fwd call, timed on the stream it runs on
-    traffic = load_traffic("fwd_bf16_d128_causal")
-    out["roofline"] = {"kernel": "fwd_bf16_kernel<128,causal>", "bound": "mfma",
-                       "achieved": round(fwd_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                       "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                       "algorithmic_bytes": fwd_bytes(w.B, w.Hq, w.Hkv, w.L, w.d)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -19,7 +19,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "strerror", "library", "library_path",
+__all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "strerror", "library", "library_path",
            "FA_DTYPE_F32", "FA_DTYPE_BF16", "EXPORTED_SYMBOLS"]
 
 FA_DTYPE_F32 = 0
@@ -27,6 +27,7 @@ FA_DTYPE_BF16 = 1
 _DTYPES = {torch.float32: FA_DTYPE_F32, torch.bfloat16: FA_DTYPE_BF16}
 
 EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_bytes",
+                    "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
                     "flash_attn_strerror", "flash_attn_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +55,12 @@ def library():
     lib.flash_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                    i, i, i, i, i, f, i, i, i, vp]
     lib.flash_attn_bwd.restype = i
+    lib.flash_attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, i, i, vp]
+    lib.flash_attn_bwd_preprocess.restype = i
+    lib.flash_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    lib.flash_attn_bwd_dkdv.restype = i
+    lib.flash_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, i, i, i, vp]
+    lib.flash_attn_bwd_dq.restype = i
     lib.flash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.flash_attn_bwd_workspace_bytes.restype = sz
     lib.flash_attn_strerror.argtypes = [i]
@@ -143,4 +150,35 @@ def bwd(q, k, v, o, lse, dout, causal=False, window=0, scale=None, workspace=Non
                                   B, Hq, Hkv, L, d, scale, int(bool(causal)), int(window),
                                   _DTYPES[q.dtype], _stream(q))
     _check(rc, "flash_attn_bwd")
+    return dq, dk, dv
+
+
+def bwd_stages(q, k, v, o, lse, dout, causal=False, window=0, scale=None, workspace=None,
+               dq=None, dk=None, dv=None, between=None):
+    """The backward as its three exported stages (preprocess, dK/dV, dQ) on the
+    current stream; same results as ``bwd``.  ``between(stage_name)`` is called
+    after each launch (for example to record timing events)."""
+    B, Hq, Hkv, L, d = _shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = bwd_workspace_bytes(B, Hq, Hkv, L, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    lib, dt, st, c = library(), _DTYPES[q.dtype], _stream(q), int(bool(causal))
+    _check(lib.flash_attn_bwd_preprocess(_ptr(o), _ptr(lse), _ptr(dout), _ptr(workspace), workspace.numel(),
+                                         B, Hq, Hkv, L, d, dt, st), "flash_attn_bwd_preprocess")
+    if between:
+        between("preprocess")
+    _check(lib.flash_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(workspace), workspace.numel(),
+                                   _ptr(dk), _ptr(dv), B, Hq, Hkv, L, d, scale, c, int(window), dt, st),
+           "flash_attn_bwd_dkdv")
+    if between:
+        between("dkdv")
+    _check(lib.flash_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(workspace), workspace.numel(),
+                                 _ptr(dq), B, Hq, Hkv, L, d, scale, c, int(window), dt, st),
+           "flash_attn_bwd_dq")
+    if between:
+        between("dq")
     return dq, dk, dv

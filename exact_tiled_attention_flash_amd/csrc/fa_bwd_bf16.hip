@@ -525,34 +525,56 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch(const BwdArgs& args, hipStream_t stream) {
-  BwdArgs a = args;
+template <int D>
+hipError_t launch_delta(const BwdArgs& a, hipStream_t stream) {
   const long long rows = (long long)a.B * a.Hq * a.L;
   constexpr int kRowsPerBlock = 256 / (D / 8);
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
                      dim3(256), 0, stream, reinterpret_cast<const bf16*>(a.o),
                      reinterpret_cast<const bf16*>(a.dout), a.lse, a.delta, a.lse2, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
 
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv(const BwdArgs& args, hipStream_t stream) {
+  BwdArgs a = args;
   a.n_tiles = (a.L + KVCfg<D>::BK - 1) / KVCfg<D>::BK;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((long long)a.B * a.Hkv * a.n_tiles)),
                      dim3(64 * KVCfg<D>::kWaves), 0, stream, a);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
 
+template <int D, bool CAUSAL>
+hipError_t launch_dq(const BwdArgs& args, hipStream_t stream) {
+  BwdArgs a = args;
   a.n_tiles = (a.L + QCfg<D>::BQ - 1) / QCfg<D>::BQ;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)a.B * a.Hq * a.n_tiles)),
-                     dim3(256), 0, stream, a);
+                     dim3(64 * QCfg<D>::kWaves), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
+hipError_t launch_bwd_preprocess_bf16(const BwdArgs& a, hipStream_t stream) {
+  return a.d == 128 ? launch_delta<128>(a, stream) : launch_delta<64>(a, stream);
+}
+
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, bool causal, hipStream_t stream) {
+  if (a.d == 128) return causal ? launch_dkdv<128, true>(a, stream) : launch_dkdv<128, false>(a, stream);
+  return causal ? launch_dkdv<64, true>(a, stream) : launch_dkdv<64, false>(a, stream);
+}
+
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, bool causal, hipStream_t stream) {
+  if (a.d == 128) return causal ? launch_dq<128, true>(a, stream) : launch_dq<128, false>(a, stream);
+  return causal ? launch_dq<64, true>(a, stream) : launch_dq<64, false>(a, stream);
+}
+
 hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream) {
-  if (a.d == 128) return causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
-  return causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+  hipError_t e = launch_bwd_preprocess_bf16(a, stream);
+  if (e != hipSuccess) return e;
+  e = launch_bwd_dkdv_bf16(a, causal, stream);
+  if (e != hipSuccess) return e;
+  return launch_bwd_dq_bf16(a, causal, stream);
 }
 
 }  // namespace fa

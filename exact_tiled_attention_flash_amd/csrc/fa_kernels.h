@@ -39,5 +39,9 @@ struct BwdArgs {
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
+// the three stages of launch_bwd_bf16, in order (stage 2 and 3 are independent)
+hipError_t launch_bwd_preprocess_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dq_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
 
 }  // namespace fa

@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <initializer_list>
+
 #include "../../include/flash_attn.h"
 #include "fa_kernels.h"
 
@@ -65,32 +67,83 @@ extern "C" size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, 
   return workspace_bytes(B, Hq, L);
 }
 
+namespace {
+
+// Common validation of the backward entry points; fills the kernel arguments.
+int bwd_setup(fa::BwdArgs& a, const void* workspace, size_t ws_bytes, int B, int Hq, int Hkv, int L, int d,
+              float scale, int causal, int window, int dtype) {
+  int rc = check_common(B, Hq, Hkv, L, d, scale, causal, window, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || ws_bytes < workspace_bytes(B, Hq, L))
+    return FA_ERR_WORKSPACE;
+  a.delta = static_cast<float*>(const_cast<void*>(workspace));
+  a.lse2 = a.delta + (size_t)B * Hq * L;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.d = d;
+  a.window = window;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  return FA_OK;
+}
+
+bool all_aligned(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return false;
+  return true;
+}
+
+}  // namespace
+
 extern "C" int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                               const void* dout, void* dq, void* dk, void* dv,
                               void* workspace, size_t workspace_bytes,
                               int B, int Hq, int Hkv, int L, int d,
                               float softmax_scale, int causal, int window, int dtype, void* stream) {
-  int rc = check_common(B, Hq, Hkv, L, d, softmax_scale, causal, window, dtype);
-  if (rc != FA_OK) return rc;
-  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
-  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_INVALID_ARG;
-  const void* ptrs[] = {q, k, v, o, lse, dout, dq, dk, dv};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return FA_ERR_INVALID_ARG;
-  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
-      workspace_bytes < ::workspace_bytes(B, Hq, L))
-    return FA_ERR_WORKSPACE;
-
   fa::BwdArgs a{};
+  int rc = bwd_setup(a, workspace, workspace_bytes, B, Hq, Hkv, L, d, softmax_scale, causal, window, dtype);
+  if (rc != FA_OK) return rc;
+  if (!all_aligned({q, k, v, o, lse, dout, dq, dk, dv})) return FA_ERR_INVALID_ARG;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.delta = static_cast<float*>(workspace);
-  a.lse2 = a.delta + (size_t)B * Hq * L;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.d = d;
-  a.window = window;
-  a.scale = softmax_scale;
-  a.scale_log2 = softmax_scale * 1.4426950408889634f;
   hipError_t e = fa::launch_bwd_bf16(a, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int flash_attn_bwd_preprocess(const void* o, const float* lse, const void* dout,
+                                         void* workspace, size_t workspace_bytes,
+                                         int B, int Hq, int Hkv, int L, int d, int dtype, void* stream) {
+  fa::BwdArgs a{};
+  int rc = bwd_setup(a, workspace, workspace_bytes, B, Hq, Hkv, L, d, 1.f, 0, 0, dtype);
+  if (rc != FA_OK) return rc;
+  if (!all_aligned({o, lse, dout})) return FA_ERR_INVALID_ARG;
+  a.o = o; a.lse = lse; a.dout = dout;
+  hipError_t e = fa::launch_bwd_preprocess_bf16(a, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                                   const void* workspace, size_t workspace_bytes, void* dk, void* dv,
+                                   int B, int Hq, int Hkv, int L, int d,
+                                   float softmax_scale, int causal, int window, int dtype, void* stream) {
+  fa::BwdArgs a{};
+  int rc = bwd_setup(a, workspace, workspace_bytes, B, Hq, Hkv, L, d, softmax_scale, causal, window, dtype);
+  if (rc != FA_OK) return rc;
+  if (!all_aligned({q, k, v, dout, dk, dv})) return FA_ERR_INVALID_ARG;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.dk = dk; a.dv = dv;
+  hipError_t e = fa::launch_bwd_dkdv_bf16(a, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                                 const void* workspace, size_t workspace_bytes, void* dq,
+                                 int B, int Hq, int Hkv, int L, int d,
+                                 float softmax_scale, int causal, int window, int dtype, void* stream) {
+  fa::BwdArgs a{};
+  int rc = bwd_setup(a, workspace, workspace_bytes, B, Hq, Hkv, L, d, softmax_scale, causal, window, dtype);
+  if (rc != FA_OK) return rc;
+  if (!all_aligned({q, k, v, dout, dq})) return FA_ERR_INVALID_ARG;
+  a.q = q; a.k = k; a.v = v; a.dout = dout; a.dq = dq;
+  hipError_t e = fa::launch_bwd_dq_bf16(a, causal != 0, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

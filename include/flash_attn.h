@@ -111,6 +111,32 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
                    int B, int Hq, int Hkv, int L, int d,
                    float softmax_scale, int causal, int window, int dtype, void* stream);
 
+/*
+ * The backward in three stages, for callers that schedule them (for example
+ * dK/dV and dQ on two streams).  flash_attn_bwd runs exactly these three in
+ * order on one stream.  Arguments mean what they mean for flash_attn_bwd.
+ *
+ * Stage 1, flash_attn_bwd_preprocess: from O, the forward's LSE and dO, writes
+ * into the workspace the per-row D_i = sum_c dO_ic * O_ic and LSE_i * log2(e)
+ * (the statistics the recomputation needs, claspmoon.cn §3.3).  Stages 2 and
+ * 3 read only those from the workspace and may run in either order or
+ * concurrently once stage 1 has completed:
+ *   flash_attn_bwd_dkdv -- dK and dV (K/V-stationary; GQA groups summed)
+ *   flash_attn_bwd_dq   -- dQ (Q-stationary)
+ * Same validation and return codes as flash_attn_bwd.
+ */
+int flash_attn_bwd_preprocess(const void* o, const float* lse, const void* dout,
+                              void* workspace, size_t workspace_bytes,
+                              int B, int Hq, int Hkv, int L, int d, int dtype, void* stream);
+int flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                        const void* workspace, size_t workspace_bytes, void* dk, void* dv,
+                        int B, int Hq, int Hkv, int L, int d,
+                        float softmax_scale, int causal, int window, int dtype, void* stream);
+int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                      const void* workspace, size_t workspace_bytes, void* dq,
+                      int B, int Hq, int Hkv, int L, int d,
+                      float softmax_scale, int causal, int window, int dtype, void* stream);
+
 /* Static, never-NULL description of a return code. */
 const char* flash_attn_strerror(int code);
 

@@ -105,6 +105,26 @@ def test_bwd_rejects_invalid_arguments(lib):
     assert call_bwd(lib, Hq=3, Hkv=2) == c["FA_ERR_GQA"]
 
 
+def test_stage_entry_points_reject_invalid_arguments(lib):
+    c = header_constants()
+    INV, UNS, WS, GQA = c["FA_ERR_INVALID_ARG"], c["FA_ERR_UNSUPPORTED"], c["FA_ERR_WORKSPACE"], c["FA_ERR_GQA"]
+    ws, nb = FAKE * 16, 1 << 20
+    pre = lambda o=FAKE, lse=FAKE, do=FAKE, ws=ws, nb=nb, B=1, Hq=2, Hkv=2, L=16, d=64, dt=fa.FA_DTYPE_BF16: \
+        lib.flash_attn_bwd_preprocess(o, lse, do, ws, nb, B, Hq, Hkv, L, d, dt, None)
+    assert pre(o=None) == INV and pre(lse=MISALIGNED) == INV
+    assert pre(ws=None) == WS and pre(nb=255) == WS
+    assert pre(d=80) == UNS and pre(dt=fa.FA_DTYPE_F32) == UNS and pre(Hq=3) == GQA and pre(L=0) == INV
+    kv = lambda q=FAKE, dk=FAKE, ws=ws, nb=nb, L=16, causal=1, window=0, Hkv=2: \
+        lib.flash_attn_bwd_dkdv(q, FAKE, FAKE, FAKE, ws, nb, dk, FAKE, 1, 2, Hkv, L, 64, 0.125, causal, window,
+                                fa.FA_DTYPE_BF16, None)
+    assert kv(q=None) == INV and kv(dk=MISALIGNED) == INV and kv(ws=FAKE * 16 + 64) == WS
+    assert kv(causal=0, window=2) == UNS and kv(Hkv=3) == GQA and kv(L=-1) == INV
+    dqf = lambda dq=FAKE, ws=ws, nb=nb, scale=0.125: \
+        lib.flash_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, ws, nb, dq, 1, 2, 2, 16, 64, scale, 1, 0,
+                              fa.FA_DTYPE_BF16, None)
+    assert dqf(dq=None) == INV and dqf(nb=0) == WS and dqf(scale=-2.0) == INV
+
+
 def test_workspace_size_formula(lib):
     f = lib.flash_attn_bwd_workspace_bytes
     assert f(2, 32, 32, 4096, 128, fa.FA_DTYPE_BF16) == 2 * 32 * 4096 * 8

@@ -127,6 +127,25 @@ def test_long_context_backward():
     check_heads_at_full_size(W.LONG_BWD_8K, [(1, 5)])
 
 
+def test_backward_stages_equal_fused_call():
+    """The three exported stages (preprocess, dK/dV, dQ) reproduce flash_attn_bwd bit for bit."""
+    for w in (W.small("stages", 1, 4, 2, 513, 128, seed=230, backward=True),
+              W.small("stages d64 window", 1, 2, 2, 300, 64, window=50, seed=231, backward=True),
+              W.LLAMA7B_CAUSAL):
+        q, k, v, do = W.make_inputs(w, with_dout=True)
+        dev = "cuda:0"
+        qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+        o, lse = fa().fwd(qd, kd, vd, causal=w.causal, window=w.window, scale=w.scale)
+        a = fa().bwd(qd, kd, vd, o, lse, dod, causal=w.causal, window=w.window, scale=w.scale)
+        seen = []
+        b = fa().bwd_stages(qd, kd, vd, o, lse, dod, causal=w.causal, window=w.window, scale=w.scale,
+                            between=seen.append)
+        torch.cuda.synchronize()
+        assert seen == ["preprocess", "dkdv", "dq"]
+        for x, y in zip(a, b):
+            assert torch.equal(x, y)
+
+
 def test_backward_is_deterministic():
     w = W.small("det", 1, 4, 2, 700, 128, seed=220, backward=True)
     q, k, v, do = W.make_inputs(w, with_dout=True)
