@@ -184,7 +184,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float stat_st0[2 * C::BQ];   // LSE*log2e, then D
   __shared__ __attribute__((aligned(16))) float stat_st1[2 * C::BQ];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 5, ln = lane & 31;
   const int kb = wave & 3, qh = wave >> 2;
   const int L = a.L, window = a.window;
@@ -422,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char k_st1[C::KT];
   __shared__ __attribute__((aligned(1024))) char v_st1[C::VT];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 5, ln = lane & 31;
   const int L = a.L, window = a.window;
 

@@ -108,6 +108,12 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float a0, float a1, float a2, float 
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 64); }
 
+// Index of the calling wave in its work-group, as a value the compiler knows to
+// be uniform across the wave: branches on quantities derived from it then
+// stay scalar branches instead of becoming exec-masked code that runs both
+// sides.
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // Forward LDS swizzles (XOR on the 16-byte chunk index of row r of a tile).
 // K is only read 16 rows at a time at one chunk: spread those rows over all
 // banks.  V is only read by the transposing read (4 rows x 4 chunks per

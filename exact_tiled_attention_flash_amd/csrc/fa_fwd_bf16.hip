@@ -205,7 +205,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char k_st1[C::KT];
   __shared__ __attribute__((aligned(1024))) char v_st1[C::VT];
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 5, ln = lane & 31;
 
   // ---- work decomposition: (batch, query head) major, heaviest query tile first
