@@ -427,8 +427,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int L = a.L, window = a.window;
 
   const int r = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = r / a.n_tiles;
-  const int qt_rank = r % a.n_tiles;
+  int bh, qt_rank;
+  head_tile_of(r, a.B * a.Hq, a.n_tiles, bh, qt_rank);
   const int qt = CAUSAL ? a.n_tiles - 1 - qt_rank : qt_rank;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int hk = h / (a.Hq / a.Hkv);

@@ -222,4 +222,24 @@ __device__ __forceinline__ int xcd_remap(int id, int n) {
   return (id % kXcds) * (n / kXcds) + id / kXcds;
 }
 
+// Logical work-group index -> (head, tile rank) for a grid of n_heads x
+// n_tiles work-groups in which tile rank 0 is the heaviest (causal masking
+// makes the tiles' work range from 1 to n_tiles units).  Heads go in pairs,
+// and inside a pair rank by rank (rank 0 of both heads, then rank 1, ...):
+// the heaviest work-groups of a pair are dispatched first, which evens out
+// when the work-group slots of a CU run dry, while only two heads' streamed
+// operands are live in an XCD's L2 at a time.  With an odd head count the
+// last head goes alone.
+__device__ __forceinline__ void head_tile_of(int r, int n_heads, int n_tiles, int& head, int& rank) {
+  const int paired = (n_heads >> 1) * 2 * n_tiles;
+  if (r < paired) {
+    const int pair = r / (2 * n_tiles), rest = r - pair * 2 * n_tiles;
+    head = 2 * pair + (rest & 1);
+    rank = rest >> 1;
+  } else {
+    head = n_heads - 1;
+    rank = r - paired;
+  }
+}
+
 }  // namespace fa

@@ -208,10 +208,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 5, ln = lane & 31;
 
-  // ---- work decomposition: (batch, query head) major, heaviest query tile first
+  // ---- work decomposition: heads in pairs, heaviest query tiles first
   const int r = xcd_remap(blockIdx.x, gridDim.x);
-  const int bh = r / a.n_qtiles;
-  const int qt_rank = r % a.n_qtiles;
+  int bh, qt_rank;
+  head_tile_of(r, a.B * a.Hq, a.n_qtiles, bh, qt_rank);
   const int qt = CAUSAL ? a.n_qtiles - 1 - qt_rank : qt_rank;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
