@@ -122,15 +122,16 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const KVAddr<D>& ad, con
   for (int i4 = 0; i4 < 4; ++i4) {
     const f32x4 l4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (32 * qh + 8 * i4 + 4 * g));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = 4 * i4 + j;
-      float pv = fast_exp2(fmaf(p[i], c, -l4[j]));
-      if (need_mask) {
-        const int q = qw0 + 8 * i4 + 4 * g + j;
-        const bool ok = q < L && (!CAUSAL || my_key <= q) && (window <= 0 || q - my_key < window);
-        pv = ok ? pv : 0.f;
-      }
-      p[i] = pv;
+    for (int j = 0; j < 4; ++j) p[4 * i4 + j] = fast_exp2(fmaf(p[4 * i4 + j], c, -l4[j]));
+  }
+  // the mask as a separate pass, so that the common unmasked tile stays one
+  // straight-line block
+  if (need_mask) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int q = qw0 + 8 * (i >> 2) + 4 * g + (i & 3);
+      const bool ok = q < L && (!CAUSAL || my_key <= q) && (window <= 0 || q - my_key < window);
+      p[i] = ok ? p[i] : 0.f;
     }
   }
   // dV += P^T dO: A = P (lane = key, K slots = queries), B = dO via the transposing read
@@ -381,14 +382,14 @@ __device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const 
     for (int k = 1; k < C::NSTEP; ++k)
       p = mfma32(lds_load16(kbuf, ad.krow[k] + kb * 32 * (2 * D)), st.qr[k], p);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float pv = fast_exp2(fmaf(p[i], c, -st.lse2));
-      if (need_mask) {
+    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(p[i], c, -st.lse2));
+    if (need_mask) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
         const int kk = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
         const bool ok = kk < L && (!CAUSAL || kk <= my_q) && (window <= 0 || kk > my_q - window);
-        pv = ok ? pv : 0.f;
+        p[i] = ok ? p[i] : 0.f;
       }
-      p[i] = pv;
     }
     // dP^T = V dO^T, dS^T = P^T * (dP^T - D)
     f32x16 dp = mfma32(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR), st.dor[0], f32x16{});
