@@ -175,13 +175,16 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = KVCfg<D>;
   // distinct LDS objects per stage so reads of one stage need not wait for the
-  // direct copies into the other (alias scopes)
+  // direct copies into the other (alias scopes).  The stage buffers carry the
+  // larger alignment so that they are laid out first, in the low 64 KiB: their
+  // swizzled per-lane offsets then take the buffer base in the 16-bit
+  // immediate of the LDS read instead of a VALU add per read.
+  __shared__ __attribute__((aligned(C::QT))) char q_st0[C::QT];
+  __shared__ __attribute__((aligned(C::QT))) char do_st0[C::QT];
+  __shared__ __attribute__((aligned(C::QT))) char q_st1[C::QT];
+  __shared__ __attribute__((aligned(C::QT))) char do_st1[C::QT];
   __shared__ __attribute__((aligned(1024))) char k_blk[C::KB];
   __shared__ __attribute__((aligned(1024))) char v_blk[C::KB];
-  __shared__ __attribute__((aligned(1024))) char q_st0[C::QT];
-  __shared__ __attribute__((aligned(1024))) char do_st0[C::QT];
-  __shared__ __attribute__((aligned(1024))) char q_st1[C::QT];
-  __shared__ __attribute__((aligned(1024))) char do_st1[C::QT];
   __shared__ __attribute__((aligned(16))) float stat_st0[2 * C::BQ];   // LSE*log2e, then D
   __shared__ __attribute__((aligned(16))) float stat_st1[2 * C::BQ];
 
