@@ -11,7 +11,13 @@ FLOPs are counted algorithmically: forward 4*B*Hq*L^2*d, halved for causal
 (the allowed band for a sliding window); backward 2.5x the forward (five
 matrix products, the recomputation of Q K^T included).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Besides the headline step, the line carries a "configs" object with forward (and,
+where the workload has one, backward) time, TFLOP/s and fraction of peak for every
+workload of the method's configuration list (fp32 tiny, the LLaMA-7B layer, GQA 16k,
+sliding window 32k, 128k forward, 8k backward), plus the extra device memory each
+call allocates beyond its inputs and outputs.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-configs]
 """
 
 import argparse
@@ -27,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0              # MI355X HBM3E, published
+PEAK_FP32_VECTOR_TFLOPS = 157.3    # MI355X fp32 vector ALU, published
 METRIC = "attention fwd/bwd TFLOP/s + % bf16 MFMA peak, B2 H32 L4096 d128 causal"
 
 
@@ -110,12 +117,82 @@ def cpu_baseline(budget_s=20.0):
                       f"{dt:.1f} s wall, {t_f:.1f} s of it forward; host os.cpu_count()={os.cpu_count()}"}
 
 
+def time_calls(fn, iters, warmup, warm_ms=150.0):
+    """Median and mean of `iters` calls, each bracketed by HIP events on the current stream.
+
+    Warm-up runs at least `warmup` calls and at least `warm_ms` of them: after a light
+    phase the clocks take on the order of 100 ms to ramp back up."""
+    import time
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while n < warmup or (time.perf_counter() - t0) * 1e3 < warm_ms:
+        fn()
+        n += 1
+        if n % 4 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    return t[len(t) // 2], sum(t) / len(t)
+
+
+def measure_config(w, iters=10, warmup=3):
+    """Forward (and backward) timing of one workload, with its extra device memory."""
+    import torch
+    import exact_tiled_attention_flash_amd as fa
+    import workloads as W
+    dev = torch.device("cuda:0")
+    q, k, v, do = W.make_inputs(w, with_dout=w.backward)
+    q, k, v = (t.to(dev) for t in (q, k, v))
+    do = do.to(dev) if do is not None else None
+    o = torch.empty_like(q)
+    torch.cuda.synchronize()
+    base = torch.cuda.memory_allocated()
+    torch.cuda.reset_peak_memory_stats()
+    _, lse = fa.fwd(q, k, v, causal=w.causal, window=w.window, scale=w.scale, out=o)
+    torch.cuda.synchronize()
+    fwd_extra = torch.cuda.max_memory_allocated() - base
+    ff = fwd_flops(w.B, w.Hq, w.L, w.d, w.causal, w.window)
+    fp32 = w.dtype == torch.float32
+    peak = PEAK_FP32_VECTOR_TFLOPS if fp32 else PEAK_BF16_TFLOPS
+    med, mean = time_calls(lambda: fa.fwd(q, k, v, causal=w.causal, window=w.window, scale=w.scale, out=o, lse=lse),
+                           iters, warmup)
+    tf = ff / (med * 1e-3) / 1e12
+    r = {"shape": f"B{w.B} Hq{w.Hq} Hkv{w.Hkv} L{w.L} d{w.d}", "dtype": "f32" if fp32 else "bf16",
+         "causal": w.causal, "window": w.window,
+         "fwd": {"ms_median": round(med, 4), "ms_mean": round(mean, 4), "tflop": ff / 1e12,
+                 "tflops": round(tf, 2), "peak_tflops": peak, "frac_peak": round(tf / peak, 4),
+                 "extra_mem_bytes": int(fwd_extra)}}
+    if w.backward:
+        nbytes = fa.bwd_workspace_bytes(w.B, w.Hq, w.Hkv, w.L, w.d, w.dtype)
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        run = lambda: fa.bwd(q, k, v, o, lse, do, causal=w.causal, window=w.window, scale=w.scale,
+                             workspace=ws, dq=dq, dk=dk, dv=dv)
+        bmed, bmean = time_calls(run, iters, warmup)
+        bf = bwd_flops(w.B, w.Hq, w.L, w.d, w.causal, w.window)
+        btf = bf / (bmed * 1e-3) / 1e12
+        r["bwd"] = {"ms_median": round(bmed, 4), "ms_mean": round(bmean, 4), "tflop": bf / 1e12,
+                    "tflops": round(btf, 2), "peak_tflops": peak, "frac_peak": round(btf / peak, 4),
+                    "extra_mem_bytes": int(nbytes)}
+    del q, k, v, do, o, lse
+    torch.cuda.empty_cache()
+    return r
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (3x), so that HBM counters "
                          "(FETCH_SIZE/WRITE_SIZE) can be scaled against a kernel of known traffic")
@@ -233,6 +310,8 @@ def main():
                      "traffic": load_traffic(kernel_names[dom]),
                      "algorithmic_per_launch": work},
     }
+    if not args.no_configs:
+        out["configs"] = {wl.name: measure_config(wl) for wl in W.ALL}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)
