@@ -7,6 +7,7 @@ fallback: if the library is missing or a call fails, a RuntimeError is raised.
 
     o, lse = fwd(q, k, v, causal=True)                 # q [B,Hq,L,d], k/v [B,Hkv,L,d]
     dq, dk, dv = bwd(q, k, v, o, lse, do, causal=True)
+    o = scaled_dot_product_attention(q, k, v, is_causal=True)   # autograd drop-in
 
 The interface mirrors the pages' ``scaled_dot_product_attention(q, k, v,
 is_causal=...)`` usage (claspmoon.cn "14 · 缩放定律与高效注意力" §3.5) plus the
@@ -20,11 +21,13 @@ import os
 import torch
 
 __all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "strerror", "library", "library_path",
-           "FA_DTYPE_F32", "FA_DTYPE_BF16", "EXPORTED_SYMBOLS"]
+           "FlashAttentionFunction", "scaled_dot_product_attention",
+           "FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "EXPORTED_SYMBOLS"]
 
 FA_DTYPE_F32 = 0
 FA_DTYPE_BF16 = 1
-_DTYPES = {torch.float32: FA_DTYPE_F32, torch.bfloat16: FA_DTYPE_BF16}
+FA_DTYPE_F16 = 2
+_DTYPES = {torch.float32: FA_DTYPE_F32, torch.bfloat16: FA_DTYPE_BF16, torch.float16: FA_DTYPE_F16}
 
 EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_bytes",
                     "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
@@ -98,7 +101,7 @@ def _shapes(q, k, v):
         if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
             raise ValueError("q, k, v must be contiguous CUDA tensors of one dtype")
     if q.dtype not in _DTYPES:
-        raise ValueError("dtype must be float32 or bfloat16")
+        raise ValueError("dtype must be float32, bfloat16 or float16")
     return B, Hq, k.shape[1], L, d
 
 
@@ -182,3 +185,37 @@ def bwd_stages(q, k, v, o, lse, dout, causal=False, window=0, scale=None, worksp
     if between:
         between("dq")
     return dq, dk, dv
+
+
+class FlashAttentionFunction(torch.autograd.Function):
+    """Exact attention as a ``torch.autograd.Function``.
+
+    The forward keeps only O and the per-row log-sum-exp for the backward, which
+    recomputes the probabilities (claspmoon.cn "14 · 缩放定律与高效注意力" §3.3).
+    Inputs are ``[B, H, L, d]`` CUDA tensors of one dtype (bfloat16 or float16 for
+    training; float32 has a forward only).
+    """
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal=False, window=0, scale=None):
+        q, k, v = (t.contiguous() for t in (q, k, v))
+        o, lse = fwd(q, k, v, causal=causal, window=window, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal, ctx.window, ctx.scale = causal, window, scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), causal=ctx.causal, window=ctx.window,
+                         scale=ctx.scale)
+        return dq, dk, dv, None, None, None
+
+
+def scaled_dot_product_attention(q, k, v, is_causal=False, scale=None, window=0):
+    """Drop-in for ``scaled_dot_product_attention(q, k, v, is_causal=...)`` on ``[B, H, L, d]``
+    tensors (claspmoon.cn "14 · 缩放定律与高效注意力" §3.5), with grouped-query K/V
+    (``k.shape[1]`` dividing ``q.shape[1]``) and an optional causal sliding ``window``
+    (kler.cn, §3.2.1 configuration keys).  Differentiable through ``FlashAttentionFunction``.
+    """
+    return FlashAttentionFunction.apply(q, k, v, bool(is_causal), int(window), scale)

@@ -36,7 +36,7 @@ __device__ __forceinline__ void wait_copies_and_barrier() {
 
 // ------------------------------------------------------------ 1. delta
 
-template <int D>
+template <int D, bool F16>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
                                                         const float* __restrict__ lse, float* __restrict__ delta,
                                                         float* __restrict__ lse2, long long rows) {
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__
     const bf16x8 x = *reinterpret_cast<const bf16x8*>(o + row * D + part * 8);
     const bf16x8 y = *reinterpret_cast<const bf16x8*>(dout + row * D + part * 8);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fmaf((float)x[i], (float)y[i], acc);
+    for (int i = 0; i < 8; ++i) acc = fmaf(unpack1<F16>(x[i]), unpack1<F16>(y[i]), acc);
   }
 #pragma unroll
   for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -100,7 +100,7 @@ struct KVAddr {
   int kv;                              // row reads of the wave's 32 keys in the padded K/V block
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void kv_tile(KVState<D>& st, const KVAddr<D>& ad, const char* kblk, const char* vblk,
                                         const char* qbuf, const char* dobuf, const float* stats, int q0, int L,
                                         int window, int qh, int key_w0, float c, int lane) {
@@ -109,10 +109,10 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const KVAddr<D>& ad, con
   const int my_key = key_w0 + (lane & 31);
 
   // S = Q K^T (32 queries x 32 keys): lane = key, registers = queries
-  f32x16 p = mfma32(lds_load16(qbuf, ad.row[0]), lds_load16(kblk, ad.kv), f32x16{});
+  f32x16 p = mfma32x<F16>(lds_load16(qbuf, ad.row[0]), lds_load16(kblk, ad.kv), f32x16{});
 #pragma unroll
   for (int k = 1; k < C::NSTEP; ++k)
-    p = mfma32(lds_load16(qbuf, ad.row[k]), lds_load16(kblk, ad.kv + 32 * k), p);
+    p = mfma32x<F16>(lds_load16(qbuf, ad.row[k]), lds_load16(kblk, ad.kv + 32 * k), p);
 
   // P = exp2(S*s*log2e - LSE*log2e), zero where masked
   const int qw0 = q0 + 32 * qh;           // first query of this wave's half
@@ -138,19 +138,19 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const KVAddr<D>& ad, con
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int o8 = 8 * u;
-    const bf16x8 pa = to_bf16x8(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5], p[o8 + 6], p[o8 + 7]);
+    const bf16x8 pa = pack8<F16>(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5], p[o8 + 6], p[o8 + 7]);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
       const bf16x8 bo = concat4(lds_load_tr(dobuf, ad.tr[db][0] + u * 16 * (2 * D)),
                                 lds_load_tr(dobuf, ad.tr[db][1] + u * 16 * (2 * D)));
-      st.dv[db] = mfma32(pa, bo, st.dv[db]);
+      st.dv[db] = mfma32x<F16>(pa, bo, st.dv[db]);
     }
   }
   // dP = dO V^T, then dS = P * (dP - D) in place
-  f32x16 dp = mfma32(lds_load16(dobuf, ad.row[0]), lds_load16(vblk, ad.kv), f32x16{});
+  f32x16 dp = mfma32x<F16>(lds_load16(dobuf, ad.row[0]), lds_load16(vblk, ad.kv), f32x16{});
 #pragma unroll
   for (int k = 1; k < C::NSTEP; ++k)
-    dp = mfma32(lds_load16(dobuf, ad.row[k]), lds_load16(vblk, ad.kv + 32 * k), dp);
+    dp = mfma32x<F16>(lds_load16(dobuf, ad.row[k]), lds_load16(vblk, ad.kv + 32 * k), dp);
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
     const f32x4 d4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (C::BQ + 32 * qh + 8 * i4 + 4 * g));
@@ -161,17 +161,17 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const KVAddr<D>& ad, con
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int o8 = 8 * u;
-    const bf16x8 da = to_bf16x8(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5], p[o8 + 6], p[o8 + 7]);
+    const bf16x8 da = pack8<F16>(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5], p[o8 + 6], p[o8 + 7]);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
       const bf16x8 bq = concat4(lds_load_tr(qbuf, ad.tr[db][0] + u * 16 * (2 * D)),
                                 lds_load_tr(qbuf, ad.tr[db][1] + u * 16 * (2 * D)));
-      st.dk[db] = mfma32(da, bq, st.dk[db]);
+      st.dk[db] = mfma32x<F16>(da, bq, st.dk[db]);
     }
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   using C = KVCfg<D>;
   // distinct LDS objects per stage so reads of one stage need not wait for the
@@ -275,12 +275,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   for (int it = 0; it < n_it; it += 2) {
     if (it + 1 < n_it) issue(it + 1, q_st1, do_st1, stat_st1);
     if (wave_needs(q0_of(it)))
-      kv_tile<D, CAUSAL>(st, ad, k_blk, v_blk, q_st0, do_st0, stat_st0, q0_of(it), L, window, qh, key_w0, c, lane);
+      kv_tile<D, CAUSAL, F16>(st, ad, k_blk, v_blk, q_st0, do_st0, stat_st0, q0_of(it), L, window, qh, key_w0, c, lane);
     wait_copies_and_barrier();
     if (it + 1 >= n_it) break;
     if (it + 2 < n_it) issue(it + 2, q_st0, do_st0, stat_st0);
     if (wave_needs(q0_of(it + 1)))
-      kv_tile<D, CAUSAL>(st, ad, k_blk, v_blk, q_st1, do_st1, stat_st1, q0_of(it + 1), L, window, qh, key_w0, c, lane);
+      kv_tile<D, CAUSAL, F16>(st, ad, k_blk, v_blk, q_st1, do_st1, stat_st1, q0_of(it + 1), L, window, qh, key_w0, c, lane);
     wait_copies_and_barrier();
   }
 
@@ -322,8 +322,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       if (key < L) {
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
-          dKh[(size_t)key * D + 32 * db + ln] = (bf16)(st.dk[db][i] * s);
-          dVh[(size_t)key * D + 32 * db + ln] = (bf16)(st.dv[db][i]);
+          dKh[(size_t)key * D + 32 * db + ln] = pack1<F16>(st.dk[db][i] * s);
+          dVh[(size_t)key * D + 32 * db + ln] = pack1<F16>(st.dv[db][i]);
         }
       }
     }
@@ -370,7 +370,7 @@ struct QAddr {
   int vrow;                     // row reads of padded V rows ln (+32 per key half)
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const char* kbuf, const char* vbuf, int k0,
                                        int L, int window, int my_q, int q_w0, int wq_hi, float c, int lane) {
   using C = QCfg<D>;
@@ -380,10 +380,10 @@ __device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const 
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     // S^T = K Q^T for keys 32kb..32kb+31: lane = query, registers = keys
-    f32x16 p = mfma32(lds_load16(kbuf, ad.krow[0] + kb * 32 * (2 * D)), st.qr[0], f32x16{});
+    f32x16 p = mfma32x<F16>(lds_load16(kbuf, ad.krow[0] + kb * 32 * (2 * D)), st.qr[0], f32x16{});
 #pragma unroll
     for (int k = 1; k < C::NSTEP; ++k)
-      p = mfma32(lds_load16(kbuf, ad.krow[k] + kb * 32 * (2 * D)), st.qr[k], p);
+      p = mfma32x<F16>(lds_load16(kbuf, ad.krow[k] + kb * 32 * (2 * D)), st.qr[k], p);
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(p[i], c, -st.lse2));
     if (need_mask) {
@@ -395,10 +395,10 @@ __device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const 
       }
     }
     // dP^T = V dO^T, dS^T = P^T * (dP^T - D)
-    f32x16 dp = mfma32(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR), st.dor[0], f32x16{});
+    f32x16 dp = mfma32x<F16>(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR), st.dor[0], f32x16{});
 #pragma unroll
     for (int k = 1; k < C::NSTEP; ++k)
-      dp = mfma32(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR + 32 * k), st.dor[k], dp);
+      dp = mfma32x<F16>(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR + 32 * k), st.dor[k], dp);
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] *= dp[i] - st.dlt;
     // dQ^T += K^T dS^T: A = K^T via the transposing read, B = dS^T (lane = query)
@@ -406,19 +406,19 @@ __device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const 
     for (int u = 0; u < 2; ++u) {
       const int o8 = 8 * u;
       const int t = 2 * kb + u;
-      const bf16x8 db8 = to_bf16x8(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5],
+      const bf16x8 db8 = pack8<F16>(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5],
                                    p[o8 + 6], p[o8 + 7]);
 #pragma unroll
       for (int db = 0; db < C::NDB; ++db) {
         const bf16x8 ka = concat4(lds_load_tr(kbuf, ad.ktr[db][0] + t * 16 * (2 * D)),
                                   lds_load_tr(kbuf, ad.ktr[db][1] + t * 16 * (2 * D)));
-        st.dq[db] = mfma32(ka, db8, st.dq[db]);
+        st.dq[db] = mfma32x<F16>(ka, db8, st.dq[db]);
       }
     }
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   using C = QCfg<D>;
   __shared__ __attribute__((aligned(1024))) char k_st0[C::KT];
@@ -501,12 +501,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   for (int j = j_lo; j <= j_hi; j += 2) {
     if (j < j_hi) issue(j + 1, k_st1, v_st1);
     if (wave_needs(j * C::BC))
-      q_tile<D, CAUSAL>(st, ad, k_st0, v_st0, j * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+      q_tile<D, CAUSAL, F16>(st, ad, k_st0, v_st0, j * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
     wait_copies_and_barrier();
     if (j + 1 > j_hi) break;
     if (j + 1 < j_hi) issue(j + 2, k_st0, v_st0);
     if (wave_needs((j + 1) * C::BC))
-      q_tile<D, CAUSAL>(st, ad, k_st1, v_st1, (j + 1) * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+      q_tile<D, CAUSAL, F16>(st, ad, k_st1, v_st1, (j + 1) * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
     wait_copies_and_barrier();
   }
 
@@ -519,40 +519,40 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         bf16x4 w;
-        w[0] = (bf16)(st.dq[db][4 * i4 + 0] * s);
-        w[1] = (bf16)(st.dq[db][4 * i4 + 1] * s);
-        w[2] = (bf16)(st.dq[db][4 * i4 + 2] * s);
-        w[3] = (bf16)(st.dq[db][4 * i4 + 3] * s);
+        w[0] = pack1<F16>(st.dq[db][4 * i4 + 0] * s);
+        w[1] = pack1<F16>(st.dq[db][4 * i4 + 1] * s);
+        w[2] = pack1<F16>(st.dq[db][4 * i4 + 2] * s);
+        w[3] = pack1<F16>(st.dq[db][4 * i4 + 3] * s);
         *reinterpret_cast<bf16x4*>(dQr + 32 * db + 8 * i4 + 4 * g) = w;
       }
     }
   }
 }
 
-template <int D>
+template <int D, bool F16>
 hipError_t launch_delta(const BwdArgs& a, hipStream_t stream) {
   const long long rows = (long long)a.B * a.Hq * a.L;
   constexpr int kRowsPerBlock = 256 / (D / 8);
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+  hipLaunchKernelGGL((bwd_delta_kernel<D, F16>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
                      dim3(256), 0, stream, reinterpret_cast<const bf16*>(a.o),
                      reinterpret_cast<const bf16*>(a.dout), a.lse, a.delta, a.lse2, rows);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 hipError_t launch_dkdv(const BwdArgs& args, hipStream_t stream) {
   BwdArgs a = args;
   a.n_tiles = (a.L + KVCfg<D>::BK - 1) / KVCfg<D>::BK;
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)((long long)a.B * a.Hkv * a.n_tiles)),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, F16>), dim3((unsigned)((long long)a.B * a.Hkv * a.n_tiles)),
                      dim3(64 * KVCfg<D>::kWaves), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 hipError_t launch_dq(const BwdArgs& args, hipStream_t stream) {
   BwdArgs a = args;
   a.n_tiles = (a.L + QCfg<D>::BQ - 1) / QCfg<D>::BQ;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)((long long)a.B * a.Hq * a.n_tiles)),
+  hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, F16>), dim3((unsigned)((long long)a.B * a.Hq * a.n_tiles)),
                      dim3(64 * QCfg<D>::kWaves), 0, stream, a);
   return hipGetLastError();
 }
@@ -560,17 +560,29 @@ hipError_t launch_dq(const BwdArgs& args, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_bwd_preprocess_bf16(const BwdArgs& a, hipStream_t stream) {
-  return a.d == 128 ? launch_delta<128>(a, stream) : launch_delta<64>(a, stream);
+  if (a.f16) return a.d == 128 ? launch_delta<128, true>(a, stream) : launch_delta<64, true>(a, stream);
+  return a.d == 128 ? launch_delta<128, false>(a, stream) : launch_delta<64, false>(a, stream);
 }
 
+namespace {
+template <bool F16>
+hipError_t dkdv_typed(const BwdArgs& a, bool causal, hipStream_t stream) {
+  if (a.d == 128) return causal ? launch_dkdv<128, true, F16>(a, stream) : launch_dkdv<128, false, F16>(a, stream);
+  return causal ? launch_dkdv<64, true, F16>(a, stream) : launch_dkdv<64, false, F16>(a, stream);
+}
+template <bool F16>
+hipError_t dq_typed(const BwdArgs& a, bool causal, hipStream_t stream) {
+  if (a.d == 128) return causal ? launch_dq<128, true, F16>(a, stream) : launch_dq<128, false, F16>(a, stream);
+  return causal ? launch_dq<64, true, F16>(a, stream) : launch_dq<64, false, F16>(a, stream);
+}
+}  // namespace
+
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, bool causal, hipStream_t stream) {
-  if (a.d == 128) return causal ? launch_dkdv<128, true>(a, stream) : launch_dkdv<128, false>(a, stream);
-  return causal ? launch_dkdv<64, true>(a, stream) : launch_dkdv<64, false>(a, stream);
+  return a.f16 ? dkdv_typed<true>(a, causal, stream) : dkdv_typed<false>(a, causal, stream);
 }
 
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, bool causal, hipStream_t stream) {
-  if (a.d == 128) return causal ? launch_dq<128, true>(a, stream) : launch_dq<128, false>(a, stream);
-  return causal ? launch_dq<64, true>(a, stream) : launch_dq<64, false>(a, stream);
+  return a.f16 ? dq_typed<true>(a, causal, stream) : dq_typed<false>(a, causal, stream);
 }
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream) {

@@ -36,6 +36,50 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// The 16-bit kernels serve bf16 and fp16 alike: bf16x8 / bf16x4 / bf16 are
+// then plain containers of 16-bit values, and the F16 template parameter
+// decides how the arithmetic reads and writes them (the MFMA opcode and the
+// fp32 <-> 16-bit conversions, both round-to-nearest-even).
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32x(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <bool F16>
+__device__ __forceinline__ bf16 pack1(float x) {
+  if constexpr (F16) return __builtin_bit_cast(bf16, (f16)x);
+  else return (bf16)x;
+}
+
+template <bool F16>
+__device__ __forceinline__ float unpack1(bf16 x) {
+  if constexpr (F16) return (float)__builtin_bit_cast(f16, x);
+  else return (float)x;
+}
+
+template <bool F16>
+__device__ __forceinline__ bf16x8 pack8(float a0, float a1, float a2, float a3, float a4, float a5, float a6,
+                                        float a7) {
+  if constexpr (F16) {
+    f16x8 r;
+    r[0] = (f16)a0; r[1] = (f16)a1; r[2] = (f16)a2; r[3] = (f16)a3;
+    r[4] = (f16)a4; r[5] = (f16)a5; r[6] = (f16)a6; r[7] = (f16)a7;
+    return __builtin_bit_cast(bf16x8, r);
+  } else {
+    bf16x8 r;
+    r[0] = (bf16)a0; r[1] = (bf16)a1; r[2] = (bf16)a2; r[3] = (bf16)a3;
+    r[4] = (bf16)a4; r[5] = (bf16)a5; r[6] = (bf16)a6; r[7] = (bf16)a7;
+    return r;
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // 16-byte LDS load at a byte offset.

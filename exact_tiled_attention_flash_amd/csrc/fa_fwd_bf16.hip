@@ -103,7 +103,7 @@ struct FwdState {
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // One key tile for one wave: S^T, mask, online softmax, O^T += V^T P^T.
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, const char* vbuf, int k0,
                                          int L, int window, int my_q, int q_w0, int wq_hi, float c,
                                          int lane) {
@@ -114,15 +114,15 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
   {
     const bf16x8 a0 = lds_load16(kbuf, row_offset_kpad<D>(ln, 0, g));
     const bf16x8 a1 = lds_load16(kbuf, row_offset_kpad<D>(32 + ln, 0, g));
-    s0 = mfma32(a0, st.qr[0], f32x16{});
-    s1 = mfma32(a1, st.qr[0], f32x16{});
+    s0 = mfma32x<F16>(a0, st.qr[0], f32x16{});
+    s1 = mfma32x<F16>(a1, st.qr[0], f32x16{});
   }
 #pragma unroll
   for (int k = 1; k < C::NSTEP; ++k) {
     const bf16x8 a0 = lds_load16(kbuf, row_offset_kpad<D>(ln, k, g));
     const bf16x8 a1 = lds_load16(kbuf, row_offset_kpad<D>(32 + ln, k, g));
-    s0 = mfma32(a0, st.qr[k], s0);
-    s1 = mfma32(a1, st.qr[k], s1);
+    s0 = mfma32x<F16>(a0, st.qr[k], s0);
+    s1 = mfma32x<F16>(a1, st.qr[k], s1);
   }
 
   // 2. mask, only on tiles that straddle a boundary (wave-uniform decision)
@@ -175,10 +175,10 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
   }
   st.l_run += rA + rB;
   bf16x8 pb[4];
-  pb[0] = to_bf16x8(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
-  pb[1] = to_bf16x8(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
-  pb[2] = to_bf16x8(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
-  pb[3] = to_bf16x8(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
+  pb[0] = pack8<F16>(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
+  pb[1] = pack8<F16>(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
+  pb[2] = pack8<F16>(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
+  pb[3] = pack8<F16>(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
 
   // 4. O^T += V^T P^T, 16 keys per MFMA step.  P^T's K slots (from the C
   // layout of step 1) are keys 16t + 8*(slot/4) + 4g + slot%4; the transposing
@@ -189,12 +189,12 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
     for (int db = 0; db < C::NDB; ++db) {
       const bf16x4 lo = lds_load_tr(vbuf, tr_offset_vpad<D>(t, db, 0, lane));
       const bf16x4 hi = lds_load_tr(vbuf, tr_offset_vpad<D>(t, db, 1, lane));
-      st.o[db] = mfma32(concat4(lo, hi), pb[t], st.o[db]);
+      st.o[db] = mfma32x<F16>(concat4(lo, hi), pb[t], st.o[db]);
     }
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
   // Four distinct LDS objects (K and V of two stages): distinct objects carry
@@ -260,12 +260,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int j = j_lo; j <= j_hi; j += 2) {
     if (j < j_hi) issue_kv<D>(cp, krs, vrs, (j + 1) * C::BC, k_st1, v_st1, wave);
     if (wave_needs(j * C::BC))
-      fwd_tile<D, CAUSAL>(st, k_st0, v_st0, j * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+      fwd_tile<D, CAUSAL, F16>(st, k_st0, v_st0, j * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
     wait_copies_and_barrier();
     if (j + 1 > j_hi) break;
     if (j + 1 < j_hi) issue_kv<D>(cp, krs, vrs, (j + 2) * C::BC, k_st0, v_st0, wave);
     if (wave_needs((j + 1) * C::BC))
-      fwd_tile<D, CAUSAL>(st, k_st1, v_st1, (j + 1) * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+      fwd_tile<D, CAUSAL, F16>(st, k_st1, v_st1, (j + 1) * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
     wait_copies_and_barrier();
   }
 
@@ -279,10 +279,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int i4 = 0; i4 < 4; ++i4) {
         bf16x4 w;
-        w[0] = (bf16)(st.o[db][4 * i4 + 0] * inv);
-        w[1] = (bf16)(st.o[db][4 * i4 + 1] * inv);
-        w[2] = (bf16)(st.o[db][4 * i4 + 2] * inv);
-        w[3] = (bf16)(st.o[db][4 * i4 + 3] * inv);
+        w[0] = pack1<F16>(st.o[db][4 * i4 + 0] * inv);
+        w[1] = pack1<F16>(st.o[db][4 * i4 + 1] * inv);
+        w[2] = pack1<F16>(st.o[db][4 * i4 + 2] * inv);
+        w[3] = pack1<F16>(st.o[db][4 * i4 + 3] * inv);
         *reinterpret_cast<bf16x4*>(Oq + 32 * db + 8 * i4 + 4 * g) = w;
       }
     }
@@ -291,21 +291,26 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool F16>
 hipError_t launch(const FwdArgs& args, hipStream_t stream) {
   using C = FwdCfg<D>;
   FwdArgs a = args;
   a.n_qtiles = (a.L + C::BR - 1) / C::BR;
   const long long nblk = (long long)a.B * a.Hq * a.n_qtiles;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL>), dim3((unsigned)nblk), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, CAUSAL, F16>), dim3((unsigned)nblk), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <bool F16>
+hipError_t launch_typed(const FwdArgs& a, bool causal, hipStream_t stream) {
+  if (a.d == 128) return causal ? launch<128, true, F16>(a, stream) : launch<128, false, F16>(a, stream);
+  return causal ? launch<64, true, F16>(a, stream) : launch<64, false, F16>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, hipStream_t stream) {
-  if (a.d == 128) return causal ? launch<128, true>(a, stream) : launch<128, false>(a, stream);
-  return causal ? launch<64, true>(a, stream) : launch<64, false>(a, stream);
+  return a.f16 ? launch_typed<true>(a, causal, stream) : launch_typed<false>(a, causal, stream);
 }
 
 }  // namespace fa

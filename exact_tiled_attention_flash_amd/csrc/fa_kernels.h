@@ -15,6 +15,7 @@ struct FwdArgs {
   int window;        // 0 = none
   float scale_log2;  // softmax scale * log2(e)
   int n_qtiles;      // filled in by the launcher
+  bool f16;          // 16-bit inputs are fp16 (else bf16)
 };
 
 struct BwdArgs {
@@ -34,8 +35,10 @@ struct BwdArgs {
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
   int n_tiles;       // filled in by the launchers
+  bool f16;          // 16-bit inputs are fp16 (else bf16)
 };
 
+// 16-bit (bf16 or fp16, by a.f16) kernels
 hipError_t launch_fwd_bf16(const FwdArgs& a, bool causal, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, bool causal, hipStream_t stream);
 hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream);

@@ -25,7 +25,7 @@ int check_common(int B, int Hq, int Hkv, int L, int d, float scale, int causal, 
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (window < 0) return FA_ERR_INVALID_ARG;
   if (window > 0 && !causal) return FA_ERR_UNSUPPORTED;
-  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (Hq % Hkv != 0) return FA_ERR_GQA;
   // grid size: one work-group per (batch, head, 64-row tile) at most
@@ -56,9 +56,10 @@ extern "C" int flash_attn_fwd(const void* q, const void* k, const void* v, void*
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.d = d;
   a.window = window;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.f16 = dtype == FA_DTYPE_F16;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = (dtype == FA_DTYPE_BF16) ? fa::launch_fwd_bf16(a, causal != 0, s)
-                                          : fa::launch_fwd_f32(a, causal != 0, s);
+  hipError_t e = (dtype == FA_DTYPE_F32) ? fa::launch_fwd_f32(a, causal != 0, s)
+                                         : fa::launch_fwd_bf16(a, causal != 0, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -74,7 +75,7 @@ int bwd_setup(fa::BwdArgs& a, const void* workspace, size_t ws_bytes, int B, int
               float scale, int causal, int window, int dtype) {
   int rc = check_common(B, Hq, Hkv, L, d, scale, causal, window, dtype);
   if (rc != FA_OK) return rc;
-  if (dtype != FA_DTYPE_BF16) return FA_ERR_UNSUPPORTED;
+  if (dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 || ws_bytes < workspace_bytes(B, Hq, L))
     return FA_ERR_WORKSPACE;
   a.delta = static_cast<float*>(const_cast<void*>(workspace));
@@ -83,6 +84,7 @@ int bwd_setup(fa::BwdArgs& a, const void* workspace, size_t ws_bytes, int B, int
   a.window = window;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.f16 = dtype == FA_DTYPE_F16;
   return FA_OK;
 }
 

@@ -54,9 +54,12 @@
 extern "C" {
 #endif
 
-/* element types */
+/* element types: 32-bit float, bfloat16, IEEE half (fp16).  The 16-bit
+ * types take the MFMA path with float32 accumulation and round-to-nearest-even
+ * outputs; float32 takes a vector-ALU path (forward only). */
 #define FA_DTYPE_F32  0
 #define FA_DTYPE_BF16 1
+#define FA_DTYPE_F16  2
 
 /* return codes */
 #define FA_OK                0
@@ -74,8 +77,8 @@ extern "C" {
  *   softmax_scale                   : s > 0 and finite (usually 1/sqrt(d))
  *   causal                          : 0 or 1
  *   window                          : 0 = none; w >= 1 requires causal = 1
- *   dtype                           : FA_DTYPE_BF16 (d in {64,128}) or
- *                                     FA_DTYPE_F32  (d in {64,128})
+ *   dtype                           : FA_DTYPE_BF16, FA_DTYPE_F16 or
+ *                                     FA_DTYPE_F32, each with d in {64,128}
  * Sizes: 1 <= L <= 2^23 (one head must stay below 4 GiB), B, Hq, Hkv >= 1.
  * Extra device memory: none.  Returns FA_OK or a negative FA_ERR_* code.
  */
@@ -102,7 +105,8 @@ size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int 
  *                                     flash_attn_bwd_workspace_bytes() bytes,
  *                                     256-byte aligned; its contents on entry
  *                                     are ignored
- *   dtype                           : FA_DTYPE_BF16 with d in {64,128}
+ *   dtype                           : FA_DTYPE_BF16 or FA_DTYPE_F16, d in
+ *                                     {64,128} (FA_DTYPE_F32: unsupported)
  * Returns FA_OK or a negative FA_ERR_* code.
  */
 int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,

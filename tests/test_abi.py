@@ -46,6 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_binding_constants_match_header():
     c = header_constants()
     assert c["FA_DTYPE_F32"] == fa.FA_DTYPE_F32 and c["FA_DTYPE_BF16"] == fa.FA_DTYPE_BF16
+    assert c["FA_DTYPE_F16"] == fa.FA_DTYPE_F16
     assert c["FA_OK"] == 0
 
 
@@ -86,6 +87,8 @@ def test_fwd_rejects_invalid_arguments(lib):
     assert call_fwd(lib, d=96) == UNS
     assert call_fwd(lib, d=256) == UNS
     assert call_fwd(lib, dtype=7) == UNS
+    assert call_fwd(lib, dtype=3) == UNS
+    assert call_fwd(lib, dtype=fa.FA_DTYPE_F16, q=None) == INV    # fp16 passes the dtype check
     assert call_fwd(lib, causal=0, window=4) == UNS
     assert call_fwd(lib, Hq=6, Hkv=4) == GQA
 
@@ -101,6 +104,8 @@ def test_bwd_rejects_invalid_arguments(lib):
     assert call_bwd(lib, dq=None) == INV
     assert call_bwd(lib, lse=MISALIGNED) == INV
     assert call_bwd(lib, dtype=fa.FA_DTYPE_F32) == UNS
+    assert call_bwd(lib, dtype=3) == UNS
+    assert call_bwd(lib, dtype=fa.FA_DTYPE_F16, dq=None) == INV   # fp16 passes the dtype check
     assert call_bwd(lib, causal=0, window=3) == UNS
     assert call_bwd(lib, Hq=3, Hkv=2) == c["FA_ERR_GQA"]
 
@@ -132,6 +137,8 @@ def test_workspace_size_formula(lib):
     assert f(1, 1, 1, 40, 64, fa.FA_DTYPE_BF16) == 512
     assert f(1, 3, 2, 5, 64, fa.FA_DTYPE_BF16) == 0       # invalid sizes -> 0
     assert f(1, 2, 2, 5, 80, fa.FA_DTYPE_BF16) == 0
+    assert f(2, 32, 32, 4096, 128, fa.FA_DTYPE_F16) == 2 * 32 * 4096 * 8
+    assert f(2, 32, 32, 4096, 128, 3) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -94,6 +94,9 @@ SMALL = [
     W.small("bwd L640 window64 gqa4", 2, 4, 1, 640, 128, window=64, seed=209),
     W.small("bwd L2048 window5000", 1, 2, 2, 2048, 128, window=5000, seed=210),
     W.small("bwd MQA L513", 1, 8, 1, 513, 128, seed=211),
+    W.small("bwd fp16 L300 causal gqa2", 1, 4, 2, 300, 128, dtype=torch.float16, seed=212),
+    W.small("bwd fp16 L640 window64 d64", 1, 2, 2, 640, 64, dtype=torch.float16, window=64, seed=213),
+    W.small("bwd fp16 L200 noncausal", 2, 2, 2, 200, 128, dtype=torch.float16, causal=False, seed=214),
 ]
 
 
@@ -121,6 +124,10 @@ def check_heads_at_full_size(w, heads):
 
 def test_llama7b_layer_backward():
     check_heads_at_full_size(W.LLAMA7B_CAUSAL, [(0, 0), (1, 17)])
+
+
+def test_llama7b_layer_backward_fp16():
+    check_heads_at_full_size(W.LLAMA7B_CAUSAL.with_(name="llama7b-layer fp16", dtype=torch.float16), [(1, 3)])
 
 
 def test_long_context_backward():
