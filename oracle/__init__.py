@@ -11,7 +11,7 @@ Source pages (cited by site, title and section):
 
 * claspmoon.cn, "14 · 缩放定律与高效注意力" (Scaling laws and efficient
   attention) -- §3.2 Tiling, §3.3 backward recomputation, §3.5 usage,
-  §6 experiment 1.
+  §5.1 (ring attention: sequence parallelism), §6 experiment 1.
 * book.anysome.cn, "高效注意力" (Efficient attention) -- §2 FlashAttention,
   §3 MQA/GQA, §4 sliding window.
 * mdooai.com, "Ch.04 注意力优化：FlashAttention 与稀疏注意力" (Attention
@@ -28,12 +28,20 @@ window >= L == causal, agreement with PyTorch's float64 CPU
 ``scaled_dot_product_attention`` and with ``scipy.special.logsumexp``,
 torch float64 autograd and central finite differences for the backward,
 the exact identities sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i, and the
-tiled online-softmax recurrence agreeing with the direct definition.  Every
-oracle function has at least one pin; none is "parity unpinned".
+tiled online-softmax recurrence agreeing with the direct definition; for the
+chunked (ring-attention) functions: a chunk covering the whole sequence equals
+the full definition, merged partials over any partition of the keys equal the
+full result, summed chunk gradients equal the full gradient, brute-force
+loops on tiny chunks, and the merge against ``numpy.logaddexp``.  Every oracle
+function has at least one pin; none is "parity unpinned".
 """
 
 from .attention import (  # noqa: F401
     allowed_mask,
+    position_mask,
+    block_forward,
+    block_backward,
+    merge_partials,
     kv_head_of,
     probabilities,
     forward,

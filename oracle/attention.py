@@ -41,15 +41,17 @@ def kv_head_of(h, hq, hkv):
     return h // (hq // hkv)
 
 
-def allowed_mask(rows, L, causal, window):
-    """Boolean ``[len(rows), L]``: may query ``rows[r]`` attend to key ``j``?
+def position_mask(q_pos, k_pos, causal, window):
+    """Boolean ``[len(q_pos), len(k_pos)]``: may the query at sequence position
+    ``q_pos[r]`` attend to the key at position ``k_pos[c]``?
 
-    Causal per claspmoon.cn §3.5 (``is_causal``); window per book.anysome.cn
-    §4 (each token attends only to the w nearby, here preceding, tokens).
+    Causal per claspmoon.cn §3.5 (``is_causal``: keys at or before the query);
+    window per book.anysome.cn §4 (each token attends only to the w nearby,
+    here preceding, tokens, itself included).
     """
-    i = np.asarray(rows, dtype=np.int64)[:, None]
-    j = np.arange(L, dtype=np.int64)[None, :]
-    ok = np.ones((i.shape[0], L), dtype=bool)
+    i = np.asarray(q_pos, dtype=np.int64)[:, None]
+    j = np.asarray(k_pos, dtype=np.int64)[None, :]
+    ok = np.ones((i.shape[0], j.shape[1]), dtype=bool)
     if causal:
         ok &= j <= i
     if window > 0:
@@ -57,6 +59,12 @@ def allowed_mask(rows, L, causal, window):
             raise ValueError("a sliding window is defined only with causal masking")
         ok &= j >= i - window + 1
     return ok
+
+
+def allowed_mask(rows, L, causal, window):
+    """Boolean ``[len(rows), L]``: may query ``rows[r]`` attend to key ``j``?
+    Queries and keys of one sequence: positions are the indices."""
+    return position_mask(rows, np.arange(L), causal, window)
 
 
 def _masked_softmax_rows(S, ok):
@@ -240,3 +248,100 @@ def tiled_online_forward(q, k, v, scale, causal=False, window=0,
                     lse[b, h, rows] = np.where(empty, -np.inf,
                                                m + np.log(np.where(empty, 1.0, ell)))
     return O, lse
+
+
+# ---------------------------------------------------------------- blocks
+#
+# Sequence parallelism (claspmoon.cn "14 · 缩放定律与高效注意力" §5.1: ring
+# attention extends exact tiled attention across devices) splits the
+# sequence into chunks.  A query chunk holds the queries at positions
+# q_offset .. q_offset + Lq - 1, a key/value chunk the keys at k_offset ..
+# k_offset + Lk - 1, and masks are decided on those global positions.  One
+# step attends a query chunk to one key/value chunk and yields a partial
+# (O, LSE) normalised over that chunk's keys; partials over disjoint key sets
+# combine exactly (the online-softmax rescaling of transformer.xph.ink
+# "原理与机制" applied to whole chunks).
+
+
+def block_forward(q, k, v, scale, causal=False, window=0, q_offset=0, k_offset=0):
+    """Attention of a query chunk against one key/value chunk: float64
+    ``(O [B,Hq,Lq,d], LSE [B,Hq,Lq])``.
+
+    Per row: S = s q K_chunk^T, masked logits (on global positions) -> -inf,
+    A = softmax over the chunk's keys, O = A V_chunk, LSE = log sum exp S over
+    the allowed keys of the chunk.  A row with no allowed key in the chunk has
+    O = 0 and LSE = -inf (it contributes nothing to a merge).
+    """
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    ok = position_mask(q_offset + np.arange(Lq), k_offset + np.arange(Lk), causal, window)
+    O = np.empty((B, Hq, Lq, d))
+    lse = np.empty((B, Hq, Lq))
+    for b in range(B):
+        for h in range(Hq):
+            kh = kv_head_of(h, Hq, Hkv)
+            S = scale * (q[b, h] @ k[b, kh].T)
+            A, lse[b, h] = _masked_softmax_rows(S, ok)
+            O[b, h] = A @ v[b, kh]
+    return O, lse
+
+
+def merge_partials(o_a, lse_a, o_b, lse_b):
+    """Exact combination of two partial results over disjoint key sets.
+
+    With LSE = log(e^{LSE_a} + e^{LSE_b}) the combined softmax weights are the
+    partial ones times e^{LSE_a - LSE} and e^{LSE_b - LSE}, so
+    O = e^{LSE_a - LSE} O_a + e^{LSE_b - LSE} O_b.  A side with LSE = -inf
+    has no keys and weight 0; both -inf gives O = 0, LSE = -inf.
+    """
+    o_a, o_b = _as64(o_a), _as64(o_b)
+    lse_a, lse_b = _as64(lse_a), _as64(lse_b)
+    m = np.maximum(lse_a, lse_b)
+    empty = np.isneginf(m)
+    m_safe = np.where(empty, 0.0, m)
+    ea = np.exp(lse_a - m_safe)                 # exp(-inf) == 0
+    eb = np.exp(lse_b - m_safe)
+    tot = ea + eb
+    with np.errstate(divide="ignore"):
+        lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, tot)))
+    wa = np.where(empty, 0.0, ea / np.where(empty, 1.0, tot))
+    wb = np.where(empty, 0.0, eb / np.where(empty, 1.0, tot))
+    return wa[..., None] * o_a + wb[..., None] * o_b, lse
+
+
+def block_backward(q, k, v, dout, o, lse, scale, causal=False, window=0, q_offset=0, k_offset=0):
+    """One chunk pair's share of the gradient of sum(O * dO): float64
+    ``(dQ part [B,Hq,Lq,d], dK part [B,Hkv,Lk,d], dV part [B,Hkv,Lk,d])``.
+
+    ``o`` and ``lse`` are the query rows' results over ALL keys (every chunk),
+    so the chunk's slice of the attention matrix is A_blk = exp(S - LSE) on the
+    allowed keys (the recomputation of claspmoon.cn §3.3, restricted to the
+    chunk).  The softmax Jacobian row term D_i = sum over all keys of A_ij dA_ij
+    equals sum_c dO_ic O_ic, which only needs the row's O:
+        dV_blk = A_blk^T dO,   dA_blk = dO V_blk^T,
+        dS     = A_blk * (dA_blk - D),
+        dQ     = s dS K_blk,   dK_blk = s dS^T Q.
+    Summing dQ over the key chunks, and taking dK/dV per key chunk summed over
+    the query chunks, gives the full gradient.
+    """
+    q, k, v, dout, o, lse = (_as64(x) for x in (q, k, v, dout, o, lse))
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    ok = position_mask(q_offset + np.arange(Lq), k_offset + np.arange(Lk), causal, window)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            kh = kv_head_of(h, Hq, Hkv)
+            S = scale * (q[b, h] @ k[b, kh].T)
+            finite = ~np.isneginf(lse[b, h])[:, None]
+            A = np.where(ok & finite, np.exp(S - np.where(finite, lse[b, h][:, None], 0.0)), 0.0)
+            dv[b, kh] += A.T @ dout[b, h]
+            dA = dout[b, h] @ v[b, kh].T
+            D = (dout[b, h] * o[b, h]).sum(axis=-1, keepdims=True)
+            dS = A * (dA - D)
+            dq[b, h] = scale * (dS @ k[b, kh])
+            dk[b, kh] += scale * (dS.T @ q[b, h])
+    return dq, dk, dv

@@ -257,11 +257,99 @@ def pin_rows_subset(o):
         assert np.array_equal(O[:, :, rows], Or) and np.array_equal(l[:, :, rows], lr)
 
 
+# ---------------------------------------------------- chunked (ring-attention) pins
+
+def pin_block_whole_sequence_equals_full(o):
+    # one chunk holding every query and key is the full definition, and moving
+    # both chunks by the same offset changes nothing
+    for causal, window in MASKS:
+        q, k, v = rnd((1, 4, 10, 5), 60), rnd((1, 2, 10, 5), 61), rnd((1, 2, 10, 5), 62)
+        O, l = o.forward(q, k, v, 0.4, causal, window)
+        for off in (0, 1000):
+            Ob, lb = o.block_forward(q, k, v, 0.4, causal, window, off, off)
+            assert np.allclose(Ob, O, atol=1e-13, rtol=0) and np.allclose(lb, l, atol=1e-13, rtol=0)
+
+
+def pin_block_brute_force(o):
+    # tiny chunks at offsets, by explicit loops over the definition (empty rows: O = 0, LSE = -inf)
+    q, k, v = rnd((1, 2, 3, 2), 70), rnd((1, 1, 5, 2), 71), rnd((1, 1, 5, 2), 72)
+    for causal, window, qo, ko in [(True, 0, 4, 2), (True, 2, 4, 2), (False, 0, 0, 7), (True, 0, 0, 3),
+                                   (True, 3, 9, 3)]:
+        O, l = o.block_forward(q, k, v, 0.7, causal, window, qo, ko)
+        for h in range(2):
+            for i in range(3):
+                keys = [j for j in range(5)
+                        if (not causal or ko + j <= qo + i) and (window <= 0 or ko + j >= qo + i - window + 1)]
+                if not keys:
+                    assert np.isneginf(l[0, h, i]) and np.all(O[0, h, i] == 0.0)
+                    continue
+                e = [math.exp(0.7 * sum(q[0, h, i, c] * k[0, 0, j, c] for c in range(2))) for j in keys]
+                assert abs(l[0, h, i] - math.log(sum(e))) < 1e-12
+                for c in range(2):
+                    ref = sum(w * v[0, 0, j, c] for w, j in zip(e, keys)) / sum(e)
+                    assert abs(O[0, h, i, c] - ref) < 1e-12
+
+
+def pin_merged_partials_equal_full(o):
+    # partial results over any partition of the keys merge to the full result
+    L = 23
+    for causal, window in MASKS:
+        q, k, v = rnd((2, 4, L, 6), 80), rnd((2, 2, L, 6), 81), rnd((2, 2, L, 6), 82)
+        O, l = o.forward(q, k, v, 0.3, causal, window)
+        for cuts in ([0, 7, 23], [0, 1, 12, 20, 23]):
+            for r0, r1 in [(0, 23), (5, 16)]:
+                acc = None
+                for c0, c1 in zip(cuts[:-1], cuts[1:]):
+                    part = o.block_forward(q[:, :, r0:r1], k[:, :, c0:c1], v[:, :, c0:c1], 0.3, causal, window,
+                                           r0, c0)
+                    acc = part if acc is None else o.merge_partials(*acc, *part)
+                assert np.allclose(acc[0], O[:, :, r0:r1], atol=1e-12, rtol=0)
+                assert np.allclose(acc[1], l[:, :, r0:r1], atol=1e-12, rtol=0)
+        a = o.block_forward(q, k[:, :, :9], v[:, :, :9], 0.3, causal, window, 0, 0)
+        b = o.block_forward(q, k[:, :, 9:], v[:, :, 9:], 0.3, causal, window, 0, 9)
+        m1, m2 = o.merge_partials(*a, *b), o.merge_partials(*b, *a)
+        assert np.allclose(m1[0], m2[0], atol=1e-14, rtol=0) and np.allclose(m1[1], m2[1], atol=1e-14, rtol=0)
+
+
+def pin_merge_edge_cases(o):
+    oa_, la = rnd((1, 1, 3, 2), 90), np.array([[[0.3, -np.inf, 2.0]]])
+    ob_, lb = rnd((1, 1, 3, 2), 91), np.array([[[-np.inf, -np.inf, -1.0]]])
+    O, l = o.merge_partials(oa_, la, ob_, lb)
+    assert np.array_equal(O[0, 0, 0], oa_[0, 0, 0]) and l[0, 0, 0] == 0.3      # an empty side is neutral
+    assert np.array_equal(O[0, 0, 1], [0.0, 0.0]) and np.isneginf(l[0, 0, 1])   # both sides empty
+    assert abs(l[0, 0, 2] - np.logaddexp(2.0, -1.0)) < 1e-14
+    w = 1.0 / (1.0 + math.exp(-3.0))
+    assert np.allclose(O[0, 0, 2], w * oa_[0, 0, 2] + (1 - w) * ob_[0, 0, 2], atol=1e-14, rtol=0)
+
+
+def pin_block_backward_sums_to_full(o):
+    L = 17
+    for causal, window in MASKS:
+        q, k, v, do = rnd((1, 4, L, 5), 100), rnd((1, 2, L, 5), 101), rnd((1, 2, L, 5), 102), rnd((1, 4, L, 5), 103)
+        dq, dk, dv = o.backward(q, k, v, do, 0.6, causal, window)
+        O, l = o.forward(q, k, v, 0.6, causal, window)
+        gq, gk, gv = np.zeros_like(dq), np.zeros_like(dk), np.zeros_like(dv)
+        qc, kc = [0, 6, 17], [0, 4, 11, 17]
+        for r0, r1 in zip(qc[:-1], qc[1:]):
+            for c0, c1 in zip(kc[:-1], kc[1:]):
+                pq, pk, pv = o.block_backward(q[:, :, r0:r1], k[:, :, c0:c1], v[:, :, c0:c1], do[:, :, r0:r1],
+                                              O[:, :, r0:r1], l[:, :, r0:r1], 0.6, causal, window, r0, c0)
+                gq[:, :, r0:r1] += pq
+                gk[:, :, c0:c1] += pk
+                gv[:, :, c0:c1] += pv
+        for g, ref in ((gq, dq), (gk, dk), (gv, dv)):
+            assert np.allclose(g, ref, atol=1e-12, rtol=0)
+
+
+BLOCK_PINS = [pin_block_whole_sequence_equals_full, pin_block_brute_force, pin_merged_partials_equal_full,
+              pin_merge_edge_cases, pin_block_backward_sums_to_full]
+
+
 PINS = [pin_rows_stochastic, pin_two_key_worked_example, pin_length_one, pin_zero_query_is_mean,
         pin_identical_keys, pin_convexity, pin_shift_invariance, pin_permutation_noncausal,
         pin_gqa_is_repeated_mha, pin_window_at_least_L_is_causal, pin_torch_sdpa_and_logsumexp,
         pin_backward_vs_torch_autograd, pin_backward_finite_differences, pin_backward_identities,
-        pin_tiled_recurrence_equals_direct, pin_rows_subset]
+        pin_tiled_recurrence_equals_direct, pin_rows_subset] + BLOCK_PINS
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -347,3 +435,44 @@ def test_unallowed_window_without_causal_is_rejected():
         oracle.allowed_mask(np.arange(4), 4, False, 2)
     with pytest.raises(ValueError):
         oracle.kv_head_of(0, 6, 4)
+
+
+def test_planted_block_offset_sign(monkeypatch):
+    good = oa.position_mask
+    # queries and keys swapped in the causal comparison
+    monkeypatch.setattr(oa, "position_mask", lambda qp, kp, causal, window: good(kp, qp, causal, window).T)
+    assert _some_pin_fails(BLOCK_PINS)
+
+
+def test_planted_merge_unnormalised(monkeypatch):
+    def bad(o_a, lse_a, o_b, lse_b):
+        lse = np.logaddexp(lse_a, lse_b)
+        return np.exp(lse_a)[..., None] * o_a + np.exp(lse_b)[..., None] * o_b, lse   # weights not divided
+    monkeypatch.setattr(oa, "merge_partials", bad)
+    monkeypatch.setattr(oracle, "merge_partials", bad)
+    assert _some_pin_fails(BLOCK_PINS)
+
+
+def test_planted_block_backward_D_over_chunk(monkeypatch):
+    # each chunk treated as if it held the whole row (its own softmax and its own D)
+    monkeypatch.setattr(oracle, "block_backward",
+                        lambda q, k, v, dout, o, lse, scale, causal=False, window=0, q_offset=0, k_offset=0:
+                        _chunk_local_backward(q, k, v, dout, scale, causal, window, q_offset, k_offset))
+    assert _some_pin_fails([pin_block_backward_sums_to_full])
+
+
+def _chunk_local_backward(q, k, v, dout, scale, causal, window, q_offset, k_offset):
+    """A wrong chunk gradient: the chunk treated as if it were the whole row (own softmax)."""
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k.shape[1], k.shape[2]
+    ok = oa.position_mask(q_offset + np.arange(Lq), k_offset + np.arange(Lk), causal, window)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            kh = oa.kv_head_of(h, Hq, Hkv)
+            A, _ = oa._masked_softmax_rows(scale * (q[b, h] @ k[b, kh].T), ok)
+            dv[b, kh] += A.T @ dout[b, h]
+            dS = oa._softmax_backward(A, dout[b, h] @ v[b, kh].T)
+            dq[b, h] = scale * (dS @ k[b, kh])
+            dk[b, kh] += scale * (dS.T @ q[b, h])
+    return dq, dk, dv
