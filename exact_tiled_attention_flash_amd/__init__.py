@@ -20,7 +20,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "strerror", "library", "library_path",
+__all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "fwd_block", "bwd_block", "merge",
+           "strerror", "library", "library_path",
            "FlashAttentionFunction", "scaled_dot_product_attention",
            "FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "EXPORTED_SYMBOLS"]
 
@@ -31,6 +32,7 @@ _DTYPES = {torch.float32: FA_DTYPE_F32, torch.bfloat16: FA_DTYPE_BF16, torch.flo
 
 EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_bytes",
                     "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
+                    "flash_attn_fwd_block", "flash_attn_merge", "flash_attn_bwd_block",
                     "flash_attn_strerror", "flash_attn_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -64,6 +66,13 @@ def library():
     lib.flash_attn_bwd_dkdv.restype = i
     lib.flash_attn_bwd_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, i, i, i, vp]
     lib.flash_attn_bwd_dq.restype = i
+    lib.flash_attn_fwd_block.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, i, i, vp]
+    lib.flash_attn_fwd_block.restype = i
+    lib.flash_attn_merge.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp]
+    lib.flash_attn_merge.restype = i
+    lib.flash_attn_bwd_block.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                         i, i, i, i, i, i, f, i, i, i, i, i, vp]
+    lib.flash_attn_bwd_block.restype = i
     lib.flash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.flash_attn_bwd_workspace_bytes.restype = sz
     lib.flash_attn_strerror.argtypes = [i]
@@ -184,6 +193,75 @@ def bwd_stages(q, k, v, o, lse, dout, causal=False, window=0, scale=None, worksp
            "flash_attn_bwd_dq")
     if between:
         between("dq")
+    return dq, dk, dv
+
+
+def _chunk_shapes(q, k, v):
+    """Shapes of a (query chunk, key/value chunk) pair: q [B,Hq,Lq,d], k/v [B,Hkv,Lk,d]."""
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B, Hq, Lq, d] and k, v [B, Hkv, Lk, d]")
+    B, Hq, Lq, d = q.shape
+    if k.shape[0] != B or k.shape[3] != d:
+        raise ValueError("k and v must share B and d with q")
+    for t in (q, k, v):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q, k, v must be contiguous CUDA tensors of one dtype")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("chunk pairs take bfloat16 or float16")
+    return B, Hq, k.shape[1], Lq, k.shape[2], d
+
+
+def fwd_block(q, k, v, causal=False, window=0, q_offset=0, k_offset=0, scale=None, out=None, lse=None):
+    """One ring-attention step: the queries at positions ``q_offset + i`` attend to the keys at
+    ``k_offset + j`` only.  Returns the partial ``(o, lse)`` over this key chunk (rows with no
+    allowed key: o = 0, lse = -inf); combine partials with ``merge``."""
+    B, Hq, Hkv, Lq, Lk, d = _chunk_shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if lse is None else lse
+    rc = library().flash_attn_fwd_block(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lk, d,
+                                        scale, int(bool(causal)), int(window), int(q_offset), int(k_offset),
+                                        _DTYPES[q.dtype], _stream(q))
+    _check(rc, "flash_attn_fwd_block")
+    return out, lse
+
+
+def merge(o_a, lse_a, o_b, lse_b, out=None, lse_out=None):
+    """Exact combination of two partial results over disjoint key sets.  ``out``/``lse_out``
+    may be ``o_a``/``lse_a`` (in-place accumulation)."""
+    if o_a.shape != o_b.shape or o_a.dtype != o_b.dtype or o_a.dim() != 4:
+        raise ValueError("partials must be [B, Hq, L, d] of one dtype")
+    B, Hq, L, d = o_a.shape
+    for t in (lse_a, lse_b):
+        if t.shape != (B, Hq, L) or t.dtype != torch.float32:
+            raise ValueError("log-sum-exp partials must be float32 [B, Hq, L]")
+    for t in (o_a, o_b, lse_a, lse_b):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("partials must be contiguous CUDA tensors")
+    out = torch.empty_like(o_a) if out is None else out
+    lse_out = torch.empty_like(lse_a) if lse_out is None else lse_out
+    rc = library().flash_attn_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out), _ptr(lse_out),
+                                    B, Hq, L, d, _DTYPES[o_a.dtype], _stream(o_a))
+    _check(rc, "flash_attn_merge")
+    return out, lse_out
+
+
+def bwd_block(q, k, v, o, lse, dout, causal=False, window=0, q_offset=0, k_offset=0, scale=None,
+              workspace=None, dq=None, dk=None, dv=None):
+    """One ring-attention backward step: this chunk pair's contributions ``(dq, dk, dv)`` to the
+    gradient, given the query rows' full ``o`` and ``lse`` (over all key chunks)."""
+    B, Hq, Hkv, Lq, Lk, d = _chunk_shapes(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = bwd_workspace_bytes(B, Hq, Hkv, Lq, d, q.dtype)
+    workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    rc = library().flash_attn_bwd_block(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                        _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), B, Hq, Hkv, Lq, Lk,
+                                        d, scale, int(bool(causal)), int(window), int(q_offset), int(k_offset),
+                                        _DTYPES[q.dtype], _stream(q))
+    _check(rc, "flash_attn_bwd_block")
     return dq, dk, dv
 
 

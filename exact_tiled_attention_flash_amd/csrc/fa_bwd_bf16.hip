@@ -103,7 +103,7 @@ struct KVAddr {
 template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void kv_tile(KVState<D>& st, const KVAddr<D>& ad, const char* kblk, const char* vblk,
                                         const char* qbuf, const char* dobuf, const float* stats, int q0, int L,
-                                        int window, int qh, int key_w0, float c, int lane) {
+                                        int shift, int window, int qh, int key_w0, float c, int lane) {
   using C = KVCfg<D>;
   const int g = lane >> 5;
   const int my_key = key_w0 + (lane & 31);
@@ -116,8 +116,8 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const KVAddr<D>& ad, con
 
   // P = exp2(S*s*log2e - LSE*log2e), zero where masked
   const int qw0 = q0 + 32 * qh;           // first query of this wave's half
-  const bool need_mask = (qw0 + 32 > L) || (CAUSAL && qw0 < key_w0 + 31) ||
-                         (window > 0 && qw0 + 31 > key_w0 + window - 1);
+  const bool need_mask = (qw0 + 32 > L) || (CAUSAL && qw0 + shift < key_w0 + 31) ||
+                         (window > 0 && qw0 + 31 + shift > key_w0 + window - 1);
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
     const f32x4 l4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (32 * qh + 8 * i4 + 4 * g));
@@ -130,7 +130,7 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const KVAddr<D>& ad, con
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int q = qw0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      const bool ok = q < L && (!CAUSAL || my_key <= q) && (window <= 0 || q - my_key < window);
+      const bool ok = q < L && (!CAUSAL || my_key <= q + shift) && (window <= 0 || q + shift - my_key < window);
       p[i] = ok ? p[i] : 0.f;
     }
   }
@@ -191,7 +191,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 5, ln = lane & 31;
   const int kb = wave & 3, qh = wave >> 2;
-  const int L = a.L, window = a.window;
+  // L query rows, Lk keys; query row i sits at key position i + shift
+  const int L = a.L, Lk = a.Lk, shift = a.shift, window = a.window;
   const int G = a.Hq / a.Hkv;
 
   // (batch, K/V head) major; the key tile with the most queries first
@@ -202,13 +203,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int key_wg0 = kt * C::BK;
   const int key_w0 = key_wg0 + 32 * kb;
 
-  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
-  const unsigned head_bytes = (unsigned)L * (2 * D);
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * Lk) * D;
+  const unsigned head_bytes = (unsigned)Lk * (2 * D);      // one K/V head
+  const unsigned qhead_bytes = (unsigned)L * (2 * D);      // one Q/dO head
 
-  // queries that can see this work-group's keys
-  const int q_begin = CAUSAL ? key_wg0 : 0;
-  const int q_end = (window > 0) ? min(L, key_wg0 + C::BK - 1 + window) : L;
-  const int qt_lo = q_begin / C::BQ, qt_hi = (q_end - 1) / C::BQ;
+  // queries that can see this work-group's keys (none: only between chunks)
+  const int q_begin = CAUSAL ? max(0, key_wg0 - shift) : 0;
+  const int q_end = (window > 0) ? min(L, key_wg0 + C::BK - 1 + window - shift) : L;
+  const bool empty = q_end <= q_begin;
+  const int qt_lo = empty ? 0 : q_begin / C::BQ, qt_hi = empty ? -1 : (q_end - 1) / C::BQ;
   const int nq = qt_hi - qt_lo + 1;
   const int n_it = G * nq;
 
@@ -228,8 +231,8 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   auto issue = [&](int it, char* qs, char* dos, float* ss) {
     const int hq = hk * G + it / nq, q0 = q0_of(it);
     const size_t qoff = ((size_t)(b * a.Hq + hq) * L) * D;
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(reinterpret_cast<const bf16*>(a.q) + qoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t drs = make_rsrc(reinterpret_cast<const bf16*>(a.dout) + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(reinterpret_cast<const bf16*>(a.q) + qoff, qhead_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(reinterpret_cast<const bf16*>(a.dout) + qoff, qhead_bytes);
     const int soff = q0 * (2 * D);
 #pragma unroll
     for (int i = 0; i < C::QPER; ++i) {
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       buf2lds16(vrs, src, soff, v_blk + n * 1024);
     }
   }
-  issue(0, q_st0, do_st0, stat_st0);
+  if (n_it > 0) issue(0, q_st0, do_st0, stat_st0);
 
   KVState<D> st;
 #pragma unroll
@@ -268,19 +271,20 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const float c = a.scale_log2;
   auto wave_needs = [&](int q0) {
     const int qw0 = q0 + 32 * qh;
-    return key_w0 < L && qw0 < L && (!CAUSAL || qw0 + 31 >= key_w0) && (window <= 0 || qw0 <= key_w0 + 31 + window - 1);
+    return key_w0 < Lk && qw0 < L && (!CAUSAL || qw0 + 31 + shift >= key_w0) &&
+           (window <= 0 || qw0 + shift <= key_w0 + 31 + window - 1);
   };
 
   wait_copies_and_barrier();
   for (int it = 0; it < n_it; it += 2) {
     if (it + 1 < n_it) issue(it + 1, q_st1, do_st1, stat_st1);
     if (wave_needs(q0_of(it)))
-      kv_tile<D, CAUSAL, F16>(st, ad, k_blk, v_blk, q_st0, do_st0, stat_st0, q0_of(it), L, window, qh, key_w0, c, lane);
+      kv_tile<D, CAUSAL, F16>(st, ad, k_blk, v_blk, q_st0, do_st0, stat_st0, q0_of(it), L, shift, window, qh, key_w0, c, lane);
     wait_copies_and_barrier();
     if (it + 1 >= n_it) break;
     if (it + 2 < n_it) issue(it + 2, q_st0, do_st0, stat_st0);
     if (wave_needs(q0_of(it + 1)))
-      kv_tile<D, CAUSAL, F16>(st, ad, k_blk, v_blk, q_st1, do_st1, stat_st1, q0_of(it + 1), L, window, qh, key_w0, c, lane);
+      kv_tile<D, CAUSAL, F16>(st, ad, k_blk, v_blk, q_st1, do_st1, stat_st1, q0_of(it + 1), L, shift, window, qh, key_w0, c, lane);
     wait_copies_and_barrier();
   }
 
@@ -319,7 +323,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = key_w0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (key < L) {
+      if (key < Lk) {
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
           dKh[(size_t)key * D + 32 * db + ln] = pack1<F16>(st.dk[db][i] * s);
@@ -372,10 +376,10 @@ struct QAddr {
 
 template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const char* kbuf, const char* vbuf, int k0,
-                                       int L, int window, int my_q, int q_w0, int wq_hi, float c, int lane) {
+                                       int Lk, int window, int my_q, int q_w0, int wq_hi, float c, int lane) {
   using C = QCfg<D>;
   const int g = lane >> 5;
-  const bool need_mask = (k0 + C::BC > L) || (CAUSAL && k0 + C::BC - 1 > q_w0) ||
+  const bool need_mask = (k0 + C::BC > Lk) || (CAUSAL && k0 + C::BC - 1 > q_w0) ||
                          (window > 0 && k0 < wq_hi - window + 1);
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
@@ -390,7 +394,7 @@ __device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const 
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int kk = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-        const bool ok = kk < L && (!CAUSAL || kk <= my_q) && (window <= 0 || kk > my_q - window);
+        const bool ok = kk < Lk && (!CAUSAL || kk <= my_q) && (window <= 0 || kk > my_q - window);
         p[i] = ok ? p[i] : 0.f;
       }
     }
@@ -428,7 +432,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 5, ln = lane & 31;
-  const int L = a.L, window = a.window;
+  // L query rows, Lk keys; query row i sits at key position i + shift
+  const int L = a.L, Lk = a.Lk, shift = a.shift, window = a.window;
 
   const int r = xcd_remap(blockIdx.x, gridDim.x);
   int bh, qt_rank;
@@ -438,8 +443,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int hk = h / (a.Hq / a.Hkv);
 
   const size_t q_off = ((size_t)(b * a.Hq + h) * L) * D;
-  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
-  const unsigned head_bytes = (unsigned)L * (2 * D);
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * Lk) * D;
+  const unsigned head_bytes = (unsigned)Lk * (2 * D);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kv_off, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16*>(a.v) + kv_off, head_bytes);
 
@@ -447,10 +452,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   const int q_w0 = q_wg0 + 32 * wave;
   const int my_q = q_w0 + ln;
   const int wq_hi = min(q_w0 + 31, L - 1);
+  // the same three in key coordinates
+  const int dq_w0 = q_w0 + shift, dmy_q = my_q + shift, dwq_hi = wq_hi + shift;
 
-  const int kv_end = CAUSAL ? min(L, q_wg0 + C::BQ) : L;
-  const int kv_begin = (window > 0) ? max(0, q_wg0 - window + 1) : 0;
-  const int j_lo = kv_begin / C::BC, j_hi = (kv_end - 1) / C::BC;
+  const int kv_end = CAUSAL ? min(Lk, min(L, q_wg0 + C::BQ) + shift) : Lk;
+  const int kv_begin = (window > 0) ? max(0, q_wg0 + shift - window + 1) : 0;
+  const bool empty = kv_end <= kv_begin;     // only between chunks of a ring step
+  const int j_lo = empty ? 0 : kv_begin / C::BC, j_hi = empty ? -1 : (kv_end - 1) / C::BC;
 
   QAddr<D> ad;
 #pragma unroll
@@ -474,7 +482,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     for (int i = 0; i < C::VPER; ++i)
       if (wave + C::kWaves * i < C::VCOPIES) buf2lds16(vrs, ad.vcopy[i], soff, vb + (wave + C::kWaves * i) * 1024);
   };
-  issue(j_lo, k_st0, v_st0);
+  if (!empty) issue(j_lo, k_st0, v_st0);
 
   QState<D> st;
   {
@@ -494,19 +502,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
   const float c = a.scale_log2;
   auto wave_needs = [&](int k0) {
-    return (q_w0 < L) && (!CAUSAL || k0 <= wq_hi) && (window <= 0 || k0 + C::BC - 1 >= q_w0 - window + 1);
+    return (q_w0 < L) && (!CAUSAL || k0 <= dwq_hi) && (window <= 0 || k0 + C::BC - 1 >= dq_w0 - window + 1);
   };
 
   wait_copies_and_barrier();
   for (int j = j_lo; j <= j_hi; j += 2) {
     if (j < j_hi) issue(j + 1, k_st1, v_st1);
     if (wave_needs(j * C::BC))
-      q_tile<D, CAUSAL, F16>(st, ad, k_st0, v_st0, j * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+      q_tile<D, CAUSAL, F16>(st, ad, k_st0, v_st0, j * C::BC, Lk, window, dmy_q, dq_w0, dwq_hi, c, lane);
     wait_copies_and_barrier();
     if (j + 1 > j_hi) break;
     if (j + 1 < j_hi) issue(j + 2, k_st0, v_st0);
     if (wave_needs((j + 1) * C::BC))
-      q_tile<D, CAUSAL, F16>(st, ad, k_st1, v_st1, (j + 1) * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+      q_tile<D, CAUSAL, F16>(st, ad, k_st1, v_st1, (j + 1) * C::BC, Lk, window, dmy_q, dq_w0, dwq_hi, c, lane);
     wait_copies_and_barrier();
   }
 
@@ -542,7 +550,7 @@ hipError_t launch_delta(const BwdArgs& a, hipStream_t stream) {
 template <int D, bool CAUSAL, bool F16>
 hipError_t launch_dkdv(const BwdArgs& args, hipStream_t stream) {
   BwdArgs a = args;
-  a.n_tiles = (a.L + KVCfg<D>::BK - 1) / KVCfg<D>::BK;
+  a.n_tiles = (a.Lk + KVCfg<D>::BK - 1) / KVCfg<D>::BK;
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, F16>), dim3((unsigned)((long long)a.B * a.Hkv * a.n_tiles)),
                      dim3(64 * KVCfg<D>::kWaves), 0, stream, a);
   return hipGetLastError();

@@ -105,7 +105,7 @@ __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(
 // One key tile for one wave: S^T, mask, online softmax, O^T += V^T P^T.
 template <int D, bool CAUSAL, bool F16>
 __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, const char* vbuf, int k0,
-                                         int L, int window, int my_q, int q_w0, int wq_hi, float c,
+                                         int Lk, int window, int my_q, int q_w0, int wq_hi, float c,
                                          int lane) {
   using C = FwdCfg<D>;
   const int g = lane >> 5, ln = lane & 31;
@@ -126,15 +126,15 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
   }
 
   // 2. mask, only on tiles that straddle a boundary (wave-uniform decision)
-  const bool need_mask = (k0 + C::BC > L) || (CAUSAL && k0 + C::BC - 1 > q_w0) ||
+  const bool need_mask = (k0 + C::BC > Lk) || (CAUSAL && k0 + C::BC - 1 > q_w0) ||
                          (window > 0 && k0 < wq_hi - window + 1);
   if (need_mask) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kk0 = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
       const int kk1 = kk0 + 32;
-      const bool ok0 = kk0 < L && (!CAUSAL || kk0 <= my_q) && (window <= 0 || kk0 > my_q - window);
-      const bool ok1 = kk1 < L && (!CAUSAL || kk1 <= my_q) && (window <= 0 || kk1 > my_q - window);
+      const bool ok0 = kk0 < Lk && (!CAUSAL || kk0 <= my_q) && (window <= 0 || kk0 > my_q - window);
+      const bool ok1 = kk1 < Lk && (!CAUSAL || kk1 <= my_q) && (window <= 0 || kk1 > my_q - window);
       if (!ok0) s0[i] = -INFINITY;
       if (!ok1) s1[i] = -INFINITY;
     }
@@ -215,11 +215,13 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int qt = CAUSAL ? a.n_qtiles - 1 - qt_rank : qt_rank;
   const int b = bh / a.Hq, h = bh % a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
-  const int L = a.L;
+  // L query rows; Lk keys; query row i sits at key position i + shift (the
+  // chunks of a ring step), so every mask compares key j with i + shift
+  const int L = a.L, Lk = a.Lk, shift = a.shift;
 
   const bf16* __restrict__ Qh = reinterpret_cast<const bf16*>(a.q) + ((size_t)(b * a.Hq + h) * L) * D;
-  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
-  const unsigned head_bytes = (unsigned)L * (2 * D);
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * Lk) * D;
+  const unsigned head_bytes = (unsigned)Lk * (2 * D);
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kv_off, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16*>(a.v) + kv_off, head_bytes);
 
@@ -227,16 +229,19 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int q_w0 = q_wg0 + 32 * wave;
   const int my_q = q_w0 + ln;
   const int wq_hi = min(q_w0 + 31, L - 1);
+  // the same three in key coordinates
+  const int dq_w0 = q_w0 + shift, dmy_q = my_q + shift, dwq_hi = wq_hi + shift;
   const int window = a.window;
 
   // ---- key-tile range of the work-group
-  const int kv_end = CAUSAL ? min(L, q_wg0 + C::BR) : L;
-  const int kv_begin = (window > 0) ? max(0, q_wg0 - window + 1) : 0;
-  const int j_lo = kv_begin / C::BC, j_hi = (kv_end - 1) / C::BC;
+  const int kv_end = CAUSAL ? min(Lk, min(L, q_wg0 + C::BR) + shift) : Lk;
+  const int kv_begin = (window > 0) ? max(0, q_wg0 + shift - window + 1) : 0;
+  const bool empty = kv_end <= kv_begin;     // possible between chunks of a ring step
+  const int j_lo = empty ? 0 : kv_begin / C::BC, j_hi = empty ? -1 : (kv_end - 1) / C::BC;
 
   CopyPlan<D> cp;
   make_copy_plan<D>(cp, wave, lane);
-  issue_kv<D>(cp, krs, vrs, j_lo * C::BC, k_st0, v_st0, wave);
+  if (!empty) issue_kv<D>(cp, krs, vrs, j_lo * C::BC, k_st0, v_st0, wave);
 
   FwdState<D> st;
 #pragma unroll
@@ -251,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const float c = a.scale_log2;
 
   auto wave_needs = [&](int k0) {
-    return (q_w0 < L) && (!CAUSAL || k0 <= wq_hi) && (window <= 0 || k0 + C::BC - 1 >= q_w0 - window + 1);
+    return (q_w0 < L) && (!CAUSAL || k0 <= dwq_hi) && (window <= 0 || k0 + C::BC - 1 >= dq_w0 - window + 1);
   };
 
   wait_copies_and_barrier();
@@ -260,19 +265,20 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int j = j_lo; j <= j_hi; j += 2) {
     if (j < j_hi) issue_kv<D>(cp, krs, vrs, (j + 1) * C::BC, k_st1, v_st1, wave);
     if (wave_needs(j * C::BC))
-      fwd_tile<D, CAUSAL, F16>(st, k_st0, v_st0, j * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+      fwd_tile<D, CAUSAL, F16>(st, k_st0, v_st0, j * C::BC, Lk, window, dmy_q, dq_w0, dwq_hi, c, lane);
     wait_copies_and_barrier();
     if (j + 1 > j_hi) break;
     if (j + 1 < j_hi) issue_kv<D>(cp, krs, vrs, (j + 2) * C::BC, k_st0, v_st0, wave);
     if (wave_needs((j + 1) * C::BC))
-      fwd_tile<D, CAUSAL, F16>(st, k_st1, v_st1, (j + 1) * C::BC, L, window, my_q, q_w0, wq_hi, c, lane);
+      fwd_tile<D, CAUSAL, F16>(st, k_st1, v_st1, (j + 1) * C::BC, Lk, window, dmy_q, dq_w0, dwq_hi, c, lane);
     wait_copies_and_barrier();
   }
 
-  // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2
+  // ---- epilogue: O = O_acc / l, LSE = (m + log2 l) * ln 2; a row that saw no
+  // allowed key (only between chunks of a ring step) gets O = 0, LSE = -inf
   const float l_tot = pair_sum(st.l_run);
   if (my_q < L) {
-    const float inv = 1.f / l_tot;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     bf16* Oq = reinterpret_cast<bf16*>(a.o) + ((size_t)(b * a.Hq + h) * L + my_q) * D;
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
@@ -287,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
       }
     }
     if (a.lse != nullptr && g == 0)
-      a.lse[(size_t)(b * a.Hq + h) * L + my_q] = (st.m_run + __log2f(l_tot)) * kLn2;
+      a.lse[(size_t)(b * a.Hq + h) * L + my_q] = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 

@@ -11,7 +11,9 @@ struct FwdArgs {
   const void* v;
   void* o;
   float* lse;        // may be null
-  int B, Hq, Hkv, L, d;
+  int B, Hq, Hkv, L, d;  // L = query rows
+  int Lk;            // keys (= L except for chunk pairs)
+  int shift;         // query row i sits at key position i + shift (0 except for chunk pairs)
   int window;        // 0 = none
   float scale_log2;  // softmax scale * log2(e)
   int n_qtiles;      // filled in by the launcher
@@ -30,12 +32,24 @@ struct BwdArgs {
   void* dv;
   float* delta;      // workspace: D_i = sum_c dO_ic * O_ic, [B, Hq, L]
   float* lse2;       // workspace: LSE_i * log2(e), [B, Hq, L]
-  int B, Hq, Hkv, L, d;
+  int B, Hq, Hkv, L, d;  // L = query rows
+  int Lk;            // keys (= L except for chunk pairs)
+  int shift;         // query row i sits at key position i + shift (0 except for chunk pairs)
   int window;
   float scale;       // softmax scale
   float scale_log2;  // softmax scale * log2(e)
   int n_tiles;       // filled in by the launchers
   bool f16;          // 16-bit inputs are fp16 (else bf16)
+};
+
+struct MergeArgs {
+  const void* o_a;
+  const float* lse_a;
+  const void* o_b;
+  const float* lse_b;
+  void* o;           // may be o_a (in-place accumulation)
+  float* lse;        // may be lse_a
+  long long rows;    // B * Hq * L
 };
 
 // 16-bit (bf16 or fp16, by a.f16) kernels
@@ -46,5 +60,7 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
 hipError_t launch_bwd_preprocess_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
+// exact combination of two partial results; dtype 0 fp32, 1 bf16, 2 fp16
+hipError_t launch_merge(const MergeArgs& a, int d, int dtype, hipStream_t stream);
 
 }  // namespace fa

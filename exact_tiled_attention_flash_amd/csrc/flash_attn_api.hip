@@ -40,20 +40,28 @@ size_t workspace_bytes(int B, int Hq, int L) {
   return (raw + 255) & ~(size_t)255;
 }
 
-}  // namespace
+// Chunk positions: offsets are non-negative and at most 2^30, so every
+// position (offset + index < 2^30 + 2^23) fits an int.
+constexpr int kMaxOffset = 1 << 30;
 
-extern "C" int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                              int B, int Hq, int Hkv, int L, int d,
-                              float softmax_scale, int causal, int window, int dtype, void* stream) {
-  int rc = check_common(B, Hq, Hkv, L, d, softmax_scale, causal, window, dtype);
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Lq,
+               int Lk, int d, float softmax_scale, int causal, int window, int q_offset, int k_offset, int dtype,
+               void* stream) {
+  int rc = check_common(B, Hq, Hkv, Lq, d, softmax_scale, causal, window, dtype);
   if (rc != FA_OK) return rc;
+  if (Lk < 1 || Lk > kMaxL || q_offset < 0 || k_offset < 0 || q_offset > kMaxOffset || k_offset > kMaxOffset)
+    return FA_ERR_INVALID_ARG;
+  // the float32 path covers whole sequences only
+  if (dtype == FA_DTYPE_F32 && (Lk != Lq || q_offset != k_offset)) return FA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !o) return FA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return FA_ERR_INVALID_ARG;
 
   fa::FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.d = d;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = Lq; a.d = d;
+  a.Lk = Lk;
+  a.shift = q_offset - k_offset;
   a.window = window;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.f16 = dtype == FA_DTYPE_F16;
@@ -61,6 +69,22 @@ extern "C" int flash_attn_fwd(const void* q, const void* k, const void* v, void*
   hipError_t e = (dtype == FA_DTYPE_F32) ? fa::launch_fwd_f32(a, causal != 0, s)
                                          : fa::launch_fwd_bf16(a, causal != 0, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int L, int d,
+                              float softmax_scale, int causal, int window, int dtype, void* stream) {
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, L, L, d, softmax_scale, causal, window, 0, 0, dtype, stream);
+}
+
+extern "C" int flash_attn_fwd_block(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    int B, int Hq, int Hkv, int Lq, int Lk, int d, float softmax_scale,
+                                    int causal, int window, int q_offset, int k_offset, int dtype, void* stream) {
+  if (dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+  return fwd_common(q, k, v, o, lse, B, Hq, Hkv, Lq, Lk, d, softmax_scale, causal, window, q_offset, k_offset,
+                    dtype, stream);
 }
 
 extern "C" size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int dtype) {
@@ -81,6 +105,8 @@ int bwd_setup(fa::BwdArgs& a, const void* workspace, size_t ws_bytes, int B, int
   a.delta = static_cast<float*>(const_cast<void*>(workspace));
   a.lse2 = a.delta + (size_t)B * Hq * L;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.d = d;
+  a.Lk = L;
+  a.shift = 0;
   a.window = window;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
@@ -146,6 +172,38 @@ extern "C" int flash_attn_bwd_dq(const void* q, const void* k, const void* v, co
   if (!all_aligned({q, k, v, dout, dq})) return FA_ERR_INVALID_ARG;
   a.q = q; a.k = k; a.v = v; a.dout = dout; a.dq = dq;
   hipError_t e = fa::launch_bwd_dq_bf16(a, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int flash_attn_bwd_block(const void* q, const void* k, const void* v, const void* o,
+                                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                    void* workspace, size_t workspace_bytes,
+                                    int B, int Hq, int Hkv, int Lq, int Lk, int d, float softmax_scale,
+                                    int causal, int window, int q_offset, int k_offset, int dtype, void* stream) {
+  fa::BwdArgs a{};
+  int rc = bwd_setup(a, workspace, workspace_bytes, B, Hq, Hkv, Lq, d, softmax_scale, causal, window, dtype);
+  if (rc != FA_OK) return rc;
+  if (Lk < 1 || Lk > kMaxL || q_offset < 0 || k_offset < 0 || q_offset > kMaxOffset || k_offset > kMaxOffset)
+    return FA_ERR_INVALID_ARG;
+  if (!all_aligned({q, k, v, o, lse, dout, dq, dk, dv})) return FA_ERR_INVALID_ARG;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.Lk = Lk;
+  a.shift = q_offset - k_offset;
+  hipError_t e = fa::launch_bwd_bf16(a, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int flash_attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                                void* o, float* lse, int B, int Hq, int L, int d, int dtype, void* stream) {
+  if (B < 1 || Hq < 1 || L < 1 || L > kMaxL) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!all_aligned({o_a, lse_a, o_b, lse_b, o, lse})) return FA_ERR_INVALID_ARG;
+  fa::MergeArgs a{};
+  a.o_a = o_a; a.lse_a = lse_a; a.o_b = o_b; a.lse_b = lse_b; a.o = o; a.lse = lse;
+  a.rows = (long long)B * Hq * L;
+  hipError_t e = fa::launch_merge(a, d, dtype, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

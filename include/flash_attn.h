@@ -141,6 +141,57 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* d
                       int B, int Hq, int Hkv, int L, int d,
                       float softmax_scale, int causal, int window, int dtype, void* stream);
 
+/*
+ * Chunk pairs for sequence parallelism (ring attention, claspmoon.cn "14 ·
+ * 缩放定律与高效注意力" §5.1: exact tiled attention extended across devices by
+ * splitting the sequence).  A query chunk holds the Lq queries at sequence
+ * positions q_offset .. q_offset + Lq - 1, a key/value chunk the Lk keys at
+ * k_offset .. k_offset + Lk - 1; causal and window masks are decided on those
+ * positions.  Layouts are the ones above with L replaced by Lq for Q, O, dO,
+ * dQ, LSE and by Lk for K, V, dK, dV.  16-bit dtypes only (FA_DTYPE_F32
+ * returns FA_ERR_UNSUPPORTED); 0 <= q_offset, k_offset <= 2^30 and
+ * 1 <= Lq, Lk <= 2^23, else FA_ERR_INVALID_ARG.
+ *
+ * flash_attn_fwd_block: attention of the query chunk to this key/value chunk
+ * only -- O normalised over the chunk's allowed keys and LSE their natural
+ * log-sum-exp (the partial result of one ring step).  A row with no allowed
+ * key in the chunk gets O = 0 and LSE = -inf.  With Lq = Lk and equal offsets
+ * it is flash_attn_fwd.
+ */
+int flash_attn_fwd_block(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int Lq, int Lk, int d, float softmax_scale,
+                         int causal, int window, int q_offset, int k_offset, int dtype, void* stream);
+
+/*
+ * flash_attn_merge: exact combination of two partial results over disjoint
+ * key sets (the online-softmax rescaling of transformer.xph.ink "高效注意力：
+ * FlashAttention 与线性注意力", 原理与机制, applied to whole chunks):
+ *   LSE = log(exp(LSE_a) + exp(LSE_b)),
+ *   O   = exp(LSE_a - LSE) * O_a + exp(LSE_b - LSE) * O_b;
+ * a side with LSE = -inf has weight 0, both -inf give O = 0, LSE = -inf.
+ *   o_a, o_b, o [B,Hq,L,d] (dtype: any of the three), lse_a, lse_b, lse
+ *   [B,Hq,L] float32.  o may be o_a and lse may be lse_a (accumulation in
+ *   place); no other aliasing.  HBM-bound elementwise kernel, no workspace.
+ */
+int flash_attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                     void* o, float* lse, int B, int Hq, int L, int d, int dtype, void* stream);
+
+/*
+ * flash_attn_bwd_block: this chunk pair's share of the gradient.  o and lse
+ * are the query rows' results over ALL key chunks (after every merge), dout
+ * their upstream gradient; the chunk's probabilities are recomputed as
+ * exp(s*q.k - LSE) on its allowed keys.  Writes (does not accumulate) dq
+ * [B,Hq,Lq,d] = this key chunk's contribution to dQ, and dk, dv [B,Hkv,Lk,d]
+ * = this query chunk's contribution to dK, dV; summing over the chunk pairs
+ * gives the full gradient.  The workspace is the one flash_attn_bwd needs for
+ * Lq query rows (flash_attn_bwd_workspace_bytes(B, Hq, Hkv, Lq, d, dtype)).
+ */
+int flash_attn_bwd_block(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int Hq, int Hkv, int Lq, int Lk, int d, float softmax_scale,
+                         int causal, int window, int q_offset, int k_offset, int dtype, void* stream);
+
 /* Static, never-NULL description of a return code. */
 const char* flash_attn_strerror(int code);
 

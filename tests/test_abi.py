@@ -146,3 +146,29 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fa, "library_path", lambda: str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError):
         fa.library()
+
+
+def test_chunk_and_merge_entry_points_reject_invalid_arguments(lib):
+    c = header_constants()
+    INV, UNS, WS, GQA = c["FA_ERR_INVALID_ARG"], c["FA_ERR_UNSUPPORTED"], c["FA_ERR_WORKSPACE"], c["FA_ERR_GQA"]
+
+    def fb(q=FAKE, Lq=16, Lk=32, d=64, causal=1, window=0, qo=0, ko=0, dt=fa.FA_DTYPE_BF16, Hkv=2):
+        return lib.flash_attn_fwd_block(q, FAKE, FAKE, FAKE, FAKE, 1, 2, Hkv, Lq, Lk, d, 0.125, causal, window,
+                                        qo, ko, dt, None)
+    assert fb(q=None) == INV and fb(Lk=0) == INV and fb(Lq=0) == INV
+    assert fb(qo=-1) == INV and fb(ko=(1 << 30) + 1) == INV and fb(Lk=(1 << 23) + 1) == INV
+    assert fb(dt=fa.FA_DTYPE_F32) == UNS and fb(dt=3) == UNS and fb(d=96) == UNS
+    assert fb(causal=0, window=2) == UNS and fb(Hkv=3) == GQA
+    assert fb(dt=fa.FA_DTYPE_F16, q=None) == INV                     # fp16 passes the dtype check
+
+    def mg(oa=FAKE, la=FAKE, o=FAKE, L=16, d=64, dt=fa.FA_DTYPE_BF16):
+        return lib.flash_attn_merge(oa, la, FAKE, FAKE, o, FAKE, 1, 2, L, d, dt, None)
+    assert mg(oa=None) == INV and mg(la=MISALIGNED) == INV and mg(o=None) == INV and mg(L=0) == INV
+    assert mg(d=80) == UNS and mg(dt=3) == UNS
+    assert mg(dt=fa.FA_DTYPE_F32, oa=None) == INV                    # fp32 partials are accepted
+
+    def bb(ws=FAKE * 16, nb=1 << 20, Lk=32, qo=0, dt=fa.FA_DTYPE_BF16, dq=FAKE):
+        return lib.flash_attn_bwd_block(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, ws, nb, 1, 2, 2, 16, Lk,
+                                        64, 0.125, 1, 0, qo, 0, dt, None)
+    assert bb(ws=None) == WS and bb(nb=16) == WS and bb(Lk=-1) == INV and bb(qo=-5) == INV
+    assert bb(dt=fa.FA_DTYPE_F32) == UNS and bb(dq=None) == INV
