@@ -32,7 +32,11 @@ tiled online-softmax recurrence agreeing with the direct definition; for the
 chunked (ring-attention) functions: a chunk covering the whole sequence equals
 the full definition, merged partials over any partition of the keys equal the
 full result, summed chunk gradients equal the full gradient, brute-force
-loops on tiny chunks, and the merge against ``numpy.logaddexp``.  Every oracle
+loops on tiny chunks, and the merge against ``numpy.logaddexp``; for decode:
+a cache holding exactly the new tokens equals the full causal forward, each
+new token equals the matching row of the whole-sequence forward (with and
+without a window), per-sequence cache lengths, and a single-token rolling
+window buffer in any slot order equals the windowed row.  Every oracle
 function has at least one pin; none is "parity unpinned".
 """
 
@@ -42,6 +46,7 @@ from .attention import (  # noqa: F401
     block_forward,
     block_backward,
     merge_partials,
+    decode_forward,
     kv_head_of,
     probabilities,
     forward,

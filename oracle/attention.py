@@ -345,3 +345,36 @@ def block_backward(q, k, v, dout, o, lse, scale, causal=False, window=0, q_offse
             dq[b, h] = scale * (dS @ k[b, kh])
             dk[b, kh] += scale * (dS.T @ q[b, h])
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------- decode
+#
+# Autoregressive generation keeps the keys and values of every earlier token
+# in a cache and attends only the newest tokens' queries to it (book.anysome.cn
+# "高效注意力" §1: the KV cache is one of the two large costs; §3: GQA shrinks
+# it by sharing K/V heads).
+
+
+def decode_forward(q, k_cache, v_cache, cache_len, scale, causal=True, window=0):
+    """Attention of the Lq newest tokens to a KV cache: float64 ``(O [B,Hq,Lq,d], LSE [B,Hq,Lq])``.
+
+    ``k_cache``/``v_cache`` are ``[B,Hkv,Lk_max,d]``; sequence b uses its first
+    ``cache_len[b]`` entries, which already include the Lq new tokens at the
+    end.  New token t of sequence b sits at position cache_len[b] - Lq + t
+    (bottom-right alignment), so with ``causal`` it sees cache entries 0 ..
+    that position (and with a window the last ``window`` of them); without
+    ``causal`` it sees all cache_len[b] entries.  This is the chunk-pair
+    forward with the query chunk at offset cache_len[b] - Lq and the key chunk
+    at 0.
+    """
+    q, k_cache, v_cache = _as64(q), _as64(k_cache), _as64(v_cache)
+    B, Hq, Lq, d = q.shape
+    O = np.empty((B, Hq, Lq, d))
+    lse = np.empty((B, Hq, Lq))
+    for b in range(B):
+        n = int(cache_len[b])
+        if not Lq <= n <= k_cache.shape[2]:
+            raise ValueError("each cache length must hold the new tokens and fit the cache")
+        O[b:b + 1], lse[b:b + 1] = block_forward(q[b:b + 1], k_cache[b:b + 1, :, :n], v_cache[b:b + 1, :, :n],
+                                                 scale, causal, window, n - Lq, 0)
+    return O, lse

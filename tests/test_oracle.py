@@ -341,15 +341,58 @@ def pin_block_backward_sums_to_full(o):
             assert np.allclose(g, ref, atol=1e-12, rtol=0)
 
 
+def pin_decode_new_tokens_only_is_full_causal(o):
+    # a cache holding exactly the Lq new tokens: bottom-right alignment is the plain causal forward
+    q, k, v = rnd((2, 4, 6, 5), 110), rnd((2, 2, 6, 5), 111), rnd((2, 2, 6, 5), 112)
+    for window in (0, 2):
+        O, l = o.decode_forward(q, k, v, [6, 6], 0.5, True, window)
+        Of, lf = o.forward(q, k, v, 0.5, True, window)
+        assert np.allclose(O, Of, atol=1e-13, rtol=0) and np.allclose(l, lf, atol=1e-13, rtol=0)
+
+
+def pin_decode_rows_match_whole_sequence(o):
+    # new token t of a sequence of length n is row n - Lq + t of the whole-sequence forward;
+    # sequences of different lengths share one padded cache
+    L, Lq = 19, 3
+    q_all, k, v = rnd((2, 4, L, 6), 120), rnd((2, 2, L, 6), 121), rnd((2, 2, L, 6), 122)
+    lens = [L, 11]
+    for causal, window in [(True, 0), (True, 4), (False, 0)]:
+        q = np.stack([q_all[b, :, n - Lq:n] for b, n in enumerate(lens)])
+        kc = k.copy()
+        kc[1, :, lens[1]:] = 1e3          # entries past a sequence's length must be ignored
+        O, l = o.decode_forward(q, kc, v, lens, 0.45, causal, window)
+        for b, n in enumerate(lens):
+            Of, lf = o.forward(q_all[b:b + 1, :, :n], k[b:b + 1, :, :n], v[b:b + 1, :, :n], 0.45, causal, window)
+            assert np.allclose(O[b], Of[0, :, n - Lq:n], atol=1e-12, rtol=0)
+            assert np.allclose(l[b], lf[0, :, n - Lq:n], atol=1e-12, rtol=0)
+
+
+def pin_decode_rolling_window_buffer(o):
+    # a single new token with a rolling buffer of the last W keys (slots in any order) needs no
+    # mask: the non-causal decode over the W valid slots equals the windowed causal row
+    L, W = 23, 6
+    q_all, k, v = rnd((1, 2, L, 4), 130), rnd((1, 1, L, 4), 131), rnd((1, 1, L, 4), 132)
+    Of, lf = o.forward(q_all, k, v, 0.6, True, W)
+    pos = np.arange(L - W, L)
+    slots = pos % W                                   # position p lives in slot p mod W
+    kb, vb = np.empty((1, 1, W, 4)), np.empty((1, 1, W, 4))
+    kb[:, :, slots], vb[:, :, slots] = k[:, :, pos], v[:, :, pos]
+    O, l = o.decode_forward(q_all[:, :, L - 1:], kb, vb, [W], 0.6, False, 0)
+    assert np.allclose(O[0, :, 0], Of[0, :, L - 1], atol=1e-12, rtol=0)
+    assert np.allclose(l[0, :, 0], lf[0, :, L - 1], atol=1e-12, rtol=0)
+
+
 BLOCK_PINS = [pin_block_whole_sequence_equals_full, pin_block_brute_force, pin_merged_partials_equal_full,
               pin_merge_edge_cases, pin_block_backward_sums_to_full]
+DECODE_PINS = [pin_decode_new_tokens_only_is_full_causal, pin_decode_rows_match_whole_sequence,
+               pin_decode_rolling_window_buffer]
 
 
 PINS = [pin_rows_stochastic, pin_two_key_worked_example, pin_length_one, pin_zero_query_is_mean,
         pin_identical_keys, pin_convexity, pin_shift_invariance, pin_permutation_noncausal,
         pin_gqa_is_repeated_mha, pin_window_at_least_L_is_causal, pin_torch_sdpa_and_logsumexp,
         pin_backward_vs_torch_autograd, pin_backward_finite_differences, pin_backward_identities,
-        pin_tiled_recurrence_equals_direct, pin_rows_subset] + BLOCK_PINS
+        pin_tiled_recurrence_equals_direct, pin_rows_subset] + BLOCK_PINS + DECODE_PINS
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -476,3 +519,11 @@ def _chunk_local_backward(q, k, v, dout, scale, causal, window, q_offset, k_offs
             dq[b, h] = scale * (dS @ k[b, kh])
             dk[b, kh] += scale * (dS.T @ q[b, h])
     return dq, dk, dv
+
+
+def test_planted_decode_top_left_alignment(monkeypatch):
+    # new tokens placed at the start of the cache instead of its end
+    good = oa.block_forward
+    monkeypatch.setattr(oa, "block_forward", lambda q, k, v, scale, causal=False, window=0, q_offset=0, k_offset=0:
+                        good(q, k, v, scale, causal, window, 0, k_offset))
+    assert _some_pin_fails(DECODE_PINS)
