@@ -186,6 +186,29 @@ def measure_config(w, iters=10, warmup=3):
     return r
 
 
+def measure_decode(B=8, Hq=32, Hkv=8, Lq=1, Lk=32768, d=128, iters=20, warmup=5):
+    """KV-cache decode: one new token per sequence against a 32k-entry GQA cache.
+
+    The call reads the whole cache once (HBM-bound), so it is reported as bytes of
+    K and V read per second against the HBM peak."""
+    import torch
+    import exact_tiled_attention_flash_amd as fa
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(9)
+    q = torch.randn(B, Hq, Lq, d, generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, Lk, d, generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, Lk, d, generator=g, device=dev).to(torch.bfloat16)
+    ws = torch.empty(fa.decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, d), dtype=torch.uint8, device=dev)
+    o, lse = torch.empty_like(q), torch.empty(B, Hq, Lq, device=dev)
+    med, mean = time_calls(lambda: fa.decode(q, k, v, None, causal=True, workspace=ws, out=o, lse=lse), iters, warmup)
+    cache_bytes = 2 * B * Hkv * Lk * d * 2
+    gbs = cache_bytes / (med * 1e-3) / 1e9
+    return {"shape": f"B{B} Hq{Hq} Hkv{Hkv} new tokens {Lq} cache {Lk} d{d} bf16 causal",
+            "ms_median": round(med, 4), "ms_mean": round(mean, 4), "cache_bytes": cache_bytes,
+            "hbm_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS, "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "workspace_bytes": int(ws.numel()), "data": "synthetic N(0,1), generated on the device"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -312,6 +335,7 @@ def main():
     }
     if not args.no_configs:
         out["configs"] = {wl.name: measure_config(wl) for wl in W.ALL}
+        out["decode"] = measure_decode()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

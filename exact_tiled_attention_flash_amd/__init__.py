@@ -21,6 +21,7 @@ import os
 import torch
 
 __all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "fwd_block", "bwd_block", "merge",
+           "decode", "decode_workspace_bytes",
            "strerror", "library", "library_path",
            "FlashAttentionFunction", "scaled_dot_product_attention",
            "FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "EXPORTED_SYMBOLS"]
@@ -33,6 +34,7 @@ _DTYPES = {torch.float32: FA_DTYPE_F32, torch.bfloat16: FA_DTYPE_BF16, torch.flo
 EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_bytes",
                     "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
                     "flash_attn_fwd_block", "flash_attn_merge", "flash_attn_bwd_block",
+                    "flash_attn_decode", "flash_attn_decode_workspace_bytes",
                     "flash_attn_strerror", "flash_attn_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -73,6 +75,10 @@ def library():
     lib.flash_attn_bwd_block.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                          i, i, i, i, i, i, f, i, i, i, i, i, vp]
     lib.flash_attn_bwd_block.restype = i
+    lib.flash_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, i, i, vp]
+    lib.flash_attn_decode.restype = i
+    lib.flash_attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.flash_attn_decode_workspace_bytes.restype = sz
     lib.flash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.flash_attn_bwd_workspace_bytes.restype = sz
     lib.flash_attn_strerror.argtypes = [i]
@@ -263,6 +269,45 @@ def bwd_block(q, k, v, o, lse, dout, causal=False, window=0, q_offset=0, k_offse
                                         _DTYPES[q.dtype], _stream(q))
     _check(rc, "flash_attn_bwd_block")
     return dq, dk, dv
+
+
+def decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, d, dtype=torch.bfloat16):
+    return int(library().flash_attn_decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, d, _DTYPES[dtype]))
+
+
+def decode(q, k_cache, v_cache, cache_len=None, causal=True, window=0, scale=None, workspace=None,
+           out=None, lse=None):
+    """The ``Lq`` newest tokens ``q [B,Hq,Lq,d]`` attend to a KV cache ``[B,Hkv,Lk,d]``.
+
+    ``cache_len`` (int32 CUDA tensor ``[B]``, optional) holds each sequence's valid
+    entries, the new tokens' K/V being the last ``Lq`` of them.  Returns ``(o, lse)``.
+    """
+    if q.dim() != 4 or k_cache.dim() != 4 or k_cache.shape != v_cache.shape:
+        raise ValueError("q must be [B, Hq, Lq, d] and the caches [B, Hkv, Lk, d]")
+    B, Hq, Lq, d = q.shape
+    Hkv, Lk = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[0] != B or k_cache.shape[3] != d:
+        raise ValueError("the caches must share B and d with q")
+    for t in (q, k_cache, v_cache):
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
+            raise ValueError("q and the caches must be contiguous CUDA tensors of one dtype")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("decode takes bfloat16 or float16")
+    if cache_len is not None and (cache_len.dtype != torch.int32 or not cache_len.is_cuda
+                                  or cache_len.shape != (B,) or not cache_len.is_contiguous()):
+        raise ValueError("cache_len must be a contiguous int32 CUDA tensor [B]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, d, q.dtype)
+    if nbytes == 0:
+        raise RuntimeError("flash_attn_decode: unsupported sizes (Hq/Hkv * Lq must be <= 32)")
+    workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if lse is None else lse
+    rc = library().flash_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(out), _ptr(lse),
+                                     _ptr(workspace), workspace.numel(), B, Hq, Hkv, Lq, Lk, d, scale,
+                                     int(bool(causal)), int(window), _DTYPES[q.dtype], _stream(q))
+    _check(rc, "flash_attn_decode")
+    return out, lse
 
 
 class FlashAttentionFunction(torch.autograd.Function):

@@ -63,4 +63,24 @@ hipError_t launch_bwd_dq_bf16(const BwdArgs& a, bool causal, hipStream_t stream)
 // exact combination of two partial results; dtype 0 fp32, 1 bf16, 2 fp16
 hipError_t launch_merge(const MergeArgs& a, int d, int dtype, hipStream_t stream);
 
+struct DecodeArgs {
+  const void* q;          // [B, Hq, Lq, d] newest tokens' queries
+  const void* k;          // [B, Hkv, Lk, d] cache
+  const void* v;
+  const int* cache_len;   // [B] valid cache entries per sequence, or null (= Lk)
+  void* o;                // [B, Hq, Lq, d]
+  float* lse;             // [B, Hq, Lq] or null
+  float* part_o;          // workspace: [n_splits, rows, d] float32
+  float* part_lse;        // workspace: [n_splits, rows] float32
+  int B, Hq, Hkv, Lq, Lk, d;
+  int window;
+  float scale_log2;
+  bool f16;
+  int n_splits, split_keys;
+  long long rows;         // B * Hq * Lq
+};
+// key splits for a decode call (deterministic in its sizes)
+void decode_plan(int B, int Hkv, int Lk, int& n_splits, int& split_keys);
+hipError_t launch_decode(const DecodeArgs& a, bool causal, hipStream_t stream);
+
 }  // namespace fa

@@ -207,6 +207,64 @@ extern "C" int flash_attn_merge(const void* o_a, const float* lse_a, const void*
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+namespace {
+
+// Validation shared by the decode entry points; fills the plan.
+int decode_check(int B, int Hq, int Hkv, int Lq, int Lk, int d, int dtype, int& n_splits, int& split_keys) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < Lq || Lk > kMaxL) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (Hq % Hkv != 0) return FA_ERR_GQA;
+  if ((Hq / Hkv) * Lq > 32) return FA_ERR_UNSUPPORTED;    // rows of one K/V head: one MFMA column block
+  if ((long long)B * Hkv > 65535) return FA_ERR_INVALID_ARG;
+  fa::decode_plan(B, Hkv, Lk, n_splits, split_keys);
+  return FA_OK;
+}
+
+size_t decode_bytes(int B, int Hq, int Lq, int d, int n_splits) {
+  const size_t rows = (size_t)B * Hq * Lq;
+  const size_t raw = (size_t)n_splits * rows * (size_t)(d + 1) * sizeof(float);
+  return (raw + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int d, int dtype) {
+  int ns = 0, sk = 0;
+  if (decode_check(B, Hq, Hkv, Lq, Lk, d, dtype, ns, sk) != FA_OK) return 0;
+  return decode_bytes(B, Hq, Lq, d, ns);
+}
+
+extern "C" int flash_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cache_len,
+                                 void* o, float* lse, void* workspace, size_t workspace_bytes,
+                                 int B, int Hq, int Hkv, int Lq, int Lk, int d, float softmax_scale,
+                                 int causal, int window, int dtype, void* stream) {
+  int ns = 0, sk = 0;
+  int rc = decode_check(B, Hq, Hkv, Lq, Lk, d, dtype, ns, sk);
+  if (rc != FA_OK) return rc;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
+  if ((causal != 0 && causal != 1) || window < 0) return FA_ERR_INVALID_ARG;
+  if (window > 0 && !causal) return FA_ERR_UNSUPPORTED;
+  if (!all_aligned({q, k_cache, v_cache, o})) return FA_ERR_INVALID_ARG;
+  if ((lse && !aligned16(lse)) || (reinterpret_cast<uintptr_t>(cache_len) & 3u) != 0) return FA_ERR_INVALID_ARG;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      workspace_bytes < decode_bytes(B, Hq, Lq, d, ns))
+    return FA_ERR_WORKSPACE;
+  fa::DecodeArgs a{};
+  a.q = q; a.k = k_cache; a.v = v_cache; a.cache_len = cache_len; a.o = o; a.lse = lse;
+  a.rows = (long long)B * Hq * Lq;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_lse = a.part_o + (size_t)ns * (size_t)a.rows * d;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.d = d;
+  a.window = window;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.f16 = dtype == FA_DTYPE_F16;
+  a.n_splits = ns;
+  a.split_keys = sk;
+  hipError_t e = fa::launch_decode(a, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 extern "C" const char* flash_attn_strerror(int code) {
   switch (code) {
     case FA_OK: return "ok";

@@ -192,6 +192,40 @@ int flash_attn_bwd_block(const void* q, const void* k, const void* v, const void
                          int B, int Hq, int Hkv, int Lq, int Lk, int d, float softmax_scale,
                          int causal, int window, int q_offset, int k_offset, int dtype, void* stream);
 
+/*
+ * KV-cache decode (book.anysome.cn "高效注意力" §1: autoregressive generation
+ * caches every earlier token's K and V; §3: the G = Hq/Hkv query heads of a
+ * group share one K/V head).  The Lq newest tokens of each sequence attend to
+ * its cache:
+ *   q [B,Hq,Lq,d]                    : the new tokens' queries (dtype)
+ *   k_cache, v_cache [B,Hkv,Lk,d]    : the cache (dtype), the new tokens' K/V
+ *                                      already written at its end
+ *   cache_len [B] int32 (device)     : valid entries per sequence, Lq <= n <=
+ *                                      Lk; NULL means every sequence has Lk.
+ *                                      Entries past n are never read.  An
+ *                                      out-of-range entry is clamped into
+ *                                      [Lq, Lk] (results then are meaningless
+ *                                      but every access stays in bounds).
+ *   o [B,Hq,Lq,d] (dtype), lse [B,Hq,Lq] float32 (may be NULL)
+ * New token t of sequence b sits at position n_b - Lq + t (bottom-right
+ * alignment): causal = 1 lets it see entries 0 .. that position (window w:
+ * the last w of them); causal = 0 lets every new token see all n_b entries.
+ * A rolling window buffer (transformer.xph.ink 实例或案例: Mistral's sliding
+ * window keeps the last W keys in a ring of W slots) is served with causal = 0
+ * and cache_len = the number of filled slots: for one new token the slot order
+ * does not matter.  The keys are split across work-groups and the partials
+ * merged exactly, so the cache is read once per K/V head whatever G and Lq.
+ * Requires (Hq/Hkv) * Lq <= 32 (else FA_ERR_UNSUPPORTED: use
+ * flash_attn_fwd_block for longer chunks), d in {64,128}, bf16 or fp16,
+ * B * Hkv <= 65535.  workspace: at least flash_attn_decode_workspace_bytes()
+ * bytes, 256-byte aligned (float32 partials of every key split).
+ */
+size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int d, int dtype);
+int flash_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cache_len,
+                      void* o, float* lse, void* workspace, size_t workspace_bytes,
+                      int B, int Hq, int Hkv, int Lq, int Lk, int d, float softmax_scale,
+                      int causal, int window, int dtype, void* stream);
+
 /* Static, never-NULL description of a return code. */
 const char* flash_attn_strerror(int code);
 

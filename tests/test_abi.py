@@ -172,3 +172,23 @@ def test_chunk_and_merge_entry_points_reject_invalid_arguments(lib):
                                         64, 0.125, 1, 0, qo, 0, dt, None)
     assert bb(ws=None) == WS and bb(nb=16) == WS and bb(Lk=-1) == INV and bb(qo=-5) == INV
     assert bb(dt=fa.FA_DTYPE_F32) == UNS and bb(dq=None) == INV
+
+
+def test_decode_entry_points_reject_invalid_arguments(lib):
+    c = header_constants()
+    INV, UNS, WS, GQA = c["FA_ERR_INVALID_ARG"], c["FA_ERR_UNSUPPORTED"], c["FA_ERR_WORKSPACE"], c["FA_ERR_GQA"]
+    wsb = lib.flash_attn_decode_workspace_bytes
+    assert wsb(1, 8, 2, 1, 4096, 128, fa.FA_DTYPE_BF16) > 0
+    assert wsb(1, 8, 2, 9, 4096, 128, fa.FA_DTYPE_BF16) == 0        # 4 heads x 9 tokens > 32 rows
+    assert wsb(1, 8, 2, 1, 4096, 128, fa.FA_DTYPE_F32) == 0
+    assert wsb(1, 8, 3, 1, 4096, 128, fa.FA_DTYPE_BF16) == 0
+    assert wsb(1, 8, 2, 5, 4, 128, fa.FA_DTYPE_BF16) == 0           # cache shorter than the new tokens
+
+    def dec(q=FAKE, cl=None, ws=FAKE * 16, nb=1 << 30, Hq=8, Hkv=2, Lq=1, Lk=4096, d=128, scale=0.1, causal=1,
+            window=0, dt=fa.FA_DTYPE_BF16):
+        return lib.flash_attn_decode(q, FAKE, FAKE, cl, FAKE, FAKE, ws, nb, 1, Hq, Hkv, Lq, Lk, d, scale, causal,
+                                     window, dt, None)
+    assert dec(q=None) == INV and dec(cl=FAKE + 2) == INV and dec(scale=0.0) == INV and dec(causal=3) == INV
+    assert dec(ws=None) == WS and dec(nb=16) == WS and dec(ws=FAKE * 16 + 128) == WS
+    assert dec(Lq=40) == UNS and dec(dt=fa.FA_DTYPE_F32) == UNS and dec(d=96) == UNS
+    assert dec(causal=0, window=8) == UNS and dec(Hkv=3) == GQA and dec(Lk=0) == INV
