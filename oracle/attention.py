@@ -378,3 +378,73 @@ def decode_forward(q, k_cache, v_cache, cache_len, scale, causal=True, window=0)
         O[b:b + 1], lse[b:b + 1] = block_forward(q[b:b + 1], k_cache[b:b + 1, :, :n], v_cache[b:b + 1, :, :n],
                                                  scale, causal, window, n - Lq, 0)
     return O, lse
+
+
+# ---------------------------------------------------------------- general masks
+#
+# Sparse patterns that keep attention exact on the positions they allow
+# (claspmoon.cn "14 · 缩放定律与高效注意力" §4.3, Longformer / BigBird: a
+# sliding window plus a few global tokens; kler.cn §3.2.1: a sliding window
+# looks at positions before and after; kler.cn §4.1.2: block-sparse masks in
+# which a query block attends to nearby key blocks; kler.cn's hybrid
+# configuration: window 512 with the first and last token global).
+
+
+def general_mask(q_pos, k_pos, causal=False, window=0, block_mask=None, block=64, global_pos=()):
+    """Boolean ``[len(q_pos), len(k_pos)]`` of the general mask family:
+
+        allowed(i, j) = causal_ok(i, j) and ((window_ok(i, j) and block_ok(i, j))
+                                            or i is global or j is global)
+
+    causal_ok: j <= i when ``causal``; window_ok: |i - j| < window when
+    window > 0 (with causal this is the usual i - w < j <= i; without it the
+    window is symmetric); block_ok: ``block_mask[i // block][j // block]``
+    when a block mask is given; global: the position is in ``global_pos``.
+    """
+    i = np.asarray(q_pos, dtype=np.int64)[:, None]
+    j = np.asarray(k_pos, dtype=np.int64)[None, :]
+    local = np.ones((i.shape[0], j.shape[1]), dtype=bool)
+    if window > 0:
+        local &= np.abs(i - j) < window
+    if block_mask is not None:
+        bm = np.asarray(block_mask, dtype=bool)
+        local &= bm[i // block, j // block]
+    g = np.asarray(sorted(set(int(x) for x in global_pos)), dtype=np.int64)
+    ok = local | np.isin(i, g) | np.isin(j, g)
+    if causal:
+        ok &= j <= i
+    return ok
+
+
+def forward_with_mask(q, k, v, scale, ok):
+    """Exact attention under an explicit boolean mask ``ok [L, L]`` (same for every head):
+    the definition of ``forward_rows`` with ``ok`` in place of the causal/window mask."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    O = np.empty((B, Hq, L, d))
+    lse = np.empty((B, Hq, L))
+    for b in range(B):
+        for h in range(Hq):
+            kh = kv_head_of(h, Hq, Hkv)
+            S = scale * (q[b, h] @ k[b, kh].T)
+            A, lse[b, h] = _masked_softmax_rows(S, ok)
+            O[b, h] = A @ v[b, kh]
+    return O, lse
+
+
+def backward_with_mask(q, k, v, dout, scale, ok):
+    """Gradient of sum(O * dO) under an explicit boolean mask: ``backward`` with ``ok``."""
+    q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for b in range(B):
+        for h in range(Hq):
+            kh = kv_head_of(h, Hq, Hkv)
+            A, _ = _masked_softmax_rows(scale * (q[b, h] @ k[b, kh].T), ok)
+            dv[b, kh] += A.T @ dout[b, h]
+            dS = _softmax_backward(A, dout[b, h] @ v[b, kh].T)
+            dq[b, h] = scale * (dS @ k[b, kh])
+            dk[b, kh] += scale * (dS.T @ q[b, h])
+    return dq, dk, dv

@@ -382,6 +382,85 @@ def pin_decode_rolling_window_buffer(o):
     assert np.allclose(l[0, :, 0], lf[0, :, L - 1], atol=1e-12, rtol=0)
 
 
+def pin_general_mask_reduces_to_causal_window(o):
+    L = 13
+    pos = np.arange(L)
+    for causal, window in MASKS:
+        assert np.array_equal(o.general_mask(pos, pos, causal, window), o.allowed_mask(pos, L, causal, window))
+    ones = np.ones((1, 1), dtype=bool)
+    assert np.array_equal(o.general_mask(pos, pos, True, 0, ones, 64), o.allowed_mask(pos, L, True, 0))
+
+
+def pin_general_mask_brute_force(o):
+    L, blk = 11, 3
+    rng = np.random.default_rng(140)
+    bm = rng.integers(0, 2, size=(4, 4)).astype(bool)
+    for causal, window, glob in [(False, 3, ()), (False, 0, (0, 10)), (True, 2, (5,)), (False, 4, (0, 10)),
+                                 (True, 0, (3, 7))]:
+        for use_bm in (False, True):
+            ok = o.general_mask(np.arange(L), np.arange(L), causal, window, bm if use_bm else None, blk, glob)
+            for i in range(L):
+                for j in range(L):
+                    local = (window <= 0 or abs(i - j) < window) and (not use_bm or bm[i // blk][j // blk])
+                    want = (local or i in glob or j in glob) and (not causal or j <= i)
+                    assert ok[i, j] == want, (causal, window, glob, use_bm, i, j)
+
+
+def pin_masked_forward_backward_reduce_to_plain(o):
+    L = 12
+    for causal, window in MASKS:
+        q, k, v, do = rnd((1, 4, L, 5), 150), rnd((1, 2, L, 5), 151), rnd((1, 2, L, 5), 152), rnd((1, 4, L, 5), 153)
+        ok = o.allowed_mask(np.arange(L), L, causal, window)
+        O, l = o.forward_with_mask(q, k, v, 0.4, ok)
+        Of, lf = o.forward(q, k, v, 0.4, causal, window)
+        assert np.allclose(O, Of, atol=1e-13, rtol=0) and np.allclose(l, lf, atol=1e-13, rtol=0)
+        g = o.backward_with_mask(q, k, v, do, 0.4, ok)
+        gf = o.backward(q, k, v, do, 0.4, causal, window)
+        for a, b in zip(g, gf):
+            assert np.allclose(a, b, atol=1e-12, rtol=0)
+
+
+def pin_global_rows_are_unmasked(o):
+    # a global query attends to every key: its row equals the unmasked row; a local row with a
+    # symmetric window sees the global keys in addition to its window
+    L = 16
+    q, k, v = rnd((1, 2, L, 4), 160), rnd((1, 2, L, 4), 161), rnd((1, 2, L, 4), 162)
+    ok = o.general_mask(np.arange(L), np.arange(L), False, 3, None, 64, (0, L - 1))
+    O, l = o.forward_with_mask(q, k, v, 0.5, ok)
+    Of, lf = o.forward(q, k, v, 0.5, False, 0)
+    for r in (0, L - 1):
+        assert np.allclose(O[:, :, r], Of[:, :, r], atol=1e-13, rtol=0)
+    i = 7
+    keys = sorted({0, L - 1} | set(range(i - 2, i + 3)))
+    s = 0.5 * q[0, 1, i] @ k[0, 1, keys].T
+    assert abs(l[0, 1, i] - scipy.special.logsumexp(s)) < 1e-12
+
+
+def pin_masked_backward_finite_differences(o):
+    L, d = 6, 3
+    q, k, v, do = rnd((1, 1, L, d), 170), rnd((1, 1, L, d), 171), rnd((1, 1, L, d), 172), rnd((1, 1, L, d), 173)
+    ok = o.general_mask(np.arange(L), np.arange(L), False, 2, [[1, 0], [1, 1]], 3, (2,))
+    dq, dk, dv = o.backward_with_mask(q, k, v, do, 0.7, ok)
+    f = lambda q_, k_, v_: float((o.forward_with_mask(q_, k_, v_, 0.7, ok)[0] * do).sum())
+    eps = 1e-6
+    for x, g, which in ((q, dq, 0), (k, dk, 1), (v, dv, 2)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = [q, k, v]
+            args_m = [q, k, v]
+            args_p[which], args_m[which] = xp, xm
+            num[idx] = (f(*args_p) - f(*args_m)) / (2 * eps)
+        assert np.allclose(num, g, rtol=1e-6, atol=1e-8)
+
+
+MASK_PINS = [pin_general_mask_reduces_to_causal_window, pin_general_mask_brute_force,
+             pin_masked_forward_backward_reduce_to_plain, pin_global_rows_are_unmasked,
+             pin_masked_backward_finite_differences]
+
+
 BLOCK_PINS = [pin_block_whole_sequence_equals_full, pin_block_brute_force, pin_merged_partials_equal_full,
               pin_merge_edge_cases, pin_block_backward_sums_to_full]
 DECODE_PINS = [pin_decode_new_tokens_only_is_full_causal, pin_decode_rows_match_whole_sequence,
@@ -392,7 +471,7 @@ PINS = [pin_rows_stochastic, pin_two_key_worked_example, pin_length_one, pin_zer
         pin_identical_keys, pin_convexity, pin_shift_invariance, pin_permutation_noncausal,
         pin_gqa_is_repeated_mha, pin_window_at_least_L_is_causal, pin_torch_sdpa_and_logsumexp,
         pin_backward_vs_torch_autograd, pin_backward_finite_differences, pin_backward_identities,
-        pin_tiled_recurrence_equals_direct, pin_rows_subset] + BLOCK_PINS + DECODE_PINS
+        pin_tiled_recurrence_equals_direct, pin_rows_subset] + BLOCK_PINS + DECODE_PINS + MASK_PINS
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -527,3 +606,25 @@ def test_planted_decode_top_left_alignment(monkeypatch):
     monkeypatch.setattr(oa, "block_forward", lambda q, k, v, scale, causal=False, window=0, q_offset=0, k_offset=0:
                         good(q, k, v, scale, causal, window, 0, k_offset))
     assert _some_pin_fails(DECODE_PINS)
+
+
+def test_planted_general_mask_window_off_by_one(monkeypatch):
+    good = oa.general_mask
+
+    def bad(q_pos, k_pos, causal=False, window=0, block_mask=None, block=64, global_pos=()):
+        return good(q_pos, k_pos, causal, window + 1 if window > 0 else 0, block_mask, block, global_pos)
+    monkeypatch.setattr(oa, "general_mask", bad)
+    monkeypatch.setattr(oracle, "general_mask", bad)
+    assert _some_pin_fails(MASK_PINS)
+
+
+def test_planted_global_keys_ignored(monkeypatch):
+    good = oa.general_mask
+
+    def bad(q_pos, k_pos, causal=False, window=0, block_mask=None, block=64, global_pos=()):
+        ok = good(q_pos, k_pos, causal, window, block_mask, block, ())
+        return ok | good(q_pos, k_pos, causal, window, block_mask, block, global_pos) & np.isin(
+            np.asarray(q_pos)[:, None], list(global_pos))       # global queries kept, global keys dropped
+    monkeypatch.setattr(oa, "general_mask", bad)
+    monkeypatch.setattr(oracle, "general_mask", bad)
+    assert _some_pin_fails(MASK_PINS)
