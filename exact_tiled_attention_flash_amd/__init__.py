@@ -123,7 +123,8 @@ def _shapes(q, k, v):
 def fwd(q, k, v, causal=False, window=0, scale=None, out=None, lse=None):
     """Exact attention forward.  Returns ``(o, lse)``; ``lse`` is float32 ``[B,Hq,L]``.
 
-    ``window`` (>= 1, with ``causal``) limits query i to keys i-window+1..i.
+    ``window`` (>= 1) limits query i to keys i-window+1..i with ``causal`` and to
+    keys j with |i - j| < window without it (a window reaching both ways).
     ``scale`` defaults to 1/sqrt(d).
     """
     B, Hq, Hkv, L, d = _shapes(q, k, v)
@@ -338,7 +339,8 @@ class FlashAttentionFunction(torch.autograd.Function):
 def scaled_dot_product_attention(q, k, v, is_causal=False, scale=None, window=0):
     """Drop-in for ``scaled_dot_product_attention(q, k, v, is_causal=...)`` on ``[B, H, L, d]``
     tensors (claspmoon.cn "14 · 缩放定律与高效注意力" §3.5), with grouped-query K/V
-    (``k.shape[1]`` dividing ``q.shape[1]``) and an optional causal sliding ``window``
+    (``k.shape[1]`` dividing ``q.shape[1]``) and an optional sliding ``window`` (one-sided
+    with ``is_causal``, symmetric without)
     (kler.cn, §3.2.1 configuration keys).  Differentiable through ``FlashAttentionFunction``.
     """
     return FlashAttentionFunction.apply(q, k, v, bool(is_causal), int(window), scale)

@@ -22,12 +22,13 @@
 // gfx950 transposing LDS read.  As in the forward, every LDS address is a
 // loop-invariant per-lane offset plus an immediate and all tile copies are
 // buffer->LDS loads, which keeps the VALU work per tile small.
-#include "fa_common.hpp"
-#include "fa_kernels.h"
+#include "fa_bwd_tile.hpp"
 
 namespace fa {
 
 namespace {
+
+using namespace bwdtile;
 
 __device__ __forceinline__ void wait_copies_and_barrier() {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -70,106 +71,6 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__
 // the swz_dual layout.  Every LDS address is a loop-invariant per-lane offset
 // plus an immediate, and all copies are buffer->LDS loads (rows past the end
 // of the sequence read as zeros).
-template <int D>
-struct KVCfg {
-  static constexpr int kWaves = 8;
-  static constexpr int BK = 128;                 // keys per work-group
-  static constexpr int BQ = 64;                  // queries per streamed tile
-  static constexpr int QT = BQ * D * 2;          // bytes of a Q (or dO) tile (swz_dual)
-  static constexpr int KB = BK * Pad<D>::KSTR;   // bytes of the padded K (or V) block
-  static constexpr int QCOPIES = QT / 1024;
-  static constexpr int QPER = QCOPIES / kWaves;  // copies per wave per tensor
-  static constexpr int KBCOPIES = KB / 1024;
-  static constexpr int NSTEP = D / 16;
-  static constexpr int NDB = D / 32;
-  static_assert(QCOPIES % kWaves == 0 && KB % 1024 == 0, "tiles must split into whole wave copies");
-};
-
-template <int D>
-struct KVState {
-  f32x16 dv[KVCfg<D>::NDB];     // dV accumulator: lane = head-dim column, registers = keys
-  f32x16 dk[KVCfg<D>::NDB];     // dK accumulator (scale applied at the end)
-};
-
-// Loop-invariant per-lane offsets of one wave.
-template <int D>
-struct KVAddr {
-  int qcopy[KVCfg<D>::QPER];           // source offsets of this wave's Q / dO tile copies
-  int row[KVCfg<D>::NSTEP];            // row reads of the wave's 32 queries, per K-step
-  int tr[KVCfg<D>::NDB][2];            // transposing reads (t = 2*qh), per column block and half
-  int kv;                              // row reads of the wave's 32 keys in the padded K/V block
-};
-
-template <int D, bool CAUSAL, bool F16>
-__device__ __forceinline__ void kv_tile(KVState<D>& st, const KVAddr<D>& ad, const char* kblk, const char* vblk,
-                                        const char* qbuf, const char* dobuf, const float* stats, int q0, int L,
-                                        int shift, int window, int qh, int key_w0, float c, int lane) {
-  using C = KVCfg<D>;
-  const int g = lane >> 5;
-  const int my_key = key_w0 + (lane & 31);
-
-  // S = Q K^T (32 queries x 32 keys): lane = key, registers = queries
-  f32x16 p = mfma32x<F16>(lds_load16(qbuf, ad.row[0]), lds_load16(kblk, ad.kv), f32x16{});
-#pragma unroll
-  for (int k = 1; k < C::NSTEP; ++k)
-    p = mfma32x<F16>(lds_load16(qbuf, ad.row[k]), lds_load16(kblk, ad.kv + 32 * k), p);
-
-  // P = exp2(S*s*log2e - LSE*log2e), zero where masked
-  const int qw0 = q0 + 32 * qh;           // first query of this wave's half
-  const bool need_mask = (qw0 + 32 > L) || (CAUSAL && qw0 + shift < key_w0 + 31) ||
-                         (window > 0 && qw0 + 31 + shift > key_w0 + window - 1);
-#pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4) {
-    const f32x4 l4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (32 * qh + 8 * i4 + 4 * g));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) p[4 * i4 + j] = fast_exp2(fmaf(p[4 * i4 + j], c, -l4[j]));
-  }
-  // the mask as a separate pass, so that the common unmasked tile stays one
-  // straight-line block
-  if (need_mask) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int q = qw0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      const bool ok = q < L && (!CAUSAL || my_key <= q + shift) && (window <= 0 || q + shift - my_key < window);
-      p[i] = ok ? p[i] : 0.f;
-    }
-  }
-  // dV += P^T dO: A = P (lane = key, K slots = queries), B = dO via the transposing read
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int o8 = 8 * u;
-    const bf16x8 pa = pack8<F16>(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5], p[o8 + 6], p[o8 + 7]);
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      const bf16x8 bo = concat4(lds_load_tr(dobuf, ad.tr[db][0] + u * 16 * (2 * D)),
-                                lds_load_tr(dobuf, ad.tr[db][1] + u * 16 * (2 * D)));
-      st.dv[db] = mfma32x<F16>(pa, bo, st.dv[db]);
-    }
-  }
-  // dP = dO V^T, then dS = P * (dP - D) in place
-  f32x16 dp = mfma32x<F16>(lds_load16(dobuf, ad.row[0]), lds_load16(vblk, ad.kv), f32x16{});
-#pragma unroll
-  for (int k = 1; k < C::NSTEP; ++k)
-    dp = mfma32x<F16>(lds_load16(dobuf, ad.row[k]), lds_load16(vblk, ad.kv + 32 * k), dp);
-#pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4) {
-    const f32x4 d4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (C::BQ + 32 * qh + 8 * i4 + 4 * g));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) p[4 * i4 + j] *= dp[4 * i4 + j] - d4[j];
-  }
-  // dK += dS^T Q: A = dS (lane = key), B = Q via the transposing read
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int o8 = 8 * u;
-    const bf16x8 da = pack8<F16>(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5], p[o8 + 6], p[o8 + 7]);
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-      const bf16x8 bq = concat4(lds_load_tr(qbuf, ad.tr[db][0] + u * 16 * (2 * D)),
-                                lds_load_tr(qbuf, ad.tr[db][1] + u * 16 * (2 * D)));
-      st.dk[db] = mfma32x<F16>(da, bq, st.dk[db]);
-    }
-  }
-}
 
 template <int D, bool CAUSAL, bool F16>
 __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
@@ -208,7 +109,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const unsigned qhead_bytes = (unsigned)L * (2 * D);      // one Q/dO head
 
   // queries that can see this work-group's keys (none: only between chunks)
-  const int q_begin = CAUSAL ? max(0, key_wg0 - shift) : 0;
+  const int q_begin = CAUSAL ? max(0, key_wg0 - shift) : (window > 0 ? max(0, key_wg0 - shift - window + 1) : 0);
   const int q_end = (window > 0) ? min(L, key_wg0 + C::BK - 1 + window - shift) : L;
   const bool empty = q_end <= q_begin;
   const int qt_lo = empty ? 0 : q_begin / C::BQ, qt_hi = empty ? -1 : (q_end - 1) / C::BQ;
@@ -272,19 +173,30 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   auto wave_needs = [&](int q0) {
     const int qw0 = q0 + 32 * qh;
     return key_w0 < Lk && qw0 < L && (!CAUSAL || qw0 + 31 + shift >= key_w0) &&
-           (window <= 0 || qw0 + shift <= key_w0 + 31 + window - 1);
+           (window <= 0 || qw0 + shift <= key_w0 + 31 + window - 1) &&
+           (CAUSAL || window <= 0 || qw0 + 31 + shift >= key_w0 - window + 1);
   };
+  // the wave's 32 x 32 block straddles a mask boundary
+  auto block_mask = [&](int q0) {
+    const int qw0 = q0 + 32 * qh;
+    return (qw0 + 32 > L) || (CAUSAL && qw0 + shift < key_w0 + 31) ||
+           (window > 0 && qw0 + 31 + shift > key_w0 + window - 1) ||
+           (!CAUSAL && window > 0 && qw0 + shift < key_w0 + 31 - window + 1);
+  };
+  const RangeMaskK<CAUSAL> ok{L, shift, window, key_w0 + ln};
 
   wait_copies_and_barrier();
   for (int it = 0; it < n_it; it += 2) {
     if (it + 1 < n_it) issue(it + 1, q_st1, do_st1, stat_st1);
     if (wave_needs(q0_of(it)))
-      kv_tile<D, CAUSAL, F16>(st, ad, k_blk, v_blk, q_st0, do_st0, stat_st0, q0_of(it), L, shift, window, qh, key_w0, c, lane);
+      kv_tile<D, F16>(st, ad, k_blk, v_blk, q_st0, do_st0, stat_st0, q0_of(it), block_mask(q0_of(it)), ok, qh, c,
+                      lane);
     wait_copies_and_barrier();
     if (it + 1 >= n_it) break;
     if (it + 2 < n_it) issue(it + 2, q_st0, do_st0, stat_st0);
     if (wave_needs(q0_of(it + 1)))
-      kv_tile<D, CAUSAL, F16>(st, ad, k_blk, v_blk, q_st1, do_st1, stat_st1, q0_of(it + 1), L, shift, window, qh, key_w0, c, lane);
+      kv_tile<D, F16>(st, ad, k_blk, v_blk, q_st1, do_st1, stat_st1, q0_of(it + 1), block_mask(q0_of(it + 1)), ok,
+                      qh, c, lane);
     wait_copies_and_barrier();
   }
 
@@ -341,86 +253,6 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 // transposing read (dQ^T = K^T dS^T), so it uses the swz_dual layout; the V
 // tile is only read row-wise (dP^T = V dO^T) and is padded.  The two 32-key
 // halves of a tile are processed one after the other to keep registers low.
-template <int D>
-struct QCfg {
-  static constexpr int kWaves = 4;
-  static constexpr int BQ = 32 * kWaves;         // queries per work-group
-  static constexpr int BC = 64;                  // keys per streamed tile
-  static constexpr int KT = BC * D * 2;          // bytes of a K tile (swz_dual)
-  static constexpr int VT = BC * Pad<D>::KSTR;   // bytes of a padded V tile
-  static constexpr int KCOPIES = KT / 1024;
-  static constexpr int VCOPIES = VT / 1024;
-  static constexpr int KPER = KCOPIES / kWaves;
-  static constexpr int VPER = (VCOPIES + kWaves - 1) / kWaves;
-  static constexpr int NSTEP = D / 16;
-  static constexpr int NDB = D / 32;
-  static_assert(KCOPIES % kWaves == 0 && VT % 1024 == 0, "tiles must split into whole wave copies");
-};
-
-template <int D>
-struct QState {
-  bf16x8 qr[QCfg<D>::NSTEP];    // this wave's 32 Q rows (B operand of S^T = K Q^T)
-  bf16x8 dor[QCfg<D>::NSTEP];   // this wave's 32 dO rows (B operand of dP^T = V dO^T)
-  f32x16 dq[QCfg<D>::NDB];      // dQ^T accumulator: lane = query, registers = head dims
-  float lse2, dlt;              // this lane's query statistics
-};
-
-template <int D>
-struct QAddr {
-  int kcopy[QCfg<D>::KPER];     // source offsets of this wave's K tile copies (swz_dual)
-  int vcopy[QCfg<D>::VPER];     // source offsets of this wave's V tile copies (padded)
-  int krow[QCfg<D>::NSTEP];     // row reads of K rows ln (+32 per key half), per K-step
-  int ktr[QCfg<D>::NDB][2];     // transposing reads of K (t = 0), per column block and half
-  int vrow;                     // row reads of padded V rows ln (+32 per key half)
-};
-
-template <int D, bool CAUSAL, bool F16>
-__device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const char* kbuf, const char* vbuf, int k0,
-                                       int Lk, int window, int my_q, int q_w0, int wq_hi, float c, int lane) {
-  using C = QCfg<D>;
-  const int g = lane >> 5;
-  const bool need_mask = (k0 + C::BC > Lk) || (CAUSAL && k0 + C::BC - 1 > q_w0) ||
-                         (window > 0 && k0 < wq_hi - window + 1);
-#pragma unroll
-  for (int kb = 0; kb < 2; ++kb) {
-    // S^T = K Q^T for keys 32kb..32kb+31: lane = query, registers = keys
-    f32x16 p = mfma32x<F16>(lds_load16(kbuf, ad.krow[0] + kb * 32 * (2 * D)), st.qr[0], f32x16{});
-#pragma unroll
-    for (int k = 1; k < C::NSTEP; ++k)
-      p = mfma32x<F16>(lds_load16(kbuf, ad.krow[k] + kb * 32 * (2 * D)), st.qr[k], p);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(p[i], c, -st.lse2));
-    if (need_mask) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kk = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-        const bool ok = kk < Lk && (!CAUSAL || kk <= my_q) && (window <= 0 || kk > my_q - window);
-        p[i] = ok ? p[i] : 0.f;
-      }
-    }
-    // dP^T = V dO^T, dS^T = P^T * (dP^T - D)
-    f32x16 dp = mfma32x<F16>(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR), st.dor[0], f32x16{});
-#pragma unroll
-    for (int k = 1; k < C::NSTEP; ++k)
-      dp = mfma32x<F16>(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR + 32 * k), st.dor[k], dp);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] *= dp[i] - st.dlt;
-    // dQ^T += K^T dS^T: A = K^T via the transposing read, B = dS^T (lane = query)
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int o8 = 8 * u;
-      const int t = 2 * kb + u;
-      const bf16x8 db8 = pack8<F16>(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5],
-                                   p[o8 + 6], p[o8 + 7]);
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db) {
-        const bf16x8 ka = concat4(lds_load_tr(kbuf, ad.ktr[db][0] + t * 16 * (2 * D)),
-                                  lds_load_tr(kbuf, ad.ktr[db][1] + t * 16 * (2 * D)));
-        st.dq[db] = mfma32x<F16>(ka, db8, st.dq[db]);
-      }
-    }
-  }
-}
 
 template <int D, bool CAUSAL, bool F16>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
@@ -455,7 +287,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   // the same three in key coordinates
   const int dq_w0 = q_w0 + shift, dmy_q = my_q + shift, dwq_hi = wq_hi + shift;
 
-  const int kv_end = CAUSAL ? min(Lk, min(L, q_wg0 + C::BQ) + shift) : Lk;
+  const int kv_end = range_key_end<CAUSAL>(Lk, window, min(L, q_wg0 + C::BQ) - 1 + shift);
   const int kv_begin = (window > 0) ? max(0, q_wg0 + shift - window + 1) : 0;
   const bool empty = kv_end <= kv_begin;     // only between chunks of a ring step
   const int j_lo = empty ? 0 : kv_begin / C::BC, j_hi = empty ? -1 : (kv_end - 1) / C::BC;
@@ -501,20 +333,20 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     for (int db = 0; db < C::NDB; ++db) st.dq[db] = f32x16{};
   }
   const float c = a.scale_log2;
-  auto wave_needs = [&](int k0) {
-    return (q_w0 < L) && (!CAUSAL || k0 <= dwq_hi) && (window <= 0 || k0 + C::BC - 1 >= dq_w0 - window + 1);
-  };
+  auto wave_needs = [&](int k0) { return (q_w0 < L) && range_tile_any<CAUSAL, C::BC>(k0, window, dq_w0, dwq_hi); };
+  auto tile_mask = [&](int k0) { return range_tile_needs_mask<CAUSAL, C::BC>(k0, Lk, window, dq_w0, dwq_hi); };
+  const RangeMaskQ<CAUSAL> ok{Lk, window, dmy_q};
 
   wait_copies_and_barrier();
   for (int j = j_lo; j <= j_hi; j += 2) {
     if (j < j_hi) issue(j + 1, k_st1, v_st1);
     if (wave_needs(j * C::BC))
-      q_tile<D, CAUSAL, F16>(st, ad, k_st0, v_st0, j * C::BC, Lk, window, dmy_q, dq_w0, dwq_hi, c, lane);
+      q_tile<D, F16>(st, ad, k_st0, v_st0, j * C::BC, tile_mask(j * C::BC), ok, c, lane);
     wait_copies_and_barrier();
     if (j + 1 > j_hi) break;
     if (j + 1 < j_hi) issue(j + 2, k_st0, v_st0);
     if (wave_needs((j + 1) * C::BC))
-      q_tile<D, CAUSAL, F16>(st, ad, k_st1, v_st1, (j + 1) * C::BC, Lk, window, dmy_q, dq_w0, dwq_hi, c, lane);
+      q_tile<D, F16>(st, ad, k_st1, v_st1, (j + 1) * C::BC, tile_mask((j + 1) * C::BC), ok, c, lane);
     wait_copies_and_barrier();
   }
 

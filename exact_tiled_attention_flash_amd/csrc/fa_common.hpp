@@ -286,4 +286,42 @@ __device__ __forceinline__ void head_tile_of(int r, int n_heads, int n_tiles, in
   }
 }
 
+// ---- masks of the range-tiled kernels (positions in key coordinates)
+// Key j is visible to the query at position i iff j < Lk, j <= i when causal,
+// and, for a window w > 0, i - w < j -- plus j < i + w when not causal: the
+// window then reaches both ways, |i - j| < w (kler.cn "大模型高效注意力机制全
+// 解析" §3.2.1; book.anysome.cn "高效注意力" §4 for the one-sided form).
+template <bool CAUSAL>
+__device__ __forceinline__ bool range_ok(int j, int i, int Lk, int window) {
+  return j < Lk && (!CAUSAL || j <= i) && (window <= 0 || (j > i - window && (CAUSAL || j < i + window)));
+}
+
+// Query-major element mask: the lane's query position is fixed.
+template <bool CAUSAL>
+struct RangeMaskQ {
+  int Lk, window, i;
+  __device__ __forceinline__ bool operator()(int j) const { return range_ok<CAUSAL>(j, i, Lk, window); }
+};
+
+// Do the keys [k0, k0 + BC) need the elementwise mask for queries [i_lo, i_hi]?
+template <bool CAUSAL, int BC>
+__device__ __forceinline__ bool range_tile_needs_mask(int k0, int Lk, int window, int i_lo, int i_hi) {
+  return (k0 + BC > Lk) || (CAUSAL && k0 + BC - 1 > i_lo) || (window > 0 && k0 < i_hi - window + 1) ||
+         (!CAUSAL && window > 0 && k0 + BC - 1 > i_lo + window - 1);
+}
+
+// Does any query in [i_lo, i_hi] see any key in [k0, k0 + BC)?
+template <bool CAUSAL, int BC>
+__device__ __forceinline__ bool range_tile_any(int k0, int window, int i_lo, int i_hi) {
+  return (!CAUSAL || k0 <= i_hi) && (window <= 0 || k0 + BC - 1 >= i_lo - window + 1) &&
+         (CAUSAL || window <= 0 || k0 <= i_hi + window - 1);
+}
+
+// One past the last key any query in [.., i_hi] may see (i_hi = the last query
+// row of a work-group, in key coordinates).
+template <bool CAUSAL>
+__device__ __forceinline__ int range_key_end(int Lk, int window, int i_hi) {
+  return CAUSAL ? min(Lk, i_hi + 1) : (window > 0 ? min(Lk, i_hi + window) : Lk);
+}
+
 }  // namespace fa

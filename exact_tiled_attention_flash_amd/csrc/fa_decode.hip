@@ -86,14 +86,19 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   for (int db = 0; db < C::NDB; ++db) st.o[db] = f32x16{};
   const float c = a.scale_log2;
 
+  // the window of a decode call is one-sided (causal): the key range above
+  // already ends at the newest entry
+  auto tile_mask = [&](int k0) { return range_tile_needs_mask<CAUSAL, C::BC>(k0, n, a.window, min_pos, max_pos); };
+  const RangeMaskQ<CAUSAL> ok{n, a.window, my_pos};
+
   wait_copies_and_barrier();
   for (int j = j_lo; j <= j_hi; j += 2) {
     if (j < j_hi) issue(j + 1, k_st1, v_st1);
-    fwd_tile<D, CAUSAL, F16>(st, k_st0, v_st0, j * C::BC, n, a.window, my_pos, min_pos, max_pos, c, lane);
+    fwd_tile<D, F16>(st, k_st0, v_st0, j * C::BC, tile_mask(j * C::BC), ok, c, lane);
     wait_copies_and_barrier();
     if (j + 1 > j_hi) break;
     if (j + 1 < j_hi) issue(j + 2, k_st0, v_st0);
-    fwd_tile<D, CAUSAL, F16>(st, k_st1, v_st1, (j + 1) * C::BC, n, a.window, my_pos, min_pos, max_pos, c, lane);
+    fwd_tile<D, F16>(st, k_st1, v_st1, (j + 1) * C::BC, tile_mask((j + 1) * C::BC), ok, c, lane);
     wait_copies_and_barrier();
   }
 

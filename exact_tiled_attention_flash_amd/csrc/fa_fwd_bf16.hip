@@ -6,8 +6,8 @@
 // while the previous tile is being used), and for every tile each wave
 //   1. S^T = K Q^T on MFMA (keys as rows, the wave's 32 queries as columns:
 //      every lane then holds 32 scores of ONE query),
-//   2. masks the scores (only on tiles that straddle the causal diagonal, the
-//      window's left edge or the end of the sequence),
+//   2. masks the scores (only on tiles that straddle the causal diagonal, an
+//      edge of the window or the end of the sequence),
 //   3. runs the online-softmax update in registers -- running maximum m and
 //      running sum l per query, rescale of the partial output by
 //      exp(m_old - m_new) (transformer.xph.ink "高效注意力：FlashAttention 与
@@ -76,7 +76,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   const int window = a.window;
 
   // ---- key-tile range of the work-group
-  const int kv_end = CAUSAL ? min(Lk, min(L, q_wg0 + C::BR) + shift) : Lk;
+  const int kv_end = range_key_end<CAUSAL>(Lk, window, min(L, q_wg0 + C::BR) - 1 + shift);
   const int kv_begin = (window > 0) ? max(0, q_wg0 + shift - window + 1) : 0;
   const bool empty = kv_end <= kv_begin;     // possible between chunks of a ring step
   const int j_lo = empty ? 0 : kv_begin / C::BC, j_hi = empty ? -1 : (kv_end - 1) / C::BC;
@@ -97,9 +97,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int db = 0; db < C::NDB; ++db) st.o[db] = f32x16{};
   const float c = a.scale_log2;
 
-  auto wave_needs = [&](int k0) {
-    return (q_w0 < L) && (!CAUSAL || k0 <= dwq_hi) && (window <= 0 || k0 + C::BC - 1 >= dq_w0 - window + 1);
-  };
+  auto wave_needs = [&](int k0) { return (q_w0 < L) && range_tile_any<CAUSAL, C::BC>(k0, window, dq_w0, dwq_hi); };
+  auto tile_mask = [&](int k0) { return range_tile_needs_mask<CAUSAL, C::BC>(k0, Lk, window, dq_w0, dwq_hi); };
+  const RangeMaskQ<CAUSAL> ok{Lk, window, dmy_q};
 
   wait_copies_and_barrier();
   // Tiles alternate between the two stages; the loop is unrolled by two so
@@ -107,12 +107,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   for (int j = j_lo; j <= j_hi; j += 2) {
     if (j < j_hi) issue_kv<D>(cp, krs, vrs, (j + 1) * C::BC, k_st1, v_st1, wave);
     if (wave_needs(j * C::BC))
-      fwd_tile<D, CAUSAL, F16>(st, k_st0, v_st0, j * C::BC, Lk, window, dmy_q, dq_w0, dwq_hi, c, lane);
+      fwd_tile<D, F16>(st, k_st0, v_st0, j * C::BC, tile_mask(j * C::BC), ok, c, lane);
     wait_copies_and_barrier();
     if (j + 1 > j_hi) break;
     if (j + 1 < j_hi) issue_kv<D>(cp, krs, vrs, (j + 2) * C::BC, k_st0, v_st0, wave);
     if (wave_needs((j + 1) * C::BC))
-      fwd_tile<D, CAUSAL, F16>(st, k_st1, v_st1, (j + 1) * C::BC, Lk, window, dmy_q, dq_w0, dwq_hi, c, lane);
+      fwd_tile<D, F16>(st, k_st1, v_st1, (j + 1) * C::BC, tile_mask((j + 1) * C::BC), ok, c, lane);
     wait_copies_and_barrier();
   }
 

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
   const float cs = a.scale_log2;
   float m_run = kNegBig, l_run = 0.f;
 
-  const int kv_end = CAUSAL ? qmax + 1 : L;
+  const int kv_end = range_key_end<CAUSAL>(L, window, qmax);
   const int kv_begin = (window > 0) ? max(0, q0 - window + 1) : 0;
   for (int k0 = (kv_begin / kKeys) * kKeys; k0 < kv_end; k0 += kKeys) {
     __syncthreads();
@@ -64,8 +64,7 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(FwdArgs a) {
 #pragma unroll
       for (int c = 0; c < D; ++c) dot = fmaf(qv[c], ks[j][c], dot);
       const int kk = k0 + j;
-      const bool ok = kk < L && (!CAUSAL || kk <= my_q) && (window <= 0 || kk > my_q - window);
-      s[j] = ok ? dot : -INFINITY;
+      s[j] = range_ok<CAUSAL>(kk, my_q, L, window) ? dot : -INFINITY;
       mx = fmaxf(mx, s[j]);
     }
     const float m_new = fmaxf(m_run, mx * cs);

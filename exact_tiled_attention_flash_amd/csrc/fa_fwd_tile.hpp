@@ -90,10 +90,11 @@ struct FwdState {
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
 // One key tile for one wave: S^T, mask, online softmax, O^T += V^T P^T.
-template <int D, bool CAUSAL, bool F16>
+// need_mask (wave-uniform) says whether the tile straddles a mask boundary;
+// ok(j) then says whether key j is visible to the lane's query.
+template <int D, bool F16, class Mask>
 __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, const char* vbuf, int k0,
-                                         int Lk, int window, int my_q, int q_w0, int wq_hi, float c,
-                                         int lane) {
+                                         bool need_mask, const Mask& ok, float c, int lane) {
   using C = FwdCfg<D>;
   const int g = lane >> 5, ln = lane & 31;
   // 1. S^T (64 keys x 32 queries) as two 32x32 blocks
@@ -113,17 +114,12 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
   }
 
   // 2. mask, only on tiles that straddle a boundary (wave-uniform decision)
-  const bool need_mask = (k0 + C::BC > Lk) || (CAUSAL && k0 + C::BC - 1 > q_w0) ||
-                         (window > 0 && k0 < wq_hi - window + 1);
   if (need_mask) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kk0 = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      const int kk1 = kk0 + 32;
-      const bool ok0 = kk0 < Lk && (!CAUSAL || kk0 <= my_q) && (window <= 0 || kk0 > my_q - window);
-      const bool ok1 = kk1 < Lk && (!CAUSAL || kk1 <= my_q) && (window <= 0 || kk1 > my_q - window);
-      if (!ok0) s0[i] = -INFINITY;
-      if (!ok1) s1[i] = -INFINITY;
+      if (!ok(kk0)) s0[i] = -INFINITY;
+      if (!ok(kk0 + 32)) s1[i] = -INFINITY;
     }
   }
 

@@ -24,7 +24,6 @@ int check_common(int B, int Hq, int Hkv, int L, int d, float scale, int causal, 
   if (!(scale > 0.f) || !isfinite(scale)) return FA_ERR_INVALID_ARG;
   if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (window < 0) return FA_ERR_INVALID_ARG;
-  if (window > 0 && !causal) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (Hq % Hkv != 0) return FA_ERR_GQA;
@@ -269,7 +268,7 @@ extern "C" const char* flash_attn_strerror(int code) {
   switch (code) {
     case FA_OK: return "ok";
     case FA_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, non-positive size, or bad scale)";
-    case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dim, dtype, or window without causal)";
+    case FA_ERR_UNSUPPORTED: return "unsupported configuration (head dim, dtype, or a decode window without causal)";
     case FA_ERR_GQA: return "number of query heads is not a multiple of the number of key/value heads";
     case FA_ERR_WORKSPACE: return "backward workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "HIP launch or runtime error";

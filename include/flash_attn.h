@@ -21,9 +21,11 @@
  * mdooai.com "Ch.04", sparse-attention formula):
  *   causal  -- key j is allowed for query i iff j <= i (claspmoon.cn §3.5,
  *              is_causal);
- *   window  -- w >= 1 together with causal: allowed iff i-w+1 <= j <= i, the
- *              w most recent keys including the query itself
- *              (book.anysome.cn, "高效注意力", §4 sliding window).
+ *   window  -- w >= 1 with causal: allowed iff i-w+1 <= j <= i, the w most
+ *              recent keys including the query itself (book.anysome.cn,
+ *              "高效注意力", §4 sliding window); w >= 1 without causal: the
+ *              window reaches both ways, allowed iff |i - j| < w (kler.cn
+ *              §3.2.1: positions before and after the query).
  * Grouped-query attention (book.anysome.cn "高效注意力" §3): Hkv divides Hq
  * and query head h reads K/V head h / (Hq / Hkv).
  *
@@ -64,7 +66,7 @@ extern "C" {
 /* return codes */
 #define FA_OK                0
 #define FA_ERR_INVALID_ARG  (-1)  /* null/misaligned pointer, non-positive size, bad scale */
-#define FA_ERR_UNSUPPORTED  (-2)  /* head dim, dtype, or window without causal */
+#define FA_ERR_UNSUPPORTED  (-2)  /* head dim, dtype, or an unsupported mask combination */
 #define FA_ERR_GQA          (-3)  /* Hq is not a multiple of Hkv */
 #define FA_ERR_WORKSPACE    (-4)  /* backward workspace missing or too small */
 #define FA_ERR_HIP          (-5)  /* a HIP launch or runtime call failed */
@@ -76,7 +78,8 @@ extern "C" {
  *   lse [B,Hq,L] float32            : output log-sum-exp; may be NULL if not wanted
  *   softmax_scale                   : s > 0 and finite (usually 1/sqrt(d))
  *   causal                          : 0 or 1
- *   window                          : 0 = none; w >= 1 requires causal = 1
+ *   window                          : 0 = none; w >= 1 (one-sided with causal,
+ *                                     symmetric without)
  *   dtype                           : FA_DTYPE_BF16, FA_DTYPE_F16 or
  *                                     FA_DTYPE_F32, each with d in {64,128}
  * Sizes: 1 <= L <= 2^23 (one head must stay below 4 GiB), B, Hq, Hkv >= 1.
@@ -215,6 +218,7 @@ int flash_attn_bwd_block(const void* q, const void* k, const void* v, const void
  * and cache_len = the number of filled slots: for one new token the slot order
  * does not matter.  The keys are split across work-groups and the partials
  * merged exactly, so the cache is read once per K/V head whatever G and Lq.
+ * A window needs causal = 1 here (FA_ERR_UNSUPPORTED otherwise).
  * Requires (Hq/Hkv) * Lq <= 32 (else FA_ERR_UNSUPPORTED: use
  * flash_attn_fwd_block for longer chunks), d in {64,128}, bf16 or fp16,
  * B * Hkv <= 65535.  workspace: at least flash_attn_decode_workspace_bytes()

@@ -46,8 +46,10 @@ def position_mask(q_pos, k_pos, causal, window):
     ``q_pos[r]`` attend to the key at position ``k_pos[c]``?
 
     Causal per claspmoon.cn §3.5 (``is_causal``: keys at or before the query);
-    window per book.anysome.cn §4 (each token attends only to the w nearby,
-    here preceding, tokens, itself included).
+    window per book.anysome.cn §4 (each token attends only to the w nearby
+    tokens, itself included): with causal masking the w - 1 preceding ones;
+    without it the window reaches both ways (kler.cn §3.2.1, positions before
+    and after), |i - j| < w.
     """
     i = np.asarray(q_pos, dtype=np.int64)[:, None]
     j = np.asarray(k_pos, dtype=np.int64)[None, :]
@@ -55,9 +57,9 @@ def position_mask(q_pos, k_pos, causal, window):
     if causal:
         ok &= j <= i
     if window > 0:
-        if not causal:
-            raise ValueError("a sliding window is defined only with causal masking")
         ok &= j >= i - window + 1
+        if not causal:
+            ok &= j <= i + window - 1
     return ok
 
 

@@ -89,7 +89,7 @@ def test_fwd_rejects_invalid_arguments(lib):
     assert call_fwd(lib, dtype=7) == UNS
     assert call_fwd(lib, dtype=3) == UNS
     assert call_fwd(lib, dtype=fa.FA_DTYPE_F16, q=None) == INV    # fp16 passes the dtype check
-    assert call_fwd(lib, causal=0, window=4) == UNS
+    assert call_fwd(lib, causal=0, window=4, q=None) == INV     # a symmetric window passes the mask check
     assert call_fwd(lib, Hq=6, Hkv=4) == GQA
 
 
@@ -106,7 +106,7 @@ def test_bwd_rejects_invalid_arguments(lib):
     assert call_bwd(lib, dtype=fa.FA_DTYPE_F32) == UNS
     assert call_bwd(lib, dtype=3) == UNS
     assert call_bwd(lib, dtype=fa.FA_DTYPE_F16, dq=None) == INV   # fp16 passes the dtype check
-    assert call_bwd(lib, causal=0, window=3) == UNS
+    assert call_bwd(lib, causal=0, window=3, dq=None) == INV    # a symmetric window passes the mask check
     assert call_bwd(lib, Hq=3, Hkv=2) == c["FA_ERR_GQA"]
 
 
@@ -123,7 +123,7 @@ def test_stage_entry_points_reject_invalid_arguments(lib):
         lib.flash_attn_bwd_dkdv(q, FAKE, FAKE, FAKE, ws, nb, dk, FAKE, 1, 2, Hkv, L, 64, 0.125, causal, window,
                                 fa.FA_DTYPE_BF16, None)
     assert kv(q=None) == INV and kv(dk=MISALIGNED) == INV and kv(ws=FAKE * 16 + 64) == WS
-    assert kv(causal=0, window=2) == UNS and kv(Hkv=3) == GQA and kv(L=-1) == INV
+    assert kv(causal=0, window=2, q=None) == INV and kv(Hkv=3) == GQA and kv(L=-1) == INV
     dqf = lambda dq=FAKE, ws=ws, nb=nb, scale=0.125: \
         lib.flash_attn_bwd_dq(FAKE, FAKE, FAKE, FAKE, ws, nb, dq, 1, 2, 2, 16, 64, scale, 1, 0,
                               fa.FA_DTYPE_BF16, None)
@@ -158,7 +158,7 @@ def test_chunk_and_merge_entry_points_reject_invalid_arguments(lib):
     assert fb(q=None) == INV and fb(Lk=0) == INV and fb(Lq=0) == INV
     assert fb(qo=-1) == INV and fb(ko=(1 << 30) + 1) == INV and fb(Lk=(1 << 23) + 1) == INV
     assert fb(dt=fa.FA_DTYPE_F32) == UNS and fb(dt=3) == UNS and fb(d=96) == UNS
-    assert fb(causal=0, window=2) == UNS and fb(Hkv=3) == GQA
+    assert fb(causal=0, window=2, q=None) == INV and fb(Hkv=3) == GQA
     assert fb(dt=fa.FA_DTYPE_F16, q=None) == INV                     # fp16 passes the dtype check
 
     def mg(oa=FAKE, la=FAKE, o=FAKE, L=16, d=64, dt=fa.FA_DTYPE_BF16):

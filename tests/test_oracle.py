@@ -31,11 +31,15 @@ def rnd(shape, seed, scale=1.0):
 def allowed_range(i, L, causal, window):
     """Allowed keys of query i as a Python range (written independently of the mask code)."""
     hi = i if causal else L - 1
-    lo = max(0, i - window + 1) if window > 0 else 0
+    lo = 0
+    if window > 0:
+        lo = max(0, i - window + 1)
+        if not causal:
+            hi = min(L - 1, i + window - 1)
     return range(lo, hi + 1)
 
 
-MASKS = [(False, 0), (True, 0), (True, 1), (True, 3), (True, 7)]
+MASKS = [(False, 0), (True, 0), (True, 1), (True, 3), (True, 7), (False, 1), (False, 3), (False, 5)]
 
 
 # ----------------------------------------------------------------------------- pins
@@ -156,10 +160,11 @@ def pin_gqa_is_repeated_mha(o):
 def pin_window_at_least_L_is_causal(o):
     L = 8
     q, k, v = rnd((1, 2, L, 3), 26), rnd((1, 2, L, 3), 27), rnd((1, 2, L, 3), 28)
-    O1, l1 = o.forward(q, k, v, 1.0, True, 0)
-    for w in (L, L + 5):
-        O2, l2 = o.forward(q, k, v, 1.0, True, w)
-        assert np.array_equal(O1, O2) and np.array_equal(l1, l2)
+    for causal in (True, False):
+        O1, l1 = o.forward(q, k, v, 1.0, causal, 0)
+        for w in (L, L + 5):
+            O2, l2 = o.forward(q, k, v, 1.0, causal, w)
+            assert np.array_equal(O1, O2) and np.array_equal(l1, l2)
 
 
 def _torch_mask(L, causal, window):
@@ -204,7 +209,7 @@ def pin_backward_finite_differences(o):
     B, Hq, Hkv, L, d = 1, 2, 1, 5, 3
     q, k, v, do = rnd((B, Hq, L, d), 36), rnd((B, Hkv, L, d), 37), rnd((B, Hkv, L, d), 38), rnd((B, Hq, L, d), 39)
     h = 1e-6
-    for causal, window in [(False, 0), (True, 0), (True, 2)]:
+    for causal, window in [(False, 0), (True, 0), (True, 2), (False, 2)]:
         grads = o.backward(q, k, v, do, 0.8, causal, window)
 
         def f(q_, k_, v_):
@@ -274,12 +279,13 @@ def pin_block_brute_force(o):
     # tiny chunks at offsets, by explicit loops over the definition (empty rows: O = 0, LSE = -inf)
     q, k, v = rnd((1, 2, 3, 2), 70), rnd((1, 1, 5, 2), 71), rnd((1, 1, 5, 2), 72)
     for causal, window, qo, ko in [(True, 0, 4, 2), (True, 2, 4, 2), (False, 0, 0, 7), (True, 0, 0, 3),
-                                   (True, 3, 9, 3)]:
+                                   (True, 3, 9, 3), (False, 2, 4, 2), (False, 3, 1, 4)]:
         O, l = o.block_forward(q, k, v, 0.7, causal, window, qo, ko)
         for h in range(2):
             for i in range(3):
                 keys = [j for j in range(5)
-                        if (not causal or ko + j <= qo + i) and (window <= 0 or ko + j >= qo + i - window + 1)]
+                        if (not causal or ko + j <= qo + i) and (window <= 0 or ko + j >= qo + i - window + 1)
+                        and (causal or window <= 0 or ko + j <= qo + i + window - 1)]
                 if not keys:
                     assert np.isneginf(l[0, h, i]) and np.all(O[0, h, i] == 0.0)
                     continue
@@ -552,9 +558,10 @@ def test_planted_softmax_backward_sign(monkeypatch):
     assert _some_pin_fails(BWD_PINS)
 
 
-def test_unallowed_window_without_causal_is_rejected():
-    with pytest.raises(ValueError):
-        oracle.allowed_mask(np.arange(4), 4, False, 2)
+def test_symmetric_window_mask_and_bad_gqa():
+    # w = 2 without causal: each position sees itself and one neighbour on each side
+    want = np.array([[1, 1, 0, 0], [1, 1, 1, 0], [0, 1, 1, 1], [0, 0, 1, 1]], dtype=bool)
+    assert np.array_equal(oracle.allowed_mask(np.arange(4), 4, False, 2), want)
     with pytest.raises(ValueError):
         oracle.kv_head_of(0, 6, 4)
 
@@ -628,3 +635,17 @@ def test_planted_global_keys_ignored(monkeypatch):
     monkeypatch.setattr(oa, "general_mask", bad)
     monkeypatch.setattr(oracle, "general_mask", bad)
     assert _some_pin_fails(MASK_PINS)
+
+
+def test_planted_symmetric_window_one_sided(monkeypatch):
+    good = oa.position_mask
+
+    def bad(q_pos, k_pos, causal, window):
+        # the window's upper edge dropped: a non-causal window reaching back only
+        if window > 0 and not causal:
+            i = np.asarray(q_pos)[:, None]
+            j = np.asarray(k_pos)[None, :]
+            return j >= i - window + 1
+        return good(q_pos, k_pos, causal, window)
+    monkeypatch.setattr(oa, "position_mask", bad)
+    assert _some_pin_fails(PINS)

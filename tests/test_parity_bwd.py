@@ -97,6 +97,11 @@ SMALL = [
     W.small("bwd fp16 L300 causal gqa2", 1, 4, 2, 300, 128, dtype=torch.float16, seed=212),
     W.small("bwd fp16 L640 window64 d64", 1, 2, 2, 640, 64, dtype=torch.float16, window=64, seed=213),
     W.small("bwd fp16 L200 noncausal", 2, 2, 2, 200, 128, dtype=torch.float16, causal=False, seed=214),
+    W.small("bwd sym window1", 1, 2, 2, 300, 128, causal=False, window=1, seed=215),
+    W.small("bwd sym window7 d64 gqa2", 1, 4, 2, 777, 64, causal=False, window=7, seed=216),
+    W.small("bwd sym window200 L1500", 1, 2, 2, 1500, 128, causal=False, window=200, seed=217, std=0.5),
+    W.small("bwd sym window513 L2100", 1, 2, 1, 2100, 128, causal=False, window=513, seed=218),
+    W.small("bwd fp16 sym window64 L640", 1, 2, 2, 640, 64, dtype=torch.float16, causal=False, window=64, seed=219),
 ]
 
 

@@ -66,6 +66,9 @@ PAIRS = [
     (1, 2, 2, 100, 100, 64, True, 0, 0, 400, torch.bfloat16),        # keys after all queries: every row empty
     (1, 2, 2, 150, 333, 128, False, 0, 1000, 7, torch.float16),      # non-causal: offsets irrelevant
     (1, 2, 2, 96, 64, 128, True, 16, 1000, 0, torch.bfloat16),       # window far past the chunk: all empty
+    (1, 2, 2, 200, 300, 128, False, 64, 300, 200, torch.bfloat16),   # symmetric window across both chunk edges
+    (1, 4, 2, 130, 250, 64, False, 100, 0, 180, torch.float16),      # symmetric window, keys partly after queries
+    (1, 2, 2, 64, 64, 128, False, 8, 0, 500, torch.bfloat16),        # symmetric window far away: all empty
 ]
 
 
@@ -149,6 +152,7 @@ RINGS = [
     (W.small("ring window100 fp16 P3", 1, 2, 2, 768, 64, dtype=torch.float16, window=100, seed=611,
              backward=True), 3),
     (W.small("ring noncausal P2", 2, 2, 2, 300, 128, causal=False, seed=612, backward=True), 2),
+    (W.small("ring sym window150 P3", 1, 2, 2, 900, 128, causal=False, window=150, seed=613, backward=True), 3),
 ]
 
 

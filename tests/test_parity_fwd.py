@@ -109,6 +109,14 @@ SMALL = [
     W.small("fp16 L1000 window200 d64", 1, 2, 2, 1000, 64, dtype=torch.float16, window=200, seed=115),
     W.small("fp16 L257 noncausal d128 mqa", 1, 2, 1, 257, 128, dtype=torch.float16, causal=False, seed=116),
     W.small("fp16 large scores", 1, 2, 2, 384, 128, dtype=torch.float16, seed=117, std=3.0),
+    # windows reaching both ways (no causal mask): |i - j| < w
+    W.small("sym window1", 1, 2, 2, 300, 128, causal=False, window=1, seed=118),
+    W.small("sym window5 d64 gqa2", 1, 4, 2, 777, 64, causal=False, window=5, seed=119),
+    W.small("sym window200 L1500", 1, 2, 2, 1500, 128, causal=False, window=200, seed=123, std=0.5),
+    W.small("sym window513 L2100", 1, 2, 1, 2100, 128, causal=False, window=513, seed=124),
+    W.small("sym window5000 L2048", 1, 2, 2, 2048, 64, causal=False, window=5000, seed=125),
+    W.small("fp32 sym window9 L150", 1, 2, 2, 150, 64, dtype=torch.float32, causal=False, window=9, seed=126),
+    W.small("fp16 sym window64 L640", 1, 2, 2, 640, 128, dtype=torch.float16, causal=False, window=64, seed=127),
 ]
 
 
