@@ -22,6 +22,7 @@ import torch
 
 __all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "fwd_block", "bwd_block", "merge",
            "decode", "decode_workspace_bytes",
+           "MaskPlan", "fwd_masked", "bwd_masked", "block_band_mask", "allowed_pairs",
            "strerror", "library", "library_path",
            "FlashAttentionFunction", "scaled_dot_product_attention",
            "FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "EXPORTED_SYMBOLS"]
@@ -35,10 +36,18 @@ EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspac
                     "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
                     "flash_attn_fwd_block", "flash_attn_merge", "flash_attn_bwd_block",
                     "flash_attn_decode", "flash_attn_decode_workspace_bytes",
+                    "flash_attn_mask_plan_bytes", "flash_attn_mask_plan", "flash_attn_fwd_masked",
+                    "flash_attn_bwd_masked",
                     "flash_attn_strerror", "flash_attn_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
+
+
+class FaMask(ctypes.Structure):
+    """``fa_mask`` of ``include/flash_attn.h``."""
+    _fields_ = [("causal", ctypes.c_int), ("window", ctypes.c_int), ("global_pos", ctypes.c_void_p),
+                ("n_global", ctypes.c_int), ("block_mask", ctypes.c_void_p), ("block", ctypes.c_int)]
 
 
 def library_path():
@@ -81,6 +90,16 @@ def library():
     lib.flash_attn_decode_workspace_bytes.restype = sz
     lib.flash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.flash_attn_bwd_workspace_bytes.restype = sz
+    mp = ctypes.POINTER(FaMask)
+    lib.flash_attn_mask_plan_bytes.argtypes = [i]
+    lib.flash_attn_mask_plan_bytes.restype = sz
+    lib.flash_attn_mask_plan.argtypes = [mp, i, vp, sz, vp]
+    lib.flash_attn_mask_plan.restype = i
+    lib.flash_attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, mp, vp, sz, i, vp]
+    lib.flash_attn_fwd_masked.restype = i
+    lib.flash_attn_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                          i, i, i, i, i, f, mp, vp, sz, i, vp]
+    lib.flash_attn_bwd_masked.restype = i
     lib.flash_attn_strerror.argtypes = [i]
     lib.flash_attn_strerror.restype = ctypes.c_char_p
     lib.flash_attn_version.argtypes = []
@@ -311,6 +330,118 @@ def decode(q, k_cache, v_cache, cache_len=None, causal=True, window=0, scale=Non
     return out, lse
 
 
+def block_band_mask(L, block=64, radius=1):
+    """Block-sparse pattern in which query block a attends to key blocks b with
+    |a - b| <= radius (kler.cn §4.1.2: each block attends to itself and its
+    neighbouring blocks).  Returns a bool CPU tensor ``[nbm, nbm]``, nbm = ceil(L / block)."""
+    nbm = (int(L) + block - 1) // block
+    idx = torch.arange(nbm)
+    return (idx[:, None] - idx[None, :]).abs() <= int(radius)
+
+
+def allowed_pairs(L, causal=False, window=0, global_tokens=(), block_mask=None, block=64):
+    """Number of allowed (query, key) pairs of the general mask over one sequence of
+    length L (the same rule as ``MaskPlan``): the algorithmic work of one head is
+    4 * d * allowed_pairs flops forward.  Counted row by row on the host in O(L) memory."""
+    L = int(L)
+    glob = sorted({(p + L if p < 0 else p) for p in global_tokens if -L <= p < L})
+    is_g = torch.zeros(L, dtype=torch.bool)
+    if glob:
+        is_g[torch.tensor(glob)] = True
+    bm = None if block_mask is None else torch.as_tensor(block_mask).bool().cpu()
+    total = 0
+    chunk = max(1, (1 << 24) // L)
+    j = torch.arange(L)
+    for r0 in range(0, L, chunk):
+        i = torch.arange(r0, min(L, r0 + chunk))[:, None]
+        local = torch.ones(i.shape[0], L, dtype=torch.bool)
+        if window > 0:
+            local &= (i - j[None, :]).abs() < window
+        if bm is not None:
+            local &= bm[(i // block), (j // block)[None, :]]
+        ok = local | is_g[i] | is_g[None, :]
+        if causal:
+            ok &= j[None, :] <= i
+        total += int(ok.sum())
+    return total
+
+
+class MaskPlan:
+    """A general sparse mask over sequences of length ``L`` and its device plan.
+
+    allowed(i, j) = causal_ok and ((|i - j| < window and block_mask[i // block, j // block])
+                                   or i global or j global)
+    (claspmoon.cn "14 · 缩放定律与高效注意力" §4.3: local window plus global tokens;
+    kler.cn §4.1.2: block-sparse masks; §3.2.1 / §5.1.2: a window before and after,
+    first and last token global).  ``global_tokens`` are positions (negative ones count
+    from the end); ``block_mask`` is a ``[nbm, nbm]`` bool tensor with nbm = ceil(L / block)
+    and ``block`` a multiple of 64.  The plan is built once on the device and serves every
+    masked call of that length (all heads and layers, forward and backward).
+    """
+
+    def __init__(self, L, causal=False, window=0, global_tokens=(), block_mask=None, block=64, device="cuda"):
+        self.L, self.causal, self.window, self.block = int(L), bool(causal), int(window), int(block)
+        self.global_tokens = tuple(int(p) for p in global_tokens)
+        dev = torch.device(device)
+        self._gpos = (torch.tensor(self.global_tokens, dtype=torch.int32, device=dev)
+                      if self.global_tokens else None)
+        self._bmask = None
+        if block_mask is not None:
+            nbm = (self.L + self.block - 1) // self.block
+            bm = torch.as_tensor(block_mask)
+            if bm.shape != (nbm, nbm):
+                raise ValueError("block_mask must be [ceil(L / block)] * 2 = [%d, %d]" % (nbm, nbm))
+            self._bmask = bm.to(dtype=torch.uint8, device=dev).contiguous()
+        self.block_mask = None if block_mask is None else torch.as_tensor(block_mask).bool().cpu()
+        nbytes = int(library().flash_attn_mask_plan_bytes(self.L))
+        if nbytes == 0:
+            raise RuntimeError("MaskPlan: unsupported length %d (1 <= L <= 2^18)" % self.L)
+        self.plan = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        self.desc = FaMask(int(self.causal), self.window, _ptr(self._gpos), len(self.global_tokens),
+                           _ptr(self._bmask), self.block)
+        rc = library().flash_attn_mask_plan(ctypes.byref(self.desc), self.L, _ptr(self.plan), nbytes,
+                                            _stream(self.plan))
+        _check(rc, "flash_attn_mask_plan")
+
+    def allowed_pairs(self):
+        return allowed_pairs(self.L, self.causal, self.window, self.global_tokens, self.block_mask, self.block)
+
+
+def fwd_masked(q, k, v, plan, scale=None, out=None, lse=None):
+    """Exact attention under a ``MaskPlan`` (16-bit dtypes).  Returns ``(o, lse)``; rows
+    with no allowed key get o = 0, lse = -inf."""
+    B, Hq, Hkv, L, d = _shapes(q, k, v)
+    if L != plan.L:
+        raise ValueError("the plan was built for L = %d" % plan.L)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device) if lse is None else lse
+    rc = library().flash_attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, L, d, scale,
+                                         ctypes.byref(plan.desc), _ptr(plan.plan), plan.plan.numel(),
+                                         _DTYPES[q.dtype], _stream(q))
+    _check(rc, "flash_attn_fwd_masked")
+    return out, lse
+
+
+def bwd_masked(q, k, v, o, lse, dout, plan, scale=None, workspace=None, dq=None, dk=None, dv=None):
+    """Gradient of sum(o * dout) under a ``MaskPlan``; returns ``(dq, dk, dv)``."""
+    B, Hq, Hkv, L, d = _shapes(q, k, v)
+    if L != plan.L:
+        raise ValueError("the plan was built for L = %d" % plan.L)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    nbytes = bwd_workspace_bytes(B, Hq, Hkv, L, d, q.dtype)
+    workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if workspace is None else workspace
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    rc = library().flash_attn_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                         _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), B, Hq, Hkv, L, d,
+                                         scale, ctypes.byref(plan.desc), _ptr(plan.plan), plan.plan.numel(),
+                                         _DTYPES[q.dtype], _stream(q))
+    _check(rc, "flash_attn_bwd_masked")
+    return dq, dk, dv
+
+
 class FlashAttentionFunction(torch.autograd.Function):
     """Exact attention as a ``torch.autograd.Function``.
 
@@ -321,26 +452,36 @@ class FlashAttentionFunction(torch.autograd.Function):
     """
 
     @staticmethod
-    def forward(ctx, q, k, v, causal=False, window=0, scale=None):
+    def forward(ctx, q, k, v, causal=False, window=0, scale=None, plan=None):
         q, k, v = (t.contiguous() for t in (q, k, v))
-        o, lse = fwd(q, k, v, causal=causal, window=window, scale=scale)
+        if plan is None:
+            o, lse = fwd(q, k, v, causal=causal, window=window, scale=scale)
+        else:
+            o, lse = fwd_masked(q, k, v, plan, scale=scale)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.causal, ctx.window, ctx.scale = causal, window, scale
+        ctx.causal, ctx.window, ctx.scale, ctx.plan = causal, window, scale, plan
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), causal=ctx.causal, window=ctx.window,
-                         scale=ctx.scale)
-        return dq, dk, dv, None, None, None
+        if ctx.plan is None:
+            dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), causal=ctx.causal, window=ctx.window,
+                             scale=ctx.scale)
+        else:
+            dq, dk, dv = bwd_masked(q, k, v, o, lse, do.contiguous(), ctx.plan, scale=ctx.scale)
+        return dq, dk, dv, None, None, None, None
 
 
-def scaled_dot_product_attention(q, k, v, is_causal=False, scale=None, window=0):
+def scaled_dot_product_attention(q, k, v, is_causal=False, scale=None, window=0, mask_plan=None):
     """Drop-in for ``scaled_dot_product_attention(q, k, v, is_causal=...)`` on ``[B, H, L, d]``
     tensors (claspmoon.cn "14 · 缩放定律与高效注意力" §3.5), with grouped-query K/V
     (``k.shape[1]`` dividing ``q.shape[1]``) and an optional sliding ``window`` (one-sided
     with ``is_causal``, symmetric without)
-    (kler.cn, §3.2.1 configuration keys).  Differentiable through ``FlashAttentionFunction``.
+    (kler.cn, §3.2.1 configuration keys).  A ``mask_plan`` (``MaskPlan``) replaces
+    ``is_causal`` and ``window`` by its general sparse mask.  Differentiable through
+    ``FlashAttentionFunction``.
     """
-    return FlashAttentionFunction.apply(q, k, v, bool(is_causal), int(window), scale)
+    if mask_plan is not None:
+        return FlashAttentionFunction.apply(q, k, v, False, 0, scale, mask_plan)
+    return FlashAttentionFunction.apply(q, k, v, bool(is_causal), int(window), scale, None)

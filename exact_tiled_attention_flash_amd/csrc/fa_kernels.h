@@ -83,4 +83,50 @@ struct DecodeArgs {
 void decode_plan(int B, int Hkv, int Lk, int& n_splits, int& split_keys);
 hipError_t launch_decode(const DecodeArgs& a, bool causal, hipStream_t stream);
 
+// ---- general masks through a mask plan
+// A mask over one sequence of L positions (queries and keys alike):
+//   allowed(i, j) = causal_ok && ((window_ok && block_ok) || global(i) || global(j))
+// with causal_ok: j <= i (when causal); window_ok: |i - j| < window (when
+// window > 0); block_ok: block_mask[i / block][j / block] != 0 (when given);
+// global: the position is one of global_pos (negative entries count from L).
+struct MaskDesc {
+  int causal, window;
+  const int* global_pos;             // device, n_global entries (may be null when n_global == 0)
+  int n_global;
+  const unsigned char* block_mask;   // device, [nbm][nbm] with nbm = ceil(L / block), or null
+  int block;                         // multiple of 64
+};
+
+// A plan classifies every 64 x 64 block of the L x L mask as empty, partial or
+// full and lists, for every 128-row work-group of the forward and dQ kernels,
+// the 64-key tiles it must visit (and, for every 128-key work-group of the
+// dK/dV kernel, the 64-query tiles), plus a heaviest-first work-group order.
+// List entry: tile index | class(first 64 rows or keys) << 16 | class(second)
+// << 18 | block_ok(first) << 20 | block_ok(second) << 21; class 0 empty,
+// 1 partial (elementwise mask), 2 full.
+struct PlanLayout {
+  int L, nb, nw;                     // nb 64-blocks, nw 128-wide work-group rows (= columns)
+  size_t gbits, row_cnt, row_ord, col_cnt, col_ord, meta, row_ent, col_ent, total;   // byte offsets
+};
+PlanLayout plan_layout(int L);
+
+struct PlanPtrs {
+  const unsigned long long* gbits;   // [nb] bit t of word b: position 64b + t is global
+  const int* row_cnt;                // [nw] entries per work-group row
+  const int* row_ord;                // [nw] work-group rows by descending entry count
+  const unsigned* row_ent;           // [nw][nb] entries (key tiles), ascending
+  const int* col_cnt;
+  const int* col_ord;
+  const unsigned* col_ent;           // [nw][nb] entries (query tiles), ascending
+  const int* meta;                   // [0], [1]: leading heavy ranks of row_ord, col_ord
+  int nb, nw;
+};
+PlanPtrs plan_ptrs(const void* plan, int L);
+
+hipError_t launch_mask_plan(const MaskDesc& m, int L, void* plan, hipStream_t stream);
+// forward / backward (preprocess, dK/dV, dQ) under a plan; a.L is the sequence
+// length the plan was built for, a.window its window
+hipError_t launch_fwd_masked(const FwdArgs& a, const PlanPtrs& p, bool causal, hipStream_t stream);
+hipError_t launch_bwd_masked(const BwdArgs& a, const PlanPtrs& p, bool causal, hipStream_t stream);
+
 }  // namespace fa

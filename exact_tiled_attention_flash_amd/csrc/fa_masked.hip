@@ -1,0 +1,693 @@
+// fa_masked.hip -- exact attention under general sparse masks, driven by a
+// mask plan (gfx950).
+//
+// The mask family: a sliding window (one-sided with causal masking, else
+// reaching both ways), a block-sparse pattern over b x b blocks, and global
+// positions that see and are seen by every position, all under an optional
+// causal mask (claspmoon.cn "14 · 缩放定律与高效注意力" §4.3: Longformer /
+// BigBird combine a local window with a few global tokens; kler.cn
+// "大模型高效注意力机制全解析" §4.1.2: block-sparse attention over b x b blocks,
+// §3.2.1 and §5.1.2: a window of positions before and after, the first and
+// last token global).  The masked positions are exactly excluded, so the
+// result is exact attention over the allowed pairs.
+//
+// 1. Plan (three small kernels, once per mask and length; reused by every
+//    head, layer and by the backward): the global positions become a bitmap,
+//    every 64 x 64 block of the L x L mask is classified as empty, partial or
+//    full from interval arithmetic on its corners, and every work-group row
+//    (128 queries) and column (128 keys) gets the compact, ascending list of
+//    the 64-wide tiles it must visit.  Work-groups are then ordered heaviest
+//    first: a global row visits every tile and must not start last.
+// 2. Attention: the range-tiled kernels' tile steps, unchanged, iterate over
+//    the lists instead of an index range.  Full tiles run unmasked; partial
+//    tiles evaluate the mask per element (window, causal, block bit and the
+//    global bits of the tile); empty tiles are never loaded.
+#include "fa_bwd_tile.hpp"
+#include "fa_fwd_tile.hpp"
+
+namespace fa {
+
+PlanLayout plan_layout(int L) {
+  PlanLayout y{};
+  y.L = L;
+  y.nb = (L + 63) / 64;
+  y.nw = (L + 127) / 128;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = (off + bytes + 255) & ~(size_t)255;
+    return at;
+  };
+  y.gbits = take(8 * (size_t)y.nb);
+  y.row_cnt = take(4 * (size_t)y.nw);
+  y.row_ord = take(4 * (size_t)y.nw);
+  y.col_cnt = take(4 * (size_t)y.nw);
+  y.col_ord = take(4 * (size_t)y.nw);
+  y.meta = take(16);
+  y.row_ent = take(4 * (size_t)y.nw * y.nb);
+  y.col_ent = take(4 * (size_t)y.nw * y.nb);
+  y.total = off;
+  return y;
+}
+
+PlanPtrs plan_ptrs(const void* plan, int L) {
+  const PlanLayout y = plan_layout(L);
+  const char* b = static_cast<const char*>(plan);
+  PlanPtrs p{};
+  p.gbits = reinterpret_cast<const unsigned long long*>(b + y.gbits);
+  p.row_cnt = reinterpret_cast<const int*>(b + y.row_cnt);
+  p.row_ord = reinterpret_cast<const int*>(b + y.row_ord);
+  p.row_ent = reinterpret_cast<const unsigned*>(b + y.row_ent);
+  p.col_cnt = reinterpret_cast<const int*>(b + y.col_cnt);
+  p.col_ord = reinterpret_cast<const int*>(b + y.col_ord);
+  p.col_ent = reinterpret_cast<const unsigned*>(b + y.col_ent);
+  p.meta = reinterpret_cast<const int*>(b + y.meta);
+  p.nb = y.nb;
+  p.nw = y.nw;
+  return p;
+}
+
+namespace {
+
+// ------------------------------------------------------------ 1. plan
+
+struct PlanBuild {
+  MaskDesc m;
+  int L, nb, nw, nbm;
+  unsigned long long* gbits;
+  int* row_cnt;
+  int* row_ord;
+  unsigned* row_ent;
+  int* col_cnt;
+  int* col_ord;
+  unsigned* col_ent;
+  int* meta;
+};
+
+// One thread per 64-block: the bitmap word of the global positions in it.
+__global__ __launch_bounds__(256) void plan_gbits_kernel(PlanBuild p) {
+  const int blk = blockIdx.x * blockDim.x + threadIdx.x;
+  if (blk >= p.nb) return;
+  unsigned long long w = 0;
+  for (int n = 0; n < p.m.n_global; ++n) {
+    int pos = p.m.global_pos[n];
+    if (pos < 0) pos += p.L;
+    if (pos >= 0 && pos < p.L && (pos >> 6) == blk) w |= 1ull << (pos & 63);
+  }
+  p.gbits[blk] = w;
+}
+
+// Class of the 64 x 64 block (query block qb, key block kb): 0 when no pair
+// is allowed, 2 when every pair is (and the block lies inside the sequence),
+// else 1.  Empty and full are decided exactly from the block's extreme
+// positions; anything undecided is partial, which only costs the per-element
+// mask.  block_ok is the block-sparse bit of the block.
+__device__ int block_class(const PlanBuild& p, int qb, int kb, int& block_ok) {
+  block_ok = 0;
+  if (qb >= p.nb || kb >= p.nb) return 0;
+  const int i0 = 64 * qb, i1 = min(i0 + 63, p.L - 1);
+  const int j0 = 64 * kb, j1 = min(j0 + 63, p.L - 1);
+  const bool inside = i0 + 63 < p.L && j0 + 63 < p.L;
+  const bool c_all = !p.m.causal || j1 <= i0;
+  const bool c_none = p.m.causal && j0 > i1;
+  bool w_all = true, w_none = false;
+  if (p.m.window > 0) {
+    const int far = max(i1 - j0, j1 - i0);                              // largest |i - j|
+    const int near = j0 > i1 ? j0 - i1 : (i0 > j1 ? i0 - j1 : 0);        // smallest |i - j|
+    w_all = far < p.m.window;
+    w_none = near >= p.m.window;
+  }
+  const bool bm = p.m.block_mask == nullptr ||
+                  p.m.block_mask[(size_t)(i0 / p.m.block) * p.nbm + j0 / p.m.block] != 0;
+  block_ok = bm ? 1 : 0;
+  const bool glob = p.gbits[qb] != 0 || p.gbits[kb] != 0;
+  if (c_none || ((w_none || !bm) && !glob)) return 0;
+  return (inside && c_all && w_all && bm) ? 2 : 1;
+}
+
+// One work-group per work-group row (blockIdx.y == 0: 128 queries against
+// every 64-key tile) or column (blockIdx.y == 1: 128 keys against every
+// 64-query tile); the non-empty tiles are compacted in ascending order.
+__global__ __launch_bounds__(256) void plan_lists_kernel(PlanBuild p) {
+  __shared__ int wave_tot[4];
+  const int w = blockIdx.x;
+  const bool cols = blockIdx.y == 1;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  unsigned* ent = (cols ? p.col_ent : p.row_ent) + (size_t)w * p.nb;
+  int base = 0;
+  for (int x0 = 0; x0 < p.nb; x0 += 256) {
+    const int x = x0 + tid;
+    unsigned e = 0;
+    bool keep = false;
+    if (x < p.nb) {
+      int bm0, bm1;
+      const int c0 = cols ? block_class(p, x, 2 * w, bm0) : block_class(p, 2 * w, x, bm0);
+      const int c1 = cols ? block_class(p, x, 2 * w + 1, bm1) : block_class(p, 2 * w + 1, x, bm1);
+      keep = (c0 | c1) != 0;
+      e = (unsigned)x | ((unsigned)c0 << 16) | ((unsigned)c1 << 18) | ((unsigned)bm0 << 20) | ((unsigned)bm1 << 21);
+    }
+    const unsigned long long bal = __ballot(keep);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_tot[wv] = __popcll(bal);
+    __syncthreads();
+    int at = base;
+    for (int k = 0; k < wv; ++k) at += wave_tot[k];
+    if (keep) ent[at + before] = e;
+    base += wave_tot[0] + wave_tot[1] + wave_tot[2] + wave_tot[3];
+    __syncthreads();
+  }
+  if (tid == 0) (cols ? p.col_cnt : p.row_cnt)[w] = base;
+}
+
+constexpr int kMaxOrder = 2048;   // work-group rows a plan can order (L <= 2^18)
+
+// One work-group: work-group rows (then columns) sorted by descending entry
+// count (ties by index), bitonic sort in LDS; the leading ranks whose count
+// exceeds twice the median (plus a margin) are marked heavy.
+__global__ __launch_bounds__(1024) void plan_order_kernel(PlanBuild p) {
+  __shared__ unsigned key[kMaxOrder];
+  for (int which = 0; which < 2; ++which) {
+    const int* cnt = which ? p.col_cnt : p.row_cnt;
+    int* ord = which ? p.col_ord : p.row_ord;
+    for (int i = threadIdx.x; i < kMaxOrder; i += blockDim.x)
+      key[i] = i < p.nw ? (((unsigned)cnt[i] << 12) | (4095u - (unsigned)i)) : 0u;
+    __syncthreads();
+    for (int k = 2; k <= kMaxOrder; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = threadIdx.x; i < kMaxOrder; i += blockDim.x) {
+          const int l = i ^ j;
+          if (l > i) {
+            const unsigned a = key[i], b = key[l];
+            const bool desc = (i & k) == 0;
+            if (desc ? a < b : a > b) {
+              key[i] = b;
+              key[l] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int r = threadIdx.x; r < p.nw; r += blockDim.x) ord[r] = 4095 - (int)(key[r] & 4095u);
+    if (threadIdx.x == 0) {
+      const unsigned med = key[p.nw / 2] >> 12;
+      int h = 0;
+      while (h < p.nw && (key[h] >> 12) > 2 * med + 8) ++h;
+      p.meta[which] = h;
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------ 2. attention
+
+// Logical work-group -> (head, work-group row or column): the heavy ranks of
+// every head first (rank-major), then the rest head by head in rank order.
+// Values read from the plan are clamped into range, so that even a buffer that
+// never held a plan keeps every access inside its arrays.
+__device__ __forceinline__ void plan_wg(int r, int n_heads, int nw, int n_heavy_raw, const int* ord, int& head,
+                                        int& tile) {
+  const int n_heavy = min(max(n_heavy_raw, 0), nw / 2);
+  const int heavy = n_heavy * n_heads;
+  int rank;
+  if (r < heavy) {
+    rank = r / n_heads;
+    head = r - rank * n_heads;
+  } else {
+    const int rr = r - heavy, per = nw - n_heavy;
+    head = rr / per;
+    rank = n_heavy + (rr - head * per);
+  }
+  tile = min(max(__builtin_amdgcn_readfirstlane(ord[rank]), 0), nw - 1);
+}
+
+// Query-major element mask: the lane's query i is fixed; k0 is the tile's
+// first key, gk the global bits of its 64 keys, gq whether i is global, bm
+// the block-sparse bit of the lane's 64 x 64 block.
+template <bool CAUSAL>
+struct GeneralMaskQ {
+  int L, window, i, k0;
+  bool gq, bm;
+  unsigned long long gk;
+  __device__ __forceinline__ bool operator()(int j) const {
+    const bool local = bm && (window <= 0 || (j > i - window && j < i + window));
+    const bool glob = gq || ((gk >> (j - k0)) & 1ull) != 0;
+    return j < L && (!CAUSAL || j <= i) && (local || glob);
+  }
+};
+
+// Key-major element mask: the lane's key j is fixed; q0 is the tile's first
+// query, gq the global bits of its 64 queries, gk whether j is global.
+template <bool CAUSAL>
+struct GeneralMaskK {
+  int L, window, j, q0;
+  bool gk, bm;
+  unsigned long long gq;
+  __device__ __forceinline__ bool operator()(int q) const {
+    const bool local = bm && (window <= 0 || (j > q - window && j < q + window));
+    const bool glob = gk || ((gq >> (q - q0)) & 1ull) != 0;
+    return q < L && (!CAUSAL || j <= q) && (local || glob);
+  }
+};
+
+__device__ __forceinline__ bool is_global(const unsigned long long* gbits, int pos, int L) {
+  return pos < L && ((gbits[pos >> 6] >> (pos & 63)) & 1ull) != 0;
+}
+
+// entry fields (the tile index is clamped by the caller's list length)
+__device__ __forceinline__ int ent_tile(unsigned e, int nb) { return min((int)(e & 0xffffu), nb - 1); }
+__device__ __forceinline__ int ent_class(unsigned e, int half) { return (int)((e >> (16 + 2 * half)) & 3u); }
+__device__ __forceinline__ bool ent_block(unsigned e, int half) { return ((e >> (20 + half)) & 1u) != 0; }
+
+// Forward: one work-group of 4 waves per (batch, query head, 128 queries), as
+// the range-tiled forward; waves 0-1 hold the first 64 rows, 2-3 the second.
+template <int D, bool CAUSAL, bool F16>
+__global__ __launch_bounds__(256, 2) void fwd_masked_kernel(FwdArgs a, PlanPtrs p) {
+  using namespace fwdtile;
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char k_st0[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st0[C::VT];
+  __shared__ __attribute__((aligned(1024))) char k_st1[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st1[C::VT];
+
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int g = lane >> 5, ln = lane & 31;
+  const int half = wave >> 1;
+  const int L = a.L, window = a.window;
+
+  int bh, qt;
+  plan_wg(xcd_remap(blockIdx.x, gridDim.x), a.B * a.Hq, p.nw, p.meta[0], p.row_ord, bh, qt);
+  const int b = bh / a.Hq, h = bh % a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+  const bf16* __restrict__ Qh = reinterpret_cast<const bf16*>(a.q) + ((size_t)(b * a.Hq + h) * L) * D;
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
+  const unsigned head_bytes = (unsigned)L * (2 * D);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16*>(a.v) + kv_off, head_bytes);
+
+  const int q_wg0 = qt * C::BR;
+  const int q_w0 = q_wg0 + 32 * wave;
+  const int my_q = q_w0 + ln;
+  const int n_ent = min(max(__builtin_amdgcn_readfirstlane(p.row_cnt[qt]), 0), p.nb);
+  const unsigned* ents = p.row_ent + (size_t)qt * p.nb;
+  const bool gq = is_global(p.gbits, my_q, L);
+
+  CopyPlan<D> cp;
+  make_copy_plan<D>(cp, wave, lane);
+  if (n_ent > 0) issue_kv<D>(cp, krs, vrs, ent_tile(ents[0], p.nb) * C::BC, k_st0, v_st0, wave);
+
+  FwdState<D> st;
+#pragma unroll
+  for (int k = 0; k < C::NSTEP; ++k) {
+    if (my_q < L) st.qr[k] = *reinterpret_cast<const bf16x8*>(Qh + (size_t)my_q * D + 16 * k + 8 * g);
+    else st.qr[k] = bf16x8{};
+  }
+  st.m_run = kNegBig;
+  st.l_run = 0.f;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) st.o[db] = f32x16{};
+  const float c = a.scale_log2;
+
+  auto step = [&](int e, const char* kb, const char* vb) {
+    const unsigned ent = ents[e];
+    const int cls = ent_class(ent, half);
+    if (cls != 0 && q_w0 < L) {
+      const int kt = ent_tile(ent, p.nb);
+      const GeneralMaskQ<CAUSAL> ok{L, window, my_q, kt * C::BC, gq, ent_block(ent, half), p.gbits[kt]};
+      fwd_tile<D, F16>(st, kb, vb, kt * C::BC, cls == 1, ok, c, lane);
+    }
+  };
+
+  wait_copies_and_barrier();
+  for (int e = 0; e < n_ent; e += 2) {
+    if (e + 1 < n_ent) issue_kv<D>(cp, krs, vrs, ent_tile(ents[e + 1], p.nb) * C::BC, k_st1, v_st1, wave);
+    step(e, k_st0, v_st0);
+    wait_copies_and_barrier();
+    if (e + 1 >= n_ent) break;
+    if (e + 2 < n_ent) issue_kv<D>(cp, krs, vrs, ent_tile(ents[e + 2], p.nb) * C::BC, k_st0, v_st0, wave);
+    step(e + 1, k_st1, v_st1);
+    wait_copies_and_barrier();
+  }
+
+  // epilogue: a row with no allowed key gets O = 0, LSE = -inf
+  const float l_tot = pair_sum(st.l_run);
+  if (my_q < L) {
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    bf16* Oq = reinterpret_cast<bf16*>(a.o) + ((size_t)(b * a.Hq + h) * L + my_q) * D;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 w;
+        w[0] = pack1<F16>(st.o[db][4 * i4 + 0] * inv);
+        w[1] = pack1<F16>(st.o[db][4 * i4 + 1] * inv);
+        w[2] = pack1<F16>(st.o[db][4 * i4 + 2] * inv);
+        w[3] = pack1<F16>(st.o[db][4 * i4 + 3] * inv);
+        *reinterpret_cast<bf16x4*>(Oq + 32 * db + 8 * i4 + 4 * g) = w;
+      }
+    }
+    if (a.lse != nullptr && g == 0)
+      a.lse[(size_t)(b * a.Hq + h) * L + my_q] = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// dK/dV: one work-group of 8 waves per (batch, K/V head, 128 keys), as the
+// range-tiled kernel, streaming the query tiles of its column list for every
+// query head of the group.
+template <int D, bool CAUSAL, bool F16>
+__global__ __launch_bounds__(512, 1) void dkdv_masked_kernel(BwdArgs a, PlanPtrs p) {
+  using namespace bwdtile;
+  using C = KVCfg<D>;
+  __shared__ __attribute__((aligned(C::QT))) char q_st0[C::QT];
+  __shared__ __attribute__((aligned(C::QT))) char do_st0[C::QT];
+  __shared__ __attribute__((aligned(C::QT))) char q_st1[C::QT];
+  __shared__ __attribute__((aligned(C::QT))) char do_st1[C::QT];
+  __shared__ __attribute__((aligned(1024))) char k_blk[C::KB];
+  __shared__ __attribute__((aligned(1024))) char v_blk[C::KB];
+  __shared__ __attribute__((aligned(16))) float stat_st0[2 * C::BQ];   // LSE*log2e, then D
+  __shared__ __attribute__((aligned(16))) float stat_st1[2 * C::BQ];
+
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int g = lane >> 5, ln = lane & 31;
+  const int kb = wave & 3, qh = wave >> 2;
+  const int half = kb >> 1;                        // which 64-key block of the 128
+  const int L = a.L, window = a.window;
+  const int G = a.Hq / a.Hkv;
+
+  int bhk, kt;
+  plan_wg(xcd_remap(blockIdx.x, gridDim.x), a.B * a.Hkv, p.nw, p.meta[1], p.col_ord, bhk, kt);
+  const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const int key_wg0 = kt * C::BK;
+  const int key_w0 = key_wg0 + 32 * kb;
+  const int my_key = key_w0 + ln;
+
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
+  const unsigned head_bytes = (unsigned)L * (2 * D);
+
+  const int n_ent = min(max(__builtin_amdgcn_readfirstlane(p.col_cnt[kt]), 0), p.nb);
+  const unsigned* ents = p.col_ent + (size_t)kt * p.nb;
+  const int n_it = G * n_ent;
+  const bool gk = is_global(p.gbits, my_key, L);
+
+  KVAddr<D> ad;
+#pragma unroll
+  for (int i = 0; i < C::QPER; ++i) ad.qcopy[i] = dual_slot_src<D>((wave + C::kWaves * i) * 64 + lane);
+#pragma unroll
+  for (int k = 0; k < C::NSTEP; ++k) ad.row[k] = row_offset_dual<D>(32 * qh + ln, k, g);
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    ad.tr[db][0] = tr_offset_dual<D>(2 * qh, db, 0, lane);
+    ad.tr[db][1] = tr_offset_dual<D>(2 * qh, db, 1, lane);
+  }
+  ad.kv = row_offset_kpad<D>(32 * kb + ln, 0, g);
+
+  // iteration it: query head hk*G + it / n_ent, entry it % n_ent
+  auto ent_of = [&](int it) { return ents[it - (it / n_ent) * n_ent]; };
+  auto issue = [&](int it, char* qs, char* dos, float* ss) {
+    const int hq = hk * G + it / n_ent, q0 = ent_tile(ent_of(it), p.nb) * C::BQ;
+    const size_t qoff = ((size_t)(b * a.Hq + hq) * L) * D;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(reinterpret_cast<const bf16*>(a.q) + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(reinterpret_cast<const bf16*>(a.dout) + qoff, head_bytes);
+    const int soff = q0 * (2 * D);
+#pragma unroll
+    for (int i = 0; i < C::QPER; ++i) {
+      buf2lds16(qrs, ad.qcopy[i], soff, qs + (wave + C::kWaves * i) * 1024);
+      buf2lds16(drs, ad.qcopy[i], soff, dos + (wave + C::kWaves * i) * 1024);
+    }
+    if (wave == 0) {
+      const size_t srow = (size_t)(b * a.Hq + hq) * L;
+      const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.lse2 + srow, (unsigned)L * 4);
+      const __amdgpu_buffer_rsrc_t ers = make_rsrc(a.delta + srow, (unsigned)L * 4);
+      buf2lds4(lrs, 4 * lane, 4 * q0, reinterpret_cast<char*>(ss));
+      buf2lds4(ers, 4 * lane, 4 * q0, reinterpret_cast<char*>(ss) + 4 * C::BQ);
+    }
+  };
+
+  {
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kv_off, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16*>(a.v) + kv_off, head_bytes);
+    const int soff = key_wg0 * (2 * D);
+#pragma unroll
+    for (int n = wave; n < C::KBCOPIES; n += C::kWaves) {
+      const int src = pad_slot_src<D, Pad<D>::KSTR>(n * 64 + lane);
+      buf2lds16(krs, src, soff, k_blk + n * 1024);
+      buf2lds16(vrs, src, soff, v_blk + n * 1024);
+    }
+  }
+  if (n_it > 0) issue(0, q_st0, do_st0, stat_st0);
+
+  KVState<D> st;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    st.dv[db] = f32x16{};
+    st.dk[db] = f32x16{};
+  }
+  const float c = a.scale_log2;
+
+  auto step = [&](int it, const char* qs, const char* dos, const float* ss) {
+    const unsigned ent = ent_of(it);
+    const int cls = ent_class(ent, half);
+    const int q0 = ent_tile(ent, p.nb) * C::BQ;
+    if (cls != 0 && key_w0 < L && q0 + 32 * qh < L) {
+      const GeneralMaskK<CAUSAL> ok{L, window, my_key, q0, gk, ent_block(ent, half), p.gbits[ent_tile(ent, p.nb)]};
+      kv_tile<D, F16>(st, ad, k_blk, v_blk, qs, dos, ss, q0, cls == 1, ok, qh, c, lane);
+    }
+  };
+
+  fwdtile::wait_copies_and_barrier();
+  for (int it = 0; it < n_it; it += 2) {
+    if (it + 1 < n_it) issue(it + 1, q_st1, do_st1, stat_st1);
+    step(it, q_st0, do_st0, stat_st0);
+    fwdtile::wait_copies_and_barrier();
+    if (it + 1 >= n_it) break;
+    if (it + 2 < n_it) issue(it + 2, q_st0, do_st0, stat_st0);
+    step(it + 1, q_st1, do_st1, stat_st1);
+    fwdtile::wait_copies_and_barrier();
+  }
+
+  // sum the two query halves through LDS, then store (as the range-tiled kernel)
+  constexpr int kPart = C::NDB * 16 * 64 * 4;
+  static_assert(kPart <= C::QT, "a partial must fit in one stage buffer");
+  bf16* dKh = reinterpret_cast<bf16*>(a.dk) + kv_off;
+  bf16* dVh = reinterpret_cast<bf16*>(a.dv) + kv_off;
+  const float s = a.scale;
+  float* part = reinterpret_cast<float*>(kb == 0 ? q_st0 : kb == 1 ? do_st0 : kb == 2 ? q_st1 : do_st1);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    if (qh == 1) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) part[(db * 16 + i) * 64 + lane] = pass == 0 ? st.dv[db][i] : st.dk[db][i];
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (pass == 0) st.dv[db][i] += part[(db * 16 + i) * 64 + lane];
+          else st.dk[db][i] += part[(db * 16 + i) * 64 + lane];
+        }
+    }
+    __syncthreads();
+  }
+  if (qh == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = key_w0 + 8 * (i >> 2) + 4 * g + (i & 3);
+      if (key < L) {
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          dKh[(size_t)key * D + 32 * db + ln] = pack1<F16>(st.dk[db][i] * s);
+          dVh[(size_t)key * D + 32 * db + ln] = pack1<F16>(st.dv[db][i]);
+        }
+      }
+    }
+  }
+}
+
+// dQ: one work-group of 4 waves per (batch, query head, 128 queries), as the
+// range-tiled kernel, streaming the key tiles of its row list.
+template <int D, bool CAUSAL, bool F16>
+__global__ __launch_bounds__(256, 2) void dq_masked_kernel(BwdArgs a, PlanPtrs p) {
+  using namespace bwdtile;
+  using C = QCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char k_st0[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st0[C::VT];
+  __shared__ __attribute__((aligned(1024))) char k_st1[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st1[C::VT];
+
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int g = lane >> 5, ln = lane & 31;
+  const int half = wave >> 1;
+  const int L = a.L, window = a.window;
+
+  int bh, qt;
+  plan_wg(xcd_remap(blockIdx.x, gridDim.x), a.B * a.Hq, p.nw, p.meta[0], p.row_ord, bh, qt);
+  const int b = bh / a.Hq, h = bh % a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+  const size_t q_off = ((size_t)(b * a.Hq + h) * L) * D;
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
+  const unsigned head_bytes = (unsigned)L * (2 * D);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16*>(a.v) + kv_off, head_bytes);
+
+  const int q_w0 = qt * C::BQ + 32 * wave;
+  const int my_q = q_w0 + ln;
+  const int n_ent = min(max(__builtin_amdgcn_readfirstlane(p.row_cnt[qt]), 0), p.nb);
+  const unsigned* ents = p.row_ent + (size_t)qt * p.nb;
+  const bool gq = is_global(p.gbits, my_q, L);
+
+  QAddr<D> ad;
+#pragma unroll
+  for (int i = 0; i < C::KPER; ++i) ad.kcopy[i] = dual_slot_src<D>((wave + C::kWaves * i) * 64 + lane);
+#pragma unroll
+  for (int i = 0; i < C::VPER; ++i) ad.vcopy[i] = pad_slot_src<D, Pad<D>::KSTR>((wave + C::kWaves * i) * 64 + lane);
+#pragma unroll
+  for (int k = 0; k < C::NSTEP; ++k) ad.krow[k] = row_offset_dual<D>(ln, k, g);
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    ad.ktr[db][0] = tr_offset_dual<D>(0, db, 0, lane);
+    ad.ktr[db][1] = tr_offset_dual<D>(0, db, 1, lane);
+  }
+  ad.vrow = row_offset_kpad<D>(ln, 0, g);
+
+  auto issue = [&](int e, char* kb, char* vb) {
+    const int soff = ent_tile(ents[e], p.nb) * C::BC * (2 * D);
+#pragma unroll
+    for (int i = 0; i < C::KPER; ++i) buf2lds16(krs, ad.kcopy[i], soff, kb + (wave + C::kWaves * i) * 1024);
+#pragma unroll
+    for (int i = 0; i < C::VPER; ++i)
+      if (wave + C::kWaves * i < C::VCOPIES) buf2lds16(vrs, ad.vcopy[i], soff, vb + (wave + C::kWaves * i) * 1024);
+  };
+  if (n_ent > 0) issue(0, k_st0, v_st0);
+
+  QState<D> st;
+  {
+    const int qr = min(my_q, L - 1);
+    const bf16* Qr = reinterpret_cast<const bf16*>(a.q) + q_off + (size_t)qr * D;
+    const bf16* dOr = reinterpret_cast<const bf16*>(a.dout) + q_off + (size_t)qr * D;
+#pragma unroll
+    for (int k = 0; k < C::NSTEP; ++k) {
+      st.qr[k] = *reinterpret_cast<const bf16x8*>(Qr + 16 * k + 8 * g);
+      st.dor[k] = *reinterpret_cast<const bf16x8*>(dOr + 16 * k + 8 * g);
+    }
+    const size_t srow = (size_t)(b * a.Hq + h) * L + qr;
+    st.lse2 = a.lse2[srow];
+    st.dlt = a.delta[srow];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) st.dq[db] = f32x16{};
+  }
+  const float c = a.scale_log2;
+
+  auto step = [&](int e, const char* kb, const char* vb) {
+    const unsigned ent = ents[e];
+    const int cls = ent_class(ent, half);
+    if (cls != 0 && q_w0 < L) {
+      const int kt = ent_tile(ent, p.nb);
+      const GeneralMaskQ<CAUSAL> ok{L, window, my_q, kt * C::BC, gq, ent_block(ent, half), p.gbits[kt]};
+      q_tile<D, F16>(st, ad, kb, vb, kt * C::BC, cls == 1, ok, c, lane);
+    }
+  };
+
+  fwdtile::wait_copies_and_barrier();
+  for (int e = 0; e < n_ent; e += 2) {
+    if (e + 1 < n_ent) issue(e + 1, k_st1, v_st1);
+    step(e, k_st0, v_st0);
+    fwdtile::wait_copies_and_barrier();
+    if (e + 1 >= n_ent) break;
+    if (e + 2 < n_ent) issue(e + 2, k_st0, v_st0);
+    step(e + 1, k_st1, v_st1);
+    fwdtile::wait_copies_and_barrier();
+  }
+
+  if (my_q < L) {
+    bf16* dQr = reinterpret_cast<bf16*>(a.dq) + q_off + (size_t)my_q * D;
+    const float s = a.scale;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        bf16x4 w;
+        w[0] = pack1<F16>(st.dq[db][4 * i4 + 0] * s);
+        w[1] = pack1<F16>(st.dq[db][4 * i4 + 1] * s);
+        w[2] = pack1<F16>(st.dq[db][4 * i4 + 2] * s);
+        w[3] = pack1<F16>(st.dq[db][4 * i4 + 3] * s);
+        *reinterpret_cast<bf16x4*>(dQr + 32 * db + 8 * i4 + 4 * g) = w;
+      }
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool F16>
+hipError_t fwd_masked_launch(const FwdArgs& a, const PlanPtrs& p, hipStream_t stream) {
+  const long long nblk = (long long)a.B * a.Hq * p.nw;
+  hipLaunchKernelGGL((fwd_masked_kernel<D, CAUSAL, F16>), dim3((unsigned)nblk), dim3(256), 0, stream, a, p);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool F16>
+hipError_t bwd_masked_launch(const BwdArgs& a, const PlanPtrs& p, hipStream_t stream) {
+  hipError_t e = launch_bwd_preprocess_bf16(a, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dkdv_masked_kernel<D, CAUSAL, F16>), dim3((unsigned)((long long)a.B * a.Hkv * p.nw)),
+                     dim3(512), 0, stream, a, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dq_masked_kernel<D, CAUSAL, F16>), dim3((unsigned)((long long)a.B * a.Hq * p.nw)), dim3(256),
+                     0, stream, a, p);
+  return hipGetLastError();
+}
+
+template <bool F16>
+hipError_t fwd_masked_typed(const FwdArgs& a, const PlanPtrs& p, bool causal, hipStream_t s) {
+  if (a.d == 128) return causal ? fwd_masked_launch<128, true, F16>(a, p, s) : fwd_masked_launch<128, false, F16>(a, p, s);
+  return causal ? fwd_masked_launch<64, true, F16>(a, p, s) : fwd_masked_launch<64, false, F16>(a, p, s);
+}
+
+template <bool F16>
+hipError_t bwd_masked_typed(const BwdArgs& a, const PlanPtrs& p, bool causal, hipStream_t s) {
+  if (a.d == 128) return causal ? bwd_masked_launch<128, true, F16>(a, p, s) : bwd_masked_launch<128, false, F16>(a, p, s);
+  return causal ? bwd_masked_launch<64, true, F16>(a, p, s) : bwd_masked_launch<64, false, F16>(a, p, s);
+}
+
+}  // namespace
+
+hipError_t launch_mask_plan(const MaskDesc& m, int L, void* plan, hipStream_t stream) {
+  const PlanLayout y = plan_layout(L);
+  if (y.nw > kMaxOrder) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(plan);
+  PlanBuild p{};
+  p.m = m;
+  p.L = L;
+  p.nb = y.nb;
+  p.nw = y.nw;
+  p.nbm = m.block_mask != nullptr ? (L + m.block - 1) / m.block : 0;
+  p.gbits = reinterpret_cast<unsigned long long*>(base + y.gbits);
+  p.row_cnt = reinterpret_cast<int*>(base + y.row_cnt);
+  p.row_ord = reinterpret_cast<int*>(base + y.row_ord);
+  p.row_ent = reinterpret_cast<unsigned*>(base + y.row_ent);
+  p.col_cnt = reinterpret_cast<int*>(base + y.col_cnt);
+  p.col_ord = reinterpret_cast<int*>(base + y.col_ord);
+  p.col_ent = reinterpret_cast<unsigned*>(base + y.col_ent);
+  p.meta = reinterpret_cast<int*>(base + y.meta);
+  hipLaunchKernelGGL(plan_gbits_kernel, dim3((unsigned)((y.nb + 255) / 256)), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_lists_kernel, dim3((unsigned)y.nw, 2), dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_order_kernel, dim3(1), dim3(1024), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_masked(const FwdArgs& a, const PlanPtrs& p, bool causal, hipStream_t stream) {
+  return a.f16 ? fwd_masked_typed<true>(a, p, causal, stream) : fwd_masked_typed<false>(a, p, causal, stream);
+}
+
+hipError_t launch_bwd_masked(const BwdArgs& a, const PlanPtrs& p, bool causal, hipStream_t stream) {
+  return a.f16 ? bwd_masked_typed<true>(a, p, causal, stream) : bwd_masked_typed<false>(a, p, causal, stream);
+}
+
+}  // namespace fa

@@ -264,6 +264,101 @@ extern "C" int flash_attn_decode(const void* q, const void* k_cache, const void*
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+namespace {
+
+// General masks: the plan's per-row lists hold at most 2^18 / 64 tiles and its
+// work-group order covers at most 2048 work-group rows.
+constexpr int kMaxMaskL = 1 << 18;
+constexpr int kMaxGlobal = 1 << 16;
+
+int check_mask(const fa_mask* m, int L) {
+  if (m == nullptr || L < 1) return FA_ERR_INVALID_ARG;
+  if ((m->causal != 0 && m->causal != 1) || m->window < 0) return FA_ERR_INVALID_ARG;
+  if (m->n_global < 0 || m->n_global > kMaxGlobal || (m->n_global > 0 && m->global_pos == nullptr))
+    return FA_ERR_INVALID_ARG;
+  if (m->block_mask != nullptr && (m->block < 64 || m->block % 64 != 0)) return FA_ERR_UNSUPPORTED;
+  if (L > kMaxMaskL) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+int check_plan(const void* plan, size_t plan_bytes, int L) {
+  if (plan == nullptr || (reinterpret_cast<uintptr_t>(plan) & 255u) != 0 || plan_bytes < fa::plan_layout(L).total)
+    return FA_ERR_WORKSPACE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" size_t flash_attn_mask_plan_bytes(int L) {
+  if (L < 1 || L > kMaxMaskL) return 0;
+  return fa::plan_layout(L).total;
+}
+
+extern "C" int flash_attn_mask_plan(const fa_mask* mask, int L, void* plan, size_t plan_bytes, void* stream) {
+  int rc = check_mask(mask, L);
+  if (rc != FA_OK) return rc;
+  rc = check_plan(plan, plan_bytes, L);
+  if (rc != FA_OK) return rc;
+  fa::MaskDesc m{};
+  m.causal = mask->causal;
+  m.window = mask->window;
+  m.global_pos = mask->n_global > 0 ? mask->global_pos : nullptr;
+  m.n_global = mask->n_global;
+  m.block_mask = mask->block_mask;
+  m.block = mask->block_mask != nullptr ? mask->block : 64;
+  hipError_t e = fa::launch_mask_plan(m, L, plan, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     int B, int Hq, int Hkv, int L, int d, float softmax_scale,
+                                     const fa_mask* mask, const void* plan, size_t plan_bytes, int dtype,
+                                     void* stream) {
+  if (mask == nullptr) return FA_ERR_INVALID_ARG;
+  int rc = check_common(B, Hq, Hkv, L, d, softmax_scale, mask->causal, mask->window, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+  rc = check_mask(mask, L);
+  if (rc != FA_OK) return rc;
+  rc = check_plan(plan, plan_bytes, L);
+  if (rc != FA_OK) return rc;
+  if (!all_aligned({q, k, v, o}) || (lse && !aligned16(lse))) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.d = d;
+  a.Lk = L;
+  a.shift = 0;
+  a.window = mask->window;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.f16 = dtype == FA_DTYPE_F16;
+  hipError_t e = fa::launch_fwd_masked(a, fa::plan_ptrs(plan, L), mask->causal != 0,
+                                       reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int flash_attn_bwd_masked(const void* q, const void* k, const void* v, const void* o,
+                                     const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                     void* workspace, size_t workspace_bytes,
+                                     int B, int Hq, int Hkv, int L, int d, float softmax_scale,
+                                     const fa_mask* mask, const void* plan, size_t plan_bytes, int dtype,
+                                     void* stream) {
+  if (mask == nullptr) return FA_ERR_INVALID_ARG;
+  fa::BwdArgs a{};
+  int rc = bwd_setup(a, workspace, workspace_bytes, B, Hq, Hkv, L, d, softmax_scale, mask->causal, mask->window,
+                     dtype);
+  if (rc != FA_OK) return rc;
+  rc = check_mask(mask, L);
+  if (rc != FA_OK) return rc;
+  rc = check_plan(plan, plan_bytes, L);
+  if (rc != FA_OK) return rc;
+  if (!all_aligned({q, k, v, o, lse, dout, dq, dk, dv})) return FA_ERR_INVALID_ARG;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  hipError_t e = fa::launch_bwd_masked(a, fa::plan_ptrs(plan, L), mask->causal != 0,
+                                       reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 extern "C" const char* flash_attn_strerror(int code) {
   switch (code) {
     case FA_OK: return "ok";

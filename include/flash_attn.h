@@ -230,6 +230,74 @@ int flash_attn_decode(const void* q, const void* k_cache, const void* v_cache, c
                       int B, int Hq, int Hkv, int Lq, int Lk, int d, float softmax_scale,
                       int causal, int window, int dtype, void* stream);
 
+/*
+ * General sparse masks over one sequence of L positions (queries and keys are
+ * the same positions: self-attention, layouts as for flash_attn_fwd).  Key j
+ * is allowed for query i iff
+ *   causal_ok(i, j) && ((window_ok(i, j) && block_ok(i, j)) || global(i) || global(j))
+ * where
+ *   causal_ok  -- j <= i when causal = 1, else always;
+ *   window_ok  -- |i - j| < window when window >= 1 (with causal: the w most
+ *                 recent keys, book.anysome.cn "高效注意力" §4; without: w - 1
+ *                 positions before and after, kler.cn §3.2.1), else always;
+ *   block_ok   -- block_mask[i / block][j / block] != 0: block-sparse
+ *                 attention over block x block tiles (kler.cn §4.1.2), or
+ *                 always when block_mask is NULL;
+ *   global(p)  -- p is one of global_pos: a global position attends to and is
+ *                 attended by every position, Longformer / BigBird style
+ *                 (claspmoon.cn "14 · 缩放定律与高效注意力" §4.3; kler.cn
+ *                 §5.1.2: first and last token global, entries 0 and -1).
+ * A row with no allowed key gets O = 0 and LSE = -inf (its gradients are 0).
+ *
+ *   global_pos  : device int32[n_global]; an entry p < 0 means L + p; entries
+ *                 outside [-L, L) are ignored; 0 <= n_global <= 65536.
+ *   block_mask  : device uint8[nbm * nbm], row-major, nbm = ceil(L / block);
+ *                 block a multiple of 64 (else FA_ERR_UNSUPPORTED).  Its
+ *                 size is the caller's promise.
+ */
+typedef struct fa_mask {
+  int causal;
+  int window;
+  const int* global_pos;
+  int n_global;
+  const unsigned char* block_mask;
+  int block;
+} fa_mask;
+
+/*
+ * flash_attn_mask_plan: classifies every 64 x 64 block of the mask (empty,
+ * partial or full) and writes, into the caller's device buffer `plan`, the
+ * tile lists and the work-group order the masked kernels follow.  Runs three
+ * small kernels on `stream`; reads the mask's device arrays there.  A plan
+ * depends on the mask and L only: build it once and pass it to every masked
+ * call (every head, layer, forward and backward) with that same mask and L.
+ * 1 <= L <= 2^18 (FA_ERR_UNSUPPORTED above).  plan: at least
+ * flash_attn_mask_plan_bytes(L) bytes, 256-byte aligned (else
+ * FA_ERR_WORKSPACE).  flash_attn_mask_plan_bytes returns 0 for an
+ * unsupported L.
+ */
+size_t flash_attn_mask_plan_bytes(int L);
+int flash_attn_mask_plan(const fa_mask* mask, int L, void* plan, size_t plan_bytes, void* stream);
+
+/*
+ * flash_attn_fwd_masked / flash_attn_bwd_masked: flash_attn_fwd and
+ * flash_attn_bwd under the mask (16-bit dtypes; FA_DTYPE_F32 returns
+ * FA_ERR_UNSUPPORTED).  `mask` supplies causal and window to the kernels; its
+ * global positions and block mask are read from the plan, which must have
+ * been built from this mask and this L (a plan for another mask gives that
+ * mask's result).  The backward's workspace is flash_attn_bwd's.  Tiles the
+ * mask leaves empty are never loaded, so the work scales with the allowed
+ * pairs.
+ */
+int flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int L, int d, float softmax_scale,
+                          const fa_mask* mask, const void* plan, size_t plan_bytes, int dtype, void* stream);
+int flash_attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv,
+                          void* workspace, size_t workspace_bytes,
+                          int B, int Hq, int Hkv, int L, int d, float softmax_scale,
+                          const fa_mask* mask, const void* plan, size_t plan_bytes, int dtype, void* stream);
+
 /* Static, never-NULL description of a return code. */
 const char* flash_attn_strerror(int code);
 

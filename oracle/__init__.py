@@ -39,8 +39,9 @@ without a window), per-sequence cache lengths, and a single-token rolling
 window buffer in any slot order equals the windowed row; for general masks:
 the family reduces to the causal/window mask, brute-force loops over
 symmetric windows, global tokens and block masks, the masked forward and
-backward reduce to the plain ones, global rows equal unmasked rows, and
-finite differences on a sparse pattern.  Every oracle
+backward reduce to the plain ones, global rows equal unmasked rows,
+finite differences on a sparse pattern, and the row-sampled forward and dQ
+equal the matching rows of the whole-sequence functions.  Every oracle
 function has at least one pin; none is "parity unpinned".
 """
 
@@ -54,6 +55,8 @@ from .attention import (  # noqa: F401
     general_mask,
     forward_with_mask,
     backward_with_mask,
+    forward_rows_with_mask,
+    dq_rows_with_mask,
     kv_head_of,
     probabilities,
     forward,

@@ -450,3 +450,39 @@ def backward_with_mask(q, k, v, dout, scale, ok):
             dq[b, h] = scale * (dS @ k[b, kh])
             dk[b, kh] += scale * (dS.T @ q[b, h])
     return dq, dk, dv
+
+
+def forward_rows_with_mask(q, k, v, rows, scale, ok_rows):
+    """Rows ``rows`` of ``forward_with_mask``: ``ok_rows [len(rows), L]`` is the mask of those
+    query rows (for example ``general_mask(rows, arange(L), ...)``).  Each row of the
+    definition depends on its own query only, so sampled rows of a long sequence are exact."""
+    q, k, v = _as64(q), _as64(k), _as64(v)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    rows = np.asarray(rows)
+    O = np.empty((B, Hq, len(rows), d))
+    lse = np.empty((B, Hq, len(rows)))
+    for b in range(B):
+        for h in range(Hq):
+            kh = kv_head_of(h, Hq, Hkv)
+            S = scale * (q[b, h, rows] @ k[b, kh].T)
+            A, lse[b, h] = _masked_softmax_rows(S, ok_rows)
+            O[b, h] = A @ v[b, kh]
+    return O, lse
+
+
+def dq_rows_with_mask(q, k, v, dout, rows, scale, ok_rows):
+    """Rows ``rows`` of dQ from ``backward_with_mask``.  dQ_i needs only row i: its
+    probabilities P_i, dP_i = dO_i V^T and D_i = sum_j P_ij dP_ij (claspmoon.cn §3.3)."""
+    q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
+    B, Hq, L, d = q.shape
+    Hkv = k.shape[1]
+    rows = np.asarray(rows)
+    dq = np.empty((B, Hq, len(rows), d))
+    for b in range(B):
+        for h in range(Hq):
+            kh = kv_head_of(h, Hq, Hkv)
+            A, _ = _masked_softmax_rows(scale * (q[b, h, rows] @ k[b, kh].T), ok_rows)
+            dS = _softmax_backward(A, dout[b, h, rows] @ v[b, kh].T)
+            dq[b, h] = scale * (dS @ k[b, kh])
+    return dq

@@ -192,3 +192,57 @@ def test_decode_entry_points_reject_invalid_arguments(lib):
     assert dec(ws=None) == WS and dec(nb=16) == WS and dec(ws=FAKE * 16 + 128) == WS
     assert dec(Lq=40) == UNS and dec(dt=fa.FA_DTYPE_F32) == UNS and dec(d=96) == UNS
     assert dec(causal=0, window=8) == UNS and dec(Hkv=3) == GQA and dec(Lk=0) == INV
+
+
+def test_mask_entry_points_reject_invalid_arguments(lib):
+    c = header_constants()
+    INV, UNS, WS, GQA = c["FA_ERR_INVALID_ARG"], c["FA_ERR_UNSUPPORTED"], c["FA_ERR_WORKSPACE"], c["FA_ERR_GQA"]
+    pb = lib.flash_attn_mask_plan_bytes
+    assert pb(1) == 8 * 256                      # eight 256-byte aligned sections
+    assert pb(0) == 0 and pb((1 << 18) + 1) == 0
+    assert pb(1 << 18) > pb(4096) > 0
+    need = pb(1000)
+
+    def mask(causal=0, window=0, gpos=None, ng=0, bmask=None, block=64):
+        return ctypes.byref(fa.FaMask(causal, window, gpos, ng, bmask, block))
+
+    def plan(m=None, L=1000, p=FAKE * 256, nb=need):
+        return lib.flash_attn_mask_plan(mask() if m is None else m, L, p, nb, None)
+    assert lib.flash_attn_mask_plan(None, 1000, FAKE * 256, need, None) == INV
+    assert plan(m=mask(causal=2)) == INV and plan(m=mask(window=-1)) == INV
+    assert plan(m=mask(ng=3)) == INV and plan(m=mask(gpos=FAKE, ng=-1)) == INV
+    assert plan(m=mask(gpos=FAKE, ng=(1 << 16) + 1)) == INV
+    assert plan(m=mask(bmask=FAKE, block=96)) == UNS and plan(m=mask(bmask=FAKE, block=32)) == UNS
+    assert plan(L=(1 << 18) + 1) == UNS and plan(L=0) == INV
+    assert plan(p=None) == WS and plan(p=FAKE * 256 + 64) == WS and plan(nb=need - 1) == WS
+
+    def fm(q=FAKE, m=None, p=FAKE * 256, nb=need, L=1000, dt=fa.FA_DTYPE_BF16, Hkv=2, d=128):
+        return lib.flash_attn_fwd_masked(q, FAKE, FAKE, FAKE, None, 1, 2, Hkv, L, d, 0.125,
+                                         mask() if m is None else m, p, nb, dt, None)
+    assert lib.flash_attn_fwd_masked(FAKE, FAKE, FAKE, FAKE, None, 1, 2, 2, 1000, 128, 0.125, None, FAKE * 256,
+                                     need, fa.FA_DTYPE_BF16, None) == INV
+    assert fm(q=None) == INV and fm(dt=fa.FA_DTYPE_F32) == UNS and fm(d=80) == UNS and fm(Hkv=3) == GQA
+    assert fm(p=None) == WS and fm(nb=need - 1) == WS and fm(m=mask(bmask=FAKE, block=100)) == UNS
+    assert fm(m=mask(causal=1, window=-2)) == INV and fm(L=(1 << 18) + 2, nb=1 << 40) == UNS
+
+    wsb = lib.flash_attn_bwd_workspace_bytes(1, 2, 2, 1000, 128, fa.FA_DTYPE_BF16)
+
+    def bm(dq=FAKE, ws=FAKE * 256, wn=wsb, p=FAKE * 256, nb=need, m=None):
+        return lib.flash_attn_bwd_masked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, ws, wn, 1, 2, 2, 1000,
+                                         128, 0.125, mask() if m is None else m, p, nb, fa.FA_DTYPE_BF16, None)
+    assert bm(dq=None) == INV and bm(ws=None) == WS and bm(wn=wsb - 1) == WS
+    assert bm(p=None) == WS and bm(nb=16) == WS and bm(m=mask(ng=1)) == INV
+
+
+def test_allowed_pairs_counts_the_oracle_mask():
+    """The host pair count (the bench's flop count) against the oracle's mask."""
+    import numpy as np
+    import oracle
+    bmask = fa.block_band_mask(300, 64, 1).numpy()
+    assert bmask.shape == (5, 5) and bmask[0, 1] and not bmask[0, 2]
+    for L, causal, window, glob, bm, blk in [(300, False, 0, (), None, 64), (300, True, 0, (), None, 64),
+                                           (300, False, 7, (0, -1), None, 64), (300, True, 20, (5, 299), bmask, 64),
+                                           (257, False, 0, (3,), fa.block_band_mask(257, 128, 0).numpy(), 128)]:
+        gl = tuple(p + L if p < 0 else p for p in glob)
+        ok = oracle.general_mask(np.arange(L), np.arange(L), causal, window, bm, blk, gl)
+        assert fa.allowed_pairs(L, causal, window, glob, bm, blk) == int(ok.sum())

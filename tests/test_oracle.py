@@ -462,7 +462,24 @@ def pin_masked_backward_finite_differences(o):
         assert np.allclose(num, g, rtol=1e-6, atol=1e-8)
 
 
-MASK_PINS = [pin_general_mask_reduces_to_causal_window, pin_general_mask_brute_force,
+def pin_masked_rows_equal_whole_sequence(o):
+    L = 40
+    q, k, v, do = rnd((2, 4, L, 6), 180), rnd((2, 2, L, 6), 181), rnd((2, 2, L, 6), 182), rnd((2, 4, L, 6), 183)
+    bm = np.array([[1, 0, 1], [0, 1, 0], [1, 1, 1]], dtype=bool)
+    for causal, window, glob, blk in [(False, 5, (0, -1), None), (True, 7, (13,), None), (False, 0, (), bm),
+                                      (True, 4, (2, 30), bm)]:
+        gl = tuple(p + L if p < 0 else p for p in glob)
+        ok = o.general_mask(np.arange(L), np.arange(L), causal, window, blk, 16, gl)
+        O, l = o.forward_with_mask(q, k, v, 0.45, ok)
+        dq = o.backward_with_mask(q, k, v, do, 0.45, ok)[0]
+        rows = np.array([0, 3, 17, 39])
+        Or, lr = o.forward_rows_with_mask(q, k, v, rows, 0.45, ok[rows])
+        assert np.allclose(Or, O[:, :, rows], atol=1e-13, rtol=0) and np.allclose(lr, l[:, :, rows], atol=1e-13, rtol=0)
+        dqr = o.dq_rows_with_mask(q, k, v, do, rows, 0.45, ok[rows])
+        assert np.allclose(dqr, dq[:, :, rows], atol=1e-12, rtol=0)
+
+
+MASK_PINS = [pin_general_mask_reduces_to_causal_window, pin_general_mask_brute_force, pin_masked_rows_equal_whole_sequence,
              pin_masked_forward_backward_reduce_to_plain, pin_global_rows_are_unmasked,
              pin_masked_backward_finite_differences]
 

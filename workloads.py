@@ -27,10 +27,11 @@ class Workload:
     d: int
     dtype: torch.dtype
     causal: bool
-    window: int          # 0 = no window; w >= 1 = keys i-w+1..i (causal only)
+    window: int          # 0 = no window; w >= 1: |i - j| < w (keys i-w+1..i with causal)
     seed: int
     std: float = 1.0
     backward: bool = False
+    global_tokens: tuple = ()   # positions seen by and seeing every position (negative: from the end)
 
     @property
     def scale(self) -> float:
@@ -55,6 +56,13 @@ LONG_BWD_8K = Workload("long-context bwd B2 H32 L8192 d128 causal bf16", 2, 32, 
                        torch.bfloat16, True, 0, seed=5, backward=True)
 
 ALL = [TINY_FP32, LLAMA7B_CAUSAL, GQA_16K, WINDOW_32K, LONG_FWD_128K, LONG_BWD_8K]
+
+# A general sparse mask: the hybrid configuration of kler.cn §5.1.2 (a window of
+# 512 positions before and after each position, i.e. |i - j| < 513, the first
+# and last token global, sequences of 131072 tokens, batch 2) on the
+# llama7b-shaped heads (32 heads of 128).
+HYBRID_SPARSE_128K = Workload("hybrid-sparse B2 H32 L131072 d128 window513 global[0,-1] bf16", 2, 32, 32, 131072,
+                              128, torch.bfloat16, False, 513, seed=6, backward=True, global_tokens=(0, -1))
 
 
 def make_inputs(w: Workload, with_dout: bool = None):
