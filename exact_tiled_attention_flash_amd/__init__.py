@@ -22,7 +22,7 @@ import torch
 
 __all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "fwd_block", "bwd_block", "merge",
            "decode", "decode_workspace_bytes",
-           "MaskPlan", "fwd_masked", "bwd_masked", "block_band_mask", "allowed_pairs",
+           "MaskPlan", "fwd_masked", "bwd_masked", "masked_workspace_bytes", "block_band_mask", "allowed_pairs",
            "strerror", "library", "library_path",
            "FlashAttentionFunction", "scaled_dot_product_attention",
            "FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "EXPORTED_SYMBOLS"]
@@ -36,8 +36,8 @@ EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspac
                     "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
                     "flash_attn_fwd_block", "flash_attn_merge", "flash_attn_bwd_block",
                     "flash_attn_decode", "flash_attn_decode_workspace_bytes",
-                    "flash_attn_mask_plan_bytes", "flash_attn_mask_plan", "flash_attn_fwd_masked",
-                    "flash_attn_bwd_masked",
+                    "flash_attn_mask_plan_bytes", "flash_attn_mask_plan", "flash_attn_masked_workspace_bytes",
+                    "flash_attn_fwd_masked", "flash_attn_bwd_masked",
                     "flash_attn_strerror", "flash_attn_version")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,7 +95,9 @@ def library():
     lib.flash_attn_mask_plan_bytes.restype = sz
     lib.flash_attn_mask_plan.argtypes = [mp, i, vp, sz, vp]
     lib.flash_attn_mask_plan.restype = i
-    lib.flash_attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, mp, vp, sz, i, vp]
+    lib.flash_attn_masked_workspace_bytes.argtypes = [i, i, i, i, i, mp, i]
+    lib.flash_attn_masked_workspace_bytes.restype = sz
+    lib.flash_attn_fwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, f, mp, vp, sz, i, vp]
     lib.flash_attn_fwd_masked.restype = i
     lib.flash_attn_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                           i, i, i, i, i, f, mp, vp, sz, i, vp]
@@ -407,7 +409,12 @@ class MaskPlan:
         return allowed_pairs(self.L, self.causal, self.window, self.global_tokens, self.block_mask, self.block)
 
 
-def fwd_masked(q, k, v, plan, scale=None, out=None, lse=None):
+def masked_workspace_bytes(B, Hq, Hkv, L, d, plan, backward):
+    return int(library().flash_attn_masked_workspace_bytes(B, Hq, Hkv, L, d, ctypes.byref(plan.desc),
+                                                           int(bool(backward))))
+
+
+def fwd_masked(q, k, v, plan, scale=None, out=None, lse=None, workspace=None):
     """Exact attention under a ``MaskPlan`` (16-bit dtypes).  Returns ``(o, lse)``; rows
     with no allowed key get o = 0, lse = -inf."""
     B, Hq, Hkv, L, d = _shapes(q, k, v)
@@ -416,7 +423,11 @@ def fwd_masked(q, k, v, plan, scale=None, out=None, lse=None):
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     out = torch.empty_like(q) if out is None else out
     lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device) if lse is None else lse
-    rc = library().flash_attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, L, d, scale,
+    nbytes = masked_workspace_bytes(B, Hq, Hkv, L, d, plan, False)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    rc = library().flash_attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
+                                         0 if workspace is None else workspace.numel(), B, Hq, Hkv, L, d, scale,
                                          ctypes.byref(plan.desc), _ptr(plan.plan), plan.plan.numel(),
                                          _DTYPES[q.dtype], _stream(q))
     _check(rc, "flash_attn_fwd_masked")
@@ -429,7 +440,7 @@ def bwd_masked(q, k, v, o, lse, dout, plan, scale=None, workspace=None, dq=None,
     if L != plan.L:
         raise ValueError("the plan was built for L = %d" % plan.L)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    nbytes = bwd_workspace_bytes(B, Hq, Hkv, L, d, q.dtype)
+    nbytes = masked_workspace_bytes(B, Hq, Hkv, L, d, plan, True)
     workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if workspace is None else workspace
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk

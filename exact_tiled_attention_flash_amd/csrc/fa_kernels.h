@@ -101,12 +101,16 @@ struct MaskDesc {
 // full and lists, for every 128-row work-group of the forward and dQ kernels,
 // the 64-key tiles it must visit (and, for every 128-key work-group of the
 // dK/dV kernel, the 64-query tiles), plus a heaviest-first work-group order.
+// Global query rows (for the forward and dQ) and global keys (for dK/dV) see
+// the whole sequence; the lists leave them out and separate split passes over
+// every key (every query) compute them, so no work-group has to walk a whole
+// row.
 // List entry: tile index | class(first 64 rows or keys) << 16 | class(second)
 // << 18 | block_ok(first) << 20 | block_ok(second) << 21; class 0 empty,
 // 1 partial (elementwise mask), 2 full.
 struct PlanLayout {
   int L, nb, nw;                     // nb 64-blocks, nw 128-wide work-group rows (= columns)
-  size_t gbits, row_cnt, row_ord, col_cnt, col_ord, meta, row_ent, col_ent, total;   // byte offsets
+  size_t gbits, row_cnt, row_ord, col_cnt, col_ord, meta, gpos, row_ent, col_ent, total;   // byte offsets
 };
 PlanLayout plan_layout(int L);
 
@@ -118,15 +122,32 @@ struct PlanPtrs {
   const int* col_cnt;
   const int* col_ord;
   const unsigned* col_ent;           // [nw][nb] entries (query tiles), ascending
-  const int* meta;                   // [0], [1]: leading heavy ranks of row_ord, col_ord
+  const int* meta;                   // [0], [1]: leading heavy ranks of row_ord, col_ord; [2]: global count
+  const int* gpos;                   // [meta[2]] global positions, ascending
   int nb, nw;
 };
 PlanPtrs plan_ptrs(const void* plan, int L);
 
 hipError_t launch_mask_plan(const MaskDesc& m, int L, void* plan, hipStream_t stream);
+
+// Split passes for the global positions (rows for the forward and dQ, keys for
+// dK/dV): ngp = the global count rounded up to 32 (0: no pass), n_splits
+// splits of `per` tiles, float32 partials in `part` (and `part_lse`).
+struct GlobalArgs {
+  int n_splits, per, ngp;
+  float* part;
+  float* part_lse;
+};
+GlobalArgs global_plan(int L, int n_global, int n_heads);
+size_t global_fwd_bytes(const GlobalArgs& g, int n_heads, int d);
+size_t global_dq_bytes(const GlobalArgs& g, int n_heads, int d);
+size_t global_dkdv_bytes(const GlobalArgs& g, int n_kv_heads, int d);
+
 // forward / backward (preprocess, dK/dV, dQ) under a plan; a.L is the sequence
 // length the plan was built for, a.window its window
-hipError_t launch_fwd_masked(const FwdArgs& a, const PlanPtrs& p, bool causal, hipStream_t stream);
-hipError_t launch_bwd_masked(const BwdArgs& a, const PlanPtrs& p, bool causal, hipStream_t stream);
+hipError_t launch_fwd_masked(const FwdArgs& a, const PlanPtrs& p, const GlobalArgs& ga, bool causal,
+                             hipStream_t stream);
+hipError_t launch_bwd_masked(const BwdArgs& a, const PlanPtrs& p, const GlobalArgs& gr, const GlobalArgs& gc,
+                             bool causal, hipStream_t stream);
 
 }  // namespace fa

@@ -44,6 +44,7 @@ PlanLayout plan_layout(int L) {
   y.col_cnt = take(4 * (size_t)y.nw);
   y.col_ord = take(4 * (size_t)y.nw);
   y.meta = take(16);
+  y.gpos = take(4 * (size_t)L);
   y.row_ent = take(4 * (size_t)y.nw * y.nb);
   y.col_ent = take(4 * (size_t)y.nw * y.nb);
   y.total = off;
@@ -62,6 +63,7 @@ PlanPtrs plan_ptrs(const void* plan, int L) {
   p.col_ord = reinterpret_cast<const int*>(b + y.col_ord);
   p.col_ent = reinterpret_cast<const unsigned*>(b + y.col_ent);
   p.meta = reinterpret_cast<const int*>(b + y.meta);
+  p.gpos = reinterpret_cast<const int*>(b + y.gpos);
   p.nb = y.nb;
   p.nw = y.nw;
   return p;
@@ -82,6 +84,7 @@ struct PlanBuild {
   int* col_ord;
   unsigned* col_ent;
   int* meta;
+  int* gpos;
 };
 
 // One thread per 64-block: the bitmap word of the global positions in it.
@@ -97,12 +100,48 @@ __global__ __launch_bounds__(256) void plan_gbits_kernel(PlanBuild p) {
   p.gbits[blk] = w;
 }
 
+// One work-group: the global positions in ascending order (from the bitmap,
+// so each appears once) and their count in meta[2].
+__global__ __launch_bounds__(1024) void plan_gpos_kernel(PlanBuild p) {
+  __shared__ int wave_tot[16];
+  int base = 0;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int x0 = 0; x0 < p.nb; x0 += 1024) {
+    const int x = x0 + tid;
+    const unsigned long long w = x < p.nb ? p.gbits[x] : 0ull;
+    const int n = __popcll(w);
+    // exclusive prefix of n over the work-group: within the wave, then across waves
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    if (lane == 63) wave_tot[wv] = incl;
+    __syncthreads();
+    int at = base + incl - n;
+    for (int k = 0; k < wv; ++k) at += wave_tot[k];
+    unsigned long long rest = w;
+    while (rest != 0ull) {
+      const int b = __builtin_ctzll(rest);
+      p.gpos[at++] = 64 * x + b;
+      rest &= rest - 1ull;
+    }
+    for (int k = 0; k < 16; ++k) base += wave_tot[k];
+    __syncthreads();
+  }
+  if (tid == 0) p.meta[2] = base;
+}
+
 // Class of the 64 x 64 block (query block qb, key block kb): 0 when no pair
 // is allowed, 2 when every pair is (and the block lies inside the sequence),
 // else 1.  Empty and full are decided exactly from the block's extreme
 // positions; anything undecided is partial, which only costs the per-element
-// mask.  block_ok is the block-sparse bit of the block.
-__device__ int block_class(const PlanBuild& p, int qb, int kb, int& block_ok) {
+// mask.  block_ok is the block-sparse bit of the block.  Global queries (keys)
+// count only when use_gq (use_gk) is set: a global query row sees every key,
+// so the row lists leave it to the global-row pass instead of visiting every
+// tile; likewise the column lists leave global keys to the global-key pass.
+__device__ int block_class(const PlanBuild& p, int qb, int kb, bool use_gq, bool use_gk, int& block_ok) {
   block_ok = 0;
   if (qb >= p.nb || kb >= p.nb) return 0;
   const int i0 = 64 * qb, i1 = min(i0 + 63, p.L - 1);
@@ -120,7 +159,7 @@ __device__ int block_class(const PlanBuild& p, int qb, int kb, int& block_ok) {
   const bool bm = p.m.block_mask == nullptr ||
                   p.m.block_mask[(size_t)(i0 / p.m.block) * p.nbm + j0 / p.m.block] != 0;
   block_ok = bm ? 1 : 0;
-  const bool glob = p.gbits[qb] != 0 || p.gbits[kb] != 0;
+  const bool glob = (use_gq && p.gbits[qb] != 0) || (use_gk && p.gbits[kb] != 0);
   if (c_none || ((w_none || !bm) && !glob)) return 0;
   return (inside && c_all && w_all && bm) ? 2 : 1;
 }
@@ -141,8 +180,9 @@ __global__ __launch_bounds__(256) void plan_lists_kernel(PlanBuild p) {
     bool keep = false;
     if (x < p.nb) {
       int bm0, bm1;
-      const int c0 = cols ? block_class(p, x, 2 * w, bm0) : block_class(p, 2 * w, x, bm0);
-      const int c1 = cols ? block_class(p, x, 2 * w + 1, bm1) : block_class(p, 2 * w + 1, x, bm1);
+      const int c0 = cols ? block_class(p, x, 2 * w, true, false, bm0) : block_class(p, 2 * w, x, false, true, bm0);
+      const int c1 = cols ? block_class(p, x, 2 * w + 1, true, false, bm1)
+                          : block_class(p, 2 * w + 1, x, false, true, bm1);
       keep = (c0 | c1) != 0;
       e = (unsigned)x | ((unsigned)c0 << 16) | ((unsigned)c1 << 18) | ((unsigned)bm0 << 20) | ((unsigned)bm1 << 21);
     }
@@ -329,9 +369,10 @@ __global__ __launch_bounds__(256, 2) void fwd_masked_kernel(FwdArgs a, PlanPtrs 
     wait_copies_and_barrier();
   }
 
-  // epilogue: a row with no allowed key gets O = 0, LSE = -inf
+  // epilogue: a row with no allowed key gets O = 0, LSE = -inf; a global row
+  // is left to the global-row pass
   const float l_tot = pair_sum(st.l_run);
-  if (my_q < L) {
+  if (my_q < L && !gq) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     bf16* Oq = reinterpret_cast<bf16*>(a.o) + ((size_t)(b * a.Hq + h) * L + my_q) * D;
 #pragma unroll
@@ -493,10 +534,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_masked_kernel(BwdArgs a, PlanPtrs
     __syncthreads();
   }
   if (qh == 0) {
+    // global keys are left to the global-key pass
+    const int b0 = min(2 * kt, p.nb - 1), b1 = min(2 * kt + 1, p.nb - 1);
+    const unsigned long long gw0 = p.gbits[b0], gw1 = p.gbits[b1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int key = key_w0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (key < L) {
+      const bool kglob = (((key >> 6) == b0 ? gw0 : gw1) >> (key & 63)) & 1ull;
+      if (key < L && !kglob) {
 #pragma unroll
         for (int db = 0; db < C::NDB; ++db) {
           dKh[(size_t)key * D + 32 * db + ln] = pack1<F16>(st.dk[db][i] * s);
@@ -602,7 +647,7 @@ __global__ __launch_bounds__(256, 2) void dq_masked_kernel(BwdArgs a, PlanPtrs p
     fwdtile::wait_copies_and_barrier();
   }
 
-  if (my_q < L) {
+  if (my_q < L && !gq) {         // global rows: the global-row pass
     bf16* dQr = reinterpret_cast<bf16*>(a.dq) + q_off + (size_t)my_q * D;
     const float s = a.scale;
 #pragma unroll
@@ -620,36 +665,494 @@ __global__ __launch_bounds__(256, 2) void dq_masked_kernel(BwdArgs a, PlanPtrs p
   }
 }
 
+// ------------------------------------------------------------ 3. global positions
+//
+// A global query row attends to every key and a global key is attended by
+// every query, so each is a whole row (column) of the mask: the lists leave
+// them out and these passes compute them, split over the sequence so that a
+// handful of long rows still spread over the chip ("split-K"), each split
+// writing a float32 partial to the workspace and a last kernel combining the
+// splits exactly (forward: LSE = log sum_s e^{LSE_s}, O = sum_s e^{LSE_s - LSE}
+// O_s; gradients: plain sums).  One work-group holds 32 global positions of
+// one head as the 32 MFMA columns of the tile steps.  A global position sees
+// every position (subject to the causal mask): the element mask is j <= i.
+
+template <bool CAUSAL>
+struct DenseMask {                 // the lane's position `self` against position x
+  int L, self;
+  bool key_side;                   // self is a key (x a query) or a query (x a key)
+  __device__ __forceinline__ bool operator()(int x) const {
+    return x < L && (!CAUSAL || (key_side ? self <= x : x <= self));
+  }
+};
+
+// Forward of the global query rows over key tiles [split*per, split*per + per):
+// one wave per (split, batch*query head, 32 rows).
 template <int D, bool CAUSAL, bool F16>
-hipError_t fwd_masked_launch(const FwdArgs& a, const PlanPtrs& p, hipStream_t stream) {
+__global__ __launch_bounds__(64) void grows_fwd_kernel(FwdArgs a, PlanPtrs p, GlobalArgs ga) {
+  using namespace fwdtile;
+  using C = FwdCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char k_st0[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st0[C::VT];
+  __shared__ __attribute__((aligned(1024))) char k_st1[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st1[C::VT];
+
+  const int lane = threadIdx.x, g = lane >> 5, ln = lane & 31;
+  const int split = blockIdx.x, bh = blockIdx.y, r0 = 32 * blockIdx.z;
+  const int L = a.L;
+  const int n_g = min(max(p.meta[2], 0), ga.ngp);
+  if (r0 >= n_g) return;
+  const int r = r0 + ln;
+  const bool valid = r < n_g;
+  const int pos = min(max(p.gpos[valid ? r : r0], 0), L - 1);
+  const int lo_pos = min(max(p.gpos[r0], 0), L - 1);                        // ascending: the wave's first
+  const int hi_pos = min(max(p.gpos[min(n_g, r0 + 32) - 1], 0), L - 1);     // and last row
+  const int b = bh / a.Hq, h = bh % a.Hq, hk = h / (a.Hq / a.Hkv);
+
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
+  const unsigned head_bytes = (unsigned)L * (2 * D);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16*>(a.v) + kv_off, head_bytes);
+
+  const int t_lo = split * ga.per;
+  int t_hi = min(p.nb, t_lo + ga.per) - 1;
+  if (CAUSAL) t_hi = min(t_hi, hi_pos / C::BC);
+
+  int koff[C::KCOPIES], voff[C::VCOPIES];
+#pragma unroll
+  for (int i = 0; i < C::KCOPIES; ++i) koff[i] = pad_slot_src<D, Pad<D>::KSTR>(i * 64 + lane);
+#pragma unroll
+  for (int i = 0; i < C::VCOPIES; ++i) voff[i] = pad_slot_src<D, Pad<D>::VSTR>(i * 64 + lane);
+  auto issue = [&](int j, char* kbuf, char* vbuf) {
+    const int soff = j * C::BC * (2 * D);
+#pragma unroll
+    for (int i = 0; i < C::KCOPIES; ++i) buf2lds16(krs, koff[i], soff, kbuf + i * 1024);
+#pragma unroll
+    for (int i = 0; i < C::VCOPIES; ++i) buf2lds16(vrs, voff[i], soff, vbuf + i * 1024);
+  };
+  if (t_lo <= t_hi) issue(t_lo, k_st0, v_st0);
+
+  FwdState<D> st;
+  const bf16* Qr = reinterpret_cast<const bf16*>(a.q) + ((size_t)(b * a.Hq + h) * L + pos) * D;
+#pragma unroll
+  for (int k = 0; k < C::NSTEP; ++k) st.qr[k] = valid ? *reinterpret_cast<const bf16x8*>(Qr + 16 * k + 8 * g) : bf16x8{};
+  st.m_run = kNegBig;
+  st.l_run = 0.f;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) st.o[db] = f32x16{};
+  const float c = a.scale_log2;
+  const DenseMask<CAUSAL> ok{L, pos, false};
+  auto tile_mask = [&](int k0) { return k0 + C::BC > L || (CAUSAL && k0 + C::BC - 1 > lo_pos); };
+
+  wait_copies_and_barrier();
+  for (int j = t_lo; j <= t_hi; j += 2) {
+    if (j < t_hi) issue(j + 1, k_st1, v_st1);
+    fwd_tile<D, F16>(st, k_st0, v_st0, j * C::BC, tile_mask(j * C::BC), ok, c, lane);
+    wait_copies_and_barrier();
+    if (j + 1 > t_hi) break;
+    if (j + 1 < t_hi) issue(j + 2, k_st0, v_st0);
+    fwd_tile<D, F16>(st, k_st1, v_st1, (j + 1) * C::BC, tile_mask((j + 1) * C::BC), ok, c, lane);
+    wait_copies_and_barrier();
+  }
+
+  const float l_tot = pair_sum(st.l_run);
+  if (valid) {
+    const size_t prow = ((size_t)split * a.B * a.Hq + bh) * ga.ngp + r;
+    float* po = ga.part + prow * D;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * i4 + 4 * g) =
+            f32x4{st.o[db][4 * i4] * inv, st.o[db][4 * i4 + 1] * inv, st.o[db][4 * i4 + 2] * inv,
+                  st.o[db][4 * i4 + 3] * inv};
+    if (g == 0)
+      ga.part_lse[prow] = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+// Merge the splits of every (head, global row) into O and LSE at the row's position.
+template <int D, bool F16>
+__global__ __launch_bounds__(256) void grows_combine_kernel(FwdArgs a, PlanPtrs p, GlobalArgs ga) {
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
+  const long long rows = (long long)a.B * a.Hq * ga.ngp;
+  const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
+  const int part = threadIdx.x % kLanesPerRow;
+  if (row >= rows) return;
+  const int bh = (int)(row / ga.ngp), r = (int)(row % ga.ngp);
+  const int n_g = min(max(p.meta[2], 0), ga.ngp);
+  if (r >= n_g) return;
+  const int pos = min(max(p.gpos[r], 0), a.L - 1);
+  float m = -INFINITY;
+  for (int s = 0; s < ga.n_splits; ++s) m = fmaxf(m, ga.part_lse[(size_t)s * rows + row]);
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < ga.n_splits; ++s) {
+      const float w = __expf(ga.part_lse[(size_t)s * rows + row] - m);
+      if (w == 0.f) continue;
+      const f32x4* x = reinterpret_cast<const f32x4*>(ga.part + ((size_t)s * rows + row) * D + 8 * part);
+      const f32x4 x0 = x[0], x1 = x[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += w * x0[i];
+        acc[4 + i] += w * x1[i];
+      }
+      tot += w;
+    }
+  }
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const size_t orow = (size_t)bh * a.L + pos;
+  bf16* out = static_cast<bf16*>(a.o) + orow * D + 8 * part;
+  *reinterpret_cast<bf16x8*>(out) = pack8<F16>(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv,
+                                                acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  if (part == 0 && a.lse != nullptr) a.lse[orow] = tot > 0.f ? m + __logf(tot) : -INFINITY;
+}
+
+// dQ of the global query rows over key tiles [split*per, split*per + per):
+// one wave per (split, batch*query head, 32 rows); float32 partial sums.
+template <int D, bool CAUSAL, bool F16>
+__global__ __launch_bounds__(64) void grows_dq_kernel(BwdArgs a, PlanPtrs p, GlobalArgs ga) {
+  using namespace bwdtile;
+  using C = QCfg<D>;
+  __shared__ __attribute__((aligned(1024))) char k_st0[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st0[C::VT];
+  __shared__ __attribute__((aligned(1024))) char k_st1[C::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st1[C::VT];
+
+  const int lane = threadIdx.x, g = lane >> 5, ln = lane & 31;
+  const int split = blockIdx.x, bh = blockIdx.y, r0 = 32 * blockIdx.z;
+  const int L = a.L;
+  const int n_g = min(max(p.meta[2], 0), ga.ngp);
+  if (r0 >= n_g) return;
+  const int r = r0 + ln;
+  const bool valid = r < n_g;
+  const int pos = min(max(p.gpos[valid ? r : r0], 0), L - 1);
+  const int lo_pos = min(max(p.gpos[r0], 0), L - 1);
+  const int hi_pos = min(max(p.gpos[min(n_g, r0 + 32) - 1], 0), L - 1);
+  const int b = bh / a.Hq, h = bh % a.Hq, hk = h / (a.Hq / a.Hkv);
+
+  const size_t q_off = ((size_t)(b * a.Hq + h) * L) * D;
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
+  const unsigned head_bytes = (unsigned)L * (2 * D);
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16*>(a.v) + kv_off, head_bytes);
+
+  const int t_lo = split * ga.per;
+  int t_hi = min(p.nb, t_lo + ga.per) - 1;
+  if (CAUSAL) t_hi = min(t_hi, hi_pos / C::BC);
+
+  QAddr<D> ad;
+#pragma unroll
+  for (int k = 0; k < C::NSTEP; ++k) ad.krow[k] = row_offset_dual<D>(ln, k, g);
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    ad.ktr[db][0] = tr_offset_dual<D>(0, db, 0, lane);
+    ad.ktr[db][1] = tr_offset_dual<D>(0, db, 1, lane);
+  }
+  ad.vrow = row_offset_kpad<D>(ln, 0, g);
+  int koff[C::KCOPIES], voff[C::VCOPIES];
+#pragma unroll
+  for (int i = 0; i < C::KCOPIES; ++i) koff[i] = dual_slot_src<D>(i * 64 + lane);
+#pragma unroll
+  for (int i = 0; i < C::VCOPIES; ++i) voff[i] = pad_slot_src<D, Pad<D>::KSTR>(i * 64 + lane);
+  auto issue = [&](int j, char* kb, char* vb) {
+    const int soff = j * C::BC * (2 * D);
+#pragma unroll
+    for (int i = 0; i < C::KCOPIES; ++i) buf2lds16(krs, koff[i], soff, kb + i * 1024);
+#pragma unroll
+    for (int i = 0; i < C::VCOPIES; ++i) buf2lds16(vrs, voff[i], soff, vb + i * 1024);
+  };
+  if (t_lo <= t_hi) issue(t_lo, k_st0, v_st0);
+
+  QState<D> st;
+  {
+    const bf16* Qr = reinterpret_cast<const bf16*>(a.q) + q_off + (size_t)pos * D;
+    const bf16* dOr = reinterpret_cast<const bf16*>(a.dout) + q_off + (size_t)pos * D;
+#pragma unroll
+    for (int k = 0; k < C::NSTEP; ++k) {
+      st.qr[k] = *reinterpret_cast<const bf16x8*>(Qr + 16 * k + 8 * g);
+      st.dor[k] = *reinterpret_cast<const bf16x8*>(dOr + 16 * k + 8 * g);
+    }
+    const size_t srow = (size_t)(b * a.Hq + h) * L + pos;
+    st.lse2 = a.lse2[srow];
+    st.dlt = a.delta[srow];
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db) st.dq[db] = f32x16{};
+  }
+  const float c = a.scale_log2;
+  const DenseMask<CAUSAL> ok{L, pos, false};
+  auto tile_mask = [&](int k0) { return k0 + C::BC > L || (CAUSAL && k0 + C::BC - 1 > lo_pos); };
+
+  fwdtile::wait_copies_and_barrier();
+  for (int j = t_lo; j <= t_hi; j += 2) {
+    if (j < t_hi) issue(j + 1, k_st1, v_st1);
+    q_tile<D, F16>(st, ad, k_st0, v_st0, j * C::BC, tile_mask(j * C::BC), ok, c, lane);
+    fwdtile::wait_copies_and_barrier();
+    if (j + 1 > t_hi) break;
+    if (j + 1 < t_hi) issue(j + 2, k_st0, v_st0);
+    q_tile<D, F16>(st, ad, k_st1, v_st1, (j + 1) * C::BC, tile_mask((j + 1) * C::BC), ok, c, lane);
+    fwdtile::wait_copies_and_barrier();
+  }
+
+  if (valid) {
+    float* po = ga.part + (((size_t)split * a.B * a.Hq + bh) * ga.ngp + r) * D;
+    const float s = a.scale;
+#pragma unroll
+    for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4)
+        *reinterpret_cast<f32x4*>(po + 32 * db + 8 * i4 + 4 * g) =
+            f32x4{st.dq[db][4 * i4] * s, st.dq[db][4 * i4 + 1] * s, st.dq[db][4 * i4 + 2] * s,
+                  st.dq[db][4 * i4 + 3] * s};
+  }
+}
+
+// Sum the float32 partials of every (head, global position) into the rows of
+// out0 (and out1): the partial of split s holds n_tensors rows of D floats
+// per (head, position); tensor 0 is multiplied by scale0.
+template <int D, bool F16>
+__global__ __launch_bounds__(256) void gsum_kernel(const float* __restrict__ part, int n_parts, long long rows,
+                                                   int ngp, int L, const int* meta, const int* gpos,
+                                                   bf16* __restrict__ out0, bf16* __restrict__ out1, int n_tensors,
+                                                   float scale0) {
+  constexpr int kLanesPerRow = D / 8;
+  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
+  const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
+  const int part_i = threadIdx.x % kLanesPerRow;
+  if (row >= rows) return;
+  const int head = (int)(row / ngp), r = (int)(row % ngp);
+  const int n_g = min(max(meta[2], 0), ngp);
+  if (r >= n_g) return;
+  const int pos = min(max(gpos[r], 0), L - 1);
+  for (int t = 0; t < n_tensors; ++t) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n_parts; ++s) {
+      const f32x4* x = reinterpret_cast<const f32x4*>(part + (((size_t)s * rows + row) * n_tensors + t) * D +
+                                                      8 * part_i);
+      const f32x4 x0 = x[0], x1 = x[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i] += x0[i];
+        acc[4 + i] += x1[i];
+      }
+    }
+    const float f = t == 0 ? scale0 : 1.f;
+    bf16* o = (t == 0 ? out0 : out1) + ((size_t)head * L + pos) * D + 8 * part_i;
+    *reinterpret_cast<bf16x8*>(o) = pack8<F16>(acc[0] * f, acc[1] * f, acc[2] * f, acc[3] * f, acc[4] * f,
+                                               acc[5] * f, acc[6] * f, acc[7] * f);
+  }
+}
+
+// dK and dV of the global keys over query tiles [split*per, split*per + per) of
+// every query head of the group: two waves (the halves of a 64-query tile) per
+// (split, batch*K/V head, 32 keys); float32 partials, one per (split, half).
+template <int D, bool CAUSAL, bool F16>
+__global__ __launch_bounds__(128) void gcols_dkdv_kernel(BwdArgs a, PlanPtrs p, GlobalArgs ga) {
+  using namespace bwdtile;
+  using C = KVCfg<D>;
+  constexpr int KB32 = 32 * Pad<D>::KSTR;           // a padded block of 32 keys
+  __shared__ __attribute__((aligned(C::QT))) char q_st0[C::QT];
+  __shared__ __attribute__((aligned(C::QT))) char do_st0[C::QT];
+  __shared__ __attribute__((aligned(C::QT))) char q_st1[C::QT];
+  __shared__ __attribute__((aligned(C::QT))) char do_st1[C::QT];
+  __shared__ __attribute__((aligned(1024))) char k_blk[KB32];
+  __shared__ __attribute__((aligned(1024))) char v_blk[KB32];
+  __shared__ __attribute__((aligned(16))) float stat_st0[2 * C::BQ];
+  __shared__ __attribute__((aligned(16))) float stat_st1[2 * C::BQ];
+
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int g = lane >> 5, ln = lane & 31;
+  const int qh = wave;
+  const int split = blockIdx.x, bhk = blockIdx.y, r0 = 32 * blockIdx.z;
+  const int L = a.L, G = a.Hq / a.Hkv;
+  const int n_g = min(max(p.meta[2], 0), ga.ngp);
+  if (r0 >= n_g) return;
+  const int r = r0 + ln;
+  const bool valid = r < n_g;
+  const int pos = min(max(p.gpos[valid ? r : r0], 0), L - 1);
+  const int lo_pos = min(max(p.gpos[r0], 0), L - 1);
+  const int hi_pos = min(max(p.gpos[min(n_g, r0 + 32) - 1], 0), L - 1);
+  const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * L) * D;
+  const unsigned head_bytes = (unsigned)L * (2 * D);
+
+  // query tiles of this split; with causal masking a key sees queries at or after it
+  int t_lo = split * ga.per;
+  const int t_hi = min(p.nb, t_lo + ga.per) - 1;
+  if (CAUSAL) t_lo = max(t_lo, lo_pos / C::BQ);
+  const int nq = max(0, t_hi - t_lo + 1);
+  const int n_it = G * nq;
+
+  // the 32 gathered K and V rows, padded (plain loads: 32 padded rows are not a whole number of 1 KiB copies)
+  {
+    const bf16* Kh = reinterpret_cast<const bf16*>(a.k) + kv_off;
+    const bf16* Vh = reinterpret_cast<const bf16*>(a.v) + kv_off;
+    constexpr int kChunks = D / 8;
+    for (int e = threadIdx.x; e < 32 * kChunks; e += 128) {
+      const int row = e / kChunks, ch = e % kChunks;
+      const int rr = min(r0 + row, n_g - 1);
+      const int kpos = min(max(p.gpos[rr], 0), L - 1);
+      const bf16x8 kx = *reinterpret_cast<const bf16x8*>(Kh + (size_t)kpos * D + 8 * ch);
+      const bf16x8 vx = *reinterpret_cast<const bf16x8*>(Vh + (size_t)kpos * D + 8 * ch);
+      *reinterpret_cast<bf16x8*>(k_blk + row * Pad<D>::KSTR + 16 * ch) = kx;
+      *reinterpret_cast<bf16x8*>(v_blk + row * Pad<D>::KSTR + 16 * ch) = vx;
+    }
+  }
+
+  KVAddr<D> ad;
+#pragma unroll
+  for (int k = 0; k < C::NSTEP; ++k) ad.row[k] = row_offset_dual<D>(32 * qh + ln, k, g);
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    ad.tr[db][0] = tr_offset_dual<D>(2 * qh, db, 0, lane);
+    ad.tr[db][1] = tr_offset_dual<D>(2 * qh, db, 1, lane);
+  }
+  ad.kv = row_offset_kpad<D>(ln, 0, g);
+  constexpr int kCopies = C::QT / 1024 / 2;          // per wave, per tensor
+  int qcopy[kCopies];
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) qcopy[i] = dual_slot_src<D>((wave + 2 * i) * 64 + lane);
+
+  auto issue = [&](int it, char* qs, char* dos, float* ss) {
+    const int hq = hk * G + it / nq, q0 = (t_lo + it % nq) * C::BQ;
+    const size_t qoff = ((size_t)(b * a.Hq + hq) * L) * D;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(reinterpret_cast<const bf16*>(a.q) + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(reinterpret_cast<const bf16*>(a.dout) + qoff, head_bytes);
+    const int soff = q0 * (2 * D);
+#pragma unroll
+    for (int i = 0; i < kCopies; ++i) {
+      buf2lds16(qrs, qcopy[i], soff, qs + (wave + 2 * i) * 1024);
+      buf2lds16(drs, qcopy[i], soff, dos + (wave + 2 * i) * 1024);
+    }
+    if (wave == 0) {
+      const size_t srow = (size_t)(b * a.Hq + hq) * L;
+      const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.lse2 + srow, (unsigned)L * 4);
+      const __amdgpu_buffer_rsrc_t ers = make_rsrc(a.delta + srow, (unsigned)L * 4);
+      buf2lds4(lrs, 4 * lane, 4 * q0, reinterpret_cast<char*>(ss));
+      buf2lds4(ers, 4 * lane, 4 * q0, reinterpret_cast<char*>(ss) + 4 * C::BQ);
+    }
+  };
+  if (n_it > 0) issue(0, q_st0, do_st0, stat_st0);
+
+  KVState<D> st;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    st.dv[db] = f32x16{};
+    st.dk[db] = f32x16{};
+  }
+  const float c = a.scale_log2;
+  const DenseMask<CAUSAL> ok{L, pos, true};
+  auto block_mask = [&](int q0) {
+    const int qw0 = q0 + 32 * qh;
+    return qw0 + 32 > L || (CAUSAL && qw0 < hi_pos);
+  };
+
+  fwdtile::wait_copies_and_barrier();
+  for (int it = 0; it < n_it; it += 2) {
+    if (it + 1 < n_it) issue(it + 1, q_st1, do_st1, stat_st1);
+    {
+      const int q0 = (t_lo + it % nq) * C::BQ;
+      if (q0 + 32 * qh < L) kv_tile<D, F16>(st, ad, k_blk, v_blk, q_st0, do_st0, stat_st0, q0, block_mask(q0), ok, qh, c, lane);
+    }
+    fwdtile::wait_copies_and_barrier();
+    if (it + 1 >= n_it) break;
+    if (it + 2 < n_it) issue(it + 2, q_st0, do_st0, stat_st0);
+    {
+      const int q0 = (t_lo + (it + 1) % nq) * C::BQ;
+      if (q0 + 32 * qh < L) kv_tile<D, F16>(st, ad, k_blk, v_blk, q_st1, do_st1, stat_st1, q0, block_mask(q0), ok, qh, c, lane);
+    }
+    fwdtile::wait_copies_and_barrier();
+  }
+
+  // partial (split, half): dK (unscaled) then dV; lane holds head-dim column
+  // 32db + ln of keys 8(i/4) + 4g + i%4 of the block
+  const long long rows = (long long)a.B * a.Hkv * ga.ngp;
+  const size_t pidx = (size_t)(2 * split + qh) * rows + (size_t)bhk * ga.ngp;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int kr = r0 + 8 * (i >> 2) + 4 * g + (i & 3);
+    if (kr < n_g) {
+      float* pk = ga.part + ((pidx + kr) * 2) * D;
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db) {
+        pk[32 * db + ln] = st.dk[db][i];
+        pk[D + 32 * db + ln] = st.dv[db][i];
+      }
+    }
+  }
+}
+
+template <int D, bool CAUSAL, bool F16>
+hipError_t fwd_masked_launch(const FwdArgs& a, const PlanPtrs& p, const GlobalArgs& ga, hipStream_t stream) {
   const long long nblk = (long long)a.B * a.Hq * p.nw;
   hipLaunchKernelGGL((fwd_masked_kernel<D, CAUSAL, F16>), dim3((unsigned)nblk), dim3(256), 0, stream, a, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || ga.ngp == 0) return e;
+  hipLaunchKernelGGL((grows_fwd_kernel<D, CAUSAL, F16>), dim3(ga.n_splits, a.B * a.Hq, ga.ngp / 32), dim3(64), 0,
+                     stream, a, p, ga);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  constexpr int kRowsPerBlock = 256 / (D / 8);
+  const long long rows = (long long)a.B * a.Hq * ga.ngp;
+  hipLaunchKernelGGL((grows_combine_kernel<D, F16>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
+                     dim3(256), 0, stream, a, p, ga);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool F16>
-hipError_t bwd_masked_launch(const BwdArgs& a, const PlanPtrs& p, hipStream_t stream) {
+hipError_t bwd_masked_launch(const BwdArgs& a, const PlanPtrs& p, const GlobalArgs& gr, const GlobalArgs& gc,
+                             hipStream_t stream) {
+  constexpr int kRowsPerBlock = 256 / (D / 8);
   hipError_t e = launch_bwd_preprocess_bf16(a, stream);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((dkdv_masked_kernel<D, CAUSAL, F16>), dim3((unsigned)((long long)a.B * a.Hkv * p.nw)),
                      dim3(512), 0, stream, a, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (gc.ngp > 0) {
+    hipLaunchKernelGGL((gcols_dkdv_kernel<D, CAUSAL, F16>), dim3(gc.n_splits, a.B * a.Hkv, gc.ngp / 32), dim3(128),
+                       0, stream, a, p, gc);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const long long rows = (long long)a.B * a.Hkv * gc.ngp;
+    hipLaunchKernelGGL((gsum_kernel<D, F16>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(256),
+                       0, stream, gc.part, 2 * gc.n_splits, rows, gc.ngp, a.L, p.meta, p.gpos,
+                       static_cast<bf16*>(a.dk), static_cast<bf16*>(a.dv), 2, a.scale);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((dq_masked_kernel<D, CAUSAL, F16>), dim3((unsigned)((long long)a.B * a.Hq * p.nw)), dim3(256),
                      0, stream, a, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || gr.ngp == 0) return e;
+  hipLaunchKernelGGL((grows_dq_kernel<D, CAUSAL, F16>), dim3(gr.n_splits, a.B * a.Hq, gr.ngp / 32), dim3(64), 0,
+                     stream, a, p, gr);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long rows = (long long)a.B * a.Hq * gr.ngp;
+  hipLaunchKernelGGL((gsum_kernel<D, F16>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)), dim3(256),
+                     0, stream, gr.part, gr.n_splits, rows, gr.ngp, a.L, p.meta, p.gpos, static_cast<bf16*>(a.dq),
+                     static_cast<bf16*>(nullptr), 1, 1.f);
   return hipGetLastError();
 }
 
 template <bool F16>
-hipError_t fwd_masked_typed(const FwdArgs& a, const PlanPtrs& p, bool causal, hipStream_t s) {
-  if (a.d == 128) return causal ? fwd_masked_launch<128, true, F16>(a, p, s) : fwd_masked_launch<128, false, F16>(a, p, s);
-  return causal ? fwd_masked_launch<64, true, F16>(a, p, s) : fwd_masked_launch<64, false, F16>(a, p, s);
+hipError_t fwd_masked_typed(const FwdArgs& a, const PlanPtrs& p, const GlobalArgs& ga, bool causal, hipStream_t s) {
+  if (a.d == 128)
+    return causal ? fwd_masked_launch<128, true, F16>(a, p, ga, s) : fwd_masked_launch<128, false, F16>(a, p, ga, s);
+  return causal ? fwd_masked_launch<64, true, F16>(a, p, ga, s) : fwd_masked_launch<64, false, F16>(a, p, ga, s);
 }
 
 template <bool F16>
-hipError_t bwd_masked_typed(const BwdArgs& a, const PlanPtrs& p, bool causal, hipStream_t s) {
-  if (a.d == 128) return causal ? bwd_masked_launch<128, true, F16>(a, p, s) : bwd_masked_launch<128, false, F16>(a, p, s);
-  return causal ? bwd_masked_launch<64, true, F16>(a, p, s) : bwd_masked_launch<64, false, F16>(a, p, s);
+hipError_t bwd_masked_typed(const BwdArgs& a, const PlanPtrs& p, const GlobalArgs& gr, const GlobalArgs& gc,
+                            bool causal, hipStream_t s) {
+  if (a.d == 128)
+    return causal ? bwd_masked_launch<128, true, F16>(a, p, gr, gc, s)
+                  : bwd_masked_launch<128, false, F16>(a, p, gr, gc, s);
+  return causal ? bwd_masked_launch<64, true, F16>(a, p, gr, gc, s) : bwd_masked_launch<64, false, F16>(a, p, gr, gc, s);
 }
 
 }  // namespace
@@ -672,8 +1175,12 @@ hipError_t launch_mask_plan(const MaskDesc& m, int L, void* plan, hipStream_t st
   p.col_ord = reinterpret_cast<int*>(base + y.col_ord);
   p.col_ent = reinterpret_cast<unsigned*>(base + y.col_ent);
   p.meta = reinterpret_cast<int*>(base + y.meta);
+  p.gpos = reinterpret_cast<int*>(base + y.gpos);
   hipLaunchKernelGGL(plan_gbits_kernel, dim3((unsigned)((y.nb + 255) / 256)), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_gpos_kernel, dim3(1), dim3(1024), 0, stream, p);
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(plan_lists_kernel, dim3((unsigned)y.nw, 2), dim3(256), 0, stream, p);
   e = hipGetLastError();
@@ -682,12 +1189,43 @@ hipError_t launch_mask_plan(const MaskDesc& m, int L, void* plan, hipStream_t st
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_masked(const FwdArgs& a, const PlanPtrs& p, bool causal, hipStream_t stream) {
-  return a.f16 ? fwd_masked_typed<true>(a, p, causal, stream) : fwd_masked_typed<false>(a, p, causal, stream);
+// Splits of a global-position pass: about 1024 work-groups in all, at least
+// four tiles per split.
+GlobalArgs global_plan(int L, int n_global, int n_heads) {
+  GlobalArgs g{};
+  if (n_global <= 0) return g;
+  g.ngp = (n_global + 31) / 32 * 32;
+  const int nb = (L + 63) / 64;
+  const int groups = n_heads * (g.ngp / 32);
+  int want = (1024 + groups - 1) / groups;
+  want = max(1, min(min(want, max(1, nb / 4)), 64));
+  g.per = (nb + want - 1) / want;
+  g.n_splits = (nb + g.per - 1) / g.per;
+  return g;
 }
 
-hipError_t launch_bwd_masked(const BwdArgs& a, const PlanPtrs& p, bool causal, hipStream_t stream) {
-  return a.f16 ? bwd_masked_typed<true>(a, p, causal, stream) : bwd_masked_typed<false>(a, p, causal, stream);
+size_t global_fwd_bytes(const GlobalArgs& g, int n_heads, int d) {
+  const size_t rows = (size_t)g.n_splits * n_heads * g.ngp;
+  return (rows * (size_t)(d + 1) * sizeof(float) + 255) & ~(size_t)255;
+}
+
+size_t global_dq_bytes(const GlobalArgs& g, int n_heads, int d) {
+  return ((size_t)g.n_splits * n_heads * g.ngp * (size_t)d * sizeof(float) + 255) & ~(size_t)255;
+}
+
+size_t global_dkdv_bytes(const GlobalArgs& g, int n_kv_heads, int d) {
+  return ((size_t)2 * g.n_splits * n_kv_heads * g.ngp * (size_t)(2 * d) * sizeof(float) + 255) & ~(size_t)255;
+}
+
+hipError_t launch_fwd_masked(const FwdArgs& a, const PlanPtrs& p, const GlobalArgs& ga, bool causal,
+                             hipStream_t stream) {
+  return a.f16 ? fwd_masked_typed<true>(a, p, ga, causal, stream) : fwd_masked_typed<false>(a, p, ga, causal, stream);
+}
+
+hipError_t launch_bwd_masked(const BwdArgs& a, const PlanPtrs& p, const GlobalArgs& gr, const GlobalArgs& gc,
+                             bool causal, hipStream_t stream) {
+  return a.f16 ? bwd_masked_typed<true>(a, p, gr, gc, causal, stream)
+               : bwd_masked_typed<false>(a, p, gr, gc, causal, stream);
 }
 
 }  // namespace fa

@@ -6,6 +6,7 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <initializer_list>
 
 #include "../../include/flash_attn.h"
@@ -310,7 +311,38 @@ extern "C" int flash_attn_mask_plan(const fa_mask* mask, int L, void* plan, size
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+namespace {
+
+// Workspace of the masked calls: the backward's D_i and LSE_i*log2(e) rows
+// (backward only), then the float32 partials of the global-position passes
+// (the dK/dV and dQ passes run one after the other and share one region).
+struct MaskedWs {
+  fa::GlobalArgs rows, cols;
+  size_t base, partial, total;
+};
+
+MaskedWs masked_ws(int B, int Hq, int Hkv, int L, int d, const fa_mask* m, bool backward) {
+  MaskedWs w{};
+  w.rows = fa::global_plan(L, m->n_global, B * Hq);
+  w.cols = fa::global_plan(L, m->n_global, B * Hkv);
+  w.base = backward ? workspace_bytes(B, Hq, L) : 0;
+  w.partial = backward ? std::max(fa::global_dq_bytes(w.rows, B * Hq, d), fa::global_dkdv_bytes(w.cols, B * Hkv, d))
+                       : fa::global_fwd_bytes(w.rows, B * Hq, d);
+  if (w.rows.ngp == 0) w.partial = 0;
+  w.total = w.base + w.partial;
+  return w;
+}
+
+}  // namespace
+
+extern "C" size_t flash_attn_masked_workspace_bytes(int B, int Hq, int Hkv, int L, int d, const fa_mask* mask,
+                                                    int backward) {
+  if (check_common(B, Hq, Hkv, L, d, 1.f, 0, 0, FA_DTYPE_BF16) != FA_OK || check_mask(mask, L) != FA_OK) return 0;
+  return masked_ws(B, Hq, Hkv, L, d, mask, backward != 0).total;
+}
+
 extern "C" int flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     void* workspace, size_t workspace_bytes,
                                      int B, int Hq, int Hkv, int L, int d, float softmax_scale,
                                      const fa_mask* mask, const void* plan, size_t plan_bytes, int dtype,
                                      void* stream) {
@@ -322,6 +354,11 @@ extern "C" int flash_attn_fwd_masked(const void* q, const void* k, const void* v
   if (rc != FA_OK) return rc;
   rc = check_plan(plan, plan_bytes, L);
   if (rc != FA_OK) return rc;
+  MaskedWs w = masked_ws(B, Hq, Hkv, L, d, mask, false);
+  if (w.rows.ngp > 0 && (long long)B * Hq > 65535) return FA_ERR_UNSUPPORTED;   // grid rows of the global pass
+  if (w.total > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+                      workspace_bytes < w.total))
+    return FA_ERR_WORKSPACE;
   if (!all_aligned({q, k, v, o}) || (lse && !aligned16(lse))) return FA_ERR_INVALID_ARG;
   fa::FwdArgs a{};
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
@@ -331,7 +368,11 @@ extern "C" int flash_attn_fwd_masked(const void* q, const void* k, const void* v
   a.window = mask->window;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.f16 = dtype == FA_DTYPE_F16;
-  hipError_t e = fa::launch_fwd_masked(a, fa::plan_ptrs(plan, L), mask->causal != 0,
+  if (w.rows.ngp > 0) {
+    w.rows.part = static_cast<float*>(workspace);
+    w.rows.part_lse = w.rows.part + (size_t)w.rows.n_splits * B * Hq * w.rows.ngp * d;
+  }
+  hipError_t e = fa::launch_fwd_masked(a, fa::plan_ptrs(plan, L), w.rows, mask->causal != 0,
                                        reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -343,18 +384,23 @@ extern "C" int flash_attn_bwd_masked(const void* q, const void* k, const void* v
                                      const fa_mask* mask, const void* plan, size_t plan_bytes, int dtype,
                                      void* stream) {
   if (mask == nullptr) return FA_ERR_INVALID_ARG;
-  fa::BwdArgs a{};
-  int rc = bwd_setup(a, workspace, workspace_bytes, B, Hq, Hkv, L, d, softmax_scale, mask->causal, mask->window,
-                     dtype);
+  int rc = check_mask(mask, L);
   if (rc != FA_OK) return rc;
-  rc = check_mask(mask, L);
+  fa::BwdArgs a{};
+  rc = bwd_setup(a, workspace, workspace_bytes, B, Hq, Hkv, L, d, softmax_scale, mask->causal, mask->window, dtype);
   if (rc != FA_OK) return rc;
   rc = check_plan(plan, plan_bytes, L);
   if (rc != FA_OK) return rc;
+  MaskedWs w = masked_ws(B, Hq, Hkv, L, d, mask, true);
+  if (w.rows.ngp > 0 && (long long)B * Hq > 65535) return FA_ERR_UNSUPPORTED;   // grid rows of the global passes
+  if (workspace_bytes < w.total) return FA_ERR_WORKSPACE;
   if (!all_aligned({q, k, v, o, lse, dout, dq, dk, dv})) return FA_ERR_INVALID_ARG;
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
-  hipError_t e = fa::launch_bwd_masked(a, fa::plan_ptrs(plan, L), mask->causal != 0,
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.base);
+  w.rows.part = partials;
+  w.cols.part = partials;
+  hipError_t e = fa::launch_bwd_masked(a, fa::plan_ptrs(plan, L), w.rows, w.cols, mask->causal != 0,
                                        reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }

@@ -282,14 +282,24 @@ int flash_attn_mask_plan(const fa_mask* mask, int L, void* plan, size_t plan_byt
 /*
  * flash_attn_fwd_masked / flash_attn_bwd_masked: flash_attn_fwd and
  * flash_attn_bwd under the mask (16-bit dtypes; FA_DTYPE_F32 returns
- * FA_ERR_UNSUPPORTED).  `mask` supplies causal and window to the kernels; its
- * global positions and block mask are read from the plan, which must have
- * been built from this mask and this L (a plan for another mask gives that
- * mask's result).  The backward's workspace is flash_attn_bwd's.  Tiles the
- * mask leaves empty are never loaded, so the work scales with the allowed
- * pairs.
+ * FA_ERR_UNSUPPORTED).  `mask` supplies causal, window and the number of
+ * global entries to the call; the global positions themselves and the block
+ * mask are read from the plan, which must have been built from this mask and
+ * this L (a plan for another mask gives that mask's result).  Tiles the mask
+ * leaves empty are never loaded, so the work scales with the allowed pairs.
+ * Global positions are whole rows and columns of the mask: split passes over
+ * the sequence compute them, with float32 partials in the workspace.
+ *
+ * workspace: at least flash_attn_masked_workspace_bytes(..., backward) bytes,
+ * 256-byte aligned (else FA_ERR_WORKSPACE).  The forward needs none (NULL is
+ * accepted) when n_global is 0; the backward always needs flash_attn_bwd's
+ * per-row statistics and this size includes them.  With global positions,
+ * B * Hq must be at most 65535 (else FA_ERR_UNSUPPORTED).
  */
+size_t flash_attn_masked_workspace_bytes(int B, int Hq, int Hkv, int L, int d, const fa_mask* mask,
+                                         int backward);
 int flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                          void* workspace, size_t workspace_bytes,
                           int B, int Hq, int Hkv, int L, int d, float softmax_scale,
                           const fa_mask* mask, const void* plan, size_t plan_bytes, int dtype, void* stream);
 int flash_attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,

@@ -198,7 +198,7 @@ def test_mask_entry_points_reject_invalid_arguments(lib):
     c = header_constants()
     INV, UNS, WS, GQA = c["FA_ERR_INVALID_ARG"], c["FA_ERR_UNSUPPORTED"], c["FA_ERR_WORKSPACE"], c["FA_ERR_GQA"]
     pb = lib.flash_attn_mask_plan_bytes
-    assert pb(1) == 8 * 256                      # eight 256-byte aligned sections
+    assert pb(1) == 9 * 256                      # nine 256-byte aligned sections
     assert pb(0) == 0 and pb((1 << 18) + 1) == 0
     assert pb(1 << 18) > pb(4096) > 0
     need = pb(1000)
@@ -216,16 +216,27 @@ def test_mask_entry_points_reject_invalid_arguments(lib):
     assert plan(L=(1 << 18) + 1) == UNS and plan(L=0) == INV
     assert plan(p=None) == WS and plan(p=FAKE * 256 + 64) == WS and plan(nb=need - 1) == WS
 
-    def fm(q=FAKE, m=None, p=FAKE * 256, nb=need, L=1000, dt=fa.FA_DTYPE_BF16, Hkv=2, d=128):
-        return lib.flash_attn_fwd_masked(q, FAKE, FAKE, FAKE, None, 1, 2, Hkv, L, d, 0.125,
+    def fm(q=FAKE, m=None, p=FAKE * 256, nb=need, L=1000, dt=fa.FA_DTYPE_BF16, Hkv=2, d=128, ws=None, wn=0):
+        return lib.flash_attn_fwd_masked(q, FAKE, FAKE, FAKE, None, ws, wn, 1, 2, Hkv, L, d, 0.125,
                                          mask() if m is None else m, p, nb, dt, None)
-    assert lib.flash_attn_fwd_masked(FAKE, FAKE, FAKE, FAKE, None, 1, 2, 2, 1000, 128, 0.125, None, FAKE * 256,
-                                     need, fa.FA_DTYPE_BF16, None) == INV
+    assert lib.flash_attn_fwd_masked(FAKE, FAKE, FAKE, FAKE, None, None, 0, 1, 2, 2, 1000, 128, 0.125, None,
+                                     FAKE * 256, need, fa.FA_DTYPE_BF16, None) == INV
+    # the forward needs a workspace only with global positions
+    wsb_f = lib.flash_attn_masked_workspace_bytes
+    assert wsb_f(1, 2, 2, 1000, 128, mask(), 0) == 0
+    gneed = wsb_f(1, 2, 2, 1000, 128, mask(gpos=FAKE, ng=2), 0)
+    assert gneed > 0 and gneed % 256 == 0
+    assert fm(m=mask(gpos=FAKE, ng=2)) == WS and fm(m=mask(gpos=FAKE, ng=2), ws=FAKE * 256, wn=gneed - 1) == WS
+    assert fm(m=mask(gpos=FAKE, ng=2), ws=FAKE * 256 + 16, wn=gneed) == WS
+    assert fm(m=mask(gpos=FAKE, ng=2), ws=FAKE * 256, wn=gneed, q=None) == INV
+    assert wsb_f(1, 2, 2, 1000, 128, None, 0) == 0 and wsb_f(1, 2, 2, (1 << 18) + 1, 128, mask(), 0) == 0
     assert fm(q=None) == INV and fm(dt=fa.FA_DTYPE_F32) == UNS and fm(d=80) == UNS and fm(Hkv=3) == GQA
     assert fm(p=None) == WS and fm(nb=need - 1) == WS and fm(m=mask(bmask=FAKE, block=100)) == UNS
     assert fm(m=mask(causal=1, window=-2)) == INV and fm(L=(1 << 18) + 2, nb=1 << 40) == UNS
 
     wsb = lib.flash_attn_bwd_workspace_bytes(1, 2, 2, 1000, 128, fa.FA_DTYPE_BF16)
+    assert wsb_f(1, 2, 2, 1000, 128, mask(), 1) == wsb
+    assert wsb_f(1, 2, 2, 1000, 128, mask(gpos=FAKE, ng=40), 1) > wsb
 
     def bm(dq=FAKE, ws=FAKE * 256, wn=wsb, p=FAKE * 256, nb=need, m=None):
         return lib.flash_attn_bwd_masked(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, ws, wn, 1, 2, 2, 1000,

@@ -127,14 +127,17 @@ def test_masked_forward_and_backward(case):
 
 # ---- the plan against the oracle mask, block by block (white box: the layout of
 # flash_attn_mask_plan's buffer -- 256-byte aligned sections in the order
-# gbits, row counts, row order, column counts, column order, meta, row entries,
-# column entries)
+# gbits, row counts, row order, column counts, column order, meta, global
+# positions, row entries, column entries).  The row lists leave global query
+# rows to the global-row pass and the column lists leave global keys to the
+# global-key pass, so each list is checked against the mask without them.
 
 def plan_sections(L):
     nb, nw = (L + 63) // 64, (L + 127) // 128
     off, out = 0, {}
     for name, nbytes in (("gbits", 8 * nb), ("row_cnt", 4 * nw), ("row_ord", 4 * nw), ("col_cnt", 4 * nw),
-                         ("col_ord", 4 * nw), ("meta", 16), ("row_ent", 4 * nw * nb), ("col_ent", 4 * nw * nb)):
+                         ("col_ord", 4 * nw), ("meta", 16), ("gpos", 4 * L), ("row_ent", 4 * nw * nb),
+                         ("col_ent", 4 * nw * nb)):
         out[name] = (off, nbytes)
         off = (off + nbytes + 255) & ~255
     return nb, nw, out
@@ -182,10 +185,20 @@ def test_plan_blocks_match_oracle_mask(case):
     for p in range(w.L):
         assert bool((int(gbits[p // 64]) >> (p % 64)) & 1) == (p in gl)
     meta = arr("meta", np.int32)
+    assert int(meta[2]) == len(gl) and arr("gpos", np.int32)[:len(gl)].tolist() == sorted(gl)
+    # the mask without global rows (for the row lists) and without global keys (column lists)
+    L = w.L
+    i, j = np.arange(L)[:, None], np.arange(L)[None, :]
+    causal_ok = (j <= i) if case[7] else np.ones((L, L), dtype=bool)
+    base = oracle.general_mask(np.arange(L), np.arange(L), case[7], case[8], bm, case[10], ())
+    isg = np.isin(np.arange(L), sorted(gl))
+    ok_rows = base | (isg[None, :] & causal_ok)
+    ok_cols = base | (isg[:, None] & causal_ok)
+    assert np.array_equal(ok_rows | ok_cols, ok)
     check_lists(arr("row_cnt", np.int32), arr("row_ent", np.uint32).reshape(nw, nb), arr("row_ord", np.int32),
-                int(meta[0]), nb, nw, ok, w.L, cols=False)
+                int(meta[0]), nb, nw, ok_rows, w.L, cols=False)
     check_lists(arr("col_cnt", np.int32), arr("col_ent", np.uint32).reshape(nw, nb), arr("col_ord", np.int32),
-                int(meta[1]), nb, nw, ok, w.L, cols=True)
+                int(meta[1]), nb, nw, ok_cols, w.L, cols=True)
 
 
 def test_plan_of_plain_masks_reproduces_range_kernels_bitwise():
