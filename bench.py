@@ -209,6 +209,58 @@ def measure_decode(B=8, Hq=32, Hkv=8, Lq=1, Lk=32768, d=128, iters=20, warmup=5)
             "workspace_bytes": int(ws.numel()), "data": "synthetic N(0,1), generated on the device"}
 
 
+def measure_sparse(iters=5, warmup=2):
+    """General sparse mask: the hybrid configuration (window reaching 512 positions
+    both ways, first and last token global, 131072 tokens, batch 2) on 32 heads of
+    128, forward and backward under one mask plan.
+
+    Reported as effective TFLOP/s over the allowed pairs only (4 d flops per pair
+    forward, 2.5x that backward): the work the mask leaves is the algorithmic work."""
+    import torch
+    import exact_tiled_attention_flash_amd as fa
+    import workloads as W
+    w = W.HYBRID_SPARSE_128K
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    q, k, v, do = (torch.randn(w.B, h, w.L, w.d, generator=g, device=dev).to(w.dtype)
+                   for h in (w.Hq, w.Hkv, w.Hkv, w.Hq))
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s0.record()
+    plan = fa.MaskPlan(w.L, causal=w.causal, window=w.window, global_tokens=w.global_tokens, device=dev)
+    s1.record()
+    torch.cuda.synchronize()
+    plan_ms = s0.elapsed_time(s1)
+    pairs = plan.allowed_pairs()
+    o, lse = torch.empty_like(q), torch.empty(w.B, w.Hq, w.L, dtype=torch.float32, device=dev)
+    fws = fa.masked_workspace_bytes(w.B, w.Hq, w.Hkv, w.L, w.d, plan, False)
+    bws = fa.masked_workspace_bytes(w.B, w.Hq, w.Hkv, w.L, w.d, plan, True)
+    fw = torch.empty(max(fws, 256), dtype=torch.uint8, device=dev)
+    bw = torch.empty(bws, dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    fmed, fmean = time_calls(lambda: fa.fwd_masked(q, k, v, plan, scale=w.scale, out=o, lse=lse, workspace=fw),
+                             iters, warmup)
+    bmed, bmean = time_calls(lambda: fa.bwd_masked(q, k, v, o, lse, do, plan, scale=w.scale, workspace=bw,
+                                                   dq=dq, dk=dk, dv=dv), iters, warmup)
+    ff = 4.0 * w.d * pairs * w.B * w.Hq
+    bf = 2.5 * ff
+    ftf, btf = ff / (fmed * 1e-3) / 1e12, bf / (bmed * 1e-3) / 1e12
+    out = {"workload": w.name, "mask": {"causal": w.causal, "window": w.window,
+                                        "global_tokens": list(w.global_tokens), "block_mask": None},
+           "allowed_pairs": pairs, "pairs_per_row": round(pairs / w.L, 2), "density": pairs / float(w.L) ** 2,
+           "plan_ms": round(plan_ms, 3), "plan_bytes": int(plan.plan.numel()),
+           "fwd": {"ms_median": round(fmed, 4), "ms_mean": round(fmean, 4), "tflop": ff / 1e12,
+                   "tflops": round(ftf, 2), "frac_peak": round(ftf / PEAK_BF16_TFLOPS, 4),
+                   "workspace_bytes": int(fws)},
+           "bwd": {"ms_median": round(bmed, 4), "ms_mean": round(bmean, 4), "tflop": bf / 1e12,
+                   "tflops": round(btf, 2), "frac_peak": round(btf / PEAK_BF16_TFLOPS, 4),
+                   "workspace_bytes": int(bws)},
+           "data": "synthetic N(0,1), generated on the device"}
+    del q, k, v, do, o, lse, dq, dk, dv, fw, bw, plan
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -216,6 +268,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table")
+    ap.add_argument("--sparse-only", action="store_true",
+                    help="only the general-mask workload (for profiling its kernels); prints its JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (3x), so that HBM counters "
                          "(FETCH_SIZE/WRITE_SIZE) can be scaled against a kernel of known traffic")
@@ -231,6 +285,9 @@ def main():
 
     fa.library()
     dev = torch.device("cuda:0")
+    if args.sparse_only:
+        print(json.dumps({"sparse": measure_sparse(iters=args.steps, warmup=args.warmup)}), flush=True)
+        return
     if args.calibrate_copy:
         src = torch.ones(64 * 2**20, dtype=torch.float32, device=dev)    # 256 MiB
         dst = torch.empty_like(src)
@@ -336,6 +393,7 @@ def main():
     if not args.no_configs:
         out["configs"] = {wl.name: measure_config(wl) for wl in W.ALL}
         out["decode"] = measure_decode()
+        out["sparse"] = measure_sparse()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

@@ -344,13 +344,32 @@ def block_band_mask(L, block=64, radius=1):
 def allowed_pairs(L, causal=False, window=0, global_tokens=(), block_mask=None, block=64):
     """Number of allowed (query, key) pairs of the general mask over one sequence of
     length L (the same rule as ``MaskPlan``): the algorithmic work of one head is
-    4 * d * allowed_pairs flops forward.  Counted row by row on the host in O(L) memory."""
+    4 * d * allowed_pairs flops forward.  Counted on the host: per row in interval form
+    without a block mask, else over row chunks of the boolean mask."""
     L = int(L)
     glob = sorted({(p + L if p < 0 else p) for p in global_tokens if -L <= p < L})
+    if block_mask is None:
+        # interval form: row i's local keys are one interval [lo, hi]; the global
+        # keys outside it (and visible under the causal mask) are added, and a
+        # global row sees every visible key
+        i = torch.arange(L, dtype=torch.int64)
+        hi = i.clone() if causal else torch.full((L,), L - 1, dtype=torch.int64)
+        lo = torch.zeros(L, dtype=torch.int64)
+        if window > 0:
+            lo = (i - window + 1).clamp_min(0)
+            if not causal:
+                hi = (i + window - 1).clamp_max(L - 1)
+        g = torch.tensor(glob, dtype=torch.int64)
+        inside = torch.searchsorted(g, hi, right=True) - torch.searchsorted(g, lo, right=False)
+        visible = torch.searchsorted(g, i, right=True) if causal else torch.full((L,), len(glob), dtype=torch.int64)
+        count = hi - lo + 1 + visible - inside
+        if glob:
+            count[g] = (g + 1) if causal else L
+        return int(count.sum())
     is_g = torch.zeros(L, dtype=torch.bool)
     if glob:
         is_g[torch.tensor(glob)] = True
-    bm = None if block_mask is None else torch.as_tensor(block_mask).bool().cpu()
+    bm = torch.as_tensor(block_mask).bool().cpu()
     total = 0
     chunk = max(1, (1 << 24) // L)
     j = torch.arange(L)
@@ -359,8 +378,7 @@ def allowed_pairs(L, causal=False, window=0, global_tokens=(), block_mask=None, 
         local = torch.ones(i.shape[0], L, dtype=torch.bool)
         if window > 0:
             local &= (i - j[None, :]).abs() < window
-        if bm is not None:
-            local &= bm[(i // block), (j // block)[None, :]]
+        local &= bm[(i // block), (j // block)[None, :]]
         ok = local | is_g[i] | is_g[None, :]
         if causal:
             ok &= j[None, :] <= i

@@ -299,6 +299,26 @@ __device__ __forceinline__ int ent_tile(unsigned e, int nb) { return min((int)(e
 __device__ __forceinline__ int ent_class(unsigned e, int half) { return (int)((e >> (16 + 2 * half)) & 3u); }
 __device__ __forceinline__ bool ent_block(unsigned e, int half) { return ((e >> (20 + half)) & 1u) != 0; }
 
+// A zero the compiler cannot see through.
+__device__ __forceinline__ int opaque_zero() {
+  int z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z));
+  return z;
+}
+
+// A work-group's list, read two tiles ahead through the vector memory path:
+// the load is issued with the tile copies, so the copies' own wait covers it,
+// and readfirstlane returns the (uniform) entry to scalar registers.  A scalar
+// load of the next entry would instead hold up the next tile's copies by its
+// latency on every tile.  Entries past the list read as 0.
+struct EntryStream {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ unsigned fetch(int e) const {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, opaque_zero(), 4 * e, 0);
+  }
+};
+__device__ __forceinline__ unsigned uniform(unsigned v) { return __builtin_amdgcn_readfirstlane(v); }
+
 // Forward: one work-group of 4 waves per (batch, query head, 128 queries), as
 // the range-tiled forward; waves 0-1 hold the first 64 rows, 2-3 the second.
 template <int D, bool CAUSAL, bool F16>
@@ -332,9 +352,11 @@ __global__ __launch_bounds__(256, 2) void fwd_masked_kernel(FwdArgs a, PlanPtrs 
   const unsigned* ents = p.row_ent + (size_t)qt * p.nb;
   const bool gq = is_global(p.gbits, my_q, L);
 
+  const EntryStream es{make_rsrc(ents, 4u * (unsigned)n_ent)};
+  unsigned cur = n_ent > 0 ? ents[0] : 0u, nxt = n_ent > 1 ? ents[1] : 0u;
   CopyPlan<D> cp;
   make_copy_plan<D>(cp, wave, lane);
-  if (n_ent > 0) issue_kv<D>(cp, krs, vrs, ent_tile(ents[0], p.nb) * C::BC, k_st0, v_st0, wave);
+  if (n_ent > 0) issue_kv<D>(cp, krs, vrs, ent_tile(cur, p.nb) * C::BC, k_st0, v_st0, wave);
 
   FwdState<D> st;
 #pragma unroll
@@ -348,25 +370,32 @@ __global__ __launch_bounds__(256, 2) void fwd_masked_kernel(FwdArgs a, PlanPtrs 
   for (int db = 0; db < C::NDB; ++db) st.o[db] = f32x16{};
   const float c = a.scale_log2;
 
-  auto step = [&](int e, const char* kb, const char* vb) {
-    const unsigned ent = ents[e];
+  auto step = [&](unsigned ent, const char* kb, const char* vb) {
     const int cls = ent_class(ent, half);
     if (cls != 0 && q_w0 < L) {
       const int kt = ent_tile(ent, p.nb);
-      const GeneralMaskQ<CAUSAL> ok{L, window, my_q, kt * C::BC, gq, ent_block(ent, half), p.gbits[kt]};
+      const GeneralMaskQ<CAUSAL> ok{L, window, my_q, kt * C::BC, gq, ent_block(ent, half),
+                                    cls == 1 ? p.gbits[kt] : 0ull};
       fwd_tile<D, F16>(st, kb, vb, kt * C::BC, cls == 1, ok, c, lane);
     }
   };
 
+  // stage 0 holds tile e (entry cur), stage 1 receives tile e + 1 (entry nxt)
   wait_copies_and_barrier();
   for (int e = 0; e < n_ent; e += 2) {
-    if (e + 1 < n_ent) issue_kv<D>(cp, krs, vrs, ent_tile(ents[e + 1], p.nb) * C::BC, k_st1, v_st1, wave);
-    step(e, k_st0, v_st0);
+    const unsigned far0 = es.fetch(e + 2);
+    if (e + 1 < n_ent) issue_kv<D>(cp, krs, vrs, ent_tile(nxt, p.nb) * C::BC, k_st1, v_st1, wave);
+    step(cur, k_st0, v_st0);
     wait_copies_and_barrier();
     if (e + 1 >= n_ent) break;
-    if (e + 2 < n_ent) issue_kv<D>(cp, krs, vrs, ent_tile(ents[e + 2], p.nb) * C::BC, k_st0, v_st0, wave);
-    step(e + 1, k_st1, v_st1);
+    cur = nxt;
+    nxt = uniform(far0);
+    const unsigned far1 = es.fetch(e + 3);
+    if (e + 2 < n_ent) issue_kv<D>(cp, krs, vrs, ent_tile(nxt, p.nb) * C::BC, k_st0, v_st0, wave);
+    step(cur, k_st1, v_st1);
     wait_copies_and_barrier();
+    cur = nxt;
+    nxt = uniform(far1);
   }
 
   // epilogue: a row with no allowed key gets O = 0, LSE = -inf; a global row
@@ -442,10 +471,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_masked_kernel(BwdArgs a, PlanPtrs
   }
   ad.kv = row_offset_kpad<D>(32 * kb + ln, 0, g);
 
-  // iteration it: query head hk*G + it / n_ent, entry it % n_ent
-  auto ent_of = [&](int it) { return ents[it - (it / n_ent) * n_ent]; };
-  auto issue = [&](int it, char* qs, char* dos, float* ss) {
-    const int hq = hk * G + it / n_ent, q0 = ent_tile(ent_of(it), p.nb) * C::BQ;
+  // iteration it visits entry it % n_ent for query head hk*G + it / n_ent
+  auto issue = [&](unsigned ent, int hoff, char* qs, char* dos, float* ss) {
+    const int hq = hk * G + hoff, q0 = ent_tile(ent, p.nb) * C::BQ;
     const size_t qoff = ((size_t)(b * a.Hq + hq) * L) * D;
     const __amdgpu_buffer_rsrc_t qrs = make_rsrc(reinterpret_cast<const bf16*>(a.q) + qoff, head_bytes);
     const __amdgpu_buffer_rsrc_t drs = make_rsrc(reinterpret_cast<const bf16*>(a.dout) + qoff, head_bytes);
@@ -475,7 +503,23 @@ __global__ __launch_bounds__(512, 1) void dkdv_masked_kernel(BwdArgs a, PlanPtrs
       buf2lds16(vrs, src, soff, v_blk + n * 1024);
     }
   }
-  if (n_it > 0) issue(0, q_st0, do_st0, stat_st0);
+  // cursors: entry and head offset of iterations it and it + 1, list position of it + 2
+  const EntryStream es{make_rsrc(ents, 4u * (unsigned)n_ent)};
+  unsigned cur = n_ent > 0 ? ents[0] : 0u, nxt = n_ent > 1 ? ents[1] : cur;
+  int cur_h = 0, nxt_h = n_ent > 1 ? 0 : 1;
+  int fe = 2, fh = 0;
+  if (n_ent > 0)
+    while (fe >= n_ent) {
+      fe -= n_ent;
+      ++fh;
+    }
+  auto advance = [&]() {
+    if (++fe == n_ent) {
+      fe = 0;
+      ++fh;
+    }
+  };
+  if (n_it > 0) issue(cur, cur_h, q_st0, do_st0, stat_st0);
 
   KVState<D> st;
 #pragma unroll
@@ -485,25 +529,39 @@ __global__ __launch_bounds__(512, 1) void dkdv_masked_kernel(BwdArgs a, PlanPtrs
   }
   const float c = a.scale_log2;
 
-  auto step = [&](int it, const char* qs, const char* dos, const float* ss) {
-    const unsigned ent = ent_of(it);
+  auto step = [&](unsigned ent, const char* qs, const char* dos, const float* ss) {
     const int cls = ent_class(ent, half);
     const int q0 = ent_tile(ent, p.nb) * C::BQ;
     if (cls != 0 && key_w0 < L && q0 + 32 * qh < L) {
-      const GeneralMaskK<CAUSAL> ok{L, window, my_key, q0, gk, ent_block(ent, half), p.gbits[ent_tile(ent, p.nb)]};
+      const GeneralMaskK<CAUSAL> ok{L, window, my_key, q0, gk, ent_block(ent, half),
+                                    cls == 1 ? p.gbits[ent_tile(ent, p.nb)] : 0ull};
       kv_tile<D, F16>(st, ad, k_blk, v_blk, qs, dos, ss, q0, cls == 1, ok, qh, c, lane);
     }
   };
 
   fwdtile::wait_copies_and_barrier();
   for (int it = 0; it < n_it; it += 2) {
-    if (it + 1 < n_it) issue(it + 1, q_st1, do_st1, stat_st1);
-    step(it, q_st0, do_st0, stat_st0);
+    const unsigned far0 = es.fetch(fe);
+    const int far0_h = fh;
+    advance();
+    if (it + 1 < n_it) issue(nxt, nxt_h, q_st1, do_st1, stat_st1);
+    step(cur, q_st0, do_st0, stat_st0);
     fwdtile::wait_copies_and_barrier();
     if (it + 1 >= n_it) break;
-    if (it + 2 < n_it) issue(it + 2, q_st0, do_st0, stat_st0);
-    step(it + 1, q_st1, do_st1, stat_st1);
+    cur = nxt;
+    cur_h = nxt_h;
+    nxt = uniform(far0);
+    nxt_h = far0_h;
+    const unsigned far1 = es.fetch(fe);
+    const int far1_h = fh;
+    advance();
+    if (it + 2 < n_it) issue(nxt, nxt_h, q_st0, do_st0, stat_st0);
+    step(cur, q_st1, do_st1, stat_st1);
     fwdtile::wait_copies_and_barrier();
+    cur = nxt;
+    cur_h = nxt_h;
+    nxt = uniform(far1);
+    nxt_h = far1_h;
   }
 
   // sum the two query halves through LDS, then store (as the range-tiled kernel)
@@ -598,15 +656,17 @@ __global__ __launch_bounds__(256, 2) void dq_masked_kernel(BwdArgs a, PlanPtrs p
   }
   ad.vrow = row_offset_kpad<D>(ln, 0, g);
 
-  auto issue = [&](int e, char* kb, char* vb) {
-    const int soff = ent_tile(ents[e], p.nb) * C::BC * (2 * D);
+  auto issue = [&](unsigned ent, char* kb, char* vb) {
+    const int soff = ent_tile(ent, p.nb) * C::BC * (2 * D);
 #pragma unroll
     for (int i = 0; i < C::KPER; ++i) buf2lds16(krs, ad.kcopy[i], soff, kb + (wave + C::kWaves * i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::VPER; ++i)
       if (wave + C::kWaves * i < C::VCOPIES) buf2lds16(vrs, ad.vcopy[i], soff, vb + (wave + C::kWaves * i) * 1024);
   };
-  if (n_ent > 0) issue(0, k_st0, v_st0);
+  const EntryStream es{make_rsrc(ents, 4u * (unsigned)n_ent)};
+  unsigned cur = n_ent > 0 ? ents[0] : 0u, nxt = n_ent > 1 ? ents[1] : 0u;
+  if (n_ent > 0) issue(cur, k_st0, v_st0);
 
   QState<D> st;
   {
@@ -626,25 +686,31 @@ __global__ __launch_bounds__(256, 2) void dq_masked_kernel(BwdArgs a, PlanPtrs p
   }
   const float c = a.scale_log2;
 
-  auto step = [&](int e, const char* kb, const char* vb) {
-    const unsigned ent = ents[e];
+  auto step = [&](unsigned ent, const char* kb, const char* vb) {
     const int cls = ent_class(ent, half);
     if (cls != 0 && q_w0 < L) {
       const int kt = ent_tile(ent, p.nb);
-      const GeneralMaskQ<CAUSAL> ok{L, window, my_q, kt * C::BC, gq, ent_block(ent, half), p.gbits[kt]};
+      const GeneralMaskQ<CAUSAL> ok{L, window, my_q, kt * C::BC, gq, ent_block(ent, half),
+                                    cls == 1 ? p.gbits[kt] : 0ull};
       q_tile<D, F16>(st, ad, kb, vb, kt * C::BC, cls == 1, ok, c, lane);
     }
   };
 
   fwdtile::wait_copies_and_barrier();
   for (int e = 0; e < n_ent; e += 2) {
-    if (e + 1 < n_ent) issue(e + 1, k_st1, v_st1);
-    step(e, k_st0, v_st0);
+    const unsigned far0 = es.fetch(e + 2);
+    if (e + 1 < n_ent) issue(nxt, k_st1, v_st1);
+    step(cur, k_st0, v_st0);
     fwdtile::wait_copies_and_barrier();
     if (e + 1 >= n_ent) break;
-    if (e + 2 < n_ent) issue(e + 2, k_st0, v_st0);
-    step(e + 1, k_st1, v_st1);
+    cur = nxt;
+    nxt = uniform(far0);
+    const unsigned far1 = es.fetch(e + 3);
+    if (e + 2 < n_ent) issue(nxt, k_st0, v_st0);
+    step(cur, k_st1, v_st1);
     fwdtile::wait_copies_and_barrier();
+    cur = nxt;
+    nxt = uniform(far1);
   }
 
   if (my_q < L && !gq) {         // global rows: the global-row pass

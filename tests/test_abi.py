@@ -253,7 +253,9 @@ def test_allowed_pairs_counts_the_oracle_mask():
     assert bmask.shape == (5, 5) and bmask[0, 1] and not bmask[0, 2]
     for L, causal, window, glob, bm, blk in [(300, False, 0, (), None, 64), (300, True, 0, (), None, 64),
                                            (300, False, 7, (0, -1), None, 64), (300, True, 20, (5, 299), bmask, 64),
-                                           (257, False, 0, (3,), fa.block_band_mask(257, 128, 0).numpy(), 128)]:
+                                           (257, False, 0, (3,), fa.block_band_mask(257, 128, 0).numpy(), 128),
+                                           (300, True, 9, (0, 150, -1), None, 64), (257, False, 0, (5, 5, -3), None, 64),
+                                           (200, False, 300, (7,), None, 64), (64, True, 1, tuple(range(0, 64, 5)), None, 64)]:
         gl = tuple(p + L if p < 0 else p for p in glob)
         ok = oracle.general_mask(np.arange(L), np.arange(L), causal, window, bm, blk, gl)
         assert fa.allowed_pairs(L, causal, window, glob, bm, blk) == int(ok.sum())
