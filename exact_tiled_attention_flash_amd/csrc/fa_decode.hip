@@ -13,6 +13,9 @@
 // the chip ("split-K").  Each split writes a partial (O, LSE) normalised over
 // its keys to the workspace; the combine kernel merges a row's partials
 // exactly: LSE = log sum_s e^{LSE_s}, O = sum_s e^{LSE_s - LSE} O_s.
+// A work-group stages one tile at a time (37 KiB of LDS), so four of them fit
+// on a CU: the bytes in flight that keep HBM busy come from four work-groups
+// per CU copying at once, more than two double-buffered ones would have.
 #include "fa_fwd_tile.hpp"
 
 namespace fa {
@@ -26,8 +29,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) char k_st0[C::KT];
   __shared__ __attribute__((aligned(1024))) char v_st0[C::VT];
-  __shared__ __attribute__((aligned(1024))) char k_st1[C::KT];
-  __shared__ __attribute__((aligned(1024))) char v_st1[C::VT];
 
   const int lane = threadIdx.x;
   const int g = lane >> 5, ln = lane & 31;
@@ -74,7 +75,6 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < C::VCOPIES; ++i) buf2lds16(vrs, voff[i], soff, vbuf + i * 1024);
   };
-  if (!empty) issue(j_lo, k_st0, v_st0);
 
   FwdState<D> st;
   const bf16* Qr = reinterpret_cast<const bf16*>(a.q) + ((size_t)((b * a.Hq + hq) * Lq + t)) * D;
@@ -91,15 +91,13 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   auto tile_mask = [&](int k0) { return range_tile_needs_mask<CAUSAL, C::BC>(k0, n, a.window, min_pos, max_pos); };
   const RangeMaskQ<CAUSAL> ok{n, a.window, my_pos};
 
-  wait_copies_and_barrier();
-  for (int j = j_lo; j <= j_hi; j += 2) {
-    if (j < j_hi) issue(j + 1, k_st1, v_st1);
+  // one stage: the work-group copies a tile, waits, computes; four such
+  // work-groups per CU keep several tiles in flight
+  for (int j = j_lo; j <= j_hi; ++j) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    issue(j, k_st0, v_st0);
+    wait_copies_and_barrier();
     fwd_tile<D, F16>(st, k_st0, v_st0, j * C::BC, tile_mask(j * C::BC), ok, c, lane);
-    wait_copies_and_barrier();
-    if (j + 1 > j_hi) break;
-    if (j + 1 < j_hi) issue(j + 2, k_st0, v_st0);
-    fwd_tile<D, F16>(st, k_st1, v_st1, (j + 1) * C::BC, tile_mask((j + 1) * C::BC), ok, c, lane);
-    wait_copies_and_barrier();
   }
 
   // partial for this split: O normalised over its keys (fp32), LSE in ln units
@@ -121,20 +119,33 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Merge a row's split partials (a row's d/8 threads are adjacent lanes).
+// Merge one row's split partials: one work-group per row.  The splits are
+// dealt to groups of d/8 adjacent lanes (8 elements each), so that a row with
+// many splits -- a long cache with few sequences and K/V heads -- is merged by
+// the whole work-group rather than by one group of lanes walking every split;
+// the groups' weighted sums then meet in LDS.
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   constexpr int kLanesPerRow = D / 8;
-  constexpr int kRowsPerBlock = 256 / kLanesPerRow;
-  const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
-  const int part = threadIdx.x % kLanesPerRow;
-  if (row >= a.rows) return;
+  constexpr int kGroups = 256 / kLanesPerRow;
+  __shared__ float red[kGroups][D];
+  __shared__ float gtot[kGroups];
+  __shared__ float wmax[4];
+  const long long row = blockIdx.x;
+  const int t = threadIdx.x, grp = t / kLanesPerRow, part = t % kLanesPerRow;
+  // 1. the largest split LSE of the row
   float m = -INFINITY;
-  for (int s = 0; s < a.n_splits; ++s) m = fmaxf(m, a.part_lse[(size_t)s * a.rows + row]);
+  for (int s = t; s < a.n_splits; s += 256) m = fmaxf(m, a.part_lse[(size_t)s * a.rows + row]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((t & 63) == 0) wmax[t >> 6] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  // 2. this group's splits, weighted by e^{LSE_s - m}
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
   if (m != -INFINITY) {
-    for (int s = 0; s < a.n_splits; ++s) {
+    for (int s = grp; s < a.n_splits; s += kGroups) {
       const float w = __expf(a.part_lse[(size_t)s * a.rows + row] - m);   // exp(-inf) = 0
       if (w == 0.f) continue;
       const f32x4* p = reinterpret_cast<const f32x4*>(a.part_o + ((size_t)s * a.rows + row) * D + 8 * part);
@@ -147,11 +158,26 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
       tot += w;
     }
   }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  // 3. across the groups
+#pragma unroll
+  for (int i = 0; i < 8; ++i) red[grp][8 * part + i] = acc[i];
+  if (part == 0) gtot[grp] = tot;
+  __syncthreads();
+  if (grp != 0) return;
+  float sum = 0.f;
+  for (int gi = 0; gi < kGroups; ++gi) sum += gtot[gi];
+  float o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    float x = 0.f;
+    for (int gi = 0; gi < kGroups; ++gi) x += red[gi][8 * part + i];
+    o[i] = x;
+  }
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
   bf16* out = static_cast<bf16*>(a.o) + (size_t)row * D + 8 * part;
-  *reinterpret_cast<bf16x8*>(out) = pack8<F16>(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv,
-                                                acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
-  if (part == 0 && a.lse != nullptr) a.lse[row] = tot > 0.f ? m + __logf(tot) : -INFINITY;
+  *reinterpret_cast<bf16x8*>(out) = pack8<F16>(o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv, o[4] * inv,
+                                                o[5] * inv, o[6] * inv, o[7] * inv);
+  if (part == 0 && a.lse != nullptr) a.lse[row] = sum > 0.f ? m + __logf(sum) : -INFINITY;
 }
 
 template <int D, bool CAUSAL, bool F16>
@@ -159,21 +185,26 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, F16>), dim3(a.n_splits, a.B * a.Hkv), dim3(64), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  constexpr int kRowsPerBlock = 256 / (D / 8);
-  hipLaunchKernelGGL((decode_combine_kernel<D, F16>), dim3((unsigned)((a.rows + kRowsPerBlock - 1) / kRowsPerBlock)),
-                     dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_combine_kernel<D, F16>), dim3((unsigned)a.rows), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
+namespace {
+constexpr int DECODE_TARGET = 1024;   // work-groups a decode call aims for (four per CU)
+constexpr int DECODE_CAP = 256;       // most key splits per sequence and K/V head
+}  // namespace
+
 void decode_plan(int B, int Hkv, int Lk, int& n_splits, int& split_keys) {
   constexpr int kBC = 64;
   const int tiles = (Lk + kBC - 1) / kBC;
-  // about two work-groups per CU across the 256 CUs, at least four tiles per split
-  int want = (512 + B * Hkv - 1) / (B * Hkv);
+  // about four work-groups per CU across the 256 CUs (a single-stage
+  // work-group holds 37 KiB of LDS, so four fit on a CU), at least four tiles
+  // per split
+  int want = (DECODE_TARGET + B * Hkv - 1) / (B * Hkv);
   want = min(want, max(1, tiles / 4));
-  want = max(1, min(want, 64));
+  want = max(1, min(want, DECODE_CAP));
   const int per = (tiles + want - 1) / want;
   split_keys = per * kBC;
   n_splits = (tiles + per - 1) / per;
