@@ -45,6 +45,8 @@ CASES = [
     (1, 4, 4, 8, 8, 128, True, 0, [8], torch.bfloat16),                  # cache = the new tokens only
     (1, 32, 8, 1, 131072, 128, True, 0, [131072], torch.bfloat16),       # a 128k cache
     (1, 32, 8, 1, 32768, 128, True, 4096, [30000], torch.bfloat16),      # sliding window over a long cache
+    (1, 4, 1, 1, 70000, 128, True, 0, [70000], torch.bfloat16),          # one K/V head, ~220 key splits merged
+    (1, 2, 1, 3, 50000, 64, False, 0, [49999], torch.float16),           # many splits, non-causal, ragged tile
 ]
 
 
