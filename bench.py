@@ -214,6 +214,48 @@ def measure_decode(B=8, Hq=32, Hkv=8, Lq=1, Lk=32768, d=128, iters=20, warmup=5)
             "workspace_bytes": int(ws.numel()), "data": "synthetic N(0,1), generated on the device"}
 
 
+def measure_ring(iters=10, warmup=3):
+    """One GPU's share of ring attention: a 131072-token causal sequence on 8 GPUs gives
+    each GPU a 16384-token query chunk that meets every key/value chunk in turn.  Times
+    the chunk-pair forward and backward on an off-diagonal block (queries after all keys:
+    no mask, 16384 x 16384) and on the diagonal block (causal inside the chunk), and the
+    exact merge of two partials (HBM-bound: reads two O and LSE, writes one)."""
+    import torch
+    import exact_tiled_attention_flash_amd as fa
+    B, H, C, d = 1, 32, 16384, 128
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(11)
+    q, k, v, do = (torch.randn(B, H, C, d, generator=g, device=dev).to(torch.bfloat16) for _ in range(4))
+    s = 1.0 / math.sqrt(d)
+    out = {"shape": f"B{B} H{H} chunk {C} d{d} bf16 causal (131072 tokens / 8)",
+           "data": "synthetic N(0,1), generated on the device"}
+    o, lse = torch.empty_like(q), torch.empty(B, H, C, dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.bwd_workspace_bytes(B, H, H, C, d), dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    for name, qo, ko, flops in (("off_diagonal", C, 0, 4.0 * B * H * C * C * d),
+                                ("diagonal", 0, 0, 2.0 * B * H * C * C * d)):
+        fmed, _ = time_calls(lambda: fa.fwd_block(q, k, v, causal=True, q_offset=qo, k_offset=ko, scale=s,
+                                                  out=o, lse=lse), iters, warmup)
+        bmed, _ = time_calls(lambda: fa.bwd_block(q, k, v, o, lse, do, causal=True, q_offset=qo, k_offset=ko,
+                                                  scale=s, workspace=ws, dq=dq, dk=dk, dv=dv), iters, warmup)
+        ftf, btf = flops / (fmed * 1e-3) / 1e12, 2.5 * flops / (bmed * 1e-3) / 1e12
+        out[name] = {"fwd_ms": round(fmed, 4), "fwd_tflops": round(ftf, 2),
+                     "fwd_frac_peak": round(ftf / PEAK_BF16_TFLOPS, 4),
+                     "bwd_ms": round(bmed, 4), "bwd_tflops": round(btf, 2),
+                     "bwd_frac_peak": round(btf / PEAK_BF16_TFLOPS, 4)}
+    ob, lb = torch.empty_like(q), torch.empty_like(lse)
+    fa.fwd_block(q, k, v, causal=True, q_offset=C, k_offset=0, scale=s, out=ob, lse=lb)
+    mo, ml = torch.empty_like(q), torch.empty_like(lse)
+    mmed, _ = time_calls(lambda: fa.merge(o, lse, ob, lb, out=mo, lse_out=ml), iters, warmup)
+    mbytes = 3 * B * H * C * d * 2 + 3 * B * H * C * 4
+    mgbs = mbytes / (mmed * 1e-3) / 1e9
+    out["merge"] = {"ms": round(mmed, 4), "bytes": mbytes, "hbm_gbs": round(mgbs, 1),
+                    "frac_peak": round(mgbs / PEAK_HBM_GBS, 4)}
+    del q, k, v, do, o, lse, ws, dq, dk, dv, ob, lb, mo, ml
+    torch.cuda.empty_cache()
+    return out
+
+
 def measure_sparse(iters=5, warmup=2):
     """General sparse mask: the hybrid configuration (window reaching 512 positions
     both ways, first and last token global, 131072 tokens, batch 2) on 32 heads of
@@ -275,6 +317,8 @@ def main():
     ap.add_argument("--no-configs", action="store_true", help="skip the per-workload table")
     ap.add_argument("--sparse-only", action="store_true",
                     help="only the general-mask workload (for profiling its kernels); prints its JSON")
+    ap.add_argument("--ring-only", action="store_true",
+                    help="only the ring-attention chunk-pair workload; prints its JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (3x), so that HBM counters "
                          "(FETCH_SIZE/WRITE_SIZE) can be scaled against a kernel of known traffic")
@@ -292,6 +336,9 @@ def main():
     dev = torch.device("cuda:0")
     if args.sparse_only:
         print(json.dumps({"sparse": measure_sparse(iters=args.steps, warmup=args.warmup)}), flush=True)
+        return
+    if args.ring_only:
+        print(json.dumps({"ring": measure_ring(iters=args.steps, warmup=args.warmup)}), flush=True)
         return
     if args.calibrate_copy:
         src = torch.ones(64 * 2**20, dtype=torch.float32, device=dev)    # 256 MiB
@@ -402,6 +449,7 @@ def main():
     if not args.no_configs:
         out["configs"] = {wl.name: measure_config(wl) for wl in W.ALL}
         out["decode"] = measure_decode()
+        out["ring"] = measure_ring()
         out["sparse"] = measure_sparse()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
