@@ -169,7 +169,8 @@ def measure_config(w, iters=10, warmup=3):
     med, mean = time_calls(lambda: fa.fwd(q, k, v, causal=w.causal, window=w.window, scale=w.scale, out=o, lse=lse),
                            iters, warmup)
     tf = ff / (med * 1e-3) / 1e12
-    r = {"shape": f"B{w.B} Hq{w.Hq} Hkv{w.Hkv} L{w.L} d{w.d}", "dtype": "f32" if fp32 else "bf16",
+    dname = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}[w.dtype]
+    r = {"shape": f"B{w.B} Hq{w.Hq} Hkv{w.Hkv} L{w.L} d{w.d}", "dtype": dname,
          "causal": w.causal, "window": w.window,
          "fwd": {"ms_median": round(med, 4), "ms_mean": round(mean, 4), "tflop": ff / 1e12,
                  "tflops": round(tf, 2), "peak_tflops": peak, "frac_peak": round(tf / peak, 4),
@@ -212,6 +213,36 @@ def measure_decode(B=8, Hq=32, Hkv=8, Lq=1, Lk=32768, d=128, iters=20, warmup=5)
             "ms_median": round(med, 4), "ms_mean": round(mean, 4), "cache_bytes": cache_bytes,
             "hbm_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS, "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
             "workspace_bytes": int(ws.numel()), "data": "synthetic N(0,1), generated on the device"}
+
+
+def measure_autograd(iters=10, warmup=3):
+    """The differentiable drop-in on the headline shape: scaled_dot_product_attention
+    (forward, then backward through autograd) against the same two calls made directly,
+    so the difference is what the autograd route adds."""
+    import torch
+    import exact_tiled_attention_flash_amd as fa
+    import workloads as W
+    w = W.LLAMA7B_CAUSAL
+    dev = torch.device("cuda:0")
+    q, k, v, do = (t.to(dev) for t in W.make_inputs(w, with_dout=True))
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+
+    def through_autograd():
+        o = fa.scaled_dot_product_attention(qa, ka, va, is_causal=True)
+        o.backward(do)
+        qa.grad = ka.grad = va.grad = None
+
+    def direct():
+        o, lse = fa.fwd(q, k, v, causal=True)
+        fa.bwd(q, k, v, o, lse, do, causal=True)
+
+    amed, _ = time_calls(through_autograd, iters, warmup)
+    dmed, _ = time_calls(direct, iters, warmup)
+    flops = fwd_flops(w.B, w.Hq, w.L, w.d, True, 0) * 3.5
+    return {"shape": "B2 H32 L4096 d128 causal bf16 (forward + backward)",
+            "autograd_ms": round(amed, 4), "direct_ms": round(dmed, 4),
+            "autograd_tflops": round(flops / (amed * 1e-3) / 1e12, 2),
+            "overhead_frac": round(amed / dmed - 1.0, 4)}
 
 
 def measure_ring(iters=10, warmup=3):
@@ -448,6 +479,9 @@ def main():
     }
     if not args.no_configs:
         out["configs"] = {wl.name: measure_config(wl) for wl in W.ALL}
+        f16 = W.LLAMA7B_CAUSAL.with_(name="llama7b-layer B2 H32 L4096 d128 causal fp16", dtype=torch.float16)
+        out["configs"][f16.name] = measure_config(f16)
+        out["autograd"] = measure_autograd()
         out["decode"] = measure_decode()
         out["ring"] = measure_ring()
         out["sparse"] = measure_sparse()
