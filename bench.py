@@ -287,25 +287,28 @@ def measure_ring(iters=10, warmup=3):
     return out
 
 
-def measure_sparse(iters=5, warmup=2):
-    """General sparse mask: the hybrid configuration (window reaching 512 positions
-    both ways, first and last token global, 131072 tokens, batch 2) on 32 heads of
-    128, forward and backward under one mask plan.
+def measure_sparse(iters=5, warmup=2, block_band=False):
+    """General sparse mask, forward and backward under one mask plan: by default the
+    hybrid configuration (window reaching 512 positions both ways, first and last
+    token global, 131072 tokens, batch 2) on 32 heads of 128; with `block_band` the
+    banded block-sparse mask (blocks of 128, radius 1) at the same size.
 
     Reported as effective TFLOP/s over the allowed pairs only (4 d flops per pair
     forward, 2.5x that backward): the work the mask leaves is the algorithmic work."""
     import torch
     import exact_tiled_attention_flash_amd as fa
     import workloads as W
-    w = W.HYBRID_SPARSE_128K
+    w = W.BLOCK_BAND_128K if block_band else W.HYBRID_SPARSE_128K
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev).manual_seed(w.seed)
     q, k, v, do = (torch.randn(w.B, h, w.L, w.d, generator=g, device=dev).to(w.dtype)
                    for h in (w.Hq, w.Hkv, w.Hkv, w.Hq))
+    bm = fa.block_band_mask(w.L, W.BLOCK_BAND_BLOCK, W.BLOCK_BAND_RADIUS) if block_band else None
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     s0.record()
-    plan = fa.MaskPlan(w.L, causal=w.causal, window=w.window, global_tokens=w.global_tokens, device=dev)
+    plan = fa.MaskPlan(w.L, causal=w.causal, window=w.window, global_tokens=w.global_tokens, block_mask=bm,
+                       block=W.BLOCK_BAND_BLOCK, device=dev)
     s1.record()
     torch.cuda.synchronize()
     plan_ms = s0.elapsed_time(s1)
@@ -323,8 +326,10 @@ def measure_sparse(iters=5, warmup=2):
     ff = 4.0 * w.d * pairs * w.B * w.Hq
     bf = 2.5 * ff
     ftf, btf = ff / (fmed * 1e-3) / 1e12, bf / (bmed * 1e-3) / 1e12
+    mask_desc = (f"band of radius {W.BLOCK_BAND_RADIUS} over {W.BLOCK_BAND_BLOCK}-token blocks" if block_band
+                 else None)
     out = {"workload": w.name, "mask": {"causal": w.causal, "window": w.window,
-                                        "global_tokens": list(w.global_tokens), "block_mask": None},
+                                        "global_tokens": list(w.global_tokens), "block_mask": mask_desc},
            "allowed_pairs": pairs, "pairs_per_row": round(pairs / w.L, 2), "density": pairs / float(w.L) ** 2,
            "plan_ms": round(plan_ms, 3), "plan_bytes": int(plan.plan.numel()),
            "fwd": {"ms_median": round(fmed, 4), "ms_mean": round(fmean, 4), "tflop": ff / 1e12,
@@ -366,7 +371,9 @@ def main():
     fa.library()
     dev = torch.device("cuda:0")
     if args.sparse_only:
-        print(json.dumps({"sparse": measure_sparse(iters=args.steps, warmup=args.warmup)}), flush=True)
+        print(json.dumps({"sparse": measure_sparse(iters=args.steps, warmup=args.warmup),
+                          "sparse_block": measure_sparse(iters=args.steps, warmup=args.warmup, block_band=True)}),
+              flush=True)
         return
     if args.ring_only:
         print(json.dumps({"ring": measure_ring(iters=args.steps, warmup=args.warmup)}), flush=True)
@@ -485,6 +492,7 @@ def main():
         out["decode"] = measure_decode()
         out["ring"] = measure_ring()
         out["sparse"] = measure_sparse()
+        out["sparse_block"] = measure_sparse(block_band=True)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

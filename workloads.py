@@ -61,6 +61,14 @@ ALL = [TINY_FP32, LLAMA7B_CAUSAL, GQA_16K, WINDOW_32K, LONG_FWD_128K, LONG_BWD_8
 # 512 positions before and after each position, i.e. |i - j| < 513, the first
 # and last token global, sequences of 131072 tokens, batch 2) on the
 # llama7b-shaped heads (32 heads of 128).
+# kler.cn §4.1.2's block-sparse pattern at full length: blocks of 128 tokens, each
+# query block attending to its own and the two neighbouring key blocks (the
+# banded block mask, radius 1), non-causal, on the same heads.
+BLOCK_BAND_128K = Workload("block-band B2 H32 L131072 d128 block128 radius1 bf16", 2, 32, 32, 131072, 128,
+                           torch.bfloat16, False, 0, seed=7, backward=True)
+BLOCK_BAND_BLOCK = 128
+BLOCK_BAND_RADIUS = 1
+
 HYBRID_SPARSE_128K = Workload("hybrid-sparse B2 H32 L131072 d128 window513 global[0,-1] bf16", 2, 32, 32, 131072,
                               128, torch.bfloat16, False, 513, seed=6, backward=True, global_tokens=(0, -1))
 
