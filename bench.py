@@ -59,12 +59,24 @@ def fwd_bytes(B, Hq, Hkv, L, d, elt=2):
     return (B * Hq * L * d + 2 * B * Hkv * L * d) * elt + B * Hq * L * d * elt + B * Hq * L * 4
 
 
-def kernel_source_digest():
+# The sources each timed kernel is compiled from: a counter reading stays valid
+# while these files are unchanged.
+KERNEL_SOURCES = {
+    "fwd_bf16_kernel<128,causal>": ("fa_fwd_bf16.hip", "fa_fwd_tile.hpp", "fa_common.hpp", "fa_kernels.h"),
+    "bwd_dkdv_kernel<128,causal>": ("fa_bwd_bf16.hip", "fa_bwd_tile.hpp", "fa_common.hpp", "fa_kernels.h"),
+    "bwd_dq_kernel<128,causal>": ("fa_bwd_bf16.hip", "fa_bwd_tile.hpp", "fa_common.hpp", "fa_kernels.h"),
+    "bwd_delta_kernel<128>": ("fa_bwd_bf16.hip", "fa_bwd_tile.hpp", "fa_common.hpp", "fa_kernels.h"),
+}
+
+
+def kernel_source_digest(kernel_key=None):
+    """Digest of the kernel sources: those of one timed kernel, or all of them."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "exact_tiled_attention_flash_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".hpp", ".h")):
-            h.update(open(os.path.join(csrc, f), "rb").read())
+    names = KERNEL_SOURCES[kernel_key] if kernel_key else sorted(
+        f for f in os.listdir(csrc) if f.endswith((".hip", ".hpp", ".h")))
+    for f in names:
+        h.update(open(os.path.join(csrc, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -76,7 +88,7 @@ def load_traffic(kernel_key):
     try:
         data = json.load(open(p))
         ent = data.get(kernel_key)
-        if not ent or ent.get("source_digest") != kernel_source_digest():
+        if not ent or ent.get("source_digest") != kernel_source_digest(kernel_key):
             return None
         return float(ent["bytes_per_launch"])
     except Exception:
