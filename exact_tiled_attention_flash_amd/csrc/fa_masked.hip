@@ -11,17 +11,21 @@
 // last token global).  The masked positions are exactly excluded, so the
 // result is exact attention over the allowed pairs.
 //
-// 1. Plan (three small kernels, once per mask and length; reused by every
-//    head, layer and by the backward): the global positions become a bitmap,
-//    every 64 x 64 block of the L x L mask is classified as empty, partial or
-//    full from interval arithmetic on its corners, and every work-group row
-//    (128 queries) and column (128 keys) gets the compact, ascending list of
-//    the 64-wide tiles it must visit.  Work-groups are then ordered heaviest
-//    first: a global row visits every tile and must not start last.
+// 1. Plan (four small kernels, once per mask and length; reused by every
+//    head, layer and by the backward): the global positions become a bitmap
+//    and a sorted list, every 64 x 64 block of the L x L mask is classified as
+//    empty, partial or full from interval arithmetic on its corners, and
+//    every work-group row (128 queries) and column (128 keys) gets the
+//    compact, ascending list of the 64-wide tiles it must visit, ordered
+//    heaviest first.
 // 2. Attention: the range-tiled kernels' tile steps, unchanged, iterate over
 //    the lists instead of an index range.  Full tiles run unmasked; partial
 //    tiles evaluate the mask per element (window, causal, block bit and the
 //    global bits of the tile); empty tiles are never loaded.
+// 3. Global positions are whole rows and columns of the mask.  The row lists
+//    leave global query rows out and the column lists leave global keys out;
+//    split passes over the whole sequence compute those rows and keys
+//    (section 3 below), so no work-group has to walk a whole row.
 #include "fa_bwd_tile.hpp"
 #include "fa_fwd_tile.hpp"
 

@@ -267,8 +267,10 @@ typedef struct fa_mask {
 /*
  * flash_attn_mask_plan: classifies every 64 x 64 block of the mask (empty,
  * partial or full) and writes, into the caller's device buffer `plan`, the
- * tile lists and the work-group order the masked kernels follow.  Runs three
- * small kernels on `stream`; reads the mask's device arrays there.  A plan
+ * tile lists, the global positions and the work-group order the masked
+ * kernels follow.  Runs four small kernels on `stream`; reads the mask's
+ * device arrays there.  Plan contents are clamped when used, so a buffer that
+ * never held a plan gives wrong results but no out-of-bounds access.  A plan
  * depends on the mask and L only: build it once and pass it to every masked
  * call (every head, layer, forward and backward) with that same mask and L.
  * 1 <= L <= 2^18 (FA_ERR_UNSUPPORTED above).  plan: at least
