@@ -40,9 +40,16 @@ size_t workspace_bytes(int B, int Hq, int L) {
   return (raw + 255) & ~(size_t)255;
 }
 
-// Chunk positions: offsets are non-negative and at most 2^30, so every
-// position (offset + index < 2^30 + 2^23) fits an int.
-constexpr int kMaxOffset = 1 << 30;
+// Chunk positions: offsets are non-negative and at most 2^29, so every
+// position (offset + index < 2^29 + 2^23) and every distance between a query
+// and a key position stays below 2^30.
+constexpr int kMaxOffset = 1 << 29;
+
+// A window of 2^30 or more admits every pair (all distances are below 2^30)
+// and is passed to the kernels as "no window"; smaller windows keep every
+// position +- window expression of the kernels inside an int.
+constexpr int kWindowNone = 1 << 30;
+int norm_window(int w) { return w >= kWindowNone ? 0 : w; }
 
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int Lq,
                int Lk, int d, float softmax_scale, int causal, int window, int q_offset, int k_offset, int dtype,
@@ -62,7 +69,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = Lq; a.d = d;
   a.Lk = Lk;
   a.shift = q_offset - k_offset;
-  a.window = window;
+  a.window = norm_window(window);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.f16 = dtype == FA_DTYPE_F16;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -107,7 +114,7 @@ int bwd_setup(fa::BwdArgs& a, const void* workspace, size_t ws_bytes, int B, int
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.d = d;
   a.Lk = L;
   a.shift = 0;
-  a.window = window;
+  a.window = norm_window(window);
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.f16 = dtype == FA_DTYPE_F16;
@@ -244,7 +251,7 @@ extern "C" int flash_attn_decode(const void* q, const void* k_cache, const void*
   if (rc != FA_OK) return rc;
   if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
   if ((causal != 0 && causal != 1) || window < 0) return FA_ERR_INVALID_ARG;
-  if (window > 0 && !causal) return FA_ERR_UNSUPPORTED;
+  if (norm_window(window) > 0 && !causal) return FA_ERR_UNSUPPORTED;
   if (!all_aligned({q, k_cache, v_cache, o})) return FA_ERR_INVALID_ARG;
   if ((lse && !aligned16(lse)) || (reinterpret_cast<uintptr_t>(cache_len) & 3u) != 0) return FA_ERR_INVALID_ARG;
   if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
@@ -256,7 +263,7 @@ extern "C" int flash_attn_decode(const void* q, const void* k_cache, const void*
   a.part_o = static_cast<float*>(workspace);
   a.part_lse = a.part_o + (size_t)ns * (size_t)a.rows * d;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.Lq = Lq; a.Lk = Lk; a.d = d;
-  a.window = window;
+  a.window = norm_window(window);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.f16 = dtype == FA_DTYPE_F16;
   a.n_splits = ns;
@@ -302,7 +309,7 @@ extern "C" int flash_attn_mask_plan(const fa_mask* mask, int L, void* plan, size
   if (rc != FA_OK) return rc;
   fa::MaskDesc m{};
   m.causal = mask->causal;
-  m.window = mask->window;
+  m.window = norm_window(mask->window);
   m.global_pos = mask->n_global > 0 ? mask->global_pos : nullptr;
   m.n_global = mask->n_global;
   m.block_mask = mask->block_mask;
@@ -365,7 +372,7 @@ extern "C" int flash_attn_fwd_masked(const void* q, const void* k, const void* v
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L; a.d = d;
   a.Lk = L;
   a.shift = 0;
-  a.window = mask->window;
+  a.window = norm_window(mask->window);
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
   a.f16 = dtype == FA_DTYPE_F16;
   if (w.rows.ngp > 0) {

@@ -79,7 +79,8 @@ extern "C" {
  *   softmax_scale                   : s > 0 and finite (usually 1/sqrt(d))
  *   causal                          : 0 or 1
  *   window                          : 0 = none; w >= 1 (one-sided with causal,
- *                                     symmetric without)
+ *                                     symmetric without); every w >= 2^30
+ *                                     admits all pairs and acts as none
  *   dtype                           : FA_DTYPE_BF16, FA_DTYPE_F16 or
  *                                     FA_DTYPE_F32, each with d in {64,128}
  * Sizes: 1 <= L <= 2^23 (one head must stay below 4 GiB), B, Hq, Hkv >= 1.
@@ -152,7 +153,7 @@ int flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* d
  * k_offset .. k_offset + Lk - 1; causal and window masks are decided on those
  * positions.  Layouts are the ones above with L replaced by Lq for Q, O, dO,
  * dQ, LSE and by Lk for K, V, dK, dV.  16-bit dtypes only (FA_DTYPE_F32
- * returns FA_ERR_UNSUPPORTED); 0 <= q_offset, k_offset <= 2^30 and
+ * returns FA_ERR_UNSUPPORTED); 0 <= q_offset, k_offset <= 2^29 and
  * 1 <= Lq, Lk <= 2^23, else FA_ERR_INVALID_ARG.
  *
  * flash_attn_fwd_block: attention of the query chunk to this key/value chunk

@@ -156,7 +156,8 @@ def test_chunk_and_merge_entry_points_reject_invalid_arguments(lib):
         return lib.flash_attn_fwd_block(q, FAKE, FAKE, FAKE, FAKE, 1, 2, Hkv, Lq, Lk, d, 0.125, causal, window,
                                         qo, ko, dt, None)
     assert fb(q=None) == INV and fb(Lk=0) == INV and fb(Lq=0) == INV
-    assert fb(qo=-1) == INV and fb(ko=(1 << 30) + 1) == INV and fb(Lk=(1 << 23) + 1) == INV
+    assert fb(qo=-1) == INV and fb(ko=(1 << 29) + 1) == INV and fb(qo=(1 << 29) + 1) == INV
+    assert fb(Lk=(1 << 23) + 1) == INV
     assert fb(dt=fa.FA_DTYPE_F32) == UNS and fb(dt=3) == UNS and fb(d=96) == UNS
     assert fb(causal=0, window=2, q=None) == INV and fb(Hkv=3) == GQA
     assert fb(dt=fa.FA_DTYPE_F16, q=None) == INV                     # fp16 passes the dtype check

@@ -165,3 +165,14 @@ def test_backward_is_deterministic():
     b = gpu_fwd_bwd(w, q, k, v, do)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_huge_window_backward_equals_no_window():
+    # a window >= 2^30 admits every pair: gradients equal the no-window call's
+    w = W.small("huge-window-bwd", 1, 2, 2, 300, 64, seed=221, backward=True)
+    q, k, v, do = W.make_inputs(w, with_dout=True)
+    for causal in (False, True):
+        a = gpu_fwd_bwd(w.with_(causal=causal, window=0), q, k, v, do)
+        b = gpu_fwd_bwd(w.with_(causal=causal, window=2**31 - 1), q, k, v, do)
+        for x, y in zip(a, b):
+            assert torch.equal(x, y), causal

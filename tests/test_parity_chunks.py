@@ -188,3 +188,26 @@ def test_ring_at_the_llama7b_shape_matches_whole_sequence_call():
     ref = oracle.backward(*(f64(t[sl]) for t in (q, k, v, do)), w.scale, True, 0)
     errs = [rel(x[sl], r) for x, r in zip((dq, dk, dv), ref)]
     assert max(errs) <= 2e-2
+
+
+def test_chunk_pair_at_the_largest_offsets():
+    # only q_offset - k_offset enters the masks: a pair placed at the top of the
+    # offset range (2^29) gives the bits of the same pair near position 0, for the
+    # forward and the backward, with a window that reaches across the pair (every
+    # query row keeps at least one allowed key)
+    B, Hq, Hkv, Lq, Lk, d = 1, 4, 2, 128, 160, 64
+    dev = "cuda:0"
+    q = draw((B, Hq, Lq, d), 301, torch.bfloat16).to(dev)
+    k = draw((B, Hkv, Lk, d), 302, torch.bfloat16).to(dev)
+    v = draw((B, Hkv, Lk, d), 303, torch.bfloat16).to(dev)
+    do = draw((B, Hq, Lq, d), 304, torch.bfloat16).to(dev)
+    top = 1 << 29
+    for causal, window in ((True, 100), (False, 90), (True, 0)):
+        res = []
+        for qo, ko in ((100, 0), (top, top - 100)):
+            o, lse = fa().fwd_block(q, k, v, causal=causal, window=window, q_offset=qo, k_offset=ko)
+            g = fa().bwd_block(q, k, v, o, lse, do, causal=causal, window=window, q_offset=qo, k_offset=ko)
+            torch.cuda.synchronize()
+            res.append([o.cpu(), lse.cpu()] + [x.cpu() for x in g])
+        for x, y in zip(*res):
+            assert torch.equal(x, y), (causal, window)

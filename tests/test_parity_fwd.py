@@ -189,3 +189,16 @@ def test_rows_of_probabilities_sum_to_one_via_lse():
     mask = torch.ones(300, 300, dtype=torch.bool).tril()
     P = torch.exp(S - lse.double()[..., None]).masked_fill(~mask, 0.0)
     assert torch.allclose(P.sum(-1), torch.ones(1, 2, 300, dtype=torch.float64), atol=1e-3)
+
+
+def test_huge_window_admits_every_pair():
+    # every window >= 2^30 admits all pairs (no two positions are that far apart),
+    # so it must give exactly the no-window result -- also for windows near
+    # INT_MAX, where i + w would not fit an int
+    w = W.small("huge-window", 1, 2, 2, 400, 64, seed=123)
+    q, k, v, _ = W.make_inputs(w, with_dout=False)
+    for causal in (False, True):
+        o0, l0 = gpu_fwd(w.with_(causal=causal, window=0), q, k, v)
+        for win in (1 << 30, 2**31 - 1):
+            o1, l1 = gpu_fwd(w.with_(causal=causal, window=win), q, k, v)
+            assert torch.equal(o0, o1) and torch.equal(l0, l1), (causal, win)

@@ -204,7 +204,9 @@ def test_plan_blocks_match_oracle_mask(case):
 def test_plan_of_plain_masks_reproduces_range_kernels_bitwise():
     """A plan holding only causal / window masks visits the same tiles in the same
     order with the same tile steps as the range-tiled kernels: identical bits."""
-    for causal, window, L, d in ((True, 0, 1000, 128), (True, 100, 777, 64), (False, 33, 900, 128)):
+    # (the last case: a window near INT_MAX admits every pair on both paths)
+    for causal, window, L, d in ((True, 0, 1000, 128), (True, 100, 777, 64), (False, 33, 900, 128),
+                                 (False, 2**31 - 1, 640, 64)):
         w = W.small("plain plan", 1, 4, 2, L, d, causal=causal, window=window, seed=720, backward=True)
         q, k, v, do = (t.to(DEV) for t in W.make_inputs(w, with_dout=True))
         plan = fa().MaskPlan(L, causal=causal, window=window, device=DEV)
