@@ -1,8 +1,8 @@
 """Seeded random parity cases across the GPU paths -- whole-sequence forward and
 backward, ring chunk pairs, general masks, decode -- against the fp64 oracle.
 
-Each case draws its sizes from a fixed seed (ragged lengths, offsets, windows,
-GQA ratios, dtypes, block patterns, global positions), so the set is the same
+Each case draws its sizes from a fixed seed (ragged lengths, offsets up to 2^29,
+windows up to INT_MAX, GQA ratios, dtypes, block patterns, global positions), so the set is the same
 on every run and a failing case is named by its index and parameters.
 Tolerances as everywhere: O max-abs 2e-2, LSE max-abs 1e-3 (rows with no allowed
 key exactly O = 0, LSE = -inf), gradients relative L2 2e-2.
@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
 KINDS = ("range", "chunk", "mask", "decode")
-N_CASES = 40
+N_CASES = 60
 
 
 def fa():
@@ -49,7 +49,7 @@ def case_params(i):
     p = dict(kind=KINDS[i % len(KINDS)], seed=rng.randrange(1 << 20),
              dt=rng.choice([torch.bfloat16, torch.float16]), d=rng.choice([64, 128]),
              G=rng.choice([1, 2, 4]), Hkv=rng.choice([1, 2]), B=rng.choice([1, 2]),
-             causal=rng.random() < 0.6, window=rng.choice([0, 0, 1, 7, 65, 300]))
+             causal=rng.random() < 0.6, window=rng.choice([0, 0, 1, 7, 65, 300, 1 << 30, 2**31 - 1]))
     p["Hq"] = p["G"] * p["Hkv"]
     if p["kind"] == "range":
         p["L"] = rng.randrange(1, 900)
@@ -57,6 +57,9 @@ def case_params(i):
         p["Lq"], p["Lk"] = rng.randrange(1, 500), rng.randrange(1, 500)
         p["ko"] = rng.randrange(0, 900)
         p["qo"] = max(0, p["ko"] + rng.randrange(-300, 600))
+        if rng.random() < 0.3:             # near the top of the offset range (2^29)
+            p["ko"] += (1 << 29) - 2000
+            p["qo"] += (1 << 29) - 2000
     elif p["kind"] == "mask":
         p["L"] = rng.randrange(2, 1400)
         p["blk"] = rng.choice([64, 128, 192])
