@@ -367,6 +367,8 @@ def main():
                     help="only the general-mask workload (for profiling its kernels); prints its JSON")
     ap.add_argument("--ring-only", action="store_true",
                     help="only the ring-attention chunk-pair workload; prints its JSON")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="only the KV-cache decode workload; prints its JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (3x), so that HBM counters "
                          "(FETCH_SIZE/WRITE_SIZE) can be scaled against a kernel of known traffic")
@@ -389,6 +391,9 @@ def main():
         return
     if args.ring_only:
         print(json.dumps({"ring": measure_ring(iters=args.steps, warmup=args.warmup)}), flush=True)
+        return
+    if args.decode_only:
+        print(json.dumps({"decode": measure_decode(iters=args.steps, warmup=args.warmup)}), flush=True)
         return
     if args.calibrate_copy:
         src = torch.ones(64 * 2**20, dtype=torch.float32, device=dev)    # 256 MiB
