@@ -42,10 +42,18 @@ PEAK_BF16_AT_MEASURED_CLOCK_TFLOPS = PEAK_BF16_TFLOPS * MEASURED_MFMA_CLOCK_GHZ 
 METRIC = "attention fwd/bwd TFLOP/s + % bf16 MFMA peak, B2 H32 L4096 d128 causal"
 
 
+def window_pairs(L, w, causal):
+    """Allowed (query, key) pairs of one L x L head under a window w >= 1: one-sided
+    (keys i-w+1..i) with causal, |i - j| < w without."""
+    w = min(int(w), int(L))
+    one_sided = w * L - w * (w - 1) // 2
+    return one_sided if causal else 2 * one_sided - L
+
+
 def fwd_flops(B, Hq, L, d, causal, window):
+    """4*d flops per allowed (query, key) pair: the two products S = QK^T and P.V."""
     if window and window > 0:
-        w = min(window, L)
-        return 4.0 * B * Hq * d * (w * L - w * (w - 1) / 2)
+        return 4.0 * B * Hq * d * window_pairs(L, window, causal)
     full = 4.0 * B * Hq * L * L * d
     return full / 2 if causal else full
 
@@ -57,6 +65,52 @@ def bwd_flops(B, Hq, L, d, causal, window):
 def fwd_bytes(B, Hq, Hkv, L, d, elt=2):
     """Algorithmic HBM bytes of one forward: Q, K, V read once; O and LSE written."""
     return (B * Hq * L * d + 2 * B * Hkv * L * d) * elt + B * Hq * L * d * elt + B * Hq * L * 4
+
+
+def allowed_pairs(L, causal=False, window=0, global_tokens=(), block_mask=None, block=64):
+    """Number of allowed (query, key) pairs of the general mask over one sequence of
+    length L (the same rule as ``MaskPlan``): the algorithmic work of one head is
+    4 * d * allowed_pairs flops forward.  Counted on the host: per row in interval form
+    without a block mask, else over row chunks of the boolean mask."""
+    import torch
+    L = int(L)
+    glob = sorted({(p + L if p < 0 else p) for p in global_tokens if -L <= p < L})
+    if block_mask is None:
+        # interval form: row i's local keys are one interval [lo, hi]; the global
+        # keys outside it (and visible under the causal mask) are added, and a
+        # global row sees every visible key
+        i = torch.arange(L, dtype=torch.int64)
+        hi = i.clone() if causal else torch.full((L,), L - 1, dtype=torch.int64)
+        lo = torch.zeros(L, dtype=torch.int64)
+        if window > 0:
+            lo = (i - window + 1).clamp_min(0)
+            if not causal:
+                hi = (i + window - 1).clamp_max(L - 1)
+        g = torch.tensor(glob, dtype=torch.int64)
+        inside = torch.searchsorted(g, hi, right=True) - torch.searchsorted(g, lo, right=False)
+        visible = torch.searchsorted(g, i, right=True) if causal else torch.full((L,), len(glob), dtype=torch.int64)
+        count = hi - lo + 1 + visible - inside
+        if glob:
+            count[g] = (g + 1) if causal else L
+        return int(count.sum())
+    is_g = torch.zeros(L, dtype=torch.bool)
+    if glob:
+        is_g[torch.tensor(glob)] = True
+    bm = torch.as_tensor(block_mask).bool().cpu()
+    total = 0
+    chunk = max(1, (1 << 24) // L)
+    j = torch.arange(L)
+    for r0 in range(0, L, chunk):
+        i = torch.arange(r0, min(L, r0 + chunk))[:, None]
+        local = torch.ones(i.shape[0], L, dtype=torch.bool)
+        if window > 0:
+            local &= (i - j[None, :]).abs() < window
+        local &= bm[(i // block), (j // block)[None, :]]
+        ok = local | is_g[i] | is_g[None, :]
+        if causal:
+            ok &= j[None, :] <= i
+        total += int(ok.sum())
+    return total
 
 
 # The sources each timed kernel is compiled from: a counter reading stays valid
@@ -315,7 +369,7 @@ def measure_sparse(iters=5, warmup=2, block_band=False):
     g = torch.Generator(device=dev).manual_seed(w.seed)
     q, k, v, do = (torch.randn(w.B, h, w.L, w.d, generator=g, device=dev).to(w.dtype)
                    for h in (w.Hq, w.Hkv, w.Hkv, w.Hq))
-    bm = fa.block_band_mask(w.L, W.BLOCK_BAND_BLOCK, W.BLOCK_BAND_RADIUS) if block_band else None
+    bm = W.block_band_mask(w.L, W.BLOCK_BAND_BLOCK, W.BLOCK_BAND_RADIUS) if block_band else None
     s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     s0.record()
@@ -324,7 +378,7 @@ def measure_sparse(iters=5, warmup=2, block_band=False):
     s1.record()
     torch.cuda.synchronize()
     plan_ms = s0.elapsed_time(s1)
-    pairs = plan.allowed_pairs()
+    pairs = allowed_pairs(w.L, w.causal, w.window, w.global_tokens, bm, W.BLOCK_BAND_BLOCK)
     o, lse = torch.empty_like(q), torch.empty(w.B, w.Hq, w.L, dtype=torch.float32, device=dev)
     fws = fa.masked_workspace_bytes(w.B, w.Hq, w.Hkv, w.L, w.d, plan, False)
     bws = fa.masked_workspace_bytes(w.B, w.Hq, w.Hkv, w.L, w.d, plan, True)

@@ -22,7 +22,7 @@ import torch
 
 __all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "fwd_block", "bwd_block", "merge",
            "decode", "decode_workspace_bytes",
-           "MaskPlan", "fwd_masked", "bwd_masked", "masked_workspace_bytes", "block_band_mask", "allowed_pairs",
+           "MaskPlan", "fwd_masked", "bwd_masked", "masked_workspace_bytes",
            "strerror", "library", "library_path",
            "FlashAttentionFunction", "scaled_dot_product_attention",
            "FA_DTYPE_F32", "FA_DTYPE_BF16", "FA_DTYPE_F16", "EXPORTED_SYMBOLS"]
@@ -127,6 +127,55 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
+def _expect(t, name, shape, dtype, device):
+    """Check a caller-supplied tensor before its pointer crosses the C ABI, which
+    cannot see sizes: a wrong shape, dtype, device or layout raises ValueError."""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a tensor" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda or t.device != device:
+        raise ValueError("%s must be on %s" % (name, device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _workspace(ws, nbytes, device, name="workspace"):
+    """A caller's workspace: a contiguous uint8 tensor on the device holding at least nbytes."""
+    if ws is None:
+        return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise ValueError("%s must be a 1-D uint8 tensor" % name)
+    if not ws.is_cuda or ws.device != device or not ws.is_contiguous():
+        raise ValueError("%s must be a contiguous tensor on %s" % (name, device))
+    if ws.numel() < nbytes:
+        raise ValueError("%s holds %d bytes, %d needed" % (name, ws.numel(), nbytes))
+    return ws
+
+
+_INT_MAX = 2**31 - 1
+_MAX_OFFSET = 2**29
+
+
+def _window(window):
+    """The window as the C int the boundary takes (0 = none).  Windows of 2^30 and
+    more admit every pair of positions the boundary accepts, so they are passed as 0."""
+    w = int(window)
+    if w < 0:
+        raise ValueError("window must be >= 0, got %d" % w)
+    return 0 if w >= 2**30 else w
+
+
+def _offset(x, name):
+    x = int(x)
+    if not 0 <= x <= _MAX_OFFSET:
+        raise ValueError("%s must be in [0, 2^29], got %d" % (name, x))
+    return x
+
+
 def _shapes(q, k, v):
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be [B, H, L, d]")
@@ -134,11 +183,25 @@ def _shapes(q, k, v):
     if k.shape != v.shape or k.shape[0] != B or k.shape[2] != L or k.shape[3] != d:
         raise ValueError("k and v must be [B, Hkv, L, d] matching q")
     for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
-            raise ValueError("q, k, v must be contiguous CUDA tensors of one dtype")
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous tensors of one dtype on one GPU")
     if q.dtype not in _DTYPES:
         raise ValueError("dtype must be float32, bfloat16 or float16")
     return B, Hq, k.shape[1], L, d
+
+
+def _out(t, name, shape, dtype, device):
+    """An output buffer: allocated when not given, else checked."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _expect(t, name, shape, dtype, device)
+
+
+def _scale(scale, d):
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if not (scale > 0.0 and math.isfinite(scale)):
+        raise ValueError("scale must be positive and finite")
+    return scale
 
 
 def fwd(q, k, v, causal=False, window=0, scale=None, out=None, lse=None):
@@ -149,13 +212,11 @@ def fwd(q, k, v, causal=False, window=0, scale=None, out=None, lse=None):
     ``scale`` defaults to 1/sqrt(d).
     """
     B, Hq, Hkv, L, d = _shapes(q, k, v)
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device)
+    scale, window = _scale(scale, d), _window(window)
+    out = _out(out, "out", q.shape, q.dtype, q.device)
+    lse = _out(lse, "lse", (B, Hq, L), torch.float32, q.device)
     rc = library().flash_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
-                                  B, Hq, Hkv, L, d, scale, int(bool(causal)), int(window),
+                                  B, Hq, Hkv, L, d, scale, int(bool(causal)), window,
                                   _DTYPES[q.dtype], _stream(q))
     _check(rc, "flash_attn_fwd")
     return out, lse
@@ -163,6 +224,22 @@ def fwd(q, k, v, causal=False, window=0, scale=None, out=None, lse=None):
 
 def bwd_workspace_bytes(B, Hq, Hkv, L, d, dtype=torch.bfloat16):
     return int(library().flash_attn_bwd_workspace_bytes(B, Hq, Hkv, L, d, _DTYPES[dtype]))
+
+
+def _bwd_buffers(q, k, v, o, lse, dout, Lq, workspace, dq, dk, dv):
+    """Checks the backward's tensors (Lq query rows) and allocates the missing outputs."""
+    B, Hq = q.shape[0], q.shape[1]
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(dout, "dout", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, Hq, Lq), torch.float32, q.device)
+    nbytes = bwd_workspace_bytes(B, Hq, k.shape[1], Lq, q.shape[3], q.dtype)
+    if nbytes == 0:
+        raise RuntimeError("flash_attn_bwd: unsupported sizes")
+    workspace = _workspace(workspace, nbytes, q.device)
+    dq = _out(dq, "dq", q.shape, q.dtype, q.device)
+    dk = _out(dk, "dk", k.shape, k.dtype, k.device)
+    dv = _out(dv, "dv", v.shape, v.dtype, v.device)
+    return workspace, dq, dk, dv
 
 
 def bwd(q, k, v, o, lse, dout, causal=False, window=0, scale=None, workspace=None,
@@ -173,21 +250,11 @@ def bwd(q, k, v, o, lse, dout, causal=False, window=0, scale=None, workspace=Non
     device uint8 tensor of at least ``bwd_workspace_bytes(...)`` bytes.
     """
     B, Hq, Hkv, L, d = _shapes(q, k, v)
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    for t in (o, dout):
-        if t.shape != q.shape or t.dtype != q.dtype or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError("o and dout must match q")
-    if lse.shape != (B, Hq, L) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be contiguous float32 [B, Hq, L]")
-    nbytes = bwd_workspace_bytes(B, Hq, Hkv, L, d, q.dtype)
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    scale, window = _scale(scale, d), _window(window)
+    workspace, dq, dk, dv = _bwd_buffers(q, k, v, o, lse, dout, L, workspace, dq, dk, dv)
     rc = library().flash_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
-                                  B, Hq, Hkv, L, d, scale, int(bool(causal)), int(window),
+                                  B, Hq, Hkv, L, d, scale, int(bool(causal)), window,
                                   _DTYPES[q.dtype], _stream(q))
     _check(rc, "flash_attn_bwd")
     return dq, dk, dv
@@ -199,25 +266,20 @@ def bwd_stages(q, k, v, o, lse, dout, causal=False, window=0, scale=None, worksp
     current stream; same results as ``bwd``.  ``between(stage_name)`` is called
     after each launch (for example to record timing events)."""
     B, Hq, Hkv, L, d = _shapes(q, k, v)
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    nbytes = bwd_workspace_bytes(B, Hq, Hkv, L, d, q.dtype)
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    scale, window = _scale(scale, d), _window(window)
+    workspace, dq, dk, dv = _bwd_buffers(q, k, v, o, lse, dout, L, workspace, dq, dk, dv)
     lib, dt, st, c = library(), _DTYPES[q.dtype], _stream(q), int(bool(causal))
     _check(lib.flash_attn_bwd_preprocess(_ptr(o), _ptr(lse), _ptr(dout), _ptr(workspace), workspace.numel(),
                                          B, Hq, Hkv, L, d, dt, st), "flash_attn_bwd_preprocess")
     if between:
         between("preprocess")
     _check(lib.flash_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(workspace), workspace.numel(),
-                                   _ptr(dk), _ptr(dv), B, Hq, Hkv, L, d, scale, c, int(window), dt, st),
+                                   _ptr(dk), _ptr(dv), B, Hq, Hkv, L, d, scale, c, window, dt, st),
            "flash_attn_bwd_dkdv")
     if between:
         between("dkdv")
     _check(lib.flash_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(workspace), workspace.numel(),
-                                 _ptr(dq), B, Hq, Hkv, L, d, scale, c, int(window), dt, st),
+                                 _ptr(dq), B, Hq, Hkv, L, d, scale, c, window, dt, st),
            "flash_attn_bwd_dq")
     if between:
         between("dq")
@@ -232,8 +294,8 @@ def _chunk_shapes(q, k, v):
     if k.shape[0] != B or k.shape[3] != d:
         raise ValueError("k and v must share B and d with q")
     for t in (q, k, v):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
-            raise ValueError("q, k, v must be contiguous CUDA tensors of one dtype")
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q, k, v must be contiguous tensors of one dtype on one GPU")
     if q.dtype not in (torch.bfloat16, torch.float16):
         raise ValueError("chunk pairs take bfloat16 or float16")
     return B, Hq, k.shape[1], Lq, k.shape[2], d
@@ -244,11 +306,12 @@ def fwd_block(q, k, v, causal=False, window=0, q_offset=0, k_offset=0, scale=Non
     ``k_offset + j`` only.  Returns the partial ``(o, lse)`` over this key chunk (rows with no
     allowed key: o = 0, lse = -inf); combine partials with ``merge``."""
     B, Hq, Hkv, Lq, Lk, d = _chunk_shapes(q, k, v)
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if lse is None else lse
+    scale, window = _scale(scale, d), _window(window)
+    q_offset, k_offset = _offset(q_offset, "q_offset"), _offset(k_offset, "k_offset")
+    out = _out(out, "out", q.shape, q.dtype, q.device)
+    lse = _out(lse, "lse", (B, Hq, Lq), torch.float32, q.device)
     rc = library().flash_attn_fwd_block(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, Hq, Hkv, Lq, Lk, d,
-                                        scale, int(bool(causal)), int(window), int(q_offset), int(k_offset),
+                                        scale, int(bool(causal)), window, q_offset, k_offset,
                                         _DTYPES[q.dtype], _stream(q))
     _check(rc, "flash_attn_fwd_block")
     return out, lse
@@ -259,15 +322,16 @@ def merge(o_a, lse_a, o_b, lse_b, out=None, lse_out=None):
     may be ``o_a``/``lse_a`` (in-place accumulation)."""
     if o_a.shape != o_b.shape or o_a.dtype != o_b.dtype or o_a.dim() != 4:
         raise ValueError("partials must be [B, Hq, L, d] of one dtype")
+    if o_a.dtype not in _DTYPES:
+        raise ValueError("dtype must be float32, bfloat16 or float16")
     B, Hq, L, d = o_a.shape
-    for t in (lse_a, lse_b):
-        if t.shape != (B, Hq, L) or t.dtype != torch.float32:
-            raise ValueError("log-sum-exp partials must be float32 [B, Hq, L]")
-    for t in (o_a, o_b, lse_a, lse_b):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("partials must be contiguous CUDA tensors")
-    out = torch.empty_like(o_a) if out is None else out
-    lse_out = torch.empty_like(lse_a) if lse_out is None else lse_out
+    dev = o_a.device
+    _expect(o_a, "o_a", o_a.shape, o_a.dtype, dev)
+    _expect(o_b, "o_b", o_a.shape, o_a.dtype, dev)
+    _expect(lse_a, "lse_a", (B, Hq, L), torch.float32, dev)
+    _expect(lse_b, "lse_b", (B, Hq, L), torch.float32, dev)
+    out = _out(out, "out", o_a.shape, o_a.dtype, dev)
+    lse_out = _out(lse_out, "lse_out", (B, Hq, L), torch.float32, dev)
     rc = library().flash_attn_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out), _ptr(lse_out),
                                     B, Hq, L, d, _DTYPES[o_a.dtype], _stream(o_a))
     _check(rc, "flash_attn_merge")
@@ -279,15 +343,12 @@ def bwd_block(q, k, v, o, lse, dout, causal=False, window=0, q_offset=0, k_offse
     """One ring-attention backward step: this chunk pair's contributions ``(dq, dk, dv)`` to the
     gradient, given the query rows' full ``o`` and ``lse`` (over all key chunks)."""
     B, Hq, Hkv, Lq, Lk, d = _chunk_shapes(q, k, v)
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    nbytes = bwd_workspace_bytes(B, Hq, Hkv, Lq, d, q.dtype)
-    workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if workspace is None else workspace
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    scale, window = _scale(scale, d), _window(window)
+    q_offset, k_offset = _offset(q_offset, "q_offset"), _offset(k_offset, "k_offset")
+    workspace, dq, dk, dv = _bwd_buffers(q, k, v, o, lse, dout, Lq, workspace, dq, dk, dv)
     rc = library().flash_attn_bwd_block(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                         _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), B, Hq, Hkv, Lq, Lk,
-                                        d, scale, int(bool(causal)), int(window), int(q_offset), int(k_offset),
+                                        d, scale, int(bool(causal)), window, q_offset, k_offset,
                                         _DTYPES[q.dtype], _stream(q))
     _check(rc, "flash_attn_bwd_block")
     return dq, dk, dv
@@ -311,79 +372,24 @@ def decode(q, k_cache, v_cache, cache_len=None, causal=True, window=0, scale=Non
     if k_cache.shape[0] != B or k_cache.shape[3] != d:
         raise ValueError("the caches must share B and d with q")
     for t in (q, k_cache, v_cache):
-        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype:
-            raise ValueError("q and the caches must be contiguous CUDA tensors of one dtype")
+        if not t.is_cuda or not t.is_contiguous() or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError("q and the caches must be contiguous tensors of one dtype on one GPU")
     if q.dtype not in (torch.bfloat16, torch.float16):
         raise ValueError("decode takes bfloat16 or float16")
-    if cache_len is not None and (cache_len.dtype != torch.int32 or not cache_len.is_cuda
-                                  or cache_len.shape != (B,) or not cache_len.is_contiguous()):
-        raise ValueError("cache_len must be a contiguous int32 CUDA tensor [B]")
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if cache_len is not None:
+        _expect(cache_len, "cache_len", (B,), torch.int32, q.device)
+    scale, window = _scale(scale, d), _window(window)
     nbytes = decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, d, q.dtype)
     if nbytes == 0:
         raise RuntimeError("flash_attn_decode: unsupported sizes (Hq/Hkv * Lq must be <= 32)")
-    workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if workspace is None else workspace
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, Hq, Lq), dtype=torch.float32, device=q.device) if lse is None else lse
+    workspace = _workspace(workspace, nbytes, q.device)
+    out = _out(out, "out", q.shape, q.dtype, q.device)
+    lse = _out(lse, "lse", (B, Hq, Lq), torch.float32, q.device)
     rc = library().flash_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(out), _ptr(lse),
                                      _ptr(workspace), workspace.numel(), B, Hq, Hkv, Lq, Lk, d, scale,
-                                     int(bool(causal)), int(window), _DTYPES[q.dtype], _stream(q))
+                                     int(bool(causal)), window, _DTYPES[q.dtype], _stream(q))
     _check(rc, "flash_attn_decode")
     return out, lse
-
-
-def block_band_mask(L, block=64, radius=1):
-    """Block-sparse pattern in which query block a attends to key blocks b with
-    |a - b| <= radius (kler.cn §4.1.2: each block attends to itself and its
-    neighbouring blocks).  Returns a bool CPU tensor ``[nbm, nbm]``, nbm = ceil(L / block)."""
-    nbm = (int(L) + block - 1) // block
-    idx = torch.arange(nbm)
-    return (idx[:, None] - idx[None, :]).abs() <= int(radius)
-
-
-def allowed_pairs(L, causal=False, window=0, global_tokens=(), block_mask=None, block=64):
-    """Number of allowed (query, key) pairs of the general mask over one sequence of
-    length L (the same rule as ``MaskPlan``): the algorithmic work of one head is
-    4 * d * allowed_pairs flops forward.  Counted on the host: per row in interval form
-    without a block mask, else over row chunks of the boolean mask."""
-    L = int(L)
-    glob = sorted({(p + L if p < 0 else p) for p in global_tokens if -L <= p < L})
-    if block_mask is None:
-        # interval form: row i's local keys are one interval [lo, hi]; the global
-        # keys outside it (and visible under the causal mask) are added, and a
-        # global row sees every visible key
-        i = torch.arange(L, dtype=torch.int64)
-        hi = i.clone() if causal else torch.full((L,), L - 1, dtype=torch.int64)
-        lo = torch.zeros(L, dtype=torch.int64)
-        if window > 0:
-            lo = (i - window + 1).clamp_min(0)
-            if not causal:
-                hi = (i + window - 1).clamp_max(L - 1)
-        g = torch.tensor(glob, dtype=torch.int64)
-        inside = torch.searchsorted(g, hi, right=True) - torch.searchsorted(g, lo, right=False)
-        visible = torch.searchsorted(g, i, right=True) if causal else torch.full((L,), len(glob), dtype=torch.int64)
-        count = hi - lo + 1 + visible - inside
-        if glob:
-            count[g] = (g + 1) if causal else L
-        return int(count.sum())
-    is_g = torch.zeros(L, dtype=torch.bool)
-    if glob:
-        is_g[torch.tensor(glob)] = True
-    bm = torch.as_tensor(block_mask).bool().cpu()
-    total = 0
-    chunk = max(1, (1 << 24) // L)
-    j = torch.arange(L)
-    for r0 in range(0, L, chunk):
-        i = torch.arange(r0, min(L, r0 + chunk))[:, None]
-        local = torch.ones(i.shape[0], L, dtype=torch.bool)
-        if window > 0:
-            local &= (i - j[None, :]).abs() < window
-        local &= bm[(i // block), (j // block)[None, :]]
-        ok = local | is_g[i] | is_g[None, :]
-        if causal:
-            ok &= j[None, :] <= i
-        total += int(ok.sum())
-    return total
 
 
 class MaskPlan:
@@ -400,7 +406,7 @@ class MaskPlan:
     """
 
     def __init__(self, L, causal=False, window=0, global_tokens=(), block_mask=None, block=64, device="cuda"):
-        self.L, self.causal, self.window, self.block = int(L), bool(causal), int(window), int(block)
+        self.L, self.causal, self.window, self.block = int(L), bool(causal), _window(window), int(block)
         self.global_tokens = tuple(int(p) for p in global_tokens)
         dev = torch.device(device)
         self._gpos = (torch.tensor(self.global_tokens, dtype=torch.int32, device=dev)
@@ -422,9 +428,16 @@ class MaskPlan:
         rc = library().flash_attn_mask_plan(ctypes.byref(self.desc), self.L, _ptr(self.plan), nbytes,
                                             _stream(self.plan))
         _check(rc, "flash_attn_mask_plan")
+        # The plan is built asynchronously on the stream current now; a masked call
+        # on any other stream first waits for this event.
+        self.ready = torch.cuda.Event()
+        self.ready.record(torch.cuda.current_stream(dev))
 
-    def allowed_pairs(self):
-        return allowed_pairs(self.L, self.causal, self.window, self.global_tokens, self.block_mask, self.block)
+    def wait(self, device):
+        """Make the current stream of ``device`` wait until the plan is built."""
+        if self.plan.device != device:
+            raise ValueError("the plan lives on %s" % self.plan.device)
+        torch.cuda.current_stream(device).wait_event(self.ready)
 
 
 def masked_workspace_bytes(B, Hq, Hkv, L, d, plan, backward):
@@ -438,12 +451,13 @@ def fwd_masked(q, k, v, plan, scale=None, out=None, lse=None, workspace=None):
     B, Hq, Hkv, L, d = _shapes(q, k, v)
     if L != plan.L:
         raise ValueError("the plan was built for L = %d" % plan.L)
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    out = torch.empty_like(q) if out is None else out
-    lse = torch.empty((B, Hq, L), dtype=torch.float32, device=q.device) if lse is None else lse
+    scale = _scale(scale, d)
+    out = _out(out, "out", q.shape, q.dtype, q.device)
+    lse = _out(lse, "lse", (B, Hq, L), torch.float32, q.device)
     nbytes = masked_workspace_bytes(B, Hq, Hkv, L, d, plan, False)
-    if workspace is None and nbytes > 0:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    if workspace is not None or nbytes > 0:
+        workspace = _workspace(workspace, nbytes, q.device)
+    plan.wait(q.device)
     rc = library().flash_attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
                                          0 if workspace is None else workspace.numel(), B, Hq, Hkv, L, d, scale,
                                          ctypes.byref(plan.desc), _ptr(plan.plan), plan.plan.numel(),
@@ -457,12 +471,16 @@ def bwd_masked(q, k, v, o, lse, dout, plan, scale=None, workspace=None, dq=None,
     B, Hq, Hkv, L, d = _shapes(q, k, v)
     if L != plan.L:
         raise ValueError("the plan was built for L = %d" % plan.L)
-    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    scale = _scale(scale, d)
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(dout, "dout", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, Hq, L), torch.float32, q.device)
     nbytes = masked_workspace_bytes(B, Hq, Hkv, L, d, plan, True)
-    workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device) if workspace is None else workspace
-    dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
+    workspace = _workspace(workspace, nbytes, q.device)
+    dq = _out(dq, "dq", q.shape, q.dtype, q.device)
+    dk = _out(dk, "dk", k.shape, k.dtype, k.device)
+    dv = _out(dv, "dv", v.shape, v.dtype, v.device)
+    plan.wait(q.device)
     rc = library().flash_attn_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                          _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), B, Hq, Hkv, L, d,
                                          scale, ctypes.byref(plan.desc), _ptr(plan.plan), plan.plan.numel(),

@@ -309,7 +309,7 @@ def test_block_band_mask_full_size_sampled():
     print(f"[masks] full size {w.name} seed={w.seed}", flush=True)
     q, k, v, do = W.make_inputs(w, with_dout=True)
     blk = W.BLOCK_BAND_BLOCK
-    bm = fa().block_band_mask(w.L, blk, W.BLOCK_BAND_RADIUS)
+    bm = W.block_band_mask(w.L, blk, W.BLOCK_BAND_RADIUS)
     plan = fa().MaskPlan(w.L, causal=w.causal, block_mask=bm, block=blk, device=DEV)
     qd, kd, vd, dod = (t.to(DEV) for t in (q, k, v, do))
     o, lse = fa().fwd_masked(qd, kd, vd, plan, scale=w.scale)

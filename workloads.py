@@ -73,6 +73,15 @@ HYBRID_SPARSE_128K = Workload("hybrid-sparse B2 H32 L131072 d128 window513 globa
                               128, torch.bfloat16, False, 513, seed=6, backward=True, global_tokens=(0, -1))
 
 
+def block_band_mask(L, block=64, radius=1):
+    """The block-sparse pattern of kler.cn §4.1.2 as an input: query block a attends
+    to key blocks b with |a - b| <= radius (each block sees itself and its
+    neighbours).  A bool CPU tensor ``[nbm, nbm]`` with nbm = ceil(L / block)."""
+    nbm = (int(L) + block - 1) // block
+    idx = torch.arange(nbm)
+    return (idx[:, None] - idx[None, :]).abs() <= int(radius)
+
+
 def make_inputs(w: Workload, with_dout: bool = None):
     """Seeded CPU tensors ``(q, k, v, dout_or_None)`` for workload ``w``.
 
