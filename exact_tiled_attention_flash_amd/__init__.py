@@ -20,7 +20,7 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "fwd_block", "bwd_block", "merge",
+__all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "bwd_noalloc", "NOALLOC_MAX_ROWS", "fwd_block", "bwd_block", "merge",
            "decode", "decode_workspace_bytes",
            "MaskPlan", "fwd_masked", "bwd_masked", "masked_workspace_bytes",
            "strerror", "library", "library_path",
@@ -38,7 +38,10 @@ EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspac
                     "flash_attn_decode", "flash_attn_decode_workspace_bytes",
                     "flash_attn_mask_plan_bytes", "flash_attn_mask_plan", "flash_attn_masked_workspace_bytes",
                     "flash_attn_fwd_masked", "flash_attn_bwd_masked",
-                    "flash_attn_strerror", "flash_attn_version")
+                    "flash_attn_bwd_noalloc", "flash_attn_strerror", "flash_attn_version")
+
+# B * Hq * L limit of flash_attn_bwd_noalloc (its static scratch holds two float32 per row)
+NOALLOC_MAX_ROWS = 1 << 21
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB = None
@@ -102,6 +105,8 @@ def library():
     lib.flash_attn_bwd_masked.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                           i, i, i, i, i, f, mp, vp, sz, i, vp]
     lib.flash_attn_bwd_masked.restype = i
+    lib.flash_attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp]
+    lib.flash_attn_bwd_noalloc.restype = i
     lib.flash_attn_strerror.argtypes = [i]
     lib.flash_attn_strerror.restype = ctypes.c_char_p
     lib.flash_attn_version.argtypes = []
@@ -257,6 +262,26 @@ def bwd(q, k, v, o, lse, dout, causal=False, window=0, scale=None, workspace=Non
                                   B, Hq, Hkv, L, d, scale, int(bool(causal)), window,
                                   _DTYPES[q.dtype], _stream(q))
     _check(rc, "flash_attn_bwd")
+    return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, lse, dout, dq, dk, dv, causal=False, window=0, scale=None):
+    """``bwd`` for callers that cannot allocate: the outputs ``dq, dk, dv`` are given, and
+    the library keeps the per-row statistics in its own static device array (at most
+    ``NOALLOC_MAX_ROWS`` query rows, B * Hq * L).  Calls that overlap in time on one GPU
+    share that array and race.  Nothing is allocated on this path."""
+    B, Hq, Hkv, L, d = _shapes(q, k, v)
+    scale, window = _scale(scale, d), _window(window)
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(dout, "dout", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, Hq, L), torch.float32, q.device)
+    _expect(dq, "dq", q.shape, q.dtype, q.device)
+    _expect(dk, "dk", k.shape, k.dtype, k.device)
+    _expect(dv, "dv", v.shape, v.dtype, v.device)
+    rc = library().flash_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                          _ptr(dq), _ptr(dk), _ptr(dv), B, Hq, Hkv, L, d, scale,
+                                          int(bool(causal)), window, _DTYPES[q.dtype], _stream(q))
+    _check(rc, "flash_attn_bwd_noalloc")
     return dq, dk, dv
 
 

@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <mutex>
 
 #include "../../include/flash_attn.h"
 #include "fa_kernels.h"
@@ -198,6 +199,70 @@ extern "C" int flash_attn_bwd_block(const void* q, const void* k, const void* v,
   a.Lk = Lk;
   a.shift = q_offset - k_offset;
   hipError_t e = fa::launch_bwd_bf16(a, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+// ---- backward without allocation: the per-row statistics live in a static
+// device array instead of a caller-provided workspace.
+namespace {
+
+// 16 MiB: two float32 per query row, so B * Hq * L <= 2^21 rows.  Each GPU the
+// library runs on holds its own copy until the process ends.
+constexpr size_t kNoAllocScratchBytes = (size_t)FA_NOALLOC_MAX_ROWS * 2 * sizeof(float);
+__device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The array's device address, looked up once per device.  In host code the
+// name `scratch` is only a host-side handle; kernels receive this address.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return FA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FA_ERR_UNSUPPORTED;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return FA_ERR_HIP;
+  *out = g_scratch_ptr[dev];
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                      const void* dout, void* dq, void* dk, void* dv,
+                                      int B, int Hq, int Hkv, int L, int d,
+                                      float softmax_scale, int causal, int window, int dtype, void* stream) {
+  int rc = check_common(B, Hq, Hkv, L, d, softmax_scale, causal, window, dtype);
+  if (rc != FA_OK) return rc;
+  if (dtype == FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * Hq * L > FA_NOALLOC_MAX_ROWS) return FA_ERR_TOO_LARGE;
+  if (!all_aligned({q, k, v, o, lse, dout, dq, dk, dv})) return FA_ERR_INVALID_ARG;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (s != nullptr) {
+    // the scratch is looked up on the current device: the stream must be one of its streams
+    int sdev = -1, cdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess || hipGetDevice(&cdev) != hipSuccess) return FA_ERR_HIP;
+    if (sdev != cdev) return FA_ERR_INVALID_ARG;
+  }
+  void* ws = nullptr;
+  rc = scratch_address(&ws);
+  if (rc != FA_OK) return rc;
+  fa::BwdArgs a{};
+  rc = bwd_setup(a, ws, kNoAllocScratchBytes, B, Hq, Hkv, L, d, softmax_scale, causal, window, dtype);
+  if (rc != FA_OK) return rc;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  // the three staged kernels: the preprocess overwrites every row's statistics
+  // in the scratch before the dK/dV and dQ kernels read them
+  hipError_t e = fa::launch_bwd_preprocess_bf16(a, s);
+  if (e == hipSuccess) e = fa::launch_bwd_dkdv_bf16(a, causal != 0, s);
+  if (e == hipSuccess) e = fa::launch_bwd_dq_bf16(a, causal != 0, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -420,6 +485,7 @@ extern "C" const char* flash_attn_strerror(int code) {
     case FA_ERR_GQA: return "number of query heads is not a multiple of the number of key/value heads";
     case FA_ERR_WORKSPACE: return "backward workspace missing, misaligned or too small";
     case FA_ERR_HIP: return "HIP launch or runtime error";
+    case FA_ERR_TOO_LARGE: return "sizes exceed the static scratch of flash_attn_bwd_noalloc (B * Hq * L > 2^21)";
     default: return "unknown error code";
   }
 }

@@ -70,6 +70,7 @@ extern "C" {
 #define FA_ERR_GQA          (-3)  /* Hq is not a multiple of Hkv */
 #define FA_ERR_WORKSPACE    (-4)  /* backward workspace missing or too small */
 #define FA_ERR_HIP          (-5)  /* a HIP launch or runtime call failed */
+#define FA_ERR_TOO_LARGE    (-6)  /* sizes beyond flash_attn_bwd_noalloc's static scratch */
 
 /*
  * Forward pass.
@@ -310,6 +311,29 @@ int flash_attn_bwd_masked(const void* q, const void* k, const void* v, const voi
                           void* workspace, size_t workspace_bytes,
                           int B, int Hq, int Hkv, int L, int d, float softmax_scale,
                           const fa_mask* mask, const void* plan, size_t plan_bytes, int dtype, void* stream);
+
+/*
+ * flash_attn_bwd_noalloc: flash_attn_bwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  It runs the three
+ * staged kernels of flash_attn_bwd_preprocess / _dkdv / _dq, with the per-row
+ * statistics (D_i and LSE_i * log2 e, two float32 per query row) in a static
+ * device array of 16 MiB that the library owns: B * Hq * L must be at most
+ * FA_NOALLOC_MAX_ROWS (2^21), else FA_ERR_TOO_LARGE.  The call allocates
+ * nothing and calls no allocating routine.  Each GPU has its own copy of the
+ * array, looked up on the first call on that device; `stream` must belong to
+ * the current device (else FA_ERR_INVALID_ARG).  Every call on one GPU shares
+ * that GPU's array, which keeps the last call's contents (every row used is
+ * rewritten before it is read, so nothing needs clearing): calls that overlap
+ * in time on one GPU (on different streams, or from different threads) race
+ * and give wrong results -- serialise them.  Other arguments and return codes
+ * as flash_attn_bwd.
+ */
+#define FA_NOALLOC_MAX_ROWS 2097152  /* 2^21 query rows */
+int flash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv,
+                           int B, int Hq, int Hkv, int L, int d,
+                           float softmax_scale, int causal, int window, int dtype, void* stream);
 
 /* Static, never-NULL description of a return code. */
 const char* flash_attn_strerror(int code);

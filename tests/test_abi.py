@@ -53,7 +53,7 @@ def test_binding_constants_match_header():
 def test_strerror_and_version(lib):
     c = header_constants()
     for name in ("FA_OK", "FA_ERR_INVALID_ARG", "FA_ERR_UNSUPPORTED", "FA_ERR_GQA",
-                 "FA_ERR_WORKSPACE", "FA_ERR_HIP"):
+                 "FA_ERR_WORKSPACE", "FA_ERR_HIP", "FA_ERR_TOO_LARGE"):
         s = fa.strerror(c[name])
         assert s and s != "unknown error code"
     assert fa.strerror(12345) == "unknown error code"
@@ -244,3 +244,23 @@ def test_mask_entry_points_reject_invalid_arguments(lib):
                                          128, 0.125, mask() if m is None else m, p, nb, fa.FA_DTYPE_BF16, None)
     assert bm(dq=None) == INV and bm(ws=None) == WS and bm(wn=wsb - 1) == WS
     assert bm(p=None) == WS and bm(nb=16) == WS and bm(m=mask(ng=1)) == INV
+
+
+def test_bwd_noalloc_rejects_before_any_hip_call(lib):
+    """Sizes beyond the static scratch, and the usual invalid arguments, return an
+    error code before the scratch is looked up or any kernel launched."""
+    c = header_constants()
+    assert c["FA_NOALLOC_MAX_ROWS"] == fa.NOALLOC_MAX_ROWS == 1 << 21
+
+    def call(B=1, Hq=2, Hkv=2, L=16, d=64, scale=0.125, causal=1, window=0, dtype=fa.FA_DTYPE_BF16, dq=FAKE):
+        return lib.flash_attn_bwd_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE,
+                                          B, Hq, Hkv, L, d, scale, causal, window, dtype, None)
+    assert call(B=1, Hq=32, L=(1 << 16) + 1) == c["FA_ERR_TOO_LARGE"]
+    assert call(B=2, Hq=32, L=(1 << 15) + 1, Hkv=8) == c["FA_ERR_TOO_LARGE"]
+    assert call(dtype=fa.FA_DTYPE_F32) == c["FA_ERR_UNSUPPORTED"]
+    assert call(d=96) == c["FA_ERR_UNSUPPORTED"]
+    assert call(Hkv=3) == c["FA_ERR_GQA"]
+    assert call(dq=None) == c["FA_ERR_INVALID_ARG"]
+    assert call(dq=MISALIGNED) == c["FA_ERR_INVALID_ARG"]
+    assert call(scale=0.0) == c["FA_ERR_INVALID_ARG"]
+    assert fa.strerror(c["FA_ERR_TOO_LARGE"]).startswith("sizes exceed")
