@@ -149,16 +149,26 @@ def load_traffic(kernel_key):
         return None
 
 
-def cpu_baseline(budget_s=20.0):
-    """Time the fp64 oracle on a bounded sample of the same workload (rank 0 only)."""
-    import numpy as np
-    import oracle
-    import workloads as W
+def host_cores():
+    """Host CPU counts and the BLAS threads the oracle runs with."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count()
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except Exception:
+        affinity = None
+    return {"blas_threads": threads, "os_cpu_count": os.cpu_count(), "affinity": affinity}
+
+
+def cpu_baseline(budget_s=20.0):
+    """Time the fp64 oracle on a bounded sample of the headline workload (rank 0 only)."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    cores = host_cores()
     w = W.LLAMA7B_CAUSAL
     q, k, v, do = W.make_inputs(w, with_dout=True)
     qn, kn, vn, don = (t.float().numpy() for t in (q, k, v, do))
@@ -182,10 +192,99 @@ def cpu_baseline(budget_s=20.0):
         if time.perf_counter() - t1 > budget_s / 2:
             break
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores["blas_threads"], "kind": "oracle",
+            "host": cores,
             "sample": f"fp64 NumPy oracle on {heads} head(s) forward + {bheads} head(s) backward "
                       f"of B2 H32 L4096 d128 causal (each one full 4096x4096 head); "
-                      f"{dt:.1f} s wall, {t_f:.1f} s of it forward; host os.cpu_count()={os.cpu_count()}"}
+                      f"{dt:.1f} s wall, {t_f:.1f} s of it forward"}
+
+
+def _sample_rows(L, window, n_random=256, seed=0):
+    """Rows timed for the long workloads: 0, 1, the 64-row tile edges near the
+    start and end, w - 1 and w for a window, L - 1, and seeded random rows."""
+    import numpy as np
+    fixed = {0, 1, 63, 64, 127, 128, L // 2, L - 65, L - 64, L - 2, L - 1}
+    if window:
+        fixed |= {window - 1, window, window + 1}
+    rng = np.random.default_rng(seed)
+    rows = sorted(fixed | set(int(x) for x in rng.integers(0, L, n_random)))
+    return np.array([r for r in rows if 0 <= r < L])
+
+
+def cpu_baseline_configs():
+    """The oracle timed on every workload of the configuration list (a baseline only).
+
+    Whole (batch, head) slices where one fits in a few seconds (tiny fp32: every head;
+    the 4k layer: one head forward and backward; the 8k backward: one head), sampled
+    query rows elsewhere (exact for those rows).  Each entry gives the timed sample,
+    its algorithmic TFLOP/s and the time of the full workload extrapolated from it,
+    labelled as such."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    out = {"host": host_cores(), "note": "fp64 NumPy oracle, untuned; extrapolated_full_s is "
+                                         "sample time x (full work / sampled work), not a measurement"}
+
+    def entry(name, sample, secs, flops_sample, flops_full):
+        out[name] = {"sample": sample, "seconds": round(secs, 3),
+                     "algorithmic_tflops": round(flops_sample / secs / 1e12, 5),
+                     "extrapolated_full_s": round(secs * flops_full / flops_sample, 1)}
+
+    def head_inputs(w, h=0):
+        q, k, v, do = W.make_inputs(w, with_dout=w.backward)
+        hk = h // (w.Hq // w.Hkv)
+        sl = lambda t, hh: t[:1, hh:hh + 1].float().numpy()
+        return sl(q, h), sl(k, hk), sl(v, hk), (sl(do, h) if do is not None else None)
+
+    # tiny fp32: the whole workload
+    w = W.TINY_FP32
+    q, k, v, _ = (t.float().numpy() if t is not None else None for t in W.make_inputs(w))
+    t0, n = time.perf_counter(), 0
+    while n < 3 or time.perf_counter() - t0 < 0.5:
+        oracle.forward(q, k, v, w.scale, w.causal, w.window)
+        n += 1
+    ff = fwd_flops(w.B, w.Hq, w.L, w.d, w.causal, w.window)
+    entry(w.name + " fwd", "every head (whole workload), mean of %d calls" % n, (time.perf_counter() - t0) / n, ff, ff)
+    # the 4k layer and the 8k backward: one whole head, forward and backward
+    for w in (W.LLAMA7B_CAUSAL, W.LONG_BWD_8K):
+        q, k, v, do = head_inputs(w)
+        one_f = fwd_flops(1, 1, w.L, w.d, w.causal, w.window)
+        full_f = fwd_flops(w.B, w.Hq, w.L, w.d, w.causal, w.window)
+        if w is W.LLAMA7B_CAUSAL:
+            t0 = time.perf_counter()
+            oracle.forward(q, k, v, w.scale, w.causal, w.window)
+            entry(w.name + " fwd", "1 of %d (batch, head) slices" % (w.B * w.Hq), time.perf_counter() - t0,
+                  one_f, full_f)
+        t0 = time.perf_counter()
+        oracle.backward(q, k, v, do, w.scale, w.causal, w.window)
+        entry(w.name + " bwd", "1 of %d (batch, head) slices" % (w.B * w.Hq), time.perf_counter() - t0,
+              2.5 * one_f, 2.5 * full_f)
+    # long rows: sampled query rows of one head
+    for w in (W.GQA_16K, W.WINDOW_32K, W.LONG_FWD_128K, W.LONG_BWD_8K):
+        q, k, v, _ = head_inputs(w)
+        rows = _sample_rows(w.L, w.window)
+        ok = oracle.allowed_mask(rows, w.L, w.causal, w.window)
+        t0 = time.perf_counter()
+        oracle.forward_rows(q, k, v, rows, w.scale, w.causal, w.window)
+        secs = time.perf_counter() - t0
+        pairs = float(ok.sum())
+        full_f = fwd_flops(w.B, w.Hq, w.L, w.d, w.causal, w.window)
+        entry(w.name + " fwd", "%d sampled query rows of 1 of %d heads" % (rows.size, w.B * w.Hq), secs,
+              4.0 * w.d * pairs, full_f)
+    return out
+
+
+# The pages' own figures, reported beside the measurement as context (other hardware;
+# none is a target): claspmoon.cn "14 · 缩放定律与高效注意力" §3.1 (A100 bandwidths), §2.1
+# (the full score matrix of the LLaMA-7B-shaped layer); book.anysome.cn "高效注意力" §2
+# (speed-up claimed over naive attention).
+PAGES_CONTEXT = {
+    "a100_hbm_tb_s": 2.0,
+    "a100_on_chip_sram_tb_s": 19.0,
+    "claimed_speedup_vs_naive_attention": "2-4x",
+    "score_matrix_gb_per_layer_fp16_B2_H32_L4096": 2.15,
+    "mi355x_hbm_tb_s": PEAK_HBM_GBS / 1000.0,
+}
 
 
 def time_calls(fn, iters, warmup, warm_ms=150.0):
@@ -564,8 +663,14 @@ def main():
         out["ring"] = measure_ring()
         out["sparse"] = measure_sparse()
         out["sparse_block"] = measure_sparse(block_band=True)
+    ctx = dict(PAGES_CONTEXT)
+    ctx["this_layer"] = {"score_matrix_bytes_fp16": 2 * w.B * w.Hq * w.L * w.L,
+                         "extra_bytes_fwd_lse": int(lse.numel() * 4),
+                         "extra_bytes_bwd_workspace": int(ws.numel())}
+    out["context"] = ctx
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
+        out["cpu_baseline_configs"] = cpu_baseline_configs()
     print(json.dumps(out), flush=True)
 
 

@@ -26,13 +26,27 @@ def fa():
     return m
 
 
-def scaled_tol(w):
-    """The stated tolerances hold for unit-variance inputs.  O is a convex
-    combination of V rows, so its bf16 output rounding (half an ulp of |O|)
-    grows with the spread of V: scale the O bound by the input std when it
-    exceeds 1."""
-    t_o, t_l = TOL[w.dtype]
-    return (t_o * max(1.0, w.std), t_l)
+# Unit roundoff of the 16-bit types (round to nearest even): 8 significant bits
+# for bfloat16, 11 for float16.
+UNIT_ROUNDOFF = {torch.bfloat16: 2.0 ** -8, torch.float16: 2.0 ** -11}
+
+
+def o_error_bound(w, q, k, v, O_ref):
+    """Per-element bound on |O_gpu - O| for inputs whose spread exceeds the unit
+    variance the stated tolerance assumes (std > 1).
+
+    O_ic = sum_j A_ij V_jc with A the softmax weights.  The kernels round each
+    probability P_j to the 16-bit type before P.V (relative error <= u) but sum the
+    row total l in fp32 from the unrounded P_j, so the numerator's rounding moves
+    O_ic by at most u * sum_j A_ij |V_jc|; the output rounding adds at most
+    u * |O_ic|.  fp32 accumulation and exp2 errors are below 1e-4 relative and
+    are covered by a 1e-4 term.  sum_j A_ij |V_jc| is the oracle's attention
+    output for |V|, so the bound is computed, not assumed:
+        |O_gpu - O|_ic <= (u + 1e-4) * (A |V|)_ic + u * |O_ic|.
+    """
+    u = UNIT_ROUNDOFF[w.dtype]
+    O_abs, _ = oracle.forward(np32(q), np32(k), np.abs(np32(v)), w.scale, w.causal, w.window)
+    return (u + 1e-4) * O_abs + u * np.abs(O_ref)
 
 
 def np32(t):
@@ -66,12 +80,23 @@ def check_full(w):
     q, k, v, _ = W.make_inputs(w, with_dout=False)
     o, lse = gpu_fwd(w, q, k, v)
     O_ref, lse_ref = oracle.forward(np32(q), np32(k), np32(v), w.scale, w.causal, w.window)
-    tol = scaled_tol(w)
-    err_o = float(np.abs(np32(o) - O_ref).max())
+    tol = TOL[w.dtype]
+    diff = np.abs(np32(o) - O_ref)
+    err_o = float(diff.max())
     err_l = float(np.abs(lse.numpy() - lse_ref).max())
     report(w.name, err_o, err_l, tol)
     assert np.isfinite(np32(o)).all() and np.isfinite(lse.numpy()).all()
-    assert err_o <= tol[0] and err_l <= tol[1]
+    assert err_l <= tol[1]
+    if w.std > 1.0:
+        # values beyond the unit-variance scale the stated O bound assumes:
+        # held to the derived per-element bound instead
+        bound = o_error_bound(w, q, k, v, O_ref)
+        ratio = float((diff / bound).max())
+        print(f"[parity] {w.name}: max |dO| / derived bound = {ratio:.3f} "
+              f"(largest bound {float(bound.max()):.3e})", flush=True)
+        assert ratio <= 1.0
+    else:
+        assert err_o <= tol[0]
 
 
 def check_sampled(w, n_random=48):
