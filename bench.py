@@ -357,6 +357,34 @@ def measure_config(w, iters=10, warmup=3):
     return r
 
 
+def measure_bwd_fused(iters=10, warmup=3):
+    """The single-kernel backward (dQ accumulated with float32 atomics) against the
+    staged one (dQ recomputing S and dP) on the LLaMA-7B-shaped layer and the 8k
+    backward workload: both compute the same five products' worth of gradient."""
+    import torch
+    import exact_tiled_attention_flash_amd as fa
+    import workloads as W
+    out = {}
+    dev = torch.device("cuda:0")
+    for w in (W.LLAMA7B_CAUSAL, W.LONG_BWD_8K):
+        q, k, v, do = (t.to(dev) for t in W.make_inputs(w, with_dout=True))
+        o, lse = fa.fwd(q, k, v, causal=True, scale=w.scale)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(fa.bwd_fused_workspace_bytes(w.B, w.Hq, w.Hkv, w.L, w.d), dtype=torch.uint8, device=dev)
+        fmed, _ = time_calls(lambda: fa.bwd_fused(q, k, v, o, lse, do, causal=True, scale=w.scale, workspace=ws,
+                                                  dq=dq, dk=dk, dv=dv), iters, warmup)
+        smed, _ = time_calls(lambda: fa.bwd(q, k, v, o, lse, do, causal=True, scale=w.scale, workspace=ws,
+                                            dq=dq, dk=dk, dv=dv), iters, warmup)
+        bf = bwd_flops(w.B, w.Hq, w.L, w.d, True, 0)
+        out[w.name] = {"fused_ms": round(fmed, 4), "staged_ms": round(smed, 4),
+                       "fused_tflops": round(bf / (fmed * 1e-3) / 1e12, 2),
+                       "staged_tflops": round(bf / (smed * 1e-3) / 1e12, 2),
+                       "fused_workspace_bytes": int(ws.numel())}
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def measure_decode(B=8, Hq=32, Hkv=8, Lq=1, Lk=32768, d=128, iters=20, warmup=5):
     """KV-cache decode: one new token per sequence against a 32k-entry GQA cache.
 
@@ -522,6 +550,8 @@ def main():
                     help="only the ring-attention chunk-pair workload; prints its JSON")
     ap.add_argument("--decode-only", action="store_true",
                     help="only the KV-cache decode workload; prints its JSON")
+    ap.add_argument("--bwd-fused-only", action="store_true",
+                    help="only the fused (atomic dQ) against the staged backward; prints its JSON")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (3x), so that HBM counters "
                          "(FETCH_SIZE/WRITE_SIZE) can be scaled against a kernel of known traffic")
@@ -547,6 +577,9 @@ def main():
         return
     if args.decode_only:
         print(json.dumps({"decode": measure_decode(iters=args.steps, warmup=args.warmup)}), flush=True)
+        return
+    if args.bwd_fused_only:
+        print(json.dumps({"bwd_fused": measure_bwd_fused(iters=args.steps, warmup=args.warmup)}), flush=True)
         return
     if args.calibrate_copy:
         src = torch.ones(64 * 2**20, dtype=torch.float32, device=dev)    # 256 MiB
@@ -659,6 +692,7 @@ def main():
         f16 = W.LLAMA7B_CAUSAL.with_(name="llama7b-layer B2 H32 L4096 d128 causal fp16", dtype=torch.float16)
         out["configs"][f16.name] = measure_config(f16)
         out["autograd"] = measure_autograd()
+        out["bwd_fused"] = measure_bwd_fused()
         out["decode"] = measure_decode()
         out["ring"] = measure_ring()
         out["sparse"] = measure_sparse()

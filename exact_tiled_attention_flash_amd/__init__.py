@@ -20,7 +20,8 @@ import os
 
 import torch
 
-__all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "bwd_noalloc", "NOALLOC_MAX_ROWS", "fwd_block", "bwd_block", "merge",
+__all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "bwd_fused", "bwd_fused_workspace_bytes",
+           "bwd_noalloc", "NOALLOC_MAX_ROWS", "fwd_block", "bwd_block", "merge",
            "decode", "decode_workspace_bytes",
            "MaskPlan", "fwd_masked", "bwd_masked", "masked_workspace_bytes",
            "strerror", "library", "library_path",
@@ -33,6 +34,7 @@ FA_DTYPE_F16 = 2
 _DTYPES = {torch.float32: FA_DTYPE_F32, torch.bfloat16: FA_DTYPE_BF16, torch.float16: FA_DTYPE_F16}
 
 EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspace_bytes",
+                    "flash_attn_bwd_fused", "flash_attn_bwd_fused_workspace_bytes",
                     "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
                     "flash_attn_fwd_block", "flash_attn_merge", "flash_attn_bwd_block",
                     "flash_attn_decode", "flash_attn_decode_workspace_bytes",
@@ -74,6 +76,11 @@ def library():
     lib.flash_attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                    i, i, i, i, i, f, i, i, i, vp]
     lib.flash_attn_bwd.restype = i
+    lib.flash_attn_bwd_fused.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                         i, i, i, i, i, f, i, i, i, vp]
+    lib.flash_attn_bwd_fused.restype = i
+    lib.flash_attn_bwd_fused_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.flash_attn_bwd_fused_workspace_bytes.restype = sz
     lib.flash_attn_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, i, i, vp]
     lib.flash_attn_bwd_preprocess.restype = i
     lib.flash_attn_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, f, i, i, i, vp]
@@ -262,6 +269,35 @@ def bwd(q, k, v, o, lse, dout, causal=False, window=0, scale=None, workspace=Non
                                   B, Hq, Hkv, L, d, scale, int(bool(causal)), window,
                                   _DTYPES[q.dtype], _stream(q))
     _check(rc, "flash_attn_bwd")
+    return dq, dk, dv
+
+
+def bwd_fused_workspace_bytes(B, Hq, Hkv, L, d, dtype=torch.bfloat16):
+    return int(library().flash_attn_bwd_fused_workspace_bytes(B, Hq, Hkv, L, d, _DTYPES[dtype]))
+
+
+def bwd_fused(q, k, v, o, lse, dout, causal=False, window=0, scale=None, workspace=None,
+              dq=None, dk=None, dv=None):
+    """``bwd`` by the single K/V-stationary kernel that accumulates dQ with float32
+    atomics (``flash_attn_bwd_fused``): dK and dV bit for bit as ``bwd``, dQ to
+    float32 rounding.  ``workspace`` needs ``bwd_fused_workspace_bytes(...)`` bytes."""
+    B, Hq, Hkv, L, d = _shapes(q, k, v)
+    scale, window = _scale(scale, d), _window(window)
+    nbytes = bwd_fused_workspace_bytes(B, Hq, Hkv, L, d, q.dtype)
+    if nbytes == 0:
+        raise RuntimeError("flash_attn_bwd_fused: unsupported sizes")
+    _expect(o, "o", q.shape, q.dtype, q.device)
+    _expect(dout, "dout", q.shape, q.dtype, q.device)
+    _expect(lse, "lse", (B, Hq, L), torch.float32, q.device)
+    workspace = _workspace(workspace, nbytes, q.device)
+    dq = _out(dq, "dq", q.shape, q.dtype, q.device)
+    dk = _out(dk, "dk", k.shape, k.dtype, k.device)
+    dv = _out(dv, "dv", v.shape, v.dtype, v.device)
+    rc = library().flash_attn_bwd_fused(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                                        _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
+                                        B, Hq, Hkv, L, d, scale, int(bool(causal)), window,
+                                        _DTYPES[q.dtype], _stream(q))
+    _check(rc, "flash_attn_bwd_fused")
     return dq, dk, dv
 
 

@@ -40,7 +40,8 @@ __device__ __forceinline__ void wait_copies_and_barrier() {
 template <int D, bool F16>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__ o, const bf16* __restrict__ dout,
                                                         const float* __restrict__ lse, float* __restrict__ delta,
-                                                        float* __restrict__ lse2, long long rows) {
+                                                        float* __restrict__ lse2, float* __restrict__ dq_acc,
+                                                        long long rows) {
   constexpr int kLanesPerRow = D / 8;
   constexpr int kRowsPerBlock = 256 / kLanesPerRow;
   const long long row = (long long)blockIdx.x * kRowsPerBlock + threadIdx.x / kLanesPerRow;
@@ -51,6 +52,11 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__
     const bf16x8 y = *reinterpret_cast<const bf16x8*>(dout + row * D + part * 8);
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc = fmaf(unpack1<F16>(x[i]), unpack1<F16>(y[i]), acc);
+    if (dq_acc != nullptr) {
+      f32x4* z = reinterpret_cast<f32x4*>(dq_acc + row * D + part * 8);
+      z[0] = f32x4{};
+      z[1] = f32x4{};
+    }
   }
 #pragma unroll
   for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
@@ -246,6 +252,249 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// ------------------------------------------------------------ 2'. fused dK / dV / dQ
+
+// The dK/dV kernel above plus dQ: after each streamed 64-query tile every wave
+// writes its 32 x 32 block of dS (16-bit) into an LDS exchange buffer; after a
+// barrier, wave 4 + kb computes the two 32 queries x 32 head dims blocks
+// (both query halves, head-dim block kb) of dQ = s dS K over all 128 keys of
+// the work-group -- 16 MFMAs, dS by the transposing read of the exchange
+// buffer, K by the transposing read of the K block (stored with swz_dual for
+// this) -- and adds them into the float32 accumulator with atomics.  The
+// copies of the streamed tiles are issued by waves 0-3 only, so only those
+// wait for their vector-memory counter before the tile barrier; the atomics of
+// waves 4-7 drain in the background.  The accumulator is zeroed by the
+// preprocess and converted to dQ by bwd_dq_convert_kernel.  This removes the
+// dQ kernel's recomputation of S and dP: five products instead of seven.
+template <int D, bool CAUSAL, bool F16>
+__global__ __launch_bounds__(512, 1) void bwd_fused_kernel(BwdArgs a) {
+  using C = KVCfg<D>;
+  constexpr int KBD = C::BK * D * 2;                 // K block, swz_dual
+  __shared__ __attribute__((aligned(C::QT))) char q_st0[C::QT];
+  __shared__ __attribute__((aligned(C::QT))) char do_st0[C::QT];
+  __shared__ __attribute__((aligned(C::QT))) char q_st1[C::QT];
+  __shared__ __attribute__((aligned(C::QT))) char do_st1[C::QT];
+  __shared__ __attribute__((aligned(1024))) char k_blk[KBD];
+  __shared__ __attribute__((aligned(1024))) char v_blk[C::KB];
+  __shared__ __attribute__((aligned(1024))) char ds_buf[C::BK * C::BQ * 2];
+  __shared__ __attribute__((aligned(16))) float stat_st0[2 * C::BQ];   // LSE*log2e, then D
+  __shared__ __attribute__((aligned(16))) float stat_st1[2 * C::BQ];
+
+  const int lane = threadIdx.x & 63, wave = wave_id();
+  const int g = lane >> 5, ln = lane & 31;
+  const int kb = wave & 3, qh = wave >> 2;
+  const int L = a.L, Lk = a.Lk, shift = a.shift, window = a.window;
+  const int G = a.Hq / a.Hkv;
+
+  const int r = xcd_remap(blockIdx.x, gridDim.x);
+  const int bhk = r / a.n_tiles;
+  const int kt = r % a.n_tiles;
+  const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
+  const int key_wg0 = kt * C::BK;
+  const int key_w0 = key_wg0 + 32 * kb;
+
+  const size_t kv_off = ((size_t)(b * a.Hkv + hk) * Lk) * D;
+  const unsigned head_bytes = (unsigned)Lk * (2 * D);
+  const unsigned qhead_bytes = (unsigned)L * (2 * D);
+
+  const int q_begin = CAUSAL ? max(0, key_wg0 - shift) : (window > 0 ? max(0, key_wg0 - shift - window + 1) : 0);
+  const int q_end = (window > 0) ? min(L, key_wg0 + C::BK - 1 + window - shift) : L;
+  const bool empty = q_end <= q_begin;
+  const int qt_lo = empty ? 0 : q_begin / C::BQ, qt_hi = empty ? -1 : (q_end - 1) / C::BQ;
+  const int nq = qt_hi - qt_lo + 1;
+  const int n_it = G * nq;
+
+  constexpr int kCopyWaves = 4;                         // waves 0-3 stream the Q / dO tiles
+  constexpr int kCopies = C::QCOPIES / kCopyWaves;      // copies per copy wave per tensor
+  const bool copier = wave < kCopyWaves;
+  int qcopy[kCopies];
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) qcopy[i] = dual_slot_src<D>(((wave & 3) + kCopyWaves * i) * 64 + lane);
+  KVAddrDual<D> ad;
+  ad.qrow.init(32 * qh + ln, g);
+  ad.qtr[0].init(2 * qh, 0, lane);
+  ad.qtr[1].init(2 * qh, 1, lane);
+  ad.krow.init(32 * kb + ln, g);
+  ad.kv = row_offset_kpad<D>(32 * kb + ln, 0, g);
+
+  auto q0_of = [&](int it) { return (qt_lo + it % nq) * C::BQ; };
+  auto issue = [&](int it, char* qs, char* dos, float* ss) {
+    const int hq = hk * G + it / nq, q0 = q0_of(it);
+    const size_t qoff = ((size_t)(b * a.Hq + hq) * L) * D;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(reinterpret_cast<const bf16*>(a.q) + qoff, qhead_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(reinterpret_cast<const bf16*>(a.dout) + qoff, qhead_bytes);
+    const int soff = q0 * (2 * D);
+    if (copier) {
+#pragma unroll
+      for (int i = 0; i < kCopies; ++i) {
+        buf2lds16(qrs, qcopy[i], soff, qs + (wave + kCopyWaves * i) * 1024);
+        buf2lds16(drs, qcopy[i], soff, dos + (wave + kCopyWaves * i) * 1024);
+      }
+    }
+    if (wave == 0) {
+      const size_t srow = (size_t)(b * a.Hq + hq) * L;
+      const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.lse2 + srow, (unsigned)L * 4);
+      const __amdgpu_buffer_rsrc_t ers = make_rsrc(a.delta + srow, (unsigned)L * 4);
+      buf2lds4(lrs, 4 * lane, 4 * q0, reinterpret_cast<char*>(ss));
+      buf2lds4(ers, 4 * lane, 4 * q0, reinterpret_cast<char*>(ss) + 4 * C::BQ);
+    }
+  };
+
+  // the work-group's K (swz_dual) and V (padded) rows, once; rows past Lk read zeros
+  {
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kv_off, head_bytes);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16*>(a.v) + kv_off, head_bytes);
+    const int soff = key_wg0 * (2 * D);
+#pragma unroll
+    for (int n = wave; n < KBD / 1024; n += C::kWaves)
+      buf2lds16(krs, dual_slot_src<D>(n * 64 + lane), soff, k_blk + n * 1024);
+#pragma unroll
+    for (int n = wave; n < C::KBCOPIES; n += C::kWaves)
+      buf2lds16(vrs, pad_slot_src<D, Pad<D>::KSTR>(n * 64 + lane), soff, v_blk + n * 1024);
+  }
+  if (n_it > 0) issue(0, q_st0, do_st0, stat_st0);
+
+  KVState<D> st;
+#pragma unroll
+  for (int db = 0; db < C::NDB; ++db) {
+    st.dv[db] = f32x16{};
+    st.dk[db] = f32x16{};
+  }
+  const float c = a.scale_log2;
+  auto block_mask = [&](int q0) {
+    const int qw0 = q0 + 32 * qh;
+    return (qw0 + 32 > L) || (CAUSAL && qw0 + shift < key_w0 + 31) ||
+           (window > 0 && qw0 + 31 + shift > key_w0 + window - 1) ||
+           (!CAUSAL && window > 0 && qw0 + shift < key_w0 + 31 - window + 1);
+  };
+  const RangeMaskK<CAUSAL> ok{L, shift, window, key_w0 + ln};
+  const int ds_row = 32 * kb + ln;
+
+  // one tile: dK/dV work and the dS exchange, then dQ of the tile into registers
+  auto tile = [&](int it, const char* qs, const char* dos, const float* ss) {
+    const int q0 = q0_of(it);
+    // every wave runs the tile, also one whose 32 x 32 block no query sees:
+    // its mask then zeroes all of P and dS (skipping it would need a branch
+    // around the tile that costs the kernel more registers than the ~2% of
+    // work it saves on causal masks)
+    kv_tile<D, F16, true>(st, ad, k_blk, v_blk, qs, dos, ss, q0, block_mask(q0), ok, qh, c, lane, ds_buf, ds_row);
+    __syncthreads();     // every wave's dS block is in the exchange buffer
+    if (!copier && kb < C::NDB) {
+      // dQ blocks (0, kb) and (1, kb): A = dS of either query half by the
+      // transposing read of the exchange buffer, B = K columns 32kb .. 32kb + 31
+      // by the transposing read of the K block (shared by both blocks).  The
+      // offsets are recomputed here (from a lane index the compiler cannot
+      // hoist) rather than kept live through the tile.
+      int ll = lane;
+      asm volatile("" : "+v"(ll));
+      const int kt0 = tr_offset_dual<D>(0, kb, 0, ll), kt1 = tr_offset_dual<D>(0, kb, 1, ll);
+      const int hq = hk * G + it / nq;
+      const __amdgpu_buffer_rsrc_t dq_rs =
+          make_rsrc(a.dq_acc + (size_t)(b * a.Hq + hq) * L * D, (unsigned)L * D * 4);
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int qw0 = q0 + 32 * half;
+        const bool any = key_wg0 < Lk && qw0 < L && (!CAUSAL || qw0 + 31 + shift >= key_wg0) &&
+                         (window <= 0 || qw0 + shift <= key_wg0 + C::BK - 1 + window - 1) &&
+                         (CAUSAL || window <= 0 || qw0 + 31 + shift >= key_wg0 - window + 1);
+        if (!any) continue;
+        const int dsa0 = ds_tr_offset(0, 0, half, ll), dsa1 = ds_tr_offset(0, 1, half, ll);
+        const int dsb0 = ds_tr_offset(1, 0, half, ll), dsb1 = ds_tr_offset(1, 1, half, ll);
+        f32x16 acc = f32x16{};
+#pragma unroll
+        for (int t = 0; t < C::BK / 16; ++t) {
+          const int da0 = (t & 1) ? dsb0 : dsa0, da1 = (t & 1) ? dsb1 : dsa1;
+          const int base = (t >> 1) * 32 * 128;        // the swizzle repeats every 32 rows
+          const bf16x8 av = concat4(lds_load_tr(ds_buf, da0 + base), lds_load_tr(ds_buf, da1 + base));
+          const bf16x8 bv = concat4(lds_load_tr(k_blk, kt0 + t * 16 * (2 * D)),
+                                    lds_load_tr(k_blk, kt1 + t * 16 * (2 * D)));
+          acc = mfma32x<F16>(av, bv, acc);
+        }
+        // lane holds head dim 32kb + ln of queries qw0 + 8(i/4) + 4g + i%4; rows
+        // past the sequence fall outside the resource and are dropped
+        const int voff = ((qw0 + 4 * g) * D + 32 * kb + ln) * 4;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[i] * a.scale, dq_rs,
+                                                          voff + (8 * (i >> 2) + (i & 3)) * D * 4, 0, 0);
+      }
+    }
+  };
+
+  // Only the copy waves wait for their copies; the atomics of the other waves
+  // stay in flight across the barrier.
+  auto wait_and_barrier = [&]() {
+    if (copier) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  };
+
+  wait_copies_and_barrier();    // the K / V block and the first tile, all waves
+  for (int it = 0; it < n_it; it += 2) {
+    if (it + 1 < n_it) issue(it + 1, q_st1, do_st1, stat_st1);
+    tile(it, q_st0, do_st0, stat_st0);
+    wait_and_barrier();
+    if (it + 1 >= n_it) break;
+    if (it + 2 < n_it) issue(it + 2, q_st0, do_st0, stat_st0);
+    tile(it + 1, q_st1, do_st1, stat_st1);
+    wait_and_barrier();
+  }
+
+  // Sum the two query halves' dK and dV through LDS (as bwd_dkdv_kernel)
+  constexpr int kPart = C::NDB * 16 * 64 * 4;
+  static_assert(kPart <= C::QT, "a partial must fit in one stage buffer");
+  bf16* dKh = reinterpret_cast<bf16*>(a.dk) + kv_off;
+  bf16* dVh = reinterpret_cast<bf16*>(a.dv) + kv_off;
+  const float s = a.scale;
+  float* part = reinterpret_cast<float*>(kb == 0 ? q_st0 : kb == 1 ? do_st0 : kb == 2 ? q_st1 : do_st1);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    if (qh == 1) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          part[(db * 16 + i) * 64 + lane] = pass == 0 ? st.dv[db][i] : st.dk[db][i];
+    }
+    __syncthreads();
+    if (qh == 0) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (pass == 0) st.dv[db][i] += part[(db * 16 + i) * 64 + lane];
+          else st.dk[db][i] += part[(db * 16 + i) * 64 + lane];
+        }
+    }
+    __syncthreads();
+  }
+  if (qh == 0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int key = key_w0 + 8 * (i >> 2) + 4 * g + (i & 3);
+      if (key < Lk) {
+#pragma unroll
+        for (int db = 0; db < C::NDB; ++db) {
+          dKh[(size_t)key * D + 32 * db + ln] = pack1<F16>(st.dk[db][i] * s);
+          dVh[(size_t)key * D + 32 * db + ln] = pack1<F16>(st.dv[db][i]);
+        }
+      }
+    }
+  }
+}
+
+// dQ = the float32 accumulator rounded to the 16-bit type (the scale was
+// applied before the atomics).  8 elements per thread.
+template <bool F16>
+__global__ __launch_bounds__(256) void bwd_dq_convert_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
+                                                             long long n8) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n8) {
+    const f32x4 x0 = reinterpret_cast<const f32x4*>(acc)[2 * i];
+    const f32x4 x1 = reinterpret_cast<const f32x4*>(acc)[2 * i + 1];
+    reinterpret_cast<bf16x8*>(dq)[i] = pack8<F16>(x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]);
+  }
+}
+
 // ------------------------------------------------------------ 3. dQ
 
 // One work-group of 4 waves per (batch, query head, 128 queries), mirroring the
@@ -375,7 +624,7 @@ hipError_t launch_delta(const BwdArgs& a, hipStream_t stream) {
   constexpr int kRowsPerBlock = 256 / (D / 8);
   hipLaunchKernelGGL((bwd_delta_kernel<D, F16>), dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)),
                      dim3(256), 0, stream, reinterpret_cast<const bf16*>(a.o),
-                     reinterpret_cast<const bf16*>(a.dout), a.lse, a.delta, a.lse2, rows);
+                     reinterpret_cast<const bf16*>(a.dout), a.lse, a.delta, a.lse2, a.dq_acc, rows);
   return hipGetLastError();
 }
 
@@ -394,6 +643,23 @@ hipError_t launch_dq(const BwdArgs& args, hipStream_t stream) {
   a.n_tiles = (a.L + QCfg<D>::BQ - 1) / QCfg<D>::BQ;
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL, F16>), dim3((unsigned)((long long)a.B * a.Hq * a.n_tiles)),
                      dim3(64 * QCfg<D>::kWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool F16>
+hipError_t launch_fused(const BwdArgs& args, hipStream_t stream) {
+  BwdArgs a = args;
+  a.n_tiles = (a.Lk + KVCfg<D>::BK - 1) / KVCfg<D>::BK;
+  hipLaunchKernelGGL((bwd_fused_kernel<D, CAUSAL, F16>), dim3((unsigned)((long long)a.B * a.Hkv * a.n_tiles)),
+                     dim3(64 * KVCfg<D>::kWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <bool F16>
+hipError_t launch_convert(const BwdArgs& a, hipStream_t stream) {
+  const long long n8 = (long long)a.B * a.Hq * a.L * a.d / 8;
+  hipLaunchKernelGGL((bwd_dq_convert_kernel<F16>), dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream,
+                     a.dq_acc, reinterpret_cast<bf16*>(a.dq), n8);
   return hipGetLastError();
 }
 
@@ -431,6 +697,22 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream) {
   e = launch_bwd_dkdv_bf16(a, causal, stream);
   if (e != hipSuccess) return e;
   return launch_bwd_dq_bf16(a, causal, stream);
+}
+
+namespace {
+template <bool F16>
+hipError_t fused_typed(const BwdArgs& a, bool causal, hipStream_t stream) {
+  if (a.d == 128) return causal ? launch_fused<128, true, F16>(a, stream) : launch_fused<128, false, F16>(a, stream);
+  return causal ? launch_fused<64, true, F16>(a, stream) : launch_fused<64, false, F16>(a, stream);
+}
+}  // namespace
+
+hipError_t launch_bwd_fused_bf16(const BwdArgs& a, bool causal, hipStream_t stream) {
+  hipError_t e = launch_bwd_preprocess_bf16(a, stream);
+  if (e != hipSuccess) return e;
+  e = a.f16 ? fused_typed<true>(a, causal, stream) : fused_typed<false>(a, causal, stream);
+  if (e != hipSuccess) return e;
+  return a.f16 ? launch_convert<true>(a, stream) : launch_convert<false>(a, stream);
 }
 
 }  // namespace fa

@@ -49,6 +49,49 @@ struct KVAddr {
   int kv;                              // row reads of the wave's 32 keys in the padded K/V block
 };
 
+// Compact addressing of swz_dual tiles (the fused backward, whose larger
+// register state leaves no room for one offset per read): every offset is a
+// per-lane base plus (a loop-invariant multiple of the step) XOR a per-lane
+// swizzle term, one v_xad_u32 per read.
+//   row read, head dims 16k + 8g .. +7 of row r:
+//     r * 2D + ((2k + g) ^ swz) * 16 = [r * 2D + ((g ^ swz0) << 4)] + ((32k) ^ ((swz & ~1) << 4))
+//   transposing read, column block db (16-byte chunk 4db + c, c < 4):
+//     [row * 2D + ((c ^ (swz & 3)) << 4) + 8 * (col bit 2)] + ((64 db) ^ ((swz & ~3) << 4))
+template <int D>
+struct DualRow {
+  int base, swz;
+  __device__ __forceinline__ void init(int r, int g) {
+    const int sw = swz_dual<D>(r);
+    base = r * (2 * D) + ((g ^ (sw & 1)) << 4);
+    swz = (sw & ~1) << 4;
+  }
+  __device__ __forceinline__ int at(int k) const { return base + ((32 * k) ^ swz); }
+};
+template <int D>
+struct DualTr {
+  int base, swz;
+  // the lanes' 8-byte pieces for key step t, half h (tr_offset_dual with db = 0)
+  __device__ __forceinline__ void init(int t, int h, int lane) {
+    const int s16 = lane & 15, jg = lane >> 4;
+    const int row = 16 * t + 8 * h + 4 * (lane >> 5) + (s16 >> 2);
+    const int col = 16 * (jg & 1) + 4 * (s16 & 3);
+    const int sw = swz_dual<D>(row);
+    base = row * (2 * D) + (((col >> 3) ^ (sw & 3)) << 4) + ((col & 4) << 1);
+    swz = (sw & ~3) << 4;
+  }
+  __device__ __forceinline__ int at(int db) const { return base + ((64 * db) ^ swz); }
+};
+
+// Addresses of the fused backward's dK/dV tile: Q / dO rows and transposed
+// pieces (swz_dual tiles), the K block's rows (swz_dual), V's rows (padded).
+template <int D>
+struct KVAddrDual {
+  DualRow<D> qrow;        // the wave's 32 queries, row reads
+  DualTr<D> qtr[2];       // transposing reads (t = 2*qh), halves 0 and 1
+  DualRow<D> krow;        // the wave's 32 keys in the K block
+  int kv;                 // the same keys' rows in the padded V block
+};
+
 // Key-major element mask of the range-tiled kernels: the lane's key j is
 // fixed; query row q sits at key position q + shift (visibility as range_ok).
 template <bool CAUSAL>
@@ -63,18 +106,66 @@ struct RangeMaskK {
 // One streamed 64-query tile for one wave of the dK/dV kernel.  need_mask
 // (wave-uniform) says whether the wave's 32 x 32 block straddles a mask
 // boundary; ok(q) then says whether query row q sees the lane's key.
-template <int D, bool F16, class Mask>
-__device__ __forceinline__ void kv_tile(KVState<D>& st, const KVAddr<D>& ad, const char* kblk, const char* vblk,
+//
+// KDUAL: the K block is stored with swz_dual (the fused backward also reads it
+// transposed) instead of padded rows.  DS_OUT: also write this wave's dS
+// (16-bit) into the dS exchange buffer at dsbuf, for dQ = dS K.
+// A copy of the compact addresses that the compiler cannot hoist out of the
+// tile loop: offsets derived from it are formed next to their reads instead of
+// being precomputed once and kept (or spilled) for the whole kernel.
+template <int D>
+__device__ __forceinline__ KVAddrDual<D> fresh(const KVAddrDual<D>& ad) {
+  KVAddrDual<D> r = ad;
+  asm volatile("" : "+v"(r.qrow.base), "+v"(r.qrow.swz), "+v"(r.qtr[0].base), "+v"(r.qtr[0].swz),
+               "+v"(r.qtr[1].base), "+v"(r.qtr[1].swz), "+v"(r.krow.base), "+v"(r.krow.swz));
+  return r;
+}
+template <int D>
+__device__ __forceinline__ const KVAddr<D>& fresh(const KVAddr<D>& ad) { return ad; }
+
+template <int D>
+__device__ __forceinline__ int kv_qrow(const KVAddr<D>& ad, int k) { return ad.row[k]; }
+template <int D>
+__device__ __forceinline__ int kv_qrow(const KVAddrDual<D>& ad, int k) { return ad.qrow.at(k); }
+template <int D>
+__device__ __forceinline__ int kv_qtr(const KVAddr<D>& ad, int db, int h) { return ad.tr[db][h]; }
+template <int D>
+__device__ __forceinline__ int kv_qtr(const KVAddrDual<D>& ad, int db, int h) { return ad.qtr[h].at(db); }
+template <int D>
+__device__ __forceinline__ int kv_krow(const KVAddr<D>& ad, int k) { return ad.kv + 32 * k; }
+template <int D>
+__device__ __forceinline__ int kv_krow(const KVAddrDual<D>& ad, int k) { return ad.krow.at(k); }
+
+template <int D, bool F16, bool DS_OUT = false, class Addr, class Mask>
+__device__ __forceinline__ void kv_tile(KVState<D>& st, const Addr& ad_in, const char* kblk, const char* vblk,
                                         const char* qbuf, const char* dobuf, const float* stats, int q0,
-                                        bool need_mask, const Mask& ok, int qh, float c, int lane) {
+                                        bool need_mask, const Mask& ok, int qh, float c, int lane,
+                                        char* dsbuf = nullptr, int ds_row = 0) {
   using C = KVCfg<D>;
+  const auto& ad = fresh<D>(ad_in);
   const int g = lane >> 5;
+  auto krow = [&](int k) { return kv_krow<D>(ad, k); };
+
+  // With DS_OUT (the fused backward, short of registers) the operand reads of
+  // each MFMA chain run at most two steps ahead of their MFMAs.
+  auto chain_order = [&]() {
+    if constexpr (DS_OUT) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int k = 0; k < C::NSTEP - 2; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+    }
+  };
 
   // S = Q K^T (32 queries x 32 keys): lane = key, registers = queries
-  f32x16 p = mfma32x<F16>(lds_load16(qbuf, ad.row[0]), lds_load16(kblk, ad.kv), f32x16{});
+  f32x16 p = mfma32x<F16>(lds_load16(qbuf, kv_qrow<D>(ad, 0)), lds_load16(kblk, krow(0)), f32x16{});
 #pragma unroll
   for (int k = 1; k < C::NSTEP; ++k)
-    p = mfma32x<F16>(lds_load16(qbuf, ad.row[k]), lds_load16(kblk, ad.kv + 32 * k), p);
+    p = mfma32x<F16>(lds_load16(qbuf, kv_qrow<D>(ad, k)), lds_load16(kblk, krow(k)), p);
+  chain_order();
 
   // P = exp2(S*s*log2e - LSE*log2e), zero where masked
   const int qw0 = q0 + 32 * qh;           // first query of this wave's half
@@ -100,16 +191,17 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const KVAddr<D>& ad, con
     const bf16x8 pa = pack8<F16>(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5], p[o8 + 6], p[o8 + 7]);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const bf16x8 bo = concat4(lds_load_tr(dobuf, ad.tr[db][0] + u * 16 * (2 * D)),
-                                lds_load_tr(dobuf, ad.tr[db][1] + u * 16 * (2 * D)));
+      const bf16x8 bo = concat4(lds_load_tr(dobuf, kv_qtr<D>(ad, db, 0) + u * 16 * (2 * D)),
+                                lds_load_tr(dobuf, kv_qtr<D>(ad, db, 1) + u * 16 * (2 * D)));
       st.dv[db] = mfma32x<F16>(pa, bo, st.dv[db]);
     }
   }
   // dP = dO V^T, then dS = P * (dP - D) in place
-  f32x16 dp = mfma32x<F16>(lds_load16(dobuf, ad.row[0]), lds_load16(vblk, ad.kv), f32x16{});
+  f32x16 dp = mfma32x<F16>(lds_load16(dobuf, kv_qrow<D>(ad, 0)), lds_load16(vblk, ad.kv), f32x16{});
 #pragma unroll
   for (int k = 1; k < C::NSTEP; ++k)
-    dp = mfma32x<F16>(lds_load16(dobuf, ad.row[k]), lds_load16(vblk, ad.kv + 32 * k), dp);
+    dp = mfma32x<F16>(lds_load16(dobuf, kv_qrow<D>(ad, k)), lds_load16(vblk, ad.kv + 32 * k), dp);
+  chain_order();
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
     const f32x4 d4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (C::BQ + 32 * qh + 8 * i4 + 4 * g));
@@ -121,10 +213,20 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const KVAddr<D>& ad, con
   for (int u = 0; u < 2; ++u) {
     const int o8 = 8 * u;
     const bf16x8 da = pack8<F16>(p[o8 + 0], p[o8 + 1], p[o8 + 2], p[o8 + 3], p[o8 + 4], p[o8 + 5], p[o8 + 6], p[o8 + 7]);
+    if constexpr (DS_OUT) {
+      // registers 4*i4 .. 4*i4 + 3 are queries 8*i4 + 4g .. +3 of the half:
+      // chunk 8qh + 2*i4 + g of the key's row
+      typedef short i16x8 __attribute__((ext_vector_type(8)));
+      const i16x8 w = __builtin_bit_cast(i16x8, da);
+      *(FA_LDS i16x4*)((FA_LDS char*)dsbuf + ds_offset(ds_row, 8 * qh + 4 * u + g)) =
+          __builtin_shufflevector(w, w, 0, 1, 2, 3);
+      *(FA_LDS i16x4*)((FA_LDS char*)dsbuf + ds_offset(ds_row, 8 * qh + 4 * u + 2 + g)) =
+          __builtin_shufflevector(w, w, 4, 5, 6, 7);
+    }
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) {
-      const bf16x8 bq = concat4(lds_load_tr(qbuf, ad.tr[db][0] + u * 16 * (2 * D)),
-                                lds_load_tr(qbuf, ad.tr[db][1] + u * 16 * (2 * D)));
+      const bf16x8 bq = concat4(lds_load_tr(qbuf, kv_qtr<D>(ad, db, 0) + u * 16 * (2 * D)),
+                                lds_load_tr(qbuf, kv_qtr<D>(ad, db, 1) + u * 16 * (2 * D)));
       st.dk[db] = mfma32x<F16>(da, bq, st.dk[db]);
     }
   }

@@ -256,6 +256,31 @@ __host__ __device__ __forceinline__ int row_offset_dual(int r, int k, int g) {
   return r * (2 * D) + (((2 * k + g) ^ swz_dual<D>(r)) << 4);
 }
 
+// dS exchange buffer of the fused backward: [128 keys][64 queries] of 16-bit
+// values, rows of 128 bytes.  The 8-byte chunk c of row r (queries 4c ..
+// 4c + 3) is stored at chunk c ^ ds_swz(r).  The swizzle is a bijection over
+// the 16 rows of one parity in any aligned 32-row window, and rows 4n and
+// 4n + 2 (likewise 4n + 1 and 4n + 3) differ in its bit 3, so both access
+// patterns are free of bank conflicts: the writes from an MFMA C layout (32
+// consecutive rows, one chunk each) and the transposing reads (4 consecutive
+// rows x 8 consecutive chunks per half-wave).  Its period is 32 rows.
+__host__ __device__ __forceinline__ int ds_swz(int r) {
+  const int u = (r >> 1) & 15;
+  return ((u & 1) << 3) | (u >> 1);
+}
+__host__ __device__ __forceinline__ int ds_offset(int r, int c) { return r * 128 + 8 * (c ^ ds_swz(r)); }
+
+// Byte offset of the 8 bytes lane `lane` supplies to the transposing read of
+// the dS buffer for key step t (keys 16t .. 16t + 15), half h and query half
+// qh: result lane l then holds query 32qh + l % 32 and its slots the keys
+// 16t + 8h + 4*(l/32) + slot % 4 -- the A operand of dQ = dS K in the key
+// labelling of an MFMA C layout.
+__host__ __device__ __forceinline__ int ds_tr_offset(int t, int h, int qh, int lane) {
+  const int s16 = lane & 15, jg = lane >> 4;
+  const int row = 16 * t + 8 * h + 4 * (lane >> 5) + (s16 >> 2);
+  return ds_offset(row, 8 * qh + 4 * (jg & 1) + (s16 & 3));
+}
+
 // Work-group -> (head, query-tile) remap.  Work-groups are dealt round-robin to
 // the 8 XCDs (each with its own L2), so when the grid is a multiple of 8 the
 // index is permuted such that consecutive logical indices run on one XCD:

@@ -32,6 +32,7 @@ struct BwdArgs {
   void* dv;
   float* delta;      // workspace: D_i = sum_c dO_ic * O_ic, [B, Hq, L]
   float* lse2;       // workspace: LSE_i * log2(e), [B, Hq, L]
+  float* dq_acc;     // workspace of the fused backward: float32 dQ accumulator [B, Hq, L, d], or null
   int B, Hq, Hkv, L, d;  // L = query rows
   int Lk;            // keys (= L except for chunk pairs)
   int shift;         // query row i sits at key position i + shift (0 except for chunk pairs)
@@ -60,6 +61,10 @@ hipError_t launch_bwd_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
 hipError_t launch_bwd_preprocess_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_bwd_dkdv_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
 hipError_t launch_bwd_dq_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
+// the fused backward: preprocess (also zeroing a.dq_acc), one K/V-stationary
+// kernel producing dK, dV and accumulating dQ into a.dq_acc with float32
+// atomics, and a conversion of a.dq_acc into dQ
+hipError_t launch_bwd_fused_bf16(const BwdArgs& a, bool causal, hipStream_t stream);
 // exact combination of two partial results; dtype 0 fp32, 1 bf16, 2 fp16
 hipError_t launch_merge(const MergeArgs& a, int d, int dtype, hipStream_t stream);
 

@@ -35,11 +35,21 @@ int check_common(int B, int Hq, int Hkv, int L, int d, float scale, int causal, 
   return FA_OK;
 }
 
-// Backward workspace: two float32 per query row -- D_i and LSE_i*log2(e).
+// Backward row statistics: two float32 per query row -- D_i and LSE_i*log2(e).
+// The staged (deterministic) backward needs only these.
 size_t workspace_bytes(int B, int Hq, int L) {
   const size_t raw = 2 * (size_t)B * (size_t)Hq * (size_t)L * sizeof(float);
   return (raw + 255) & ~(size_t)255;
 }
+
+// The fused backward adds its float32 dQ accumulator [B, Hq, L, d] after them.
+size_t fused_workspace_bytes(int B, int Hq, int L, int d) {
+  return workspace_bytes(B, Hq, L) + (size_t)B * Hq * L * d * sizeof(float);
+}
+
+// The fused kernel adds into one query head of the accumulator through a
+// buffer resource whose byte range is 32 bits.
+bool fused_fits(int L, int d) { return (size_t)L * d * sizeof(float) < ((size_t)1 << 32); }
 
 // Chunk positions: offsets are non-negative and at most 2^29, so every
 // position (offset + index < 2^29 + 2^23) and every distance between a query
@@ -100,6 +110,11 @@ extern "C" size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, 
   return workspace_bytes(B, Hq, L);
 }
 
+extern "C" size_t flash_attn_bwd_fused_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int dtype) {
+  if (check_common(B, Hq, Hkv, L, d, 1.f, 0, 0, dtype) != FA_OK || !fused_fits(L, d)) return 0;
+  return fused_workspace_bytes(B, Hq, L, d);
+}
+
 namespace {
 
 // Common validation of the backward entry points; fills the kernel arguments.
@@ -142,6 +157,24 @@ extern "C" int flash_attn_bwd(const void* q, const void* k, const void* v, const
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv;
   hipError_t e = fa::launch_bwd_bf16(a, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" int flash_attn_bwd_fused(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                    const void* dout, void* dq, void* dk, void* dv,
+                                    void* workspace, size_t workspace_bytes,
+                                    int B, int Hq, int Hkv, int L, int d,
+                                    float softmax_scale, int causal, int window, int dtype, void* stream) {
+  fa::BwdArgs a{};
+  int rc = bwd_setup(a, workspace, workspace_bytes, B, Hq, Hkv, L, d, softmax_scale, causal, window, dtype);
+  if (rc != FA_OK) return rc;
+  if (!fused_fits(L, d)) return FA_ERR_UNSUPPORTED;
+  if (workspace_bytes < fused_workspace_bytes(B, Hq, L, d)) return FA_ERR_WORKSPACE;
+  if (!all_aligned({q, k, v, o, lse, dout, dq, dk, dv})) return FA_ERR_INVALID_ARG;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ::workspace_bytes(B, Hq, L));
+  hipError_t e = fa::launch_bwd_fused_bf16(a, causal != 0, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -121,6 +121,31 @@ int flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, c
                    float softmax_scale, int causal, int window, int dtype, void* stream);
 
 /*
+ * flash_attn_bwd_fused: the same gradient from one K/V-stationary kernel that
+ * also produces dQ -- every work-group adds its 128 keys' share s * dS K into
+ * a float32 accumulator [B, Hq, L, d] in the workspace with atomics, and a
+ * last kernel rounds the accumulator to dQ -- so S and dP are formed once
+ * instead of twice (claspmoon.cn "14 · 缩放定律与高效注意力" §3.3: the
+ * backward recomputes the attention matrix once).  dK and dV equal
+ * flash_attn_bwd's bit for bit; dQ is summed in an order that varies from run
+ * to run, so it matches to float32 rounding, not bitwise.  On MI355X the
+ * float32 atomics make it slower than flash_attn_bwd; it is kept for callers
+ * that want the single-kernel form and for the comparison.
+ *   workspace, workspace_bytes : at least flash_attn_bwd_fused_workspace_bytes()
+ *                                bytes, 256-byte aligned: the row statistics,
+ *                                then the accumulator (4*B*Hq*L*d bytes)
+ * Requires L * d * 4 < 2^32 (one query head of the accumulator is addressed
+ * with 32-bit offsets), else FA_ERR_UNSUPPORTED; the workspace size function
+ * then returns 0.  Other arguments and return codes as flash_attn_bwd.
+ */
+size_t flash_attn_bwd_fused_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int dtype);
+int flash_attn_bwd_fused(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, void* dq, void* dk, void* dv,
+                         void* workspace, size_t workspace_bytes,
+                         int B, int Hq, int Hkv, int L, int d,
+                         float softmax_scale, int causal, int window, int dtype, void* stream);
+
+/*
  * The backward in three stages, for callers that schedule them (for example
  * dK/dV and dQ on two streams).  flash_attn_bwd runs exactly these three in
  * order on one stream.  Arguments mean what they mean for flash_attn_bwd.

@@ -151,9 +151,78 @@ void check_all() {
   check_tr_reads<D>("bwd dual", dimg, [](int t, int db, int h, int l) { return tr_offset_dual<D>(t, db, h, l); });
 }
 
+// The fused backward's dS exchange: every wave (kb, qh) of the dK/dV
+// work-group writes its 32 keys x 32 queries of dS from the C layout of
+// S = Q K^T (lane = key 32kb + l%32, register i = query 8(i/4) + 4(l/32) +
+// i%4 of the half), four 8-byte writes per lane; the transposing reads then
+// give the A operand of dQ = dS K (lane = query, slots = keys in C-row order).
+void check_ds_exchange() {
+  std::vector<int> img(128 * 64, -1);   // element id = key * 64 + query
+  for (int kb = 0; kb < 4; ++kb)
+    for (int qh = 0; qh < 2; ++qh)
+      for (int i4 = 0; i4 < 4; ++i4) {
+        std::vector<int> offs(64);
+        for (int lane = 0; lane < 64; ++lane) {
+          const int g = lane >> 5, key = 32 * kb + (lane & 31);
+          const int off = ds_offset(key, 8 * qh + 2 * i4 + g);
+          offs[lane] = off;
+          for (int e = 0; e < 4; ++e) img[off / 2 + e] = key * 64 + 32 * qh + 8 * i4 + 4 * g + e;
+        }
+        for (int half = 0; half < 2; ++half) {
+          std::vector<int> part(offs.begin() + 32 * half, offs.begin() + 32 * half + 32);
+          const int deg = bank_conflict_degree(part, 8);
+          CHECK(deg == 1, "dS write kb=%d qh=%d i4=%d half %d: %d-way bank conflict", kb, qh, i4, half, deg);
+        }
+      }
+  for (int v : img) CHECK(v >= 0, "dS buffer element never written");
+  for (int qh = 0; qh < 2; ++qh)
+    for (int t = 0; t < 8; ++t)
+      for (int h = 0; h < 2; ++h) {
+        std::vector<int> offs(64);
+        for (int lane = 0; lane < 64; ++lane) offs[lane] = ds_tr_offset(t, h, qh, lane);
+        for (int lane = 0; lane < 64; ++lane) {
+          const int grp = lane / 16, i = lane % 16, g = lane >> 5;
+          for (int r = 0; r < 4; ++r) {
+            const int sup = 16 * grp + 4 * r + i / 4;
+            const int got = img[offs[sup] / 2 + (i % 4)];
+            const int want = (16 * t + 8 * h + 4 * g + r) * 64 + 32 * qh + (lane & 31);
+            CHECK(got == want, "dS tr read qh=%d t=%d h=%d lane=%d r=%d: got (%d,%d) want (%d,%d)", qh, t, h, lane, r,
+                  got / 64, got % 64, want / 64, want % 64);
+          }
+        }
+        for (int half = 0; half < 2; ++half) {
+          std::vector<int> part(offs.begin() + 32 * half, offs.begin() + 32 * half + 32);
+          const int deg = bank_conflict_degree(part, 8);
+          CHECK(deg == 1, "dS tr read qh=%d t=%d h=%d half %d: %d-way bank conflict", qh, t, h, half, deg);
+        }
+      }
+}
+
+// The fused backward's K block in the swz_dual layout, 128 rows: row reads
+// (S = Q K^T) and the transposing reads of dQ = dS K for all 8 key steps.
+template <int D>
+void check_dual_block128() {
+  auto img = tile_image<D>(128, [](int r) { return swz_dual<D>(r); });
+  check_row_reads<D>("bwd K block dual", img, 128, [](int r, int k, int g) { return row_offset_dual<D>(r, k, g); });
+  for (int t = 0; t < 8; ++t)
+    for (int db = 0; db < D / 32; ++db)
+      for (int h = 0; h < 2; ++h)
+        for (int lane = 0; lane < 64; ++lane) {
+          // key step t is key step 0 shifted by 16t rows: the offset must be additive
+          CHECK(tr_offset_dual<D>(t, db, h, lane) == tr_offset_dual<D>(0, db, h, lane) + t * 16 * 2 * D,
+                "swz_dual tr offset not additive in t (t=%d db=%d h=%d lane=%d)", t, db, h, lane);
+          const int off = tr_offset_dual<D>(t, db, h, lane);
+          const int row = 16 * t + 8 * h + 4 * (lane >> 5) + ((lane & 15) >> 2);
+          CHECK(img[off / 2] / D == row, "dual block tr t=%d row", t);
+        }
+}
+
 int main() {
   check_all<128>();
   check_all<64>();
+  check_ds_exchange();
+  check_dual_block128<128>();
+  check_dual_block128<64>();
   if (failures) {
     std::printf("%d layout check(s) failed\n", failures);
     return 1;

@@ -131,6 +131,9 @@ def test_stage_entry_points_reject_invalid_arguments(lib):
 
 
 def test_workspace_size_formula(lib):
+    """flash_attn_bwd's workspace: two float32 per query row (D and LSE*log2 e)
+    rounded up to 256 bytes.  flash_attn_bwd_fused's adds its float32 dQ
+    accumulator [B, Hq, L, d] after them."""
     f = lib.flash_attn_bwd_workspace_bytes
     assert f(2, 32, 32, 4096, 128, fa.FA_DTYPE_BF16) == 2 * 32 * 4096 * 8
     assert f(1, 3, 1, 5, 64, fa.FA_DTYPE_BF16) == 256
@@ -139,6 +142,29 @@ def test_workspace_size_formula(lib):
     assert f(1, 2, 2, 5, 80, fa.FA_DTYPE_BF16) == 0
     assert f(2, 32, 32, 4096, 128, fa.FA_DTYPE_F16) == 2 * 32 * 4096 * 8
     assert f(2, 32, 32, 4096, 128, 3) == 0
+    ff = lib.flash_attn_bwd_fused_workspace_bytes
+    assert ff(2, 32, 32, 4096, 128, fa.FA_DTYPE_BF16) == 2 * 32 * 4096 * 8 + 2 * 32 * 4096 * 128 * 4
+    assert ff(1, 3, 1, 5, 64, fa.FA_DTYPE_BF16) == 256 + 3 * 5 * 64 * 4
+    assert ff(1, 3, 2, 5, 64, fa.FA_DTYPE_BF16) == 0
+    # one head of the accumulator must stay below 4 GiB (L * d * 4 < 2^32)
+    assert ff(1, 1, 1, 1 << 23, 128, fa.FA_DTYPE_BF16) == 0
+    assert ff(1, 1, 1, (1 << 23) - 1, 128, fa.FA_DTYPE_BF16) == -(-((1 << 23) - 1) * 8 // 256) * 256 + ((1 << 23) - 1) * 512
+
+
+def test_bwd_fused_rejects_invalid_arguments(lib):
+    c = header_constants()
+    ff = lib.flash_attn_bwd_fused_workspace_bytes
+    need = ff(1, 2, 2, 16, 64, fa.FA_DTYPE_BF16)
+
+    def call(ws=FAKE * 16, nb=need, L=16, d=64, dq=FAKE, dtype=fa.FA_DTYPE_BF16):
+        return lib.flash_attn_bwd_fused(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, ws, nb, 1, 2, 2, L, d,
+                                        0.125, 1, 0, dtype, None)
+    assert call(nb=need - 1) == c["FA_ERR_WORKSPACE"]
+    assert call(nb=lib.flash_attn_bwd_workspace_bytes(1, 2, 2, 16, 64, fa.FA_DTYPE_BF16)) == c["FA_ERR_WORKSPACE"]
+    assert call(ws=None) == c["FA_ERR_WORKSPACE"]
+    assert call(dq=None) == c["FA_ERR_INVALID_ARG"]
+    assert call(dtype=fa.FA_DTYPE_F32) == c["FA_ERR_UNSUPPORTED"]
+    assert call(L=1 << 23, d=128, nb=1 << 40) == c["FA_ERR_UNSUPPORTED"]   # one head's accumulator: 4 GiB
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -139,7 +139,21 @@ def test_long_context_backward():
     check_heads_at_full_size(W.LONG_BWD_8K, [(1, 5)])
 
 
-def test_backward_stages_equal_fused_call():
+def same_gradients(a, b, what):
+    """dK and dV bit for bit; dQ -- summed with float32 atomics in the fused
+    backward, so in an order that varies from run to run -- to float32
+    rounding before the final 16-bit rounding: each element within one unit in
+    the last place of the 16-bit result plus 1e-3 of the tensor's largest
+    element (an element that is a small difference of large terms carries the
+    float32 error of the terms), and relative L2 <= 1e-4."""
+    dq_a, dq_b = a[0].float(), b[0].float()
+    bound = dq_b.abs() * 2.0 ** -7 + 1e-3 * float(dq_b.abs().max())
+    assert bool(((dq_a - dq_b).abs() <= bound).all()), what
+    assert float((dq_a - dq_b).norm() / dq_b.norm().clamp_min(1e-30)) <= 1e-4, what
+    assert torch.equal(a[1], b[1]) and torch.equal(a[2], b[2]), what
+
+
+def test_backward_stages_equal_bwd_call():
     """The three exported stages (preprocess, dK/dV, dQ) reproduce flash_attn_bwd bit for bit."""
     for w in (W.small("stages", 1, 4, 2, 513, 128, seed=230, backward=True),
               W.small("stages d64 window", 1, 2, 2, 300, 64, window=50, seed=231, backward=True),
@@ -158,13 +172,75 @@ def test_backward_stages_equal_fused_call():
             assert torch.equal(x, y)
 
 
+FUSED = [
+    W.small("fused L513 gqa2", 1, 4, 2, 513, 128, seed=230, backward=True),
+    W.small("fused d64 window50", 1, 2, 2, 300, 64, window=50, seed=231, backward=True),
+    W.small("fused fp16 noncausal mqa", 1, 2, 1, 257, 128, dtype=torch.float16, causal=False, seed=232,
+            backward=True),
+    W.small("fused L7 noncausal d64", 1, 2, 1, 7, 64, causal=False, seed=233, backward=True),
+    W.small("fused L1", 1, 2, 2, 1, 128, seed=234, backward=True),
+    W.small("fused sym window40 L700", 2, 2, 2, 700, 128, causal=False, window=40, seed=235, backward=True),
+    W.small("fused d64 gqa4 L1000", 1, 8, 2, 1000, 64, seed=236, backward=True),
+]
+
+
+@pytest.mark.parametrize("w", FUSED, ids=[w.name for w in FUSED])
+def test_fused_backward(w):
+    """flash_attn_bwd_fused (one K/V-stationary kernel, dQ by float32 atomics)
+    against the oracle, and against flash_attn_bwd: dK and dV bit for bit, dQ to
+    float32 rounding."""
+    print(f"[parity] fused bwd case {w.name} B{w.B} Hq{w.Hq} Hkv{w.Hkv} L{w.L} d{w.d} causal={w.causal} "
+          f"window={w.window} seed={w.seed}", flush=True)
+    q, k, v, do = W.make_inputs(w, with_dout=True)
+    dev = "cuda:0"
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa().fwd(qd, kd, vd, causal=w.causal, window=w.window, scale=w.scale)
+    a = fa().bwd_fused(qd, kd, vd, o, lse, dod, causal=w.causal, window=w.window, scale=w.scale)
+    b = fa().bwd(qd, kd, vd, o, lse, dod, causal=w.causal, window=w.window, scale=w.scale)
+    torch.cuda.synchronize()
+    a = [x.cpu() for x in a]
+    ref = oracle.backward(f64(q), f64(k), f64(v), f64(do), w.scale, w.causal, w.window)
+    errs = [rel(x, r) for x, r in zip(a, ref)]
+    print(f"[parity] {w.name}: relL2 dQ={errs[0]:.3e} dK={errs[1]:.3e} dV={errs[2]:.3e}", flush=True)
+    assert max(errs) <= REL_TOL
+    same_gradients(a, [x.cpu() for x in b], w.name)
+
+
+def test_fused_backward_full_size():
+    """The fused backward at the LLaMA-7B-shaped layer: whole heads against the oracle."""
+    w = W.LLAMA7B_CAUSAL
+    q, k, v, do = W.make_inputs(w, with_dout=True)
+    dev = "cuda:0"
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa().fwd(qd, kd, vd, causal=True, scale=w.scale)
+    a = fa().bwd_fused(qd, kd, vd, o, lse, dod, causal=True, scale=w.scale)
+    b = fa().bwd(qd, kd, vd, o, lse, dod, causal=True, scale=w.scale)
+    torch.cuda.synchronize()
+    same_gradients([x.cpu() for x in a], [x.cpu() for x in b], w.name)
+    for bb, h in ((0, 0), (1, 31)):
+        sl = (slice(bb, bb + 1), slice(h, h + 1))
+        ref = oracle.backward(f64(q[sl]), f64(k[sl]), f64(v[sl]), f64(do[sl]), w.scale, True, 0)
+        errs = [rel(x.cpu()[sl], r) for x, r in zip(a, ref)]
+        print(f"[parity] fused {w.name} head ({bb},{h}): relL2 dQ={errs[0]:.3e} dK={errs[1]:.3e} dV={errs[2]:.3e}",
+              flush=True)
+        assert max(errs) <= REL_TOL
+
+
 def test_backward_is_deterministic():
+    """flash_attn_bwd is deterministic bit for bit; the fused backward repeats dK
+    and dV bit for bit and dQ to float32 rounding (the order of its atomics)."""
     w = W.small("det", 1, 4, 2, 700, 128, seed=220, backward=True)
     q, k, v, do = W.make_inputs(w, with_dout=True)
     a = gpu_fwd_bwd(w, q, k, v, do)
     b = gpu_fwd_bwd(w, q, k, v, do)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+    dev = "cuda:0"
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = fa().fwd(qd, kd, vd, causal=w.causal, window=w.window, scale=w.scale)
+    f1 = [x.cpu() for x in fa().bwd_fused(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale)]
+    f2 = [x.cpu() for x in fa().bwd_fused(qd, kd, vd, o, lse, dod, causal=w.causal, scale=w.scale)]
+    same_gradients(f1, f2, "fused, two runs")
 
 
 def test_huge_window_backward_equals_no_window():
