@@ -9,10 +9,12 @@
 //     dQ = s dS K,  dK = s dS^T Q.
 // Three kernels, all on the caller's stream, none using atomics:
 //   1. delta:  D_i and LSE_i*log2(e) per query row into the workspace;
-//   2. dK/dV:  one work-group per (batch, K/V head, 128 keys), each wave
-//              holding 32 keys' K and V rows in registers, streams the
-//              allowed 64-query tiles of Q and dO (every query head of the
-//              GQA group) through LDS and accumulates dK and dV in registers;
+//   2. dK/dV:  one work-group per (batch, K/V head, 128 keys) with its K and
+//              V rows staged once in LDS; each of its 8 waves owns 32 keys and
+//              one 32-query half of every allowed 64-query tile of Q and dO
+//              (every query head of the GQA group) streamed through LDS, and
+//              accumulates dK and dV in registers (the two halves are summed
+//              through LDS at the end);
 //   3. dQ:     one work-group per (batch, query head, 128 queries), each wave
 //              holding 32 queries' Q and dO rows in registers, streams the
 //              allowed 64-key tiles of K and V through LDS and accumulates dQ.
