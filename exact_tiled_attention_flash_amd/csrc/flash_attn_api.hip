@@ -29,9 +29,9 @@ int check_common(int B, int Hq, int Hkv, int L, int d, float scale, int causal, 
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (Hq % Hkv != 0) return FA_ERR_GQA;
-  // grid size: one work-group per (batch, head, 64-row tile) at most
-  const long long tiles = ((long long)L + 63) / 64;
-  if ((long long)B * Hq * tiles > 0x7fffffffLL) return FA_ERR_INVALID_ARG;
+  // launch sizes: a 1-D launch covers at most 2^32 - 1 work-items, and the
+  // kernels use up to 4 per query row (or key row), so B*Hq*L stays below 2^30
+  if ((long long)B * Hq * L >= (1LL << 30)) return FA_ERR_INVALID_ARG;
   return FA_OK;
 }
 

@@ -84,7 +84,8 @@ extern "C" {
  *                                     admits all pairs and acts as none
  *   dtype                           : FA_DTYPE_BF16, FA_DTYPE_F16 or
  *                                     FA_DTYPE_F32, each with d in {64,128}
- * Sizes: 1 <= L <= 2^23 (one head must stay below 4 GiB), B, Hq, Hkv >= 1.
+ * Sizes: 1 <= L <= 2^23 (one head must stay below 4 GiB), B, Hq, Hkv >= 1,
+ *        B*Hq*L < 2^30 (launch sizes; beyond 128 GiB per bf16 tensor at d=64).
  * Extra device memory: none.  Returns FA_OK or a negative FA_ERR_* code.
  */
 int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
