@@ -22,7 +22,7 @@ import torch
 
 __all__ = ["fwd", "bwd", "bwd_stages", "bwd_workspace_bytes", "bwd_fused", "bwd_fused_workspace_bytes",
            "bwd_noalloc", "NOALLOC_MAX_ROWS", "fwd_block", "bwd_block", "merge",
-           "decode", "decode_workspace_bytes",
+           "decode", "decode_workspace_bytes", "decode_rolling", "decode_rolling_workspace_bytes",
            "MaskPlan", "fwd_masked", "bwd_masked", "masked_workspace_bytes",
            "strerror", "library", "library_path",
            "FlashAttentionFunction", "scaled_dot_product_attention",
@@ -38,6 +38,7 @@ EXPORTED_SYMBOLS = ("flash_attn_fwd", "flash_attn_bwd", "flash_attn_bwd_workspac
                     "flash_attn_bwd_preprocess", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq",
                     "flash_attn_fwd_block", "flash_attn_merge", "flash_attn_bwd_block",
                     "flash_attn_decode", "flash_attn_decode_workspace_bytes",
+                    "flash_attn_decode_rolling", "flash_attn_decode_rolling_workspace_bytes",
                     "flash_attn_mask_plan_bytes", "flash_attn_mask_plan", "flash_attn_masked_workspace_bytes",
                     "flash_attn_fwd_masked", "flash_attn_bwd_masked",
                     "flash_attn_bwd_noalloc", "flash_attn_strerror", "flash_attn_version")
@@ -98,6 +99,10 @@ def library():
     lib.flash_attn_decode.restype = i
     lib.flash_attn_decode_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.flash_attn_decode_workspace_bytes.restype = sz
+    lib.flash_attn_decode_rolling.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, f, i, i, vp]
+    lib.flash_attn_decode_rolling.restype = i
+    lib.flash_attn_decode_rolling_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.flash_attn_decode_rolling_workspace_bytes.restype = sz
     lib.flash_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.flash_attn_bwd_workspace_bytes.restype = sz
     mp = ctypes.POINTER(FaMask)
@@ -442,7 +447,7 @@ def decode(q, k_cache, v_cache, cache_len=None, causal=True, window=0, scale=Non
     scale, window = _scale(scale, d), _window(window)
     nbytes = decode_workspace_bytes(B, Hq, Hkv, Lq, Lk, d, q.dtype)
     if nbytes == 0:
-        raise RuntimeError("flash_attn_decode: unsupported sizes (Hq/Hkv * Lq must be <= 32)")
+        raise RuntimeError("flash_attn_decode: unsupported sizes")
     workspace = _workspace(workspace, nbytes, q.device)
     out = _out(out, "out", q.shape, q.dtype, q.device)
     lse = _out(lse, "lse", (B, Hq, Lq), torch.float32, q.device)
@@ -450,6 +455,48 @@ def decode(q, k_cache, v_cache, cache_len=None, causal=True, window=0, scale=Non
                                      _ptr(workspace), workspace.numel(), B, Hq, Hkv, Lq, Lk, d, scale,
                                      int(bool(causal)), window, _DTYPES[q.dtype], _stream(q))
     _check(rc, "flash_attn_decode")
+    return out, lse
+
+
+def decode_rolling_workspace_bytes(B, Hq, Hkv, Lq, W, d, dtype=torch.bfloat16):
+    return int(library().flash_attn_decode_rolling_workspace_bytes(B, Hq, Hkv, Lq, W, d, _DTYPES[dtype]))
+
+
+def decode_rolling(q, k_ring, v_ring, k_new, v_new, seen, window=0, scale=None, workspace=None, out=None,
+                   lse=None):
+    """The ``Lq`` new tokens ``q [B,Hq,Lq,d]`` over a rolling buffer ``[B,Hkv,W,d]``.
+
+    Position ``p`` of sequence ``b`` lives in slot ``p % W``; ``seen`` (int32 CUDA
+    tensor ``[B]``) holds the tokens before this call, and ``k_new``/``v_new``
+    ``[B,Hkv,Lq,d]`` the new tokens' own K/V (not yet in the buffer).  New token
+    ``t`` sees positions ``seen[b] + t - w + 1 .. seen[b] + t`` with ``w = window``
+    (0: ``W``).  Returns ``(o, lse)``.
+    """
+    if q.dim() != 4 or k_ring.dim() != 4:
+        raise ValueError("q must be [B, Hq, Lq, d] and the buffers [B, Hkv, W, d]")
+    B, Hq, Lq, d = q.shape
+    Hkv, W = k_ring.shape[1], k_ring.shape[2]
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("decode_rolling takes bfloat16 or float16")
+    _expect(q, "q", (B, Hq, Lq, d), q.dtype, q.device)
+    _expect(k_ring, "k_ring", (B, Hkv, W, d), q.dtype, q.device)
+    _expect(v_ring, "v_ring", (B, Hkv, W, d), q.dtype, q.device)
+    _expect(k_new, "k_new", (B, Hkv, Lq, d), q.dtype, q.device)
+    _expect(v_new, "v_new", (B, Hkv, Lq, d), q.dtype, q.device)
+    _expect(seen, "seen", (B,), torch.int32, q.device)
+    scale, window = _scale(scale, d), int(window)
+    if window < 0 or window > W:
+        raise ValueError("window must be 0 (the whole buffer) or 1 .. W")
+    nbytes = decode_rolling_workspace_bytes(B, Hq, Hkv, Lq, W, d, q.dtype)
+    if nbytes == 0:
+        raise RuntimeError("flash_attn_decode_rolling: unsupported sizes")
+    workspace = _workspace(workspace, nbytes, q.device)
+    out = _out(out, "out", q.shape, q.dtype, q.device)
+    lse = _out(lse, "lse", (B, Hq, Lq), torch.float32, q.device)
+    rc = library().flash_attn_decode_rolling(_ptr(q), _ptr(k_ring), _ptr(v_ring), _ptr(k_new), _ptr(v_new),
+                                             _ptr(seen), _ptr(out), _ptr(lse), _ptr(workspace), workspace.numel(),
+                                             B, Hq, Hkv, Lq, W, d, scale, window, _DTYPES[q.dtype], _stream(q))
+    _check(rc, "flash_attn_decode_rolling")
     return out, lse
 
 

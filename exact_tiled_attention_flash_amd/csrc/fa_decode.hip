@@ -7,8 +7,9 @@
 // at position cache_len[b] - Lq + t (bottom-right alignment).
 //
 // The work is bound by reading the cache from HBM, so the kernel reads each
-// K/V head once for all G query heads and all Lq new tokens -- the R = G*Lq
-// rows become the 32 query columns of the forward's per-tile MFMA step (R <= 32)
+// K/V head once for up to 32 of its rows -- the R = G*Lq rows (G query heads
+// times Lq new tokens) become the 32 query columns of the forward's per-tile
+// MFMA step; R > 32 takes ceil(R/32) row groups, each reading the head again
 // -- and splits the keys across work-groups so that short batches still fill
 // the chip ("split-K").  Each split writes a partial (O, LSE) normalised over
 // its keys to the workspace; the combine kernel merges a row's partials
@@ -16,6 +17,12 @@
 // A work-group stages one tile at a time (37 KiB of LDS), so four of them fit
 // on a CU: the bytes in flight that keep HBM busy come from four work-groups
 // per CU copying at once, more than two double-buffered ones would have.
+//
+// A rolling buffer of W slots (position p in slot p mod W) is read the same way
+// with a slot -> position map: the new tokens' window over the buffer comes
+// from its splits, their own keys (passed separately, not yet in the buffer)
+// from one plain causal pass over them, and the combine merges both kinds of
+// partial.
 #include "fa_fwd_tile.hpp"
 
 namespace fa {
@@ -24,7 +31,38 @@ namespace {
 
 using namespace fwdtile;
 
-template <int D, bool CAUSAL, bool F16>
+// Key positions of a rolling buffer (transformer.xph.ink "高效注意力：FlashAttention
+// 与线性注意力", 实例或案例: Mistral keeps the last W keys in W slots, position p
+// in slot p mod W).  With n tokens seen the slots hold positions
+// max(0, n - W) .. n - 1; h = n mod W is the slot the next token goes to, so
+// slots h .. W-1 hold the oldest positions (n - W ..) and slots 0 .. h-1 the
+// newest (.. n - 1).  Before the buffer is full (n < W) h = n and slot j holds
+// position j.
+struct RingPos {
+  int n, h, W;
+  __device__ __forceinline__ int operator()(int j) const { return j < h ? n - h + j : n - W - h + j; }
+};
+
+// Query-major mask over ring slots: the slot is filled and its position is in
+// the row's window (positions lo .. the row's own; every filled slot precedes it).
+struct RingMaskQ {
+  int filled, lo;
+  RingPos pos;
+  __device__ __forceinline__ bool operator()(int j) const { return j < filled && pos(j) >= lo; }
+};
+
+constexpr int kMaxSeen = 1 << 30;   // tokens seen before a rolling-buffer call (clamped)
+
+// One split of the keys for one (sequence, K/V head, group of 32 rows).  The
+// rows of a K/V head are its G query heads times the Lq new tokens, row
+// r = head * Lq + token; blockIdx.z picks rows 32z .. 32z + 31.
+//   RING = false: the cache holds positions 0 .. n-1 in order (n = cache_len[b]
+//                 or Lk), the new tokens at positions n - Lq .. n - 1;
+//   RING = true:  the cache is a rolling buffer of Lk = W slots (RingPos) after
+//                 n = cache_len[b] tokens; the new tokens sit at positions
+//                 n .. n + Lq - 1 and see the window of a.window positions
+//                 ending at their own (their own keys come from another pass).
+template <int D, bool CAUSAL, bool F16, bool RING>
 __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   using C = FwdCfg<D>;
   __shared__ __attribute__((aligned(1024))) char k_st0[C::KT];
@@ -36,24 +74,27 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const int bhk = blockIdx.y;
   const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
   const int G = a.Hq / a.Hkv, Lq = a.Lq;
-  const int R = G * Lq;
-  // valid cache length of this sequence, clamped so that every access stays
-  // inside the cache even for an out-of-range entry
+  const long long R = (long long)G * Lq;
+  // cache length / tokens seen of this sequence, clamped so that every access
+  // stays inside the cache even for an out-of-range entry
   int n = a.cache_len != nullptr ? a.cache_len[b] : a.Lk;
-  n = __builtin_amdgcn_readfirstlane(min(max(n, Lq), a.Lk));
+  n = RING ? min(max(n, 0), kMaxSeen) : min(max(n, Lq), a.Lk);
+  n = __builtin_amdgcn_readfirstlane(n);
+  const int filled = RING ? min(n, a.Lk) : n;   // keys of the cache that hold tokens
 
   // this lane's row: query head hk*G + r/Lq, new token r%Lq (rows >= R are padding)
-  const int r = ln;
+  const long long r = 32LL * blockIdx.z + ln;
   const bool valid = r < R;
-  const int hq = hk * G + (valid ? r / Lq : 0);
-  const int t = valid ? r % Lq : Lq - 1;
-  const int my_pos = n - Lq + t;
-  const int min_pos = n - Lq, max_pos = n - 1;
+  const int hq = hk * G + (valid ? (int)(r / Lq) : 0);
+  const int t = valid ? (int)(r % Lq) : Lq - 1;
+  const int first = RING ? n : n - Lq;          // position of new token 0
+  const int my_pos = first + t;
+  const int min_pos = first, max_pos = first + Lq - 1;
 
   // keys of this split that any row may see
   const int s_lo = split * a.split_keys;
-  const int k_hi = min(n, s_lo + a.split_keys);   // causal: every row sees up to n - 1
-  const int k_lo = max(s_lo, (a.window > 0) ? max(0, min_pos - a.window + 1) : 0);
+  const int k_hi = min(filled, s_lo + a.split_keys);   // causal: every row sees up to its own position
+  const int k_lo = RING ? s_lo : max(s_lo, (a.window > 0) ? max(0, min_pos - a.window + 1) : 0);
   const bool empty = k_hi <= k_lo;
   const int j_lo = empty ? 0 : k_lo / C::BC, j_hi = empty ? -1 : (k_hi - 1) / C::BC;
 
@@ -86,18 +127,32 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   for (int db = 0; db < C::NDB; ++db) st.o[db] = f32x16{};
   const float c = a.scale_log2;
 
-  // the window of a decode call is one-sided (causal): the key range above
-  // already ends at the newest entry
-  auto tile_mask = [&](int k0) { return range_tile_needs_mask<CAUSAL, C::BC>(k0, n, a.window, min_pos, max_pos); };
-  const RangeMaskQ<CAUSAL> ok{n, a.window, my_pos};
-
   // one stage: the work-group copies a tile, waits, computes; four such
   // work-groups per CU keep several tiles in flight
-  for (int j = j_lo; j <= j_hi; ++j) {
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    issue(j, k_st0, v_st0);
-    wait_copies_and_barrier();
-    fwd_tile<D, F16>(st, k_st0, v_st0, j * C::BC, tile_mask(j * C::BC), ok, c, lane);
+  auto run = [&](const auto& tile_mask, const auto& ok) {
+    for (int j = j_lo; j <= j_hi; ++j) {
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      issue(j, k_st0, v_st0);
+      wait_copies_and_barrier();
+      fwd_tile<D, F16>(st, k_st0, v_st0, j * C::BC, tile_mask(j * C::BC), ok, c, lane);
+    }
+  };
+  if constexpr (RING) {
+    // a tile needs the mask if it holds an empty slot or a position that the
+    // last new token's window (the narrowest) no longer covers; its oldest
+    // position is at slot h when the tile holds it, else at its first slot
+    const RingPos pos{n, n % a.Lk, a.Lk};
+    const int all_lo = max_pos - a.window + 1;
+    auto tile_mask = [&](int k0) {
+      const int oldest = (pos.h >= k0 && pos.h < k0 + C::BC && pos.h < filled) ? pos(pos.h) : pos(k0);
+      return k0 + C::BC > filled || oldest < all_lo;
+    };
+    run(tile_mask, RingMaskQ{filled, my_pos - a.window + 1, pos});
+  } else {
+    // the window of a plain decode call is one-sided (causal): the key range
+    // above already ends at the newest entry
+    auto tile_mask = [&](int k0) { return range_tile_needs_mask<CAUSAL, C::BC>(k0, n, a.window, min_pos, max_pos); };
+    run(tile_mask, RangeMaskQ<CAUSAL>{n, a.window, my_pos});
   }
 
   // partial for this split: O normalised over its keys (fp32), LSE in ln units
@@ -105,7 +160,7 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   const float l_tot = pair_sum(st.l_run);
   if (valid) {
     const size_t row = (size_t)(b * a.Hq + hq) * Lq + t;
-    const size_t prow = (size_t)split * a.rows + row;
+    const size_t prow = (size_t)(a.split_base + split) * a.rows + row;
     float* po = a.part_o + prow * D;
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
 #pragma unroll
@@ -135,7 +190,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int t = threadIdx.x, grp = t / kLanesPerRow, part = t % kLanesPerRow;
   // 1. the largest split LSE of the row
   float m = -INFINITY;
-  for (int s = t; s < a.n_splits; s += 256) m = fmaxf(m, a.part_lse[(size_t)s * a.rows + row]);
+  for (int s = t; s < a.n_splits_total; s += 256) m = fmaxf(m, a.part_lse[(size_t)s * a.rows + row]);
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
   if ((t & 63) == 0) wmax[t >> 6] = m;
@@ -145,7 +200,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   float tot = 0.f;
   if (m != -INFINITY) {
-    for (int s = grp; s < a.n_splits; s += kGroups) {
+    for (int s = grp; s < a.n_splits_total; s += kGroups) {
       const float w = __expf(a.part_lse[(size_t)s * a.rows + row] - m);   // exp(-inf) = 0
       if (w == 0.f) continue;
       const f32x4* p = reinterpret_cast<const f32x4*>(a.part_o + ((size_t)s * a.rows + row) * D + 8 * part);
@@ -180,13 +235,38 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   if (part == 0 && a.lse != nullptr) a.lse[row] = sum > 0.f ? m + __logf(sum) : -INFINITY;
 }
 
-template <int D, bool CAUSAL, bool F16>
-hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, F16>), dim3(a.n_splits, a.B * a.Hkv), dim3(64), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+// groups of 32 rows (query heads x new tokens) of one K/V head
+inline unsigned row_groups(const DecodeArgs& a) {
+  return (unsigned)(((long long)(a.Hq / a.Hkv) * a.Lq + 31) / 32);
+}
+
+template <int D, bool CAUSAL, bool F16, bool RING>
+hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, F16, RING>), dim3(a.n_splits, a.B * a.Hkv, row_groups(a)),
+                     dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, bool F16>
+hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_combine_kernel<D, F16>), dim3((unsigned)a.rows), dim3(256), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool F16>
+hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  hipError_t e = launch_split<D, CAUSAL, F16, false>(a, stream);
+  if (e != hipSuccess) return e;
+  return launch_combine<D, F16>(a, stream);
+}
+
+template <int D, bool F16>
+hipError_t launch_rolling(const DecodeArgs& ring, const DecodeArgs& fresh, hipStream_t stream) {
+  hipError_t e = launch_split<D, true, F16, true>(ring, stream);
+  if (e != hipSuccess) return e;
+  e = launch_split<D, true, F16, false>(fresh, stream);
+  if (e != hipSuccess) return e;
+  return launch_combine<D, F16>(ring, stream);
 }
 
 }  // namespace
@@ -208,6 +288,11 @@ void decode_plan(int B, int Hkv, int Lk, int& n_splits, int& split_keys) {
   const int per = (tiles + want - 1) / want;
   split_keys = per * kBC;
   n_splits = (tiles + per - 1) / per;
+}
+
+hipError_t launch_decode_rolling(const DecodeArgs& ring, const DecodeArgs& fresh, hipStream_t stream) {
+  if (ring.d == 128) return ring.f16 ? launch_rolling<128, true>(ring, fresh, stream) : launch_rolling<128, false>(ring, fresh, stream);
+  return ring.f16 ? launch_rolling<64, true>(ring, fresh, stream) : launch_rolling<64, false>(ring, fresh, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, bool causal, hipStream_t stream) {

@@ -83,10 +83,16 @@ struct DecodeArgs {
   bool f16;
   int n_splits, split_keys;
   long long rows;         // B * Hq * Lq
+  int split_base;         // index of this launch's first split among the partials
+  int n_splits_total;     // partials the combine merges per row
 };
 // key splits for a decode call (deterministic in its sizes)
 void decode_plan(int B, int Hkv, int Lk, int& n_splits, int& split_keys);
 hipError_t launch_decode(const DecodeArgs& a, bool causal, hipStream_t stream);
+// Rolling (ring) cache of Lk = W slots, position p of sequence b in slot p mod W,
+// cache_len = tokens seen before the call; `fresh` holds the new tokens' own
+// K/V ([B, Hkv, Lq, d], k and v of it) with their splits after the ring's.
+hipError_t launch_decode_rolling(const DecodeArgs& ring, const DecodeArgs& fresh, hipStream_t stream);
 
 // ---- general masks through a mask plan
 // A mask over one sequence of L positions (queries and keys alike):

@@ -315,14 +315,34 @@ extern "C" int flash_attn_merge(const void* o_a, const float* lse_a, const void*
 namespace {
 
 // Validation shared by the decode entry points; fills the plan.
-int decode_check(int B, int Hq, int Hkv, int Lq, int Lk, int d, int dtype, int& n_splits, int& split_keys) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lk < Lq || Lk > kMaxL) return FA_ERR_INVALID_ARG;
+// sizes shared by the decode calls: Lq new tokens per sequence against a
+// cache (or rolling buffer) of Lk entries
+int decode_sizes(int B, int Hq, int Hkv, int Lq, int Lk, int d, int dtype) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Lq < 1 || Lq > kMaxL || Lk < 1 || Lk > kMaxL) return FA_ERR_INVALID_ARG;
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F16) return FA_ERR_UNSUPPORTED;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
   if (Hq % Hkv != 0) return FA_ERR_GQA;
-  if ((Hq / Hkv) * Lq > 32) return FA_ERR_UNSUPPORTED;    // rows of one K/V head: one MFMA column block
-  if ((long long)B * Hkv > 65535) return FA_ERR_INVALID_ARG;
+  if ((long long)B * Hkv > 65535) return FA_ERR_INVALID_ARG;               // grid rows
+  if (((long long)(Hq / Hkv) * Lq + 31) / 32 > 65535) return FA_ERR_UNSUPPORTED;   // row groups of 32
+  if ((long long)B * Hq * Lq >= (1LL << 30)) return FA_ERR_INVALID_ARG;   // combine grid
+  return FA_OK;
+}
+
+int decode_check(int B, int Hq, int Hkv, int Lq, int Lk, int d, int dtype, int& n_splits, int& split_keys) {
+  const int rc = decode_sizes(B, Hq, Hkv, Lq, Lk, d, dtype);
+  if (rc != FA_OK) return rc;
+  if (Lk < Lq) return FA_ERR_INVALID_ARG;
   fa::decode_plan(B, Hkv, Lk, n_splits, split_keys);
+  return FA_OK;
+}
+
+// the rolling-buffer decode: key splits of the W-slot buffer, then of the Lq new tokens' own keys
+int rolling_check(int B, int Hq, int Hkv, int Lq, int W, int d, int dtype, int& ns_ring, int& sk_ring, int& ns_new,
+                  int& sk_new) {
+  const int rc = decode_sizes(B, Hq, Hkv, Lq, W, d, dtype);
+  if (rc != FA_OK) return rc;
+  fa::decode_plan(B, Hkv, W, ns_ring, sk_ring);
+  fa::decode_plan(B, Hkv, Lq, ns_new, sk_new);
   return FA_OK;
 }
 
@@ -366,7 +386,53 @@ extern "C" int flash_attn_decode(const void* q, const void* k_cache, const void*
   a.f16 = dtype == FA_DTYPE_F16;
   a.n_splits = ns;
   a.split_keys = sk;
+  a.split_base = 0;
+  a.n_splits_total = ns;
   hipError_t e = fa::launch_decode(a, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+extern "C" size_t flash_attn_decode_rolling_workspace_bytes(int B, int Hq, int Hkv, int Lq, int W, int d, int dtype) {
+  int nr = 0, sr = 0, nn = 0, sn = 0;
+  if (rolling_check(B, Hq, Hkv, Lq, W, d, dtype, nr, sr, nn, sn) != FA_OK) return 0;
+  return decode_bytes(B, Hq, Lq, d, nr + nn);
+}
+
+extern "C" int flash_attn_decode_rolling(const void* q, const void* k_ring, const void* v_ring, const void* k_new,
+                                         const void* v_new, const int* seen, void* o, float* lse, void* workspace,
+                                         size_t workspace_bytes, int B, int Hq, int Hkv, int Lq, int W, int d,
+                                         float softmax_scale, int window, int dtype, void* stream) {
+  int nr = 0, sr = 0, nn = 0, sn = 0;
+  int rc = rolling_check(B, Hq, Hkv, Lq, W, d, dtype, nr, sr, nn, sn);
+  if (rc != FA_OK) return rc;
+  if (!(softmax_scale > 0.f) || !isfinite(softmax_scale)) return FA_ERR_INVALID_ARG;
+  if (window < 0 || window > W) return FA_ERR_INVALID_ARG;   // older keys are gone from the buffer
+  if (!all_aligned({q, k_ring, v_ring, k_new, v_new, o})) return FA_ERR_INVALID_ARG;
+  if (seen == nullptr || (reinterpret_cast<uintptr_t>(seen) & 3u) != 0) return FA_ERR_INVALID_ARG;
+  if (lse && !aligned16(lse)) return FA_ERR_INVALID_ARG;
+  if (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      workspace_bytes < decode_bytes(B, Hq, Lq, d, nr + nn))
+    return FA_ERR_WORKSPACE;
+  fa::DecodeArgs ring{};
+  ring.q = q; ring.k = k_ring; ring.v = v_ring; ring.cache_len = seen; ring.o = o; ring.lse = lse;
+  ring.rows = (long long)B * Hq * Lq;
+  ring.part_o = static_cast<float*>(workspace);
+  ring.part_lse = ring.part_o + (size_t)(nr + nn) * (size_t)ring.rows * d;
+  ring.B = B; ring.Hq = Hq; ring.Hkv = Hkv; ring.Lq = Lq; ring.Lk = W; ring.d = d;
+  ring.window = window == 0 ? W : window;
+  ring.scale_log2 = softmax_scale * 1.4426950408889634f;
+  ring.f16 = dtype == FA_DTYPE_F16;
+  ring.n_splits = nr;
+  ring.split_keys = sr;
+  ring.split_base = 0;
+  ring.n_splits_total = nr + nn;
+  // the new tokens against their own keys: a plain causal decode whose cache is exactly them
+  fa::DecodeArgs fresh = ring;
+  fresh.k = k_new; fresh.v = v_new; fresh.cache_len = nullptr; fresh.Lk = Lq;
+  fresh.n_splits = nn;
+  fresh.split_keys = sn;
+  fresh.split_base = nr;
+  hipError_t e = fa::launch_decode_rolling(ring, fresh, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

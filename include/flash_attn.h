@@ -241,22 +241,58 @@ int flash_attn_bwd_block(const void* q, const void* k, const void* v, const void
  * New token t of sequence b sits at position n_b - Lq + t (bottom-right
  * alignment): causal = 1 lets it see entries 0 .. that position (window w:
  * the last w of them); causal = 0 lets every new token see all n_b entries.
- * A rolling window buffer (transformer.xph.ink 实例或案例: Mistral's sliding
- * window keeps the last W keys in a ring of W slots) is served with causal = 0
- * and cache_len = the number of filled slots: for one new token the slot order
- * does not matter.  The keys are split across work-groups and the partials
- * merged exactly, so the cache is read once per K/V head whatever G and Lq.
+ * (A rolling window buffer has its own call, flash_attn_decode_rolling; for a
+ * single new token it can also be served here with causal = 0 and cache_len =
+ * the number of filled slots, since the slot order then does not matter.)
+ * The keys are split across work-groups and the partials merged exactly; the
+ * cache is read once per K/V head for every 32 rows of R = (Hq/Hkv) * Lq
+ * (query heads times new tokens), so R <= 32 reads it once.  For long chunks
+ * of new tokens flash_attn_fwd_block is the faster call.
  * A window needs causal = 1 here (FA_ERR_UNSUPPORTED otherwise).
- * Requires (Hq/Hkv) * Lq <= 32 (else FA_ERR_UNSUPPORTED: use
- * flash_attn_fwd_block for longer chunks), d in {64,128}, bf16 or fp16,
- * B * Hkv <= 65535.  workspace: at least flash_attn_decode_workspace_bytes()
- * bytes, 256-byte aligned (float32 partials of every key split).
+ * Requires 1 <= Lq <= Lk <= 2^23, d in {64,128}, bf16 or fp16, B * Hkv <=
+ * 65535, ceil(R / 32) <= 65535 (else FA_ERR_UNSUPPORTED) and B * Hq * Lq <
+ * 2^30.  workspace: at least flash_attn_decode_workspace_bytes() bytes,
+ * 256-byte aligned (float32 partials of every key split).
  */
 size_t flash_attn_decode_workspace_bytes(int B, int Hq, int Hkv, int Lq, int Lk, int d, int dtype);
 int flash_attn_decode(const void* q, const void* k_cache, const void* v_cache, const int* cache_len,
                       void* o, float* lse, void* workspace, size_t workspace_bytes,
                       int B, int Hq, int Hkv, int Lq, int Lk, int d, float softmax_scale,
                       int causal, int window, int dtype, void* stream);
+
+/*
+ * Decode over a rolling window buffer (transformer.xph.ink "高效注意力：
+ * FlashAttention 与线性注意力", 实例或案例: Mistral's sliding window keeps only
+ * the last W keys, in a ring of W slots, so the cache stays a fixed size).
+ *   q [B,Hq,Lq,d]                    : the new tokens' queries (dtype)
+ *   k_ring, v_ring [B,Hkv,W,d]       : the buffer: the K/V of position p of
+ *                                      sequence b is in slot p mod W; it holds
+ *                                      positions max(0, n_b - W) .. n_b - 1
+ *   k_new, v_new [B,Hkv,Lq,d]        : the new tokens' own K/V (positions
+ *                                      n_b .. n_b + Lq - 1), not yet written
+ *                                      to the buffer (the caller writes them to
+ *                                      slots (n_b + t) mod W after the call)
+ *   seen [B] int32 (device, not NULL): n_b, the tokens of sequence b before
+ *                                      this call; clamped into [0, 2^30]
+ *   o [B,Hq,Lq,d] (dtype), lse [B,Hq,Lq] float32 (may be NULL)
+ *   window                           : w, 1 <= w <= W; 0 means w = W
+ * New token t sits at position n_b + t and attends to positions
+ * max(0, n_b + t - w + 1) .. n_b + t: the older ones from the buffer (slot
+ * order does not matter: each slot's position is known from n_b), the newer
+ * ones from k_new / v_new, causally.  The partials of both are merged exactly
+ * (log-sum-exp weights), so any Lq and G = Hq/Hkv are exact; the buffer is
+ * read once per K/V head for every 32 rows of R = G * Lq.
+ * Sizes as for flash_attn_decode with W in place of Lk (Lq may exceed W);
+ * window > W is FA_ERR_INVALID_ARG (those keys are gone from the buffer).
+ * workspace: at least flash_attn_decode_rolling_workspace_bytes() bytes,
+ * 256-byte aligned.
+ */
+size_t flash_attn_decode_rolling_workspace_bytes(int B, int Hq, int Hkv, int Lq, int W, int d, int dtype);
+int flash_attn_decode_rolling(const void* q, const void* k_ring, const void* v_ring, const void* k_new,
+                              const void* v_new, const int* seen, void* o, float* lse,
+                              void* workspace, size_t workspace_bytes,
+                              int B, int Hq, int Hkv, int Lq, int W, int d, float softmax_scale,
+                              int window, int dtype, void* stream);
 
 /*
  * General sparse masks over one sequence of L positions (queries and keys are

@@ -36,7 +36,10 @@ loops on tiny chunks, and the merge against ``numpy.logaddexp``; for decode:
 a cache holding exactly the new tokens equals the full causal forward, each
 new token equals the matching row of the whole-sequence forward (with and
 without a window), per-sequence cache lengths, and a single-token rolling
-window buffer in any slot order equals the windowed row; for general masks:
+window buffer in any slot order equals the windowed row; for the rolling
+buffer with several new tokens: the buffer filled token by token (slot p mod
+W), read back, equals the matching rows of the whole-sequence causal windowed
+forward, before and after the buffer wraps; for general masks:
 the family reduces to the causal/window mask, brute-force loops over
 symmetric windows, global tokens and block masks, the masked forward and
 backward reduce to the plain ones, global rows equal unmasked rows,
@@ -52,6 +55,7 @@ from .attention import (  # noqa: F401
     block_backward,
     merge_partials,
     decode_forward,
+    rolling_decode_forward,
     general_mask,
     forward_with_mask,
     backward_with_mask,

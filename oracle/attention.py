@@ -382,6 +382,42 @@ def decode_forward(q, k_cache, v_cache, cache_len, scale, causal=True, window=0)
     return O, lse
 
 
+def rolling_decode_forward(q, k_ring, v_ring, k_new, v_new, seen, scale, window=0):
+    """New tokens over a rolling window buffer: float64 ``(O [B,Hq,Lq,d], LSE [B,Hq,Lq])``.
+
+    The buffer (transformer.xph.ink "高效注意力：FlashAttention 与线性注意力",
+    实例或案例: Mistral keeps only the last W keys, in W slots) is ``[B,Hkv,W,d]``:
+    the K/V of position p of sequence b sits in slot p mod W, and after
+    ``seen[b] = n`` tokens the buffer holds positions max(0, n - W) .. n - 1.
+    ``k_new``/``v_new`` ``[B,Hkv,Lq,d]`` are the new tokens' own K/V, positions
+    n .. n + Lq - 1.  New token t (position n + t) attends causally to the
+    ``window`` most recent positions (0 means W).
+
+    By definition: read the buffer back into position order, append the new
+    keys, and attend the query chunk at offset n to that key chunk at offset
+    max(0, n - W) with the causal window -- the chunk-pair forward.
+    """
+    q, k_ring, v_ring = _as64(q), _as64(k_ring), _as64(v_ring)
+    k_new, v_new = _as64(k_new), _as64(v_new)
+    B, Hq, Lq, d = q.shape
+    W = k_ring.shape[2]
+    w = W if window == 0 else int(window)
+    if not 1 <= w <= W:
+        raise ValueError("the window must fit the buffer")
+    O = np.empty((B, Hq, Lq, d))
+    lse = np.empty((B, Hq, Lq))
+    for b in range(B):
+        n = int(seen[b])
+        if n < 0:
+            raise ValueError("seen counts must be >= 0")
+        positions = np.arange(max(0, n - W), n)
+        slots = positions % W
+        k_seq = np.concatenate([k_ring[b:b + 1, :, slots], k_new[b:b + 1]], axis=2)
+        v_seq = np.concatenate([v_ring[b:b + 1, :, slots], v_new[b:b + 1]], axis=2)
+        O[b:b + 1], lse[b:b + 1] = block_forward(q[b:b + 1], k_seq, v_seq, scale, True, w, n, max(0, n - W))
+    return O, lse
+
+
 # ---------------------------------------------------------------- general masks
 #
 # Sparse patterns that keep attention exact on the positions they allow

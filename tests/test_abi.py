@@ -207,7 +207,8 @@ def test_decode_entry_points_reject_invalid_arguments(lib):
     INV, UNS, WS, GQA = c["FA_ERR_INVALID_ARG"], c["FA_ERR_UNSUPPORTED"], c["FA_ERR_WORKSPACE"], c["FA_ERR_GQA"]
     wsb = lib.flash_attn_decode_workspace_bytes
     assert wsb(1, 8, 2, 1, 4096, 128, fa.FA_DTYPE_BF16) > 0
-    assert wsb(1, 8, 2, 9, 4096, 128, fa.FA_DTYPE_BF16) == 0        # 4 heads x 9 tokens > 32 rows
+    assert wsb(1, 8, 2, 9, 4096, 128, fa.FA_DTYPE_BF16) > 0         # 4 heads x 9 tokens: two row groups
+    assert wsb(1, 1 << 16, 1, 33, 4096, 64, fa.FA_DTYPE_BF16) == 0  # more than 65535 row groups
     assert wsb(1, 8, 2, 1, 4096, 128, fa.FA_DTYPE_F32) == 0
     assert wsb(1, 8, 3, 1, 4096, 128, fa.FA_DTYPE_BF16) == 0
     assert wsb(1, 8, 2, 5, 4, 128, fa.FA_DTYPE_BF16) == 0           # cache shorter than the new tokens
@@ -218,8 +219,34 @@ def test_decode_entry_points_reject_invalid_arguments(lib):
                                      window, dt, None)
     assert dec(q=None) == INV and dec(cl=FAKE + 2) == INV and dec(scale=0.0) == INV and dec(causal=3) == INV
     assert dec(ws=None) == WS and dec(nb=16) == WS and dec(ws=FAKE * 16 + 128) == WS
-    assert dec(Lq=40) == UNS and dec(dt=fa.FA_DTYPE_F32) == UNS and dec(d=96) == UNS
+    assert dec(Lq=40, q=None) == INV                 # 160 rows per K/V head pass the size checks
+    assert dec(dt=fa.FA_DTYPE_F32) == UNS and dec(d=96) == UNS
     assert dec(causal=0, window=8) == UNS and dec(Hkv=3) == GQA and dec(Lk=0) == INV
+
+
+def test_rolling_decode_rejects_invalid_arguments(lib):
+    c = header_constants()
+    INV, UNS, WS, GQA = c["FA_ERR_INVALID_ARG"], c["FA_ERR_UNSUPPORTED"], c["FA_ERR_WORKSPACE"], c["FA_ERR_GQA"]
+    wsb = lib.flash_attn_decode_rolling_workspace_bytes
+    assert wsb(1, 8, 2, 4, 1024, 128, fa.FA_DTYPE_BF16) > 0
+    assert wsb(1, 8, 2, 4, 1024, 128, fa.FA_DTYPE_BF16) >= lib.flash_attn_decode_workspace_bytes(
+        1, 8, 2, 4, 1024, 128, fa.FA_DTYPE_BF16)                  # the buffer's splits and the new tokens'
+    assert wsb(1, 8, 2, 2000, 1024, 128, fa.FA_DTYPE_BF16) > 0      # more new tokens than slots
+    assert wsb(1, 8, 2, 4, 1024, 128, fa.FA_DTYPE_F32) == 0
+    assert wsb(1, 8, 3, 4, 1024, 128, fa.FA_DTYPE_BF16) == 0
+    assert wsb(1, 8, 2, 0, 1024, 128, fa.FA_DTYPE_BF16) == 0
+    assert wsb(1, 8, 2, 4, 0, 128, fa.FA_DTYPE_BF16) == 0
+
+    def roll(q=FAKE, seen=FAKE, ws=FAKE * 16, nb=1 << 30, Hq=8, Hkv=2, Lq=4, W=1024, d=128, scale=0.1, window=0,
+             dt=fa.FA_DTYPE_BF16, kn=FAKE):
+        return lib.flash_attn_decode_rolling(q, FAKE, FAKE, kn, FAKE, seen, FAKE, FAKE, ws, nb, 1, Hq, Hkv, Lq, W, d,
+                                             scale, window, dt, None)
+    assert roll(q=None) == INV and roll(kn=None) == INV and roll(kn=MISALIGNED) == INV
+    assert roll(seen=None) == INV and roll(seen=FAKE + 2) == INV
+    assert roll(scale=0.0) == INV and roll(window=-1) == INV and roll(window=1025) == INV
+    assert roll(ws=None) == WS and roll(nb=16) == WS and roll(ws=FAKE * 16 + 128) == WS
+    assert roll(dt=fa.FA_DTYPE_F32) == UNS and roll(d=96) == UNS and roll(Hkv=3) == GQA
+    assert roll(W=0) == INV and roll(Lq=0) == INV
 
 
 def test_mask_entry_points_reject_invalid_arguments(lib):

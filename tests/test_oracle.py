@@ -388,6 +388,26 @@ def pin_decode_rolling_window_buffer(o):
     assert np.allclose(l[0, :, 0], lf[0, :, L - 1], atol=1e-12, rtol=0)
 
 
+def pin_rolling_buffer_rows_match_whole_sequence(o):
+    # A rolling buffer of W slots, filled token by token (position p overwrites slot p mod W),
+    # plus the Lq new tokens' own K/V: new token t must equal row n + t of the whole-sequence
+    # causal forward with window w <= W -- before the buffer is full, exactly full, and wrapped
+    # (n not a multiple of W), for Lq = 1, several tokens, and more tokens than slots.
+    W, d = 5, 4
+    N = 17
+    q_all, k, v = rnd((2, 4, N, d), 140), rnd((2, 2, N, d), 141), rnd((2, 2, N, d), 142)
+    for n, Lq, w in [(0, 3, 0), (3, 2, 0), (5, 1, 0), (7, 3, 0), (11, 4, 2), (9, 1, 5), (6, 8, 0), (12, 5, 3)]:
+        kb, vb = np.full((2, 2, W, d), 1e3), np.full((2, 2, W, d), -1e3)   # never-written slots are junk
+        for p in range(n):
+            kb[:, :, p % W], vb[:, :, p % W] = k[:, :, p], v[:, :, p]
+        seen = [n, n]
+        O, l = o.rolling_decode_forward(q_all[:, :, n:n + Lq], kb, vb, k[:, :, n:n + Lq], v[:, :, n:n + Lq],
+                                        seen, 0.55, w)
+        Of, lf = o.forward(q_all[:, :, :n + Lq], k[:, :, :n + Lq], v[:, :, :n + Lq], 0.55, True, w or W)
+        assert np.allclose(O, Of[:, :, n:n + Lq], atol=1e-12, rtol=0), (n, Lq, w)
+        assert np.allclose(l, lf[:, :, n:n + Lq], atol=1e-12, rtol=0), (n, Lq, w)
+
+
 def pin_general_mask_reduces_to_causal_window(o):
     L = 13
     pos = np.arange(L)
@@ -487,7 +507,7 @@ MASK_PINS = [pin_general_mask_reduces_to_causal_window, pin_general_mask_brute_f
 BLOCK_PINS = [pin_block_whole_sequence_equals_full, pin_block_brute_force, pin_merged_partials_equal_full,
               pin_merge_edge_cases, pin_block_backward_sums_to_full]
 DECODE_PINS = [pin_decode_new_tokens_only_is_full_causal, pin_decode_rows_match_whole_sequence,
-               pin_decode_rolling_window_buffer]
+               pin_decode_rolling_window_buffer, pin_rolling_buffer_rows_match_whole_sequence]
 
 
 PINS = [pin_rows_stochastic, pin_two_key_worked_example, pin_length_one, pin_zero_query_is_mean,
@@ -630,6 +650,31 @@ def test_planted_decode_top_left_alignment(monkeypatch):
     monkeypatch.setattr(oa, "block_forward", lambda q, k, v, scale, causal=False, window=0, q_offset=0, k_offset=0:
                         good(q, k, v, scale, causal, window, 0, k_offset))
     assert _some_pin_fails(DECODE_PINS)
+
+
+def test_planted_rolling_buffer_read_in_slot_order(monkeypatch):
+    # the buffer read back in slot order 0..W-1 instead of position order
+    def bad(q, k_ring, v_ring, k_new, v_new, seen, scale, window=0):
+        q, k_ring, v_ring, k_new, v_new = (np.asarray(x, dtype=np.float64) for x in (q, k_ring, v_ring, k_new, v_new))
+        B, W = q.shape[0], k_ring.shape[2]
+        outs = []
+        for b in range(B):
+            n = int(seen[b])
+            m = min(n, W)
+            ks = np.concatenate([k_ring[b:b + 1, :, :m], k_new[b:b + 1]], axis=2)
+            vs = np.concatenate([v_ring[b:b + 1, :, :m], v_new[b:b + 1]], axis=2)
+            outs.append(oa.block_forward(q[b:b + 1], ks, vs, scale, True, window or W, n, n - m))
+        return np.concatenate([x[0] for x in outs]), np.concatenate([x[1] for x in outs])
+    monkeypatch.setattr(oracle, "rolling_decode_forward", bad)
+    assert _some_pin_fails([pin_rolling_buffer_rows_match_whole_sequence])
+
+
+def test_planted_rolling_buffer_window_off_by_one(monkeypatch):
+    good = oa.rolling_decode_forward
+    monkeypatch.setattr(oracle, "rolling_decode_forward",
+                        lambda q, kr, vr, kn, vn, seen, scale, window=0:
+                        good(q, kr, vr, kn, vn, seen, scale, (window or kr.shape[2]) - 1 or 1))
+    assert _some_pin_fails([pin_rolling_buffer_rows_match_whole_sequence])
 
 
 def test_planted_general_mask_window_off_by_one(monkeypatch):
