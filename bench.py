@@ -685,7 +685,12 @@ def main():
         "roofline": {"kernel": kernel_names[dom], "bound": bound, "achieved": round(achieved, 2),
                      "peak": peak, "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": load_traffic(kernel_names[dom]),
-                     "algorithmic_per_launch": work},
+                     "algorithmic_per_launch": work,
+                     "ms_per_launch": round(avg[dom], 4),
+                     "time_base": "mean over the timed steps of the interval between HIP events recorded "
+                                  "on the launch stream right before and right after the kernel's launch; "
+                                  "compare with the kernel-trace average of the same launches in "
+                                  "profiles/kernel_time_llama7b_fwd_bwd.txt"},
     }
     if not args.no_configs:
         out["configs"] = {wl.name: measure_config(wl) for wl in W.ALL}
