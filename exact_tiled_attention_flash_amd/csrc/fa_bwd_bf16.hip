@@ -8,7 +8,7 @@
 //     dV = P^T dO,  dP = dO V^T,  D_i = sum_c dO_ic O_ic,  dS = P * (dP - D),
 //     dQ = s dS K,  dK = s dS^T Q.
 // Three kernels, all on the caller's stream, none using atomics:
-//   1. delta:  D_i and LSE_i*log2(e) per query row into the workspace;
+//   1. delta:  -D_i and LSE_i*log2(e) per query row into the workspace;
 //   2. dK/dV:  one work-group per (batch, K/V head, 128 keys) with its K and
 //              V rows staged once in LDS; each of its 8 waves owns 32 keys and
 //              one 32-query half of every allowed 64-query tile of Q and dO
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(const bf16* __restrict__
 #pragma unroll
   for (int off = kLanesPerRow / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (row < rows && part == 0) {
-    delta[row] = acc;
+    delta[row] = -acc;               // stored negated: the dP chains start from it
     lse2[row] = lse[row] * kLog2e;
   }
 }
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(C::QT))) char do_st1[C::QT];
   __shared__ __attribute__((aligned(1024))) char k_blk[C::KB];
   __shared__ __attribute__((aligned(1024))) char v_blk[C::KB];
-  __shared__ __attribute__((aligned(16))) float stat_st0[2 * C::BQ];   // LSE*log2e, then D
+  __shared__ __attribute__((aligned(16))) float stat_st0[2 * C::BQ];   // LSE*log2e, then -D
   __shared__ __attribute__((aligned(16))) float stat_st1[2 * C::BQ];
 
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -279,7 +279,7 @@ __global__ __launch_bounds__(512, 1) void bwd_fused_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) char k_blk[KBD];
   __shared__ __attribute__((aligned(1024))) char v_blk[C::KB];
   __shared__ __attribute__((aligned(1024))) char ds_buf[C::BK * C::BQ * 2];
-  __shared__ __attribute__((aligned(16))) float stat_st0[2 * C::BQ];   // LSE*log2e, then D
+  __shared__ __attribute__((aligned(16))) float stat_st0[2 * C::BQ];   // LSE*log2e, then -D
   __shared__ __attribute__((aligned(16))) float stat_st1[2 * C::BQ];
 
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -578,8 +578,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       st.dor[k] = *reinterpret_cast<const bf16x8*>(dOr + 16 * k + 8 * g);
     }
     const size_t srow = (size_t)(b * a.Hq + h) * L + qr;
-    st.lse2 = a.lse2[srow];
-    st.dlt = a.delta[srow];
+    st.set_stats(a.lse2[srow], a.delta[srow]);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) st.dq[db] = f32x16{};
   }

@@ -98,8 +98,9 @@ template <bool CAUSAL>
 struct RangeMaskK {
   int L, shift, window, j;
   __device__ __forceinline__ bool operator()(int q) const {
+    // bitwise, not short-circuit, so that no divergent branch is formed
     const int i = q + shift;
-    return q < L && (!CAUSAL || j <= i) && (window <= 0 || (i - j < window && (CAUSAL || j - i < window)));
+    return (q < L) & (!CAUSAL | (j <= i)) & ((window <= 0) | ((i - j < window) & (CAUSAL | (j - i < window))));
   }
 };
 
@@ -176,12 +177,15 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const Addr& ad_in, const
     for (int j = 0; j < 4; ++j) p[4 * i4 + j] = fast_exp2(fmaf(p[4 * i4 + j], c, -l4[j]));
   }
   // the mask as a separate pass, so that the common unmasked tile stays one
-  // straight-line block
+  // straight-line block.  Each select is done in place (tied asm operand): a
+  // plain select writes new registers, and the join of the two versions of P
+  // then costs 16 register copies on the unmasked path.
   if (need_mask) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int q = qw0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      p[i] = ok(q) ? p[i] : 0.f;
+      const unsigned long long keep = __builtin_amdgcn_ballot_w64(ok(q));
+      asm("v_cndmask_b32_e64 %0, 0, %0, %1" : "+v"(p[i]) : "s"(keep));
     }
   }
   // dV += P^T dO: A = P (lane = key, K slots = queries), B = dO via the transposing read
@@ -196,18 +200,22 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const Addr& ad_in, const
       st.dv[db] = mfma32x<F16>(pa, bo, st.dv[db]);
     }
   }
-  // dP = dO V^T, then dS = P * (dP - D) in place
-  f32x16 dp = mfma32x<F16>(lds_load16(dobuf, kv_qrow<D>(ad, 0)), lds_load16(vblk, ad.kv), f32x16{});
-#pragma unroll
-  for (int k = 1; k < C::NSTEP; ++k)
-    dp = mfma32x<F16>(lds_load16(dobuf, kv_qrow<D>(ad, k)), lds_load16(vblk, ad.kv + 32 * k), dp);
-  chain_order();
+  // dP - D = dO V^T - D: the chain starts from the stored -D of each query
+  // row (C-layout register i is query row 8(i/4) + 4g + i%4 of the half),
+  // then dS = P * (dP - D) in place
+  f32x16 dp;
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
     const f32x4 d4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (C::BQ + 32 * qh + 8 * i4 + 4 * g));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p[4 * i4 + j] *= dp[4 * i4 + j] - d4[j];
+    for (int j = 0; j < 4; ++j) dp[4 * i4 + j] = d4[j];
   }
+#pragma unroll
+  for (int k = 0; k < C::NSTEP; ++k)
+    dp = mfma32x<F16>(lds_load16(dobuf, kv_qrow<D>(ad, k)), lds_load16(vblk, ad.kv + 32 * k), dp);
+  chain_order();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) p[i] *= dp[i];
   // dK += dS^T Q: A = dS (lane = key), B = Q via the transposing read
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
@@ -253,7 +261,13 @@ struct QState {
   bf16x8 qr[QCfg<D>::NSTEP];    // this wave's 32 Q rows (B operand of S^T = K Q^T)
   bf16x8 dor[QCfg<D>::NSTEP];   // this wave's 32 dO rows (B operand of dP^T = V dO^T)
   f32x16 dq[QCfg<D>::NDB];      // dQ^T accumulator: lane = query, registers = head dims
-  float lse2, dlt;              // this lane's query statistics
+  float lse2;                   // this lane's LSE * log2(e)
+  f32x16 negd;                  // this lane's -D in every register: the start of the dP^T chains
+  __device__ __forceinline__ void set_stats(float lse2_row, float negd_row) {
+    lse2 = lse2_row;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negd[i] = negd_row;
+  }
 };
 
 template <int D>
@@ -288,13 +302,13 @@ __device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const 
         p[i] = ok(kk) ? p[i] : 0.f;
       }
     }
-    // dP^T = V dO^T, dS^T = P^T * (dP^T - D)
-    f32x16 dp = mfma32x<F16>(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR), st.dor[0], f32x16{});
+    // dP^T - D = V dO^T - D (the chain starts from -D), dS^T = P^T * (dP^T - D)
+    f32x16 dp = mfma32x<F16>(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR), st.dor[0], st.negd);
 #pragma unroll
     for (int k = 1; k < C::NSTEP; ++k)
       dp = mfma32x<F16>(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR + 32 * k), st.dor[k], dp);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) p[i] *= dp[i] - st.dlt;
+    for (int i = 0; i < 16; ++i) p[i] *= dp[i];
     // dQ^T += K^T dS^T: A = K^T via the transposing read, B = dS^T (lane = query)
 #pragma unroll
     for (int u = 0; u < 2; ++u) {

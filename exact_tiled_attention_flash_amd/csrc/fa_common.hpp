@@ -318,7 +318,8 @@ __device__ __forceinline__ void head_tile_of(int r, int n_heads, int n_tiles, in
 // 解析" §3.2.1; book.anysome.cn "高效注意力" §4 for the one-sided form).
 template <bool CAUSAL>
 __device__ __forceinline__ bool range_ok(int j, int i, int Lk, int window) {
-  return j < Lk && (!CAUSAL || j <= i) && (window <= 0 || (j > i - window && (CAUSAL || j < i + window)));
+  // bitwise, not short-circuit, so that no divergent branch is formed
+  return (j < Lk) & (!CAUSAL | (j <= i)) & ((window <= 0) | ((j > i - window) & (CAUSAL | (j < i + window))));
 }
 
 // Query-major element mask: the lane's query position is fixed.

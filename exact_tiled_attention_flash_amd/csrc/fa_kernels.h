@@ -30,7 +30,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;      // workspace: D_i = sum_c dO_ic * O_ic, [B, Hq, L]
+  float* delta;      // workspace: -D_i = -sum_c dO_ic * O_ic, [B, Hq, L] (negated: dP - D starts from it)
   float* lse2;       // workspace: LSE_i * log2(e), [B, Hq, L]
   float* dq_acc;     // workspace of the fused backward: float32 dQ accumulator [B, Hq, L, d], or null
   int B, Hq, Hkv, L, d;  // L = query rows

@@ -438,7 +438,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_masked_kernel(BwdArgs a, PlanPtrs
   __shared__ __attribute__((aligned(C::QT))) char do_st1[C::QT];
   __shared__ __attribute__((aligned(1024))) char k_blk[C::KB];
   __shared__ __attribute__((aligned(1024))) char v_blk[C::KB];
-  __shared__ __attribute__((aligned(16))) float stat_st0[2 * C::BQ];   // LSE*log2e, then D
+  __shared__ __attribute__((aligned(16))) float stat_st0[2 * C::BQ];   // LSE*log2e, then -D
   __shared__ __attribute__((aligned(16))) float stat_st1[2 * C::BQ];
 
   const int lane = threadIdx.x & 63, wave = wave_id();
@@ -683,8 +683,7 @@ __global__ __launch_bounds__(256, 2) void dq_masked_kernel(BwdArgs a, PlanPtrs p
       st.dor[k] = *reinterpret_cast<const bf16x8*>(dOr + 16 * k + 8 * g);
     }
     const size_t srow = (size_t)(b * a.Hq + h) * L + qr;
-    st.lse2 = a.lse2[srow];
-    st.dlt = a.delta[srow];
+    st.set_stats(a.lse2[srow], a.delta[srow]);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) st.dq[db] = f32x16{};
   }
@@ -947,8 +946,7 @@ __global__ __launch_bounds__(64) void grows_dq_kernel(BwdArgs a, PlanPtrs p, Glo
       st.dor[k] = *reinterpret_cast<const bf16x8*>(dOr + 16 * k + 8 * g);
     }
     const size_t srow = (size_t)(b * a.Hq + h) * L + pos;
-    st.lse2 = a.lse2[srow];
-    st.dlt = a.delta[srow];
+    st.set_stats(a.lse2[srow], a.delta[srow]);
 #pragma unroll
     for (int db = 0; db < C::NDB; ++db) st.dq[db] = f32x16{};
   }

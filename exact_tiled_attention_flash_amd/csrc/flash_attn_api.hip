@@ -35,7 +35,7 @@ int check_common(int B, int Hq, int Hkv, int L, int d, float scale, int causal, 
   return FA_OK;
 }
 
-// Backward row statistics: two float32 per query row -- D_i and LSE_i*log2(e).
+// Backward row statistics: two float32 per query row -- -D_i and LSE_i*log2(e).
 // The staged (deterministic) backward needs only these.
 size_t workspace_bytes(int B, int Hq, int L) {
   const size_t raw = 2 * (size_t)B * (size_t)Hq * (size_t)L * sizeof(float);
@@ -484,7 +484,7 @@ extern "C" int flash_attn_mask_plan(const fa_mask* mask, int L, void* plan, size
 
 namespace {
 
-// Workspace of the masked calls: the backward's D_i and LSE_i*log2(e) rows
+// Workspace of the masked calls: the backward's -D_i and LSE_i*log2(e) rows
 // (backward only), then the float32 partials of the global-position passes
 // (the dK/dV and dQ passes run one after the other and share one region).
 struct MaskedWs {

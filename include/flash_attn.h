@@ -94,8 +94,8 @@ int flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* 
 
 /*
  * Bytes of device workspace flash_attn_bwd needs for these sizes: two
- * float32 per query row (the row dot product D_i = sum_c dO_ic * O_ic and
- * the log-sum-exp in base 2), i.e. 8*B*Hq*L rounded up to 256 bytes.
+ * float32 per query row (the row dot product D_i = sum_c dO_ic * O_ic, stored
+ * negated, and the log-sum-exp in base 2), i.e. 8*B*Hq*L rounded up to 256 bytes.
  * Returns 0 for invalid sizes.
  */
 size_t flash_attn_bwd_workspace_bytes(int B, int Hq, int Hkv, int L, int d, int dtype);
@@ -152,7 +152,7 @@ int flash_attn_bwd_fused(const void* q, const void* k, const void* v, const void
  * order on one stream.  Arguments mean what they mean for flash_attn_bwd.
  *
  * Stage 1, flash_attn_bwd_preprocess: from O, the forward's LSE and dO, writes
- * into the workspace the per-row D_i = sum_c dO_ic * O_ic and LSE_i * log2(e)
+ * into the workspace the per-row -D_i = -sum_c dO_ic * O_ic and LSE_i * log2(e)
  * (the statistics the recomputation needs, claspmoon.cn §3.3).  Stages 2 and
  * 3 read only those from the workspace and may run in either order or
  * concurrently once stage 1 has completed:
@@ -379,7 +379,7 @@ int flash_attn_bwd_masked(const void* q, const void* k, const void* v, const voi
  * callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc).  It runs the three
  * staged kernels of flash_attn_bwd_preprocess / _dkdv / _dq, with the per-row
- * statistics (D_i and LSE_i * log2 e, two float32 per query row) in a static
+ * statistics (-D_i and LSE_i * log2 e, two float32 per query row) in a static
  * device array of 16 MiB that the library owns: B * Hq * L must be at most
  * FA_NOALLOC_MAX_ROWS (2^21), else FA_ERR_TOO_LARGE.  The call allocates
  * nothing and calls no allocating routine.  Each GPU has its own copy of the
