@@ -168,6 +168,21 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const Addr& ad_in, const
     p = mfma32x<F16>(lds_load16(qbuf, kv_qrow<D>(ad, k)), lds_load16(kblk, krow(k)), p);
   chain_order();
 
+  // dP - D = dO V^T - D: the chain starts from the stored -D of each query
+  // row (C-layout register i is query row 8(i/4) + 4g + i%4 of the half).
+  // It is independent of P, so it comes first: its products can then run
+  // beside the exponentials below (one basic block up to the mask branch).
+  f32x16 dp;
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4) {
+    const f32x4 d4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (C::BQ + 32 * qh + 8 * i4 + 4 * g));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dp[4 * i4 + j] = d4[j];
+  }
+#pragma unroll
+  for (int k = 0; k < C::NSTEP; ++k)
+    dp = mfma32x<F16>(lds_load16(dobuf, kv_qrow<D>(ad, k)), lds_load16(vblk, ad.kv + 32 * k), dp);
+  chain_order();
   // P = exp2(S*s*log2e - LSE*log2e), zero where masked
   const int qw0 = q0 + 32 * qh;           // first query of this wave's half
 #pragma unroll
@@ -200,20 +215,7 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const Addr& ad_in, const
       st.dv[db] = mfma32x<F16>(pa, bo, st.dv[db]);
     }
   }
-  // dP - D = dO V^T - D: the chain starts from the stored -D of each query
-  // row (C-layout register i is query row 8(i/4) + 4g + i%4 of the half),
-  // then dS = P * (dP - D) in place
-  f32x16 dp;
-#pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4) {
-    const f32x4 d4 = *(const FA_LDS f32x4*)((const FA_LDS char*)(stats) + 4 * (C::BQ + 32 * qh + 8 * i4 + 4 * g));
-#pragma unroll
-    for (int j = 0; j < 4; ++j) dp[4 * i4 + j] = d4[j];
-  }
-#pragma unroll
-  for (int k = 0; k < C::NSTEP; ++k)
-    dp = mfma32x<F16>(lds_load16(dobuf, kv_qrow<D>(ad, k)), lds_load16(vblk, ad.kv + 32 * k), dp);
-  chain_order();
+  // dS = P * (dP - D) in place
 #pragma unroll
   for (int i = 0; i < 16; ++i) p[i] *= dp[i];
   // dK += dS^T Q: A = dS (lane = key), B = Q via the transposing read
@@ -293,6 +295,12 @@ __device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const 
 #pragma unroll
     for (int k = 1; k < C::NSTEP; ++k)
       p = mfma32x<F16>(lds_load16(kbuf, ad.krow[k] + kb * 32 * (2 * D)), st.qr[k], p);
+    // dP^T - D = V dO^T - D (the chain starts from -D); independent of P, so
+    // its products can run beside the exponentials
+    f32x16 dp = mfma32x<F16>(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR), st.dor[0], st.negd);
+#pragma unroll
+    for (int k = 1; k < C::NSTEP; ++k)
+      dp = mfma32x<F16>(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR + 32 * k), st.dor[k], dp);
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(p[i], c, -st.lse2));
     if (need_mask) {
@@ -302,11 +310,7 @@ __device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const 
         p[i] = ok(kk) ? p[i] : 0.f;
       }
     }
-    // dP^T - D = V dO^T - D (the chain starts from -D), dS^T = P^T * (dP^T - D)
-    f32x16 dp = mfma32x<F16>(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR), st.dor[0], st.negd);
-#pragma unroll
-    for (int k = 1; k < C::NSTEP; ++k)
-      dp = mfma32x<F16>(lds_load16(vbuf, ad.vrow + kb * 32 * Pad<D>::KSTR + 32 * k), st.dor[k], dp);
+    // dS^T = P^T * (dP^T - D)
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] *= dp[i];
     // dQ^T += K^T dS^T: A = K^T via the transposing read, B = dS^T (lane = query)
