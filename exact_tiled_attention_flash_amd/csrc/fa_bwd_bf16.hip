@@ -104,10 +104,12 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   const int L = a.L, Lk = a.Lk, shift = a.shift, window = a.window;
   const int G = a.Hq / a.Hkv;
 
-  // (batch, K/V head) major; the key tile with the most queries first
+  // (batch, K/V head) pairs, key tiles rank by rank within a pair; with
+  // causal masking the first key tile sees the most queries, so the heaviest
+  // work-groups go first
   const int r = xcd_remap(blockIdx.x, gridDim.x);
-  const int bhk = r / a.n_tiles;
-  const int kt = r % a.n_tiles;
+  int bhk, kt;
+  head_tile_of(r, a.B * a.Hkv, a.n_tiles, bhk, kt);
   const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
   const int key_wg0 = kt * C::BK;
   const int key_w0 = key_wg0 + 32 * kb;
