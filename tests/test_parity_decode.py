@@ -119,6 +119,8 @@ ROLLING = [
     (1, 2, 1, 100, 64, 128, [100], 0, torch.bfloat16),            # more new tokens than slots
     (1, 4, 4, 5, 256, 128, [0], 0, torch.bfloat16),               # empty buffer: the new tokens only
     (3, 4, 1, 1, 300, 64, [299, 300, 301], 0, torch.bfloat16),    # one token at the fill boundary
+    (1, 4, 2, 3, 1, 128, [7], 0, torch.bfloat16),                 # one slot: every token sees only itself
+    (2, 2, 2, 5, 3, 64, [2, 10], 2, torch.float16),               # tiny buffer, window < W, Lq > W
 ]
 
 

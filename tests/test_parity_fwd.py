@@ -142,6 +142,11 @@ SMALL = [
     W.small("sym window5000 L2048", 1, 2, 2, 2048, 64, causal=False, window=5000, seed=125),
     W.small("fp32 sym window9 L150", 1, 2, 2, 150, 64, dtype=torch.float32, causal=False, window=9, seed=126),
     W.small("fp16 sym window64 L640", 1, 2, 2, 640, 128, dtype=torch.float16, causal=False, window=64, seed=127),
+    # fp32 edge cases of the 16-rows-per-work-group kernel: one row, a partial
+    # 16-row group and a partial 64-key tile, a window wider than the sequence
+    W.small("fp32 L1", 1, 2, 2, 1, 64, dtype=torch.float32, seed=128),
+    W.small("fp32 L17 noncausal d128 gqa2", 2, 4, 2, 17, 128, dtype=torch.float32, causal=False, seed=129),
+    W.small("fp32 L129 window300", 1, 2, 1, 129, 64, dtype=torch.float32, window=300, seed=130),
 ]
 
 
