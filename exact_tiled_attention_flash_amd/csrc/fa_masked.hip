@@ -273,10 +273,11 @@ struct GeneralMaskQ {
   int L, window, i, k0;
   bool gq, bm;
   unsigned long long gk;
+  // bitwise, not short-circuit, so that no divergent branch is formed
   __device__ __forceinline__ bool operator()(int j) const {
-    const bool local = bm && (window <= 0 || (j > i - window && j < i + window));
-    const bool glob = gq || ((gk >> (j - k0)) & 1ull) != 0;
-    return j < L && (!CAUSAL || j <= i) && (local || glob);
+    const bool local = bm & ((window <= 0) | ((j > i - window) & (j < i + window)));
+    const bool glob = gq | (((gk >> (j - k0)) & 1ull) != 0);
+    return (j < L) & (!CAUSAL | (j <= i)) & (local | glob);
   }
 };
 
@@ -288,9 +289,9 @@ struct GeneralMaskK {
   bool gk, bm;
   unsigned long long gq;
   __device__ __forceinline__ bool operator()(int q) const {
-    const bool local = bm && (window <= 0 || (j > q - window && j < q + window));
-    const bool glob = gk || ((gq >> (q - q0)) & 1ull) != 0;
-    return q < L && (!CAUSAL || j <= q) && (local || glob);
+    const bool local = bm & ((window <= 0) | ((j > q - window) & (j < q + window)));
+    const bool glob = gk | (((gq >> (q - q0)) & 1ull) != 0);
+    return (q < L) & (!CAUSAL | (j <= q)) & (local | glob);
   }
 };
 
@@ -751,7 +752,7 @@ struct DenseMask {                 // the lane's position `self` against positio
   int L, self;
   bool key_side;                   // self is a key (x a query) or a query (x a key)
   __device__ __forceinline__ bool operator()(int x) const {
-    return x < L && (!CAUSAL || (key_side ? self <= x : x <= self));
+    return (x < L) & (!CAUSAL | (key_side ? self <= x : x <= self));
   }
 };
 
