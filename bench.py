@@ -408,6 +408,38 @@ def measure_decode(B=8, Hq=32, Hkv=8, Lq=1, Lk=32768, d=128, iters=20, warmup=5)
             "workspace_bytes": int(ws.numel()), "data": "synthetic N(0,1), generated on the device"}
 
 
+def measure_decode_rolling(B=8, Hq=32, Hkv=8, W=4096, d=128, iters=20, warmup=5):
+    """Decode over a full rolling window buffer of W slots (the sequences have seen
+    far more than W tokens, so the buffer has wrapped), for 1 and 16 new tokens per
+    sequence.  HBM-bound like the plain decode: reported as bytes of the buffer and
+    the new tokens' K/V read per second against the HBM peak."""
+    import torch
+    import exact_tiled_attention_flash_amd as fa
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(10)
+    kr = torch.randn(B, Hkv, W, d, generator=g, device=dev).to(torch.bfloat16)
+    vr = torch.randn(B, Hkv, W, d, generator=g, device=dev).to(torch.bfloat16)
+    seen = torch.tensor([5 * W + 123 * b for b in range(B)], dtype=torch.int32, device=dev)
+    out = {}
+    for Lq in (1, 16):
+        q = torch.randn(B, Hq, Lq, d, generator=g, device=dev).to(torch.bfloat16)
+        kn = torch.randn(B, Hkv, Lq, d, generator=g, device=dev).to(torch.bfloat16)
+        vn = torch.randn(B, Hkv, Lq, d, generator=g, device=dev).to(torch.bfloat16)
+        ws = torch.empty(fa.decode_rolling_workspace_bytes(B, Hq, Hkv, Lq, W, d), dtype=torch.uint8, device=dev)
+        o, lse = torch.empty_like(q), torch.empty(B, Hq, Lq, device=dev)
+        med, mean = time_calls(lambda: fa.decode_rolling(q, kr, vr, kn, vn, seen, workspace=ws, out=o, lse=lse),
+                               iters, warmup)
+        groups = (Hq // Hkv * Lq + 31) // 32          # the buffer is read once per group of 32 rows
+        nbytes = 2 * B * Hkv * (W + Lq) * d * 2
+        gbs = nbytes / (med * 1e-3) / 1e9
+        out[f"new tokens {Lq}"] = {
+            "ms_median": round(med, 4), "ms_mean": round(mean, 4), "kv_bytes": nbytes, "buffer_reads": groups,
+            "hbm_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS, "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
+            "workspace_bytes": int(ws.numel())}
+    return {"shape": f"B{B} Hq{Hq} Hkv{Hkv} rolling buffer W={W} (wrapped) d{d} bf16", **out,
+            "data": "synthetic N(0,1), generated on the device"}
+
+
 def measure_autograd(iters=10, warmup=3):
     """The differentiable drop-in on the headline shape: scaled_dot_product_attention
     (forward, then backward through autograd) against the same two calls made directly,
@@ -576,7 +608,9 @@ def main():
         print(json.dumps({"ring": measure_ring(iters=args.steps, warmup=args.warmup)}), flush=True)
         return
     if args.decode_only:
-        print(json.dumps({"decode": measure_decode(iters=args.steps, warmup=args.warmup)}), flush=True)
+        print(json.dumps({"decode": measure_decode(iters=args.steps, warmup=args.warmup),
+                          "decode_rolling": measure_decode_rolling(iters=args.steps, warmup=args.warmup)}),
+              flush=True)
         return
     if args.bwd_fused_only:
         print(json.dumps({"bwd_fused": measure_bwd_fused(iters=args.steps, warmup=args.warmup)}), flush=True)
@@ -720,6 +754,7 @@ def main():
         out["autograd"] = measure_autograd()
         out["bwd_fused"] = measure_bwd_fused()
         out["decode"] = measure_decode()
+        out["decode_rolling"] = measure_decode_rolling()
         out["ring"] = measure_ring()
         out["sparse"] = measure_sparse()
         out["sparse_block"] = measure_sparse(block_band=True)

@@ -63,14 +63,10 @@ constexpr int kMaxSeen = 1 << 30;   // tokens seen before a rolling-buffer call 
 //                 n .. n + Lq - 1 and see the window of a.window positions
 //                 ending at their own (their own keys come from another pass).
 template <int D, bool CAUSAL, bool F16, bool RING>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+__device__ __forceinline__ void split_body(const DecodeArgs& a, int split, char* k_st0, char* v_st0) {
   using C = FwdCfg<D>;
-  __shared__ __attribute__((aligned(1024))) char k_st0[C::KT];
-  __shared__ __attribute__((aligned(1024))) char v_st0[C::VT];
-
   const int lane = threadIdx.x;
   const int g = lane >> 5, ln = lane & 31;
-  const int split = blockIdx.x;
   const int bhk = blockIdx.y;
   const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
   const int G = a.Hq / a.Hkv, Lq = a.Lq;
@@ -174,6 +170,24 @@ __global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
   }
 }
 
+template <int D, bool CAUSAL, bool F16>
+__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) char k_st0[FwdCfg<D>::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st0[FwdCfg<D>::VT];
+  split_body<D, CAUSAL, F16, false>(a, blockIdx.x, k_st0, v_st0);
+}
+
+// The rolling-buffer decode in one launch: splits 0 .. ring.n_splits - 1 read
+// the buffer, the rest the new tokens' own keys (a plain causal decode whose
+// cache is exactly those tokens); both write partials for the one combine.
+template <int D, bool F16>
+__global__ __launch_bounds__(64) void decode_rolling_kernel(DecodeArgs ring, DecodeArgs fresh) {
+  __shared__ __attribute__((aligned(1024))) char k_st0[FwdCfg<D>::KT];
+  __shared__ __attribute__((aligned(1024))) char v_st0[FwdCfg<D>::VT];
+  if ((int)blockIdx.x < ring.n_splits) split_body<D, true, F16, true>(ring, blockIdx.x, k_st0, v_st0);
+  else split_body<D, true, F16, false>(fresh, blockIdx.x - ring.n_splits, k_st0, v_st0);
+}
+
 // Merge one row's split partials: one work-group per row.  The splits are
 // dealt to groups of d/8 adjacent lanes (8 elements each), so that a row with
 // many splits -- a long cache with few sequences and K/V heads -- is merged by
@@ -240,9 +254,9 @@ inline unsigned row_groups(const DecodeArgs& a) {
   return (unsigned)(((long long)(a.Hq / a.Hkv) * a.Lq + 31) / 32);
 }
 
-template <int D, bool CAUSAL, bool F16, bool RING>
+template <int D, bool CAUSAL, bool F16>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, F16, RING>), dim3(a.n_splits, a.B * a.Hkv, row_groups(a)),
+  hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, F16>), dim3(a.n_splits, a.B * a.Hkv, row_groups(a)),
                      dim3(64), 0, stream, a);
   return hipGetLastError();
 }
@@ -255,16 +269,17 @@ hipError_t launch_combine(const DecodeArgs& a, hipStream_t stream) {
 
 template <int D, bool CAUSAL, bool F16>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-  hipError_t e = launch_split<D, CAUSAL, F16, false>(a, stream);
+  hipError_t e = launch_split<D, CAUSAL, F16>(a, stream);
   if (e != hipSuccess) return e;
   return launch_combine<D, F16>(a, stream);
 }
 
 template <int D, bool F16>
 hipError_t launch_rolling(const DecodeArgs& ring, const DecodeArgs& fresh, hipStream_t stream) {
-  hipError_t e = launch_split<D, true, F16, true>(ring, stream);
-  if (e != hipSuccess) return e;
-  e = launch_split<D, true, F16, false>(fresh, stream);
+  hipLaunchKernelGGL((decode_rolling_kernel<D, F16>), dim3(ring.n_splits + fresh.n_splits, ring.B * ring.Hkv,
+                                                             row_groups(ring)),
+                     dim3(64), 0, stream, ring, fresh);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_combine<D, F16>(ring, stream);
 }
