@@ -385,8 +385,17 @@ def measure_bwd_fused(iters=10, warmup=3):
     return out
 
 
+def decode_cache_reads(Hq, Hkv, Lq):
+    """How often a decode call reads each K/V head: once per work-group, which
+    serves up to four groups of 32 rows (query heads x new tokens)."""
+    groups = (Hq // Hkv * Lq + 31) // 32
+    per_wg = 1 if groups == 1 else 2 if groups == 2 else 4
+    return (groups + per_wg - 1) // per_wg
+
+
 def measure_decode(B=8, Hq=32, Hkv=8, Lq=1, Lk=32768, d=128, iters=20, warmup=5):
-    """KV-cache decode: one new token per sequence against a 32k-entry GQA cache.
+    """KV-cache decode: Lq new tokens per sequence (1, or a chunk as in speculative
+    decoding) against a 32k-entry GQA cache.
 
     The call reads the whole cache once (HBM-bound), so it is reported as bytes of
     K and V read per second against the HBM peak."""
@@ -404,6 +413,7 @@ def measure_decode(B=8, Hq=32, Hkv=8, Lq=1, Lk=32768, d=128, iters=20, warmup=5)
     gbs = cache_bytes / (med * 1e-3) / 1e9
     return {"shape": f"B{B} Hq{Hq} Hkv{Hkv} new tokens {Lq} cache {Lk} d{d} bf16 causal",
             "ms_median": round(med, 4), "ms_mean": round(mean, 4), "cache_bytes": cache_bytes,
+            "cache_reads": decode_cache_reads(Hq, Hkv, Lq),
             "hbm_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS, "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
             "workspace_bytes": int(ws.numel()), "data": "synthetic N(0,1), generated on the device"}
 
@@ -429,11 +439,11 @@ def measure_decode_rolling(B=8, Hq=32, Hkv=8, W=4096, d=128, iters=20, warmup=5)
         o, lse = torch.empty_like(q), torch.empty(B, Hq, Lq, device=dev)
         med, mean = time_calls(lambda: fa.decode_rolling(q, kr, vr, kn, vn, seen, workspace=ws, out=o, lse=lse),
                                iters, warmup)
-        groups = (Hq // Hkv * Lq + 31) // 32          # the buffer is read once per group of 32 rows
         nbytes = 2 * B * Hkv * (W + Lq) * d * 2
         gbs = nbytes / (med * 1e-3) / 1e9
         out[f"new tokens {Lq}"] = {
-            "ms_median": round(med, 4), "ms_mean": round(mean, 4), "kv_bytes": nbytes, "buffer_reads": groups,
+            "ms_median": round(med, 4), "ms_mean": round(mean, 4), "kv_bytes": nbytes,
+            "buffer_reads": decode_cache_reads(Hq, Hkv, Lq),
             "hbm_gbs": round(gbs, 1), "peak_gbs": PEAK_HBM_GBS, "frac_peak": round(gbs / PEAK_HBM_GBS, 4),
             "workspace_bytes": int(ws.numel())}
     return {"shape": f"B{B} Hq{Hq} Hkv{Hkv} rolling buffer W={W} (wrapped) d{d} bf16", **out,
@@ -609,6 +619,7 @@ def main():
         return
     if args.decode_only:
         print(json.dumps({"decode": measure_decode(iters=args.steps, warmup=args.warmup),
+                          "decode_16": measure_decode(Lq=16, iters=args.steps, warmup=args.warmup),
                           "decode_rolling": measure_decode_rolling(iters=args.steps, warmup=args.warmup)}),
               flush=True)
         return
@@ -754,6 +765,7 @@ def main():
         out["autograd"] = measure_autograd()
         out["bwd_fused"] = measure_bwd_fused()
         out["decode"] = measure_decode()
+        out["decode_16"] = measure_decode(Lq=16)
         out["decode_rolling"] = measure_decode_rolling()
         out["ring"] = measure_ring()
         out["sparse"] = measure_sparse()

@@ -7,16 +7,19 @@
 // at position cache_len[b] - Lq + t (bottom-right alignment).
 //
 // The work is bound by reading the cache from HBM, so the kernel reads each
-// K/V head once for up to 32 of its rows -- the R = G*Lq rows (G query heads
-// times Lq new tokens) become the 32 query columns of the forward's per-tile
-// MFMA step; R > 32 takes ceil(R/32) row groups, each reading the head again
-// -- and splits the keys across work-groups so that short batches still fill
-// the chip ("split-K").  Each split writes a partial (O, LSE) normalised over
+// K/V head once for up to 128 of its rows -- the R = G*Lq rows (G query heads
+// times Lq new tokens) form groups of 32, the query columns of the forward's
+// per-tile MFMA step, and up to four groups (one wave each) share a work-group
+// and its staged tiles; beyond 128 rows every further work-group reads the
+// head again -- and splits the keys across work-groups so that short batches
+// still fill the chip ("split-K").  Each split writes a partial (O, LSE) normalised over
 // its keys to the workspace; the combine kernel merges a row's partials
 // exactly: LSE = log sum_s e^{LSE_s}, O = sum_s e^{LSE_s - LSE} O_s.
 // A work-group stages one tile at a time (37 KiB of LDS), so four of them fit
 // on a CU: the bytes in flight that keep HBM busy come from four work-groups
 // per CU copying at once, more than two double-buffered ones would have.
+// (Work-groups of 2 or 4 waves run at two waves per SIMD, so four resp. two
+// of them share a CU.)
 //
 // A rolling buffer of W slots (position p in slot p mod W) is read the same way
 // with a slot -> position map: the new tokens' window over the buffer comes
@@ -53,19 +56,21 @@ struct RingMaskQ {
 
 constexpr int kMaxSeen = 1 << 30;   // tokens seen before a rolling-buffer call (clamped)
 
-// One split of the keys for one (sequence, K/V head, group of 32 rows).  The
-// rows of a K/V head are its G query heads times the Lq new tokens, row
-// r = head * Lq + token; blockIdx.z picks rows 32z .. 32z + 31.
+// One split of the keys for one (sequence, K/V head, group of 32 rows) -- the
+// part of a work-group of NW waves that one wave computes.  The rows of a K/V
+// head are its G query heads times the Lq new tokens, row r = head * Lq +
+// token; wave w takes rows 32(NW z + w) .. 32(NW z + w) + 31, z = blockIdx.z.
 //   RING = false: the cache holds positions 0 .. n-1 in order (n = cache_len[b]
 //                 or Lk), the new tokens at positions n - Lq .. n - 1;
 //   RING = true:  the cache is a rolling buffer of Lk = W slots (RingPos) after
 //                 n = cache_len[b] tokens; the new tokens sit at positions
 //                 n .. n + Lq - 1 and see the window of a.window positions
 //                 ending at their own (their own keys come from another pass).
-template <int D, bool CAUSAL, bool F16, bool RING>
+template <int D, bool CAUSAL, bool F16, bool RING, int NW>
 __device__ __forceinline__ void split_body(const DecodeArgs& a, int split, char* k_st0, char* v_st0) {
   using C = FwdCfg<D>;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = NW == 1 ? 0 : wave_id();
   const int g = lane >> 5, ln = lane & 31;
   const int bhk = blockIdx.y;
   const int b = bhk / a.Hkv, hk = bhk % a.Hkv;
@@ -78,8 +83,9 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, int split, char*
   n = __builtin_amdgcn_readfirstlane(n);
   const int filled = RING ? min(n, a.Lk) : n;   // keys of the cache that hold tokens
 
-  // this lane's row: query head hk*G + r/Lq, new token r%Lq (rows >= R are padding)
-  const long long r = 32LL * blockIdx.z + ln;
+  // this lane's row: query head hk*G + r/Lq, new token r%Lq (rows >= R are
+  // padding); wave w of the work-group takes row group NW * blockIdx.z + w
+  const long long r = 32LL * (NW * (long long)blockIdx.z + wave) + ln;
   const bool valid = r < R;
   const int hq = hk * G + (valid ? (int)(r / Lq) : 0);
   const int t = valid ? (int)(r % Lq) : Lq - 1;
@@ -99,18 +105,22 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, int split, char*
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(reinterpret_cast<const bf16*>(a.k) + kv_off, head_bytes);
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(reinterpret_cast<const bf16*>(a.v) + kv_off, head_bytes);
 
-  // one wave issues every 1 KiB copy of a tile; the per-lane source offsets are loop-invariant
-  int koff[C::KCOPIES], voff[C::VCOPIES];
+  // The NW waves share the 1 KiB copies of a tile (copy n belongs to wave
+  // n % NW); the per-lane source offsets are loop-invariant
+  constexpr int KPER = (C::KCOPIES + NW - 1) / NW, VPER = (C::VCOPIES + NW - 1) / NW;
+  int koff[KPER], voff[VPER];
 #pragma unroll
-  for (int i = 0; i < C::KCOPIES; ++i) koff[i] = pad_slot_src<D, Pad<D>::KSTR>(i * 64 + lane);
+  for (int i = 0; i < KPER; ++i) koff[i] = pad_slot_src<D, Pad<D>::KSTR>((wave + NW * i) * 64 + lane);
 #pragma unroll
-  for (int i = 0; i < C::VCOPIES; ++i) voff[i] = pad_slot_src<D, Pad<D>::VSTR>(i * 64 + lane);
+  for (int i = 0; i < VPER; ++i) voff[i] = pad_slot_src<D, Pad<D>::VSTR>((wave + NW * i) * 64 + lane);
   auto issue = [&](int j, char* kbuf, char* vbuf) {
     const int soff = j * C::BC * (2 * D);
 #pragma unroll
-    for (int i = 0; i < C::KCOPIES; ++i) buf2lds16(krs, koff[i], soff, kbuf + i * 1024);
+    for (int i = 0; i < KPER; ++i)
+      if (NW == 1 || wave + NW * i < C::KCOPIES) buf2lds16(krs, koff[i], soff, kbuf + (wave + NW * i) * 1024);
 #pragma unroll
-    for (int i = 0; i < C::VCOPIES; ++i) buf2lds16(vrs, voff[i], soff, vbuf + i * 1024);
+    for (int i = 0; i < VPER; ++i)
+      if (NW == 1 || wave + NW * i < C::VCOPIES) buf2lds16(vrs, voff[i], soff, vbuf + (wave + NW * i) * 1024);
   };
 
   FwdState<D> st;
@@ -123,11 +133,14 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, int split, char*
   for (int db = 0; db < C::NDB; ++db) st.o[db] = f32x16{};
   const float c = a.scale_log2;
 
-  // one stage: the work-group copies a tile, waits, computes; four such
-  // work-groups per CU keep several tiles in flight
+  // one stage: the work-group copies a tile, waits, computes; several such
+  // work-groups per CU keep tiles in flight.  A single wave only has to see its
+  // own reads of the previous tile finish before the stage is overwritten;
+  // several waves wait for each other.
   auto run = [&](const auto& tile_mask, const auto& ok) {
     for (int j = j_lo; j <= j_hi; ++j) {
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      if (NW == 1) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      else __syncthreads();
       issue(j, k_st0, v_st0);
       wait_copies_and_barrier();
       fwd_tile<D, F16>(st, k_st0, v_st0, j * C::BC, tile_mask(j * C::BC), ok, c, lane);
@@ -170,22 +183,34 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, int split, char*
   }
 }
 
-template <int D, bool CAUSAL, bool F16>
-__global__ __launch_bounds__(64) void decode_split_kernel(DecodeArgs a) {
+// NW waves per work-group, one group of 32 rows each, share every K/V tile:
+// NW = 1 for up to 32 rows per K/V head (four work-groups per CU, one wave per
+// SIMD), 2 or 4 when there are more (two waves per SIMD; the tile is read once
+// for all the work-group's row groups).
+template <int NW>
+struct DecodeOcc {
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kWavesPerEU = NW == 1 ? 1 : 2;
+};
+
+template <int D, bool CAUSAL, bool F16, int NW>
+__global__ __launch_bounds__(DecodeOcc<NW>::kThreads) __attribute__((amdgpu_waves_per_eu(DecodeOcc<NW>::kWavesPerEU)))
+void decode_split_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) char k_st0[FwdCfg<D>::KT];
   __shared__ __attribute__((aligned(1024))) char v_st0[FwdCfg<D>::VT];
-  split_body<D, CAUSAL, F16, false>(a, blockIdx.x, k_st0, v_st0);
+  split_body<D, CAUSAL, F16, false, NW>(a, blockIdx.x, k_st0, v_st0);
 }
 
 // The rolling-buffer decode in one launch: splits 0 .. ring.n_splits - 1 read
 // the buffer, the rest the new tokens' own keys (a plain causal decode whose
 // cache is exactly those tokens); both write partials for the one combine.
-template <int D, bool F16>
-__global__ __launch_bounds__(64) void decode_rolling_kernel(DecodeArgs ring, DecodeArgs fresh) {
+template <int D, bool F16, int NW>
+__global__ __launch_bounds__(DecodeOcc<NW>::kThreads) __attribute__((amdgpu_waves_per_eu(DecodeOcc<NW>::kWavesPerEU)))
+void decode_rolling_kernel(DecodeArgs ring, DecodeArgs fresh) {
   __shared__ __attribute__((aligned(1024))) char k_st0[FwdCfg<D>::KT];
   __shared__ __attribute__((aligned(1024))) char v_st0[FwdCfg<D>::VT];
-  if ((int)blockIdx.x < ring.n_splits) split_body<D, true, F16, true>(ring, blockIdx.x, k_st0, v_st0);
-  else split_body<D, true, F16, false>(fresh, blockIdx.x - ring.n_splits, k_st0, v_st0);
+  if ((int)blockIdx.x < ring.n_splits) split_body<D, true, F16, true, NW>(ring, blockIdx.x, k_st0, v_st0);
+  else split_body<D, true, F16, false, NW>(fresh, blockIdx.x - ring.n_splits, k_st0, v_st0);
 }
 
 // Merge one row's split partials: one work-group per row.  The splits are
@@ -250,15 +275,26 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 }
 
 // groups of 32 rows (query heads x new tokens) of one K/V head
-inline unsigned row_groups(const DecodeArgs& a) {
-  return (unsigned)(((long long)(a.Hq / a.Hkv) * a.Lq + 31) / 32);
+inline long long row_groups(const DecodeArgs& a) { return ((long long)(a.Hq / a.Hkv) * a.Lq + 31) / 32; }
+
+// waves per work-group for this many row groups
+inline int waves_for(long long groups) { return groups == 1 ? 1 : groups == 2 ? 2 : 4; }
+
+template <int D, bool CAUSAL, bool F16, int NW>
+hipError_t launch_split_nw(const DecodeArgs& a, hipStream_t stream) {
+  const unsigned gz = (unsigned)((row_groups(a) + NW - 1) / NW);
+  hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, F16, NW>), dim3(a.n_splits, a.B * a.Hkv, gz),
+                     dim3(64 * NW), 0, stream, a);
+  return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool F16>
 hipError_t launch_split(const DecodeArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_split_kernel<D, CAUSAL, F16>), dim3(a.n_splits, a.B * a.Hkv, row_groups(a)),
-                     dim3(64), 0, stream, a);
-  return hipGetLastError();
+  switch (waves_for(row_groups(a))) {
+    case 1: return launch_split_nw<D, CAUSAL, F16, 1>(a, stream);
+    case 2: return launch_split_nw<D, CAUSAL, F16, 2>(a, stream);
+    default: return launch_split_nw<D, CAUSAL, F16, 4>(a, stream);
+  }
 }
 
 template <int D, bool F16>
@@ -274,12 +310,22 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
   return launch_combine<D, F16>(a, stream);
 }
 
+template <int D, bool F16, int NW>
+hipError_t launch_rolling_nw(const DecodeArgs& ring, const DecodeArgs& fresh, hipStream_t stream) {
+  const unsigned gz = (unsigned)((row_groups(ring) + NW - 1) / NW);
+  hipLaunchKernelGGL((decode_rolling_kernel<D, F16, NW>), dim3(ring.n_splits + fresh.n_splits, ring.B * ring.Hkv, gz),
+                     dim3(64 * NW), 0, stream, ring, fresh);
+  return hipGetLastError();
+}
+
 template <int D, bool F16>
 hipError_t launch_rolling(const DecodeArgs& ring, const DecodeArgs& fresh, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_rolling_kernel<D, F16>), dim3(ring.n_splits + fresh.n_splits, ring.B * ring.Hkv,
-                                                             row_groups(ring)),
-                     dim3(64), 0, stream, ring, fresh);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  switch (waves_for(row_groups(ring))) {
+    case 1: e = launch_rolling_nw<D, F16, 1>(ring, fresh, stream); break;
+    case 2: e = launch_rolling_nw<D, F16, 2>(ring, fresh, stream); break;
+    default: e = launch_rolling_nw<D, F16, 4>(ring, fresh, stream); break;
+  }
   if (e != hipSuccess) return e;
   return launch_combine<D, F16>(ring, stream);
 }

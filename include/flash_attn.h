@@ -245,8 +245,8 @@ int flash_attn_bwd_block(const void* q, const void* k, const void* v, const void
  * single new token it can also be served here with causal = 0 and cache_len =
  * the number of filled slots, since the slot order then does not matter.)
  * The keys are split across work-groups and the partials merged exactly; the
- * cache is read once per K/V head for every 32 rows of R = (Hq/Hkv) * Lq
- * (query heads times new tokens), so R <= 32 reads it once.  For long chunks
+ * cache is read once per K/V head for every 128 rows of R = (Hq/Hkv) * Lq
+ * (query heads times new tokens), so R <= 128 reads it once.  For long chunks
  * of new tokens flash_attn_fwd_block is the faster call.
  * A window needs causal = 1 here (FA_ERR_UNSUPPORTED otherwise).
  * Requires 1 <= Lq <= Lk <= 2^23, d in {64,128}, bf16 or fp16, B * Hkv <=
@@ -281,7 +281,7 @@ int flash_attn_decode(const void* q, const void* k_cache, const void* v_cache, c
  * order does not matter: each slot's position is known from n_b), the newer
  * ones from k_new / v_new, causally.  The partials of both are merged exactly
  * (log-sum-exp weights), so any Lq and G = Hq/Hkv are exact; the buffer is
- * read once per K/V head for every 32 rows of R = G * Lq.
+ * read once per K/V head for every 128 rows of R = G * Lq.
  * Sizes as for flash_attn_decode with W in place of Lk (Lq may exceed W);
  * window > W is FA_ERR_INVALID_ARG (those keys are gone from the buffer).
  * workspace: at least flash_attn_decode_rolling_workspace_bytes() bytes,

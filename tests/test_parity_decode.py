@@ -53,6 +53,8 @@ CASES = [
     (1, 2, 1, 3, 50000, 64, False, 0, [49999], torch.float16),           # many splits, non-causal, ragged tile
     (1, 32, 8, 20, 5000, 128, True, 0, [4321], torch.bfloat16),          # 80 rows per K/V head: 3 row groups
     (2, 4, 2, 40, 300, 64, True, 17, [300, 123], torch.float16),         # 80 rows, window, ragged batch
+    (1, 16, 2, 20, 3000, 64, True, 0, [2999], torch.bfloat16),           # 160 rows: 5 groups, 2 work-groups
+    (2, 8, 4, 32, 1500, 64, False, 0, [1500, 900], torch.float16),       # 64 rows (2 groups), non-causal
 ]
 
 
