@@ -18,9 +18,10 @@
 // the hardware v_exp_f32; the saved log-sum-exp is converted back to ln.
 // Only O and the per-row log-sum-exp are written (claspmoon.cn §3.3).
 //
-// On gfx950 the vector ALU work of a wave does not hide behind its matrix-core
-// work, so the kernel keeps the per-tile VALU instruction count close to the
-// softmax itself: padded LDS rows make every operand address a per-lane base
+// The vector ALU work of a tile adds to its matrix-core time more than it
+// hides under it (the products and the softmax depend on each other within a
+// wave, and the second wave of a SIMD covers only part of it), so the kernel
+// keeps the per-tile VALU instruction count close to the softmax itself: padded LDS rows make every operand address a per-lane base
 // plus an immediate, the copies use buffer loads with loop-invariant lane
 // offsets (past-the-end rows read as zeros, no clamping), the pair of lanes
 // holding one query exchange values with v_permlane32_swap, and the running

@@ -14,7 +14,13 @@
 //   split+prio               -- the same with the matrix waves at s_setprio 3;
 //   same-wave 1/SIMD, 2/SIMD -- each wave does both, MFMA and VALU interleaved
 //                               one MFMA then six VALU (does a wave's own VALU
-//                               issue under its MFMA?).
+//                               issue under its MFMA?);
+//   ... acc in AGPRs         -- mfma 2/SIMD, split and same-wave 2/SIMD again
+//                               with the accumulators (MFMA source C and
+//                               result) in AGPRs rather than VGPRs.  The
+//                               compiler picks that form for a function whose
+//                               inline asm names an AGPR operand, so these
+//                               modes carry an empty asm statement with one.
 // If two kinds of work overlap, the mixed time approaches the larger of the
 // two times alone; if they serialise, it approaches their sum.  The shader
 // clock is read with s_memtime against the 100 MHz s_memrealtime.
@@ -28,10 +34,13 @@
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-enum { M1 = 0, M2, V1, V2, SPLIT, SPLIT_PRIO, SAME1, SAME2, NMODES };
+enum { M1 = 0, M2, V1, V2, SPLIT, SPLIT_PRIO, SAME1, SAME2, M2_ACC, SPLIT_ACC, SAME2_ACC, NMODES };
 static const char* kNames[NMODES] = {"mfma 1/SIMD", "mfma 2/SIMD", "valu 1/SIMD", "valu 2/SIMD",
                                      "split (mfma | valu)", "split, mfma waves prio 3",
-                                     "same-wave 1/SIMD", "same-wave 2/SIMD"};
+                                     "same-wave 1/SIMD", "same-wave 2/SIMD",
+                                     "mfma 2/SIMD, acc in AGPRs", "split, acc in AGPRs",
+                                     "same-wave 2/SIMD, acc AGPRs"};
+constexpr bool acc_in_agprs(int mode) { return mode == M2_ACC || mode == SPLIT_ACC || mode == SAME2_ACC; }
 
 #define CHECK(x)                                                                  \
   do {                                                                            \
@@ -51,17 +60,18 @@ __global__ __launch_bounds__(512, 1) void probe(float* out, unsigned long long* 
   bool mat = false, vec = false;
   switch (MODE) {
     case M1: mat = !hi; break;
-    case M2: mat = true; break;
+    case M2: case M2_ACC: mat = true; break;
     case V1: vec = !hi; break;
     case V2: vec = true; break;
     case SPLIT:
-    case SPLIT_PRIO: mat = !hi; vec = hi; break;
+    case SPLIT_PRIO: case SPLIT_ACC: mat = !hi; vec = hi; break;
     case SAME1: mat = vec = !hi; break;
-    case SAME2: mat = vec = true; break;
+    case SAME2: case SAME2_ACC: mat = vec = true; break;
   }
   pad[threadIdx.x] = c;
   __syncthreads();
   const float seed = pad[(threadIdx.x + 1) & 511];
+  if constexpr (acc_in_agprs(MODE)) asm volatile("; AGPR operand: %0" ::"a"(seed));
   unsigned long long t0 = 0, r0 = 0;
   if (threadIdx.x == 0) {
     t0 = __builtin_amdgcn_s_memtime();
@@ -77,31 +87,36 @@ __global__ __launch_bounds__(512, 1) void probe(float* out, unsigned long long* 
   float v[16], sum[4] = {0.f, 0.f, 0.f, 0.f};
   for (int i = 0; i < 16; ++i) v[i] = seed * (float)(i + lane) * 0.01f;
   if (MODE == SPLIT_PRIO && mat) __builtin_amdgcn_s_setprio(3);
-  if (mat || vec) {
+  // three separate loops, so that no wave carries the other kind's registers
+  // through its loop (a shared loop had the vector waves copy the AGPR
+  // accumulators every iteration)
+  if (mat && vec) {
     for (int it = 0; it < iters; ++it) {
-      if (mat && vec) {
-        // one MFMA, then six VALU instructions (two elements), eight times
+      // one MFMA, then six VALU instructions (two elements), eight times
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((m & 1) ? a1 : a0, b, acc[m & 3], 0, 0, 0);
+      for (int m = 0; m < 8; ++m) {
+        acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((m & 1) ? a1 : a0, b, acc[m & 3], 0, 0, 0);
 #pragma unroll
-          for (int e = 2 * m; e < 2 * m + 2; ++e) {
-            v[e] = __builtin_amdgcn_exp2f(fmaf(v[e], c, -1.0f));
-            sum[e & 3] += v[e];
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
-        }
-      } else if (mat) {
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-          acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((m & 1) ? a1 : a0, b, acc[m & 3], 0, 0, 0);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
+        for (int e = 2 * m; e < 2 * m + 2; ++e) {
           v[e] = __builtin_amdgcn_exp2f(fmaf(v[e], c, -1.0f));
           sum[e & 3] += v[e];
         }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // six VALU
+      }
+    }
+  } else if (mat) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+        acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16((m & 1) ? a1 : a0, b, acc[m & 3], 0, 0, 0);
+    }
+  } else if (vec) {
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        v[e] = __builtin_amdgcn_exp2f(fmaf(v[e], c, -1.0f));
+        sum[e & 3] += v[e];
       }
     }
   }
@@ -145,12 +160,12 @@ static void run(int cus, int iters, float* out, unsigned long long* clk, unsigne
   int mat_waves = 0, vec_waves = 0;
   switch (MODE) {
     case M1: mat_waves = 4; break;
-    case M2: mat_waves = 8; break;
+    case M2: case M2_ACC: mat_waves = 8; break;
     case V1: vec_waves = 4; break;
     case V2: vec_waves = 8; break;
-    case SPLIT: case SPLIT_PRIO: mat_waves = 4; vec_waves = 4; break;
+    case SPLIT: case SPLIT_PRIO: case SPLIT_ACC: mat_waves = 4; vec_waves = 4; break;
     case SAME1: mat_waves = vec_waves = 4; break;
-    case SAME2: mat_waves = vec_waves = 8; break;
+    case SAME2: case SAME2_ACC: mat_waves = vec_waves = 8; break;
   }
   const double flop = (double)cus * mat_waves * iters * 8 * (2.0 * 32 * 32 * 16);
   const double mfma_per_simd = (double)mat_waves / 4 * iters * 8;
@@ -183,6 +198,17 @@ int main(int argc, char** argv) {
   run<SPLIT_PRIO>(cus, iters, out, clk, hclk);
   run<SAME1>(cus, iters, out, clk, hclk);
   run<SAME2>(cus, iters, out, clk, hclk);
+  run<M2_ACC>(cus, iters, out, clk, hclk);
+  run<SPLIT_ACC>(cus, iters, out, clk, hclk);
+  run<SAME2_ACC>(cus, iters, out, clk, hclk);
+  // the two accumulator forms once more, alternated, so that a clock
+  // difference between them is not an effect of the order
+  run<M2>(cus, iters, out, clk, hclk);
+  run<M2_ACC>(cus, iters, out, clk, hclk);
+  run<M2>(cus, iters, out, clk, hclk);
+  run<M2_ACC>(cus, iters, out, clk, hclk);
+  run<SPLIT>(cus, iters, out, clk, hclk);
+  run<SPLIT_ACC>(cus, iters, out, clk, hclk);
   CHECK(hipFree(out));
   CHECK(hipFree(clk));
   std::free(hclk);
