@@ -565,7 +565,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     for (int i = 0; i < C::KPER; ++i) buf2lds16(krs, ad.kcopy[i], soff, kb + (wave + C::kWaves * i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::VPER; ++i)
-      if (wave + C::kWaves * i < C::VCOPIES) buf2lds16(vrs, ad.vcopy[i], soff, vb + (wave + C::kWaves * i) * 1024);
+      if (owns_copy<C::kWaves, C::VCOPIES>(wave, i)) buf2lds16(vrs, ad.vcopy[i], soff, vb + (wave + C::kWaves * i) * 1024);
   };
   if (!empty) issue(j_lo, k_st0, v_st0);
 

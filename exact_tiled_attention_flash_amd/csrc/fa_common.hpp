@@ -158,6 +158,15 @@ __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32, 
 // sides.
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Does wave `wave` (< NW) of a work-group of NW waves own copy i of a tile of
+// COPIES 1 KiB copies (copy wave + NW*i)?  Every wave owns one copy in each of
+// the first COPIES / NW rounds, so those resolve at compile time and only the
+// last, partial round costs a (wave-uniform) branch.
+template <int NW, int COPIES>
+__device__ __forceinline__ bool owns_copy(int wave, int i) {
+  return i < COPIES / NW || wave + NW * i < COPIES;
+}
+
 // Forward LDS swizzles (XOR on the 16-byte chunk index of row r of a tile).
 // K is only read 16 rows at a time at one chunk: spread those rows over all
 // banks.  V is only read by the transposing read (4 rows x 4 chunks per

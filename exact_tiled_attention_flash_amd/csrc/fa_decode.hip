@@ -117,10 +117,10 @@ __device__ __forceinline__ void split_body(const DecodeArgs& a, int split, char*
     const int soff = j * C::BC * (2 * D);
 #pragma unroll
     for (int i = 0; i < KPER; ++i)
-      if (NW == 1 || wave + NW * i < C::KCOPIES) buf2lds16(krs, koff[i], soff, kbuf + (wave + NW * i) * 1024);
+      if (owns_copy<NW, C::KCOPIES>(wave, i)) buf2lds16(krs, koff[i], soff, kbuf + (wave + NW * i) * 1024);
 #pragma unroll
     for (int i = 0; i < VPER; ++i)
-      if (NW == 1 || wave + NW * i < C::VCOPIES) buf2lds16(vrs, voff[i], soff, vbuf + (wave + NW * i) * 1024);
+      if (owns_copy<NW, C::VCOPIES>(wave, i)) buf2lds16(vrs, voff[i], soff, vbuf + (wave + NW * i) * 1024);
   };
 
   FwdState<D> st;

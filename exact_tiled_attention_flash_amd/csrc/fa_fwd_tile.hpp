@@ -68,10 +68,10 @@ __device__ __forceinline__ void issue_kv(const CopyPlan<D>& cp, __amdgpu_buffer_
   const int soff = k0 * (2 * D);
 #pragma unroll
   for (int i = 0; i < C::KPER; ++i)
-    if (wave + 4 * i < C::KCOPIES) buf2lds16(kr, cp.koff[i], soff, kbuf + (wave + 4 * i) * 1024);
+    if (owns_copy<4, C::KCOPIES>(wave, i)) buf2lds16(kr, cp.koff[i], soff, kbuf + (wave + 4 * i) * 1024);
 #pragma unroll
   for (int i = 0; i < C::VPER; ++i)
-    if (wave + 4 * i < C::VCOPIES) buf2lds16(vr, cp.voff[i], soff, vbuf + (wave + 4 * i) * 1024);
+    if (owns_copy<4, C::VCOPIES>(wave, i)) buf2lds16(vr, cp.voff[i], soff, vbuf + (wave + 4 * i) * 1024);
 }
 
 __device__ __forceinline__ void wait_copies_and_barrier() {

@@ -667,7 +667,7 @@ __global__ __launch_bounds__(256, 2) void dq_masked_kernel(BwdArgs a, PlanPtrs p
     for (int i = 0; i < C::KPER; ++i) buf2lds16(krs, ad.kcopy[i], soff, kb + (wave + C::kWaves * i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::VPER; ++i)
-      if (wave + C::kWaves * i < C::VCOPIES) buf2lds16(vrs, ad.vcopy[i], soff, vb + (wave + C::kWaves * i) * 1024);
+      if (owns_copy<C::kWaves, C::VCOPIES>(wave, i)) buf2lds16(vrs, ad.vcopy[i], soff, vb + (wave + C::kWaves * i) * 1024);
   };
   const EntryStream es{make_rsrc(ents, 4u * (unsigned)n_ent)};
   unsigned cur = n_ent > 0 ? ents[0] : 0u, nxt = n_ent > 1 ? ents[1] : 0u;
