@@ -138,12 +138,19 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
   }
   ad.kv = row_offset_kpad<D>(32 * kb + ln, 0, g);
 
-  auto q0_of = [&](int it) { return (qt_lo + it % nq) * C::BQ; };
-  auto issue = [&](int it, char* qs, char* dos, float* ss) {
-    const int hq = hk * G + it / nq, q0 = q0_of(it);
-    const size_t qoff = ((size_t)(b * a.Hq + hq) * L) * D;
-    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(reinterpret_cast<const bf16*>(a.q) + qoff, qhead_bytes);
-    const __amdgpu_buffer_rsrc_t drs = make_rsrc(reinterpret_cast<const bf16*>(a.dout) + qoff, qhead_bytes);
+  // Iteration it visits query tile qt_lo + it % nq of query head hk*G + it / nq.
+  // Both are stepped incrementally (no integer division in the loop): (i_h,
+  // i_q) for the next tile to copy, c_q for the tile being computed.
+  int i_h = 0, i_q = 0, c_q = 0;
+  const bf16* q_head = reinterpret_cast<const bf16*>(a.q) + ((size_t)(b * a.Hq + hk * G) * L) * D;
+  const bf16* do_head = reinterpret_cast<const bf16*>(a.dout) + ((size_t)(b * a.Hq + hk * G) * L) * D;
+  const float* l_head = a.lse2 + (size_t)(b * a.Hq + hk * G) * L;
+  const float* e_head = a.delta + (size_t)(b * a.Hq + hk * G) * L;
+  auto issue = [&](char* qs, char* dos, float* ss) {
+    const size_t qoff = (size_t)i_h * L * D;
+    const __amdgpu_buffer_rsrc_t qrs = make_rsrc(q_head + qoff, qhead_bytes);
+    const __amdgpu_buffer_rsrc_t drs = make_rsrc(do_head + qoff, qhead_bytes);
+    const int q0 = (qt_lo + i_q) * C::BQ;
     const int soff = q0 * (2 * D);
 #pragma unroll
     for (int i = 0; i < C::QPER; ++i) {
@@ -151,12 +158,21 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       buf2lds16(drs, ad.qcopy[i], soff, dos + (wave + C::kWaves * i) * 1024);
     }
     if (wave == 0) {
-      const size_t srow = (size_t)(b * a.Hq + hq) * L;
-      const __amdgpu_buffer_rsrc_t lrs = make_rsrc(a.lse2 + srow, (unsigned)L * 4);
-      const __amdgpu_buffer_rsrc_t ers = make_rsrc(a.delta + srow, (unsigned)L * 4);
+      const size_t srow = (size_t)i_h * L;
+      const __amdgpu_buffer_rsrc_t lrs = make_rsrc(l_head + srow, (unsigned)L * 4);
+      const __amdgpu_buffer_rsrc_t ers = make_rsrc(e_head + srow, (unsigned)L * 4);
       buf2lds4(lrs, 4 * lane, 4 * q0, reinterpret_cast<char*>(ss));
       buf2lds4(ers, 4 * lane, 4 * q0, reinterpret_cast<char*>(ss) + 4 * C::BQ);
     }
+    if (++i_q == nq) {
+      i_q = 0;
+      ++i_h;
+    }
+  };
+  auto next_q0 = [&]() {
+    const int q0 = (qt_lo + c_q) * C::BQ;
+    if (++c_q == nq) c_q = 0;
+    return q0;
   };
 
   // the work-group's K and V rows, once (padded layout; rows past L read zeros)
@@ -171,7 +187,7 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
       buf2lds16(vrs, src, soff, v_blk + n * 1024);
     }
   }
-  if (n_it > 0) issue(0, q_st0, do_st0, stat_st0);
+  if (n_it > 0) issue(q_st0, do_st0, stat_st0);
 
   KVState<D> st;
 #pragma unroll
@@ -197,16 +213,16 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
 
   wait_copies_and_barrier();
   for (int it = 0; it < n_it; it += 2) {
-    if (it + 1 < n_it) issue(it + 1, q_st1, do_st1, stat_st1);
-    if (wave_needs(q0_of(it)))
-      kv_tile<D, F16>(st, ad, k_blk, v_blk, q_st0, do_st0, stat_st0, q0_of(it), block_mask(q0_of(it)), ok, qh, c,
-                      lane);
+    if (it + 1 < n_it) issue(q_st1, do_st1, stat_st1);
+    const int q0a = next_q0();
+    if (wave_needs(q0a))
+      kv_tile<D, F16>(st, ad, k_blk, v_blk, q_st0, do_st0, stat_st0, q0a, block_mask(q0a), ok, qh, c, lane);
     wait_copies_and_barrier();
     if (it + 1 >= n_it) break;
-    if (it + 2 < n_it) issue(it + 2, q_st0, do_st0, stat_st0);
-    if (wave_needs(q0_of(it + 1)))
-      kv_tile<D, F16>(st, ad, k_blk, v_blk, q_st1, do_st1, stat_st1, q0_of(it + 1), block_mask(q0_of(it + 1)), ok,
-                      qh, c, lane);
+    if (it + 2 < n_it) issue(q_st0, do_st0, stat_st0);
+    const int q0b = next_q0();
+    if (wave_needs(q0b))
+      kv_tile<D, F16>(st, ad, k_blk, v_blk, q_st1, do_st1, stat_st1, q0b, block_mask(q0b), ok, qh, c, lane);
     wait_copies_and_barrier();
   }
 
