@@ -472,8 +472,8 @@ def measure_autograd(iters=10, warmup=3):
         fa.bwd(q, k, v, o, lse, do, causal=True)
 
     # A training loop issues step after step: time back-to-back calls between two
-    # events (per-call events would also count the host's issue time whenever the
-    # GPU drains between calls), the two routes alternated three times.
+    # events, the two routes alternated three times, and report the host's issue
+    # time per call beside it.
     import time
 
     def loop_ms(fn, n):
