@@ -631,18 +631,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   if (my_q < L) {
     bf16* dQr = reinterpret_cast<bf16*>(a.dq) + q_off + (size_t)my_q * D;
     const float s = a.scale;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        bf16x4 w;
-        w[0] = pack1<F16>(st.dq[db][4 * i4 + 0] * s);
-        w[1] = pack1<F16>(st.dq[db][4 * i4 + 1] * s);
-        w[2] = pack1<F16>(st.dq[db][4 * i4 + 2] * s);
-        w[3] = pack1<F16>(st.dq[db][4 * i4 + 3] * s);
-        *reinterpret_cast<bf16x4*>(dQr + 32 * db + 8 * i4 + 4 * g) = w;
-      }
-    }
+    store_row_c<F16, C::NDB>(dQr, st.dq, s, g);
   }
 }
 

@@ -126,6 +126,36 @@ __device__ __forceinline__ float dot2_ones(bf16 a, bf16 b, float acc) {
   return __builtin_amdgcn_fdot2_f32_bf16(v, one, acc, false);
 }
 
+// Store one row held in the MFMA C layout with lane = row: in block db, the
+// lane's register i is element 32db + 8(i/4) + 4g + i%4 (g = lane / 32), so a
+// lane alone holds runs of 4.  For each pair of 8-element groups two
+// v_permlane32_swap between the lanes g = 0 and g = 1 of the row give lane g
+// elements 32db + 16p + 8g .. +7 (p = the pair), and every lane stores 16
+// contiguous bytes: 2 * NDB stores of 16 bytes instead of 4 * NDB of 8.  Both
+// lanes of a row must take part (they do when the caller's condition depends
+// on the row only).  The values are multiplied by f and rounded to 16 bits.
+template <bool F16, int NDB>
+__device__ __forceinline__ void store_row_c(bf16* row, const f32x16 (&acc)[NDB], float f, int g) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      bf16x8 v;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = pack1<F16>(acc[db][8 * p + e] * f);
+      u32x4 u = __builtin_bit_cast(u32x4, v);
+      const auto s0 = __builtin_amdgcn_permlane32_swap(u[0], u[2], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(u[1], u[3], false, false);
+      u[0] = s0[0];
+      u[2] = s0[1];
+      u[1] = s1[0];
+      u[3] = s1[1];
+      *reinterpret_cast<u32x4*>(row + 32 * db + 16 * p + 8 * g) = u;
+    }
+  }
+}
+
 __device__ __forceinline__ float pair_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);

@@ -123,18 +123,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(FwdArgs a) {
   if (my_q < L) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     bf16* Oq = reinterpret_cast<bf16*>(a.o) + ((size_t)(b * a.Hq + h) * L + my_q) * D;
-#pragma unroll
-    for (int db = 0; db < C::NDB; ++db) {
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        bf16x4 w;
-        w[0] = pack1<F16>(st.o[db][4 * i4 + 0] * inv);
-        w[1] = pack1<F16>(st.o[db][4 * i4 + 1] * inv);
-        w[2] = pack1<F16>(st.o[db][4 * i4 + 2] * inv);
-        w[3] = pack1<F16>(st.o[db][4 * i4 + 3] * inv);
-        *reinterpret_cast<bf16x4*>(Oq + 32 * db + 8 * i4 + 4 * g) = w;
-      }
-    }
+    store_row_c<F16, C::NDB>(Oq, st.o, inv, g);
     if (a.lse != nullptr && g == 0)
       a.lse[(size_t)(b * a.Hq + h) * L + my_q] = l_tot > 0.f ? (st.m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
