@@ -170,8 +170,9 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const Addr& ad_in, const
 
   // dP - D = dO V^T - D: the chain starts from the stored -D of each query
   // row (C-layout register i is query row 8(i/4) + 4g + i%4 of the half).
-  // It is independent of P, so it comes first: its products can then run
-  // beside the exponentials below (one basic block up to the mask branch).
+  // It is independent of P, so it is issued before the exponentials below and
+  // its products run beside them (one basic block up to the mask branch).
+  // (Interleaving the S and dP chains step by step measured 0.4% slower.)
   f32x16 dp;
 #pragma unroll
   for (int i4 = 0; i4 < 4; ++i4) {
