@@ -226,59 +226,15 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     wait_copies_and_barrier();
   }
 
-  // Sum the two query halves through LDS (the stage buffers are free now) and
-  // write dV, then dK.  Waves 4..7 deposit their float32 partials (16 bytes per
-  // lane and access), waves 0..3 add them, round, and lay the key block's rows
-  // out row-major in the free K block; then all eight waves store the
-  // work-group's rows to memory, 16 bytes per lane (2-byte stores straight from
-  // the MFMA layout took an eighth of the kernel's time).
-  constexpr int kPart = C::NDB * 16 * 64 * 4;     // bytes per wave per tensor
-  constexpr int kRowBytes = 2 * D;
-  constexpr int kBlockBytes = C::BK * kRowBytes;  // the work-group's rows of one tensor
-  static_assert(kPart <= C::QT, "a partial must fit in one stage buffer");
-  static_assert(kBlockBytes <= C::KB && kBlockBytes % 1024 == 0, "the rows must fit the K block");
-  char* dKh = reinterpret_cast<char*>(reinterpret_cast<bf16*>(a.dk) + kv_off) + (size_t)key_wg0 * kRowBytes;
-  char* dVh = reinterpret_cast<char*>(reinterpret_cast<bf16*>(a.dv) + kv_off) + (size_t)key_wg0 * kRowBytes;
-  const float s = a.scale;
-  f32x4* part = reinterpret_cast<f32x4*>(kb == 0 ? q_st0 : kb == 1 ? do_st0 : kb == 2 ? q_st1 : do_st1);
-  bf16* rows = reinterpret_cast<bf16*>(k_blk);
+  // Sum the two query halves and store (the stage buffers and the K block are
+  // free now).  Storing rows 16 bytes per lane instead of the 2-byte pieces of
+  // the MFMA layout took an eighth of the kernel's time off its epilogue.
+  char* stage = kb == 0 ? q_st0 : kb == 1 ? do_st0 : kb == 2 ? q_st1 : do_st1;
+  const size_t row0 = (size_t)key_wg0 * (2 * D);
   const int n_rows = min(C::BK, Lk - key_wg0);    // rows of this block inside the sequence
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    if (qh == 1) {
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x16& acc = pass == 0 ? st.dv[db] : st.dk[db];
-          part[(db * 4 + i4) * 64 + lane] = f32x4{acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]};
-        }
-    }
-    __syncthreads();
-    if (qh == 0) {
-      const float f = pass == 0 ? 1.f : s;
-      // lane holds head-dim column 32*db + ln of keys 32*kb + 8*(i/4) + 4g + i%4
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 o = part[(db * 4 + i4) * 64 + lane];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float x = ((pass == 0 ? st.dv[db][4 * i4 + j] : st.dk[db][4 * i4 + j]) + o[j]) * f;
-            rows[(32 * kb + 8 * i4 + 4 * g + j) * D + 32 * db + ln] = pack1<F16>(x);
-          }
-        }
-    }
-    __syncthreads();
-    char* dst = pass == 0 ? dVh : dKh;
-#pragma unroll
-    for (int c = wave; c < kBlockBytes / 1024; c += C::kWaves) {
-      const int off = c * 1024 + 16 * lane;
-      if (off / kRowBytes < n_rows)
-        *reinterpret_cast<bf16x8*>(dst + off) = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(rows) + off);
-    }
-  }
+  kv_store<D, F16>(st, stage, k_blk, reinterpret_cast<char*>(reinterpret_cast<bf16*>(a.dk) + kv_off) + row0,
+                   reinterpret_cast<char*>(reinterpret_cast<bf16*>(a.dv) + kv_off) + row0, a.scale, kb, qh, wave,
+                   lane, [&](int r) { return r >= n_rows; });
 }
 
 // ------------------------------------------------------------ 2'. fused dK / dV / dQ

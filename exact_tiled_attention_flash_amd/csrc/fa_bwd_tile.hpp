@@ -92,6 +92,65 @@ struct KVAddrDual {
   int kv;                 // the same keys' rows in the padded V block
 };
 
+// End of a dK/dV work-group: sum the two query halves through LDS and store dV,
+// then dK (times the softmax scale s), for the work-group's 128 keys.  Waves
+// 4..7 deposit their float32 partials in `stage` (the free stage buffer of
+// their key block, 16 bytes per lane and access); waves 0..3 add them, round,
+// and lay the rows out row-major in `rows` (at least 128 * 2D bytes of free
+// LDS); then all eight waves store the rows to dv_rows / dk_rows (the block's
+// first row in memory) 16 bytes per lane.  skip(r) says local row r is not
+// stored (past the end of the sequence, or written by another pass).
+template <int D, bool F16, class Skip>
+__device__ __forceinline__ void kv_store(KVState<D>& st, char* stage, char* rows, char* dk_rows,
+                                         char* dv_rows, float s, int kb, int qh, int wave, int lane,
+                                         const Skip& skip) {
+  using C = KVCfg<D>;
+  constexpr int kPart = C::NDB * 16 * 64 * 4;     // bytes per wave per tensor
+  constexpr int kRowBytes = 2 * D;
+  constexpr int kBlockBytes = C::BK * kRowBytes;
+  static_assert(kPart <= C::QT, "a partial must fit in one stage buffer");
+  static_assert(kBlockBytes <= C::KB && kBlockBytes % 1024 == 0, "the rows must fit the K block");
+  const int g = lane >> 5, ln = lane & 31;
+  f32x4* part = reinterpret_cast<f32x4*>(stage);
+  bf16* rows16 = reinterpret_cast<bf16*>(rows);
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass) {
+    if (qh == 1) {
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x16& acc = pass == 0 ? st.dv[db] : st.dk[db];
+          part[(db * 4 + i4) * 64 + lane] = f32x4{acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]};
+        }
+    }
+    __syncthreads();
+    if (qh == 0) {
+      const float f = pass == 0 ? 1.f : s;
+      // lane holds head-dim column 32*db + ln of keys 32*kb + 8*(i/4) + 4g + i%4
+#pragma unroll
+      for (int db = 0; db < C::NDB; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const f32x4 o = part[(db * 4 + i4) * 64 + lane];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float x = ((pass == 0 ? st.dv[db][4 * i4 + j] : st.dk[db][4 * i4 + j]) + o[j]) * f;
+            rows16[(32 * kb + 8 * i4 + 4 * g + j) * D + 32 * db + ln] = pack1<F16>(x);
+          }
+        }
+    }
+    __syncthreads();
+    char* dst = pass == 0 ? dv_rows : dk_rows;
+#pragma unroll
+    for (int c = wave; c < kBlockBytes / 1024; c += C::kWaves) {
+      const int off = c * 1024 + 16 * lane;
+      if (!skip(off / kRowBytes))
+        *reinterpret_cast<bf16x8*>(dst + off) = *reinterpret_cast<const bf16x8*>(rows + off);
+    }
+  }
+}
+
 // Key-major element mask of the range-tiled kernels: the lane's key j is
 // fixed; query row q sits at key position q + shift (visibility as range_ok).
 template <bool CAUSAL>

@@ -558,50 +558,19 @@ __global__ __launch_bounds__(512, 1) void dkdv_masked_kernel(BwdArgs a, PlanPtrs
     nxt_h = far1_h;
   }
 
-  // sum the two query halves through LDS, then store (as the range-tiled kernel)
-  constexpr int kPart = C::NDB * 16 * 64 * 4;
-  static_assert(kPart <= C::QT, "a partial must fit in one stage buffer");
-  bf16* dKh = reinterpret_cast<bf16*>(a.dk) + kv_off;
-  bf16* dVh = reinterpret_cast<bf16*>(a.dv) + kv_off;
-  const float s = a.scale;
-  float* part = reinterpret_cast<float*>(kb == 0 ? q_st0 : kb == 1 ? do_st0 : kb == 2 ? q_st1 : do_st1);
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-    if (qh == 1) {
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) part[(db * 16 + i) * 64 + lane] = pass == 0 ? st.dv[db][i] : st.dk[db][i];
-    }
-    __syncthreads();
-    if (qh == 0) {
-#pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (pass == 0) st.dv[db][i] += part[(db * 16 + i) * 64 + lane];
-          else st.dk[db][i] += part[(db * 16 + i) * 64 + lane];
-        }
-    }
-    __syncthreads();
-  }
-  if (qh == 0) {
-    // global keys are left to the global-key pass
-    const int b0 = min(2 * kt, p.nb - 1), b1 = min(2 * kt + 1, p.nb - 1);
-    const unsigned long long gw0 = p.gbits[b0], gw1 = p.gbits[b1];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = key_w0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      const bool kglob = (((key >> 6) == b0 ? gw0 : gw1) >> (key & 63)) & 1ull;
-      if (key < L && !kglob) {
-#pragma unroll
-        for (int db = 0; db < C::NDB; ++db) {
-          dKh[(size_t)key * D + 32 * db + ln] = pack1<F16>(st.dk[db][i] * s);
-          dVh[(size_t)key * D + 32 * db + ln] = pack1<F16>(st.dv[db][i]);
-        }
-      }
-    }
-  }
+  // sum the two query halves and store as the range-tiled kernel; global keys
+  // are left to the global-key pass
+  char* stage = kb == 0 ? q_st0 : kb == 1 ? do_st0 : kb == 2 ? q_st1 : do_st1;
+  const size_t row0 = (size_t)key_wg0 * (2 * D);
+  const int b0 = min(2 * kt, p.nb - 1), b1 = min(2 * kt + 1, p.nb - 1);
+  const unsigned long long gw0 = p.gbits[b0], gw1 = p.gbits[b1];
+  kv_store<D, F16>(st, stage, k_blk, reinterpret_cast<char*>(reinterpret_cast<bf16*>(a.dk) + kv_off) + row0,
+                   reinterpret_cast<char*>(reinterpret_cast<bf16*>(a.dv) + kv_off) + row0, a.scale, kb, qh, wave,
+                   lane, [&](int r) {
+                     const int key = key_wg0 + r;
+                     const bool kglob = (((key >> 6) == b0 ? gw0 : gw1) >> (key & 63)) & 1ull;
+                     return (key >= L) | kglob;
+                   });
 }
 
 // dQ: one work-group of 4 waves per (batch, query head, 128 queries), as the
