@@ -256,12 +256,10 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const Addr& ad_in, const
   // plain select writes new registers, and the join of the two versions of P
   // then costs 16 register copies on the unmasked path.
   if (need_mask) {
+    with_mask(ok, [&](const auto& m) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int q = qw0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      const unsigned long long keep = __builtin_amdgcn_ballot_w64(ok(q));
-      asm("v_cndmask_b32_e64 %0, 0, %0, %1" : "+v"(p[i]) : "s"(keep));
-    }
+      for (int i = 0; i < 16; ++i) p[i] = keep_or_zero(p[i], m(qw0 + 8 * (i >> 2) + 4 * g + (i & 3)));
+    });
   }
   // dV += P^T dO: A = P (lane = key, K slots = queries), B = dO via the transposing read
 #pragma unroll
@@ -364,11 +362,10 @@ __device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const 
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(p[i], c, -st.lse2));
     if (need_mask) {
+      with_mask(ok, [&](const auto& m) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int kk = k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3);
-        p[i] = ok(kk) ? p[i] : 0.f;
-      }
+        for (int i = 0; i < 16; ++i) p[i] = keep_or_zero(p[i], m(k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3)));
+      });
     }
     // dS^T = P^T * (dP^T - D)
 #pragma unroll

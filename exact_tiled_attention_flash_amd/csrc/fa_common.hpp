@@ -350,6 +350,40 @@ __device__ __forceinline__ void head_tile_of(int r, int n_heads, int n_tiles, in
   }
 }
 
+// ---- applying an element mask
+// Two element masks and a wave-uniform choice between them: the tile steps
+// evaluate only the chosen one (with_mask branches once per tile, outside the
+// element loop), so a cheap mask can stand in for an expensive one on the
+// tiles where both agree.
+template <class A, class B>
+struct EitherMask {
+  bool use_a;
+  A a;
+  B b;
+};
+
+template <class M, class F>
+__device__ __forceinline__ void with_mask(const M& m, const F& f) { f(m); }
+template <class A, class B, class F>
+__device__ __forceinline__ void with_mask(const EitherMask<A, B>& m, const F& f) {
+  if (m.use_a) f(m.a);
+  else f(m.b);
+}
+
+// x = keep ? x : y in place (a tied operand writes no new register, so the
+// masked and unmasked versions of a tile's values join without copies).  All
+// lanes must be active.
+__device__ __forceinline__ float keep_or(float x, bool keep, float y) {
+  const unsigned long long k = __builtin_amdgcn_ballot_w64(keep);
+  asm("v_cndmask_b32_e64 %0, %2, %0, %1" : "+v"(x) : "s"(k), "v"(y));
+  return x;
+}
+__device__ __forceinline__ float keep_or_zero(float x, bool keep) {
+  const unsigned long long k = __builtin_amdgcn_ballot_w64(keep);
+  asm("v_cndmask_b32_e64 %0, 0, %0, %1" : "+v"(x) : "s"(k));
+  return x;
+}
+
 // ---- masks of the range-tiled kernels (positions in key coordinates)
 // Key j is visible to the query at position i iff j < Lk, j <= i when causal,
 // and, for a window w > 0, i - w < j -- plus j < i + w when not causal: the

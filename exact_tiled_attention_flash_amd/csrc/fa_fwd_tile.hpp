@@ -115,12 +115,14 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
 
   // 2. mask, only on tiles that straddle a boundary (wave-uniform decision)
   if (need_mask) {
+    with_mask(ok, [&](const auto& m) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int kk0 = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
-      if (!ok(kk0)) s0[i] = -INFINITY;
-      if (!ok(kk0 + 32)) s1[i] = -INFINITY;
-    }
+      for (int i = 0; i < 16; ++i) {
+        const int kk0 = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
+        s0[i] = keep_or(s0[i], m(kk0), -INFINITY);
+        s1[i] = keep_or(s1[i], m(kk0 + 32), -INFINITY);
+      }
+    });
   }
 
   // 3. online softmax: the two lanes holding one query share the tile maximum.

@@ -379,8 +379,14 @@ __global__ __launch_bounds__(256, 2) void fwd_masked_kernel(FwdArgs a, PlanPtrs 
     const int cls = ent_class(ent, half);
     if (cls != 0 && q_w0 < L) {
       const int kt = ent_tile(ent, p.nb);
-      const GeneralMaskQ<CAUSAL> ok{L, window, my_q, kt * C::BC, gq, ent_block(ent, half),
-                                    cls == 1 ? p.gbits[kt] : 0ull};
+      const unsigned long long gk = cls == 1 ? p.gbits[kt] : 0ull;
+      const bool bm = ent_block(ent, half);
+      // without a global key in the tile and with the block allowed, the
+      // window and causal range alone decide (a global row's own output is
+      // not stored here): the range kernels' cheaper element test
+      const EitherMask<RangeMaskQ<CAUSAL>, GeneralMaskQ<CAUSAL>> ok{
+          (bool)((gk == 0ull) & bm), RangeMaskQ<CAUSAL>{L, window, my_q},
+          GeneralMaskQ<CAUSAL>{L, window, my_q, kt * C::BC, gq, bm, gk}};
       fwd_tile<D, F16>(st, kb, vb, kt * C::BC, cls == 1, ok, c, lane);
     }
   };
@@ -527,8 +533,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_masked_kernel(BwdArgs a, PlanPtrs
     const int cls = ent_class(ent, half);
     const int q0 = ent_tile(ent, p.nb) * C::BQ;
     if (cls != 0 && key_w0 < L && q0 + 32 * qh < L) {
-      const GeneralMaskK<CAUSAL> ok{L, window, my_key, q0, gk, ent_block(ent, half),
-                                    cls == 1 ? p.gbits[ent_tile(ent, p.nb)] : 0ull};
+      const unsigned long long gqb = cls == 1 ? p.gbits[ent_tile(ent, p.nb)] : 0ull;
+      const bool bm = ent_block(ent, half);
+      // without a global query in the tile and with the block allowed, the
+      // window and causal range alone decide (a global key's own dK, dV are
+      // not stored here)
+      const EitherMask<RangeMaskK<CAUSAL>, GeneralMaskK<CAUSAL>> ok{
+          (bool)((gqb == 0ull) & bm), RangeMaskK<CAUSAL>{L, 0, window, my_key},
+          GeneralMaskK<CAUSAL>{L, window, my_key, q0, gk, bm, gqb}};
       kv_tile<D, F16>(st, ad, k_blk, v_blk, qs, dos, ss, q0, cls == 1, ok, qh, c, lane);
     }
   };
@@ -652,6 +664,8 @@ __global__ __launch_bounds__(256, 2) void dq_masked_kernel(BwdArgs a, PlanPtrs p
     const int cls = ent_class(ent, half);
     if (cls != 0 && q_w0 < L) {
       const int kt = ent_tile(ent, p.nb);
+      // (the forward's choice of a cheaper element test costs this kernel
+      // spills: it keeps the general one)
       const GeneralMaskQ<CAUSAL> ok{L, window, my_q, kt * C::BC, gq, ent_block(ent, half),
                                     cls == 1 ? p.gbits[kt] : 0ull};
       q_tile<D, F16>(st, ad, kb, vb, kt * C::BC, cls == 1, ok, c, lane);
