@@ -226,13 +226,13 @@ __global__ __launch_bounds__(512, 1) void bwd_dkdv_kernel(BwdArgs a) {
     wait_copies_and_barrier();
   }
 
-  // Sum the two query halves and store (the stage buffers and the K block are
-  // free now).  Storing rows 16 bytes per lane instead of the 2-byte pieces of
-  // the MFMA layout took an eighth of the kernel's time off its epilogue.
-  char* stage = kb == 0 ? q_st0 : kb == 1 ? do_st0 : kb == 2 ? q_st1 : do_st1;
+  // Sum the two query halves and store, in the stage buffers (free now).
+  // Storing rows 16 bytes per lane instead of the 2-byte pieces of the MFMA
+  // layout took an eighth of the kernel's time off its epilogue.
   const size_t row0 = (size_t)key_wg0 * (2 * D);
   const int n_rows = min(C::BK, Lk - key_wg0);    // rows of this block inside the sequence
-  kv_store<D, F16>(st, stage, k_blk, reinterpret_cast<char*>(reinterpret_cast<bf16*>(a.dk) + kv_off) + row0,
+  kv_store<D, F16>(st, q_st0, do_st0, q_st1, do_st1,
+                   reinterpret_cast<char*>(reinterpret_cast<bf16*>(a.dk) + kv_off) + row0,
                    reinterpret_cast<char*>(reinterpret_cast<bf16*>(a.dv) + kv_off) + row0, a.scale, kb, qh, wave,
                    lane, [&](int r) { return r >= n_rows; });
 }

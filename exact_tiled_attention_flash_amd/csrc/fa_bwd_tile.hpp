@@ -92,27 +92,38 @@ struct KVAddrDual {
   int kv;                 // the same keys' rows in the padded V block
 };
 
+// A work-group barrier that waits for this wave's LDS accesses only (its
+// copies in flight keep going: __syncthreads would also wait for those).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // End of a dK/dV work-group: sum the two query halves through LDS and store dV,
-// then dK (times the softmax scale s), for the work-group's 128 keys.  Waves
-// 4..7 deposit their float32 partials in `stage` (the free stage buffer of
-// their key block, 16 bytes per lane and access); waves 0..3 add them, round,
-// and lay the rows out row-major in `rows` (at least 128 * 2D bytes of free
-// LDS); then all eight waves store the rows to dv_rows / dk_rows (the block's
-// first row in memory) 16 bytes per lane.  skip(r) says local row r is not
-// stored (past the end of the sequence, or written by another pass).
+// then dK (times the softmax scale s), for the work-group's 128 keys, using
+// only the four stage buffers st0..st3 (key block kb uses st<kb>), so that
+// the K and V blocks are free for the next copies meanwhile.  Waves 4..7
+// deposit their float32 partials (16 bytes per lane and access); waves 0..3
+// add them, round, and overwrite their own stage with the block's rows,
+// row-major; then all eight waves store the rows to dv_rows / dk_rows (the
+// work-group's first row in memory) 16 bytes per lane.  skip(r) says local
+// row r is not stored (past the end of the sequence, or written by another
+// pass).  Its barriers wait for LDS accesses only; the caller must see every
+// wave's reads of the stage buffers done (lds_barrier) before refilling them.
 template <int D, bool F16, class Skip>
-__device__ __forceinline__ void kv_store(KVState<D>& st, char* stage, char* rows, char* dk_rows,
+__device__ __forceinline__ void kv_store(KVState<D>& st, char* st0, char* st1, char* st2, char* st3, char* dk_rows,
                                          char* dv_rows, float s, int kb, int qh, int wave, int lane,
                                          const Skip& skip) {
   using C = KVCfg<D>;
   constexpr int kPart = C::NDB * 16 * 64 * 4;     // bytes per wave per tensor
   constexpr int kRowBytes = 2 * D;
-  constexpr int kBlockBytes = C::BK * kRowBytes;
-  static_assert(kPart <= C::QT, "a partial must fit in one stage buffer");
-  static_assert(kBlockBytes <= C::KB && kBlockBytes % 1024 == 0, "the rows must fit the K block");
+  constexpr int kKbBytes = 32 * kRowBytes;        // one key block's rows
+  constexpr int kKbChunks = kKbBytes / 1024;
+  static_assert(kPart <= C::QT && kKbBytes <= C::QT && kKbBytes % 1024 == 0, "stage buffers too small");
+  // the lane index laundered, so that the per-lane offsets below are formed
+  // here and not hoisted out of a caller's loop (and kept or spilled there)
+  asm volatile("" : "+v"(lane));
   const int g = lane >> 5, ln = lane & 31;
-  f32x4* part = reinterpret_cast<f32x4*>(stage);
-  bf16* rows16 = reinterpret_cast<bf16*>(rows);
+  char* mine = kb == 0 ? st0 : kb == 1 ? st1 : kb == 2 ? st2 : st3;
+  f32x4* part = reinterpret_cast<f32x4*>(mine);
+  bf16* rows16 = reinterpret_cast<bf16*>(mine);
 #pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     if (qh == 1) {
@@ -124,30 +135,50 @@ __device__ __forceinline__ void kv_store(KVState<D>& st, char* stage, char* rows
           part[(db * 4 + i4) * 64 + lane] = f32x4{acc[4 * i4], acc[4 * i4 + 1], acc[4 * i4 + 2], acc[4 * i4 + 3]};
         }
     }
-    __syncthreads();
+    lds_barrier();
     if (qh == 0) {
       const float f = pass == 0 ? 1.f : s;
-      // lane holds head-dim column 32*db + ln of keys 32*kb + 8*(i/4) + 4g + i%4
+      // The rows overwrite the first kKbBytes of the stage, which hold the
+      // partials of column blocks db < kFirst: those are read before any row
+      // is written, the others one block at a time.
+      constexpr int kFirst = kKbBytes / (16 * 64 * 4);
+      auto sum_block = [&](int db, const f32x4 (&o)[4]) __attribute__((always_inline)) {
+        // lane holds head-dim column 32*db + ln of keys 8*(i/4) + 4g + i%4 of the block
 #pragma unroll
-      for (int db = 0; db < C::NDB; ++db)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const f32x4 o = part[(db * 4 + i4) * 64 + lane];
+        for (int i4 = 0; i4 < 4; ++i4)
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const float x = ((pass == 0 ? st.dv[db][4 * i4 + j] : st.dk[db][4 * i4 + j]) + o[j]) * f;
-            rows16[(32 * kb + 8 * i4 + 4 * g + j) * D + 32 * db + ln] = pack1<F16>(x);
+            const float x = ((pass == 0 ? st.dv[db][4 * i4 + j] : st.dk[db][4 * i4 + j]) + o[i4][j]) * f;
+            rows16[(8 * i4 + 4 * g + j) * D + 32 * db + ln] = pack1<F16>(x);
           }
-        }
+      };
+      f32x4 first[kFirst][4];
+#pragma unroll
+      for (int db = 0; db < kFirst; ++db)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) first[db][i4] = part[(db * 4 + i4) * 64 + lane];
+#pragma unroll
+      for (int db = 0; db < kFirst; ++db) sum_block(db, first[db]);
+#pragma unroll
+      for (int db = kFirst; db < C::NDB; ++db) {
+        f32x4 o[4];
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) o[i4] = part[(db * 4 + i4) * 64 + lane];
+        sum_block(db, o);
+      }
     }
-    __syncthreads();
+    lds_barrier();
     char* dst = pass == 0 ? dv_rows : dk_rows;
 #pragma unroll
-    for (int c = wave; c < kBlockBytes / 1024; c += C::kWaves) {
-      const int off = c * 1024 + 16 * lane;
+    for (int c = wave; c < 4 * kKbChunks; c += C::kWaves) {
+      const int kbc = c / kKbChunks;
+      const char* src = kbc == 0 ? st0 : kbc == 1 ? st1 : kbc == 2 ? st2 : st3;
+      const int in_kb = (c % kKbChunks) * 1024 + 16 * lane;
+      const int off = kbc * kKbBytes + in_kb;
       if (!skip(off / kRowBytes))
-        *reinterpret_cast<bf16x8*>(dst + off) = *reinterpret_cast<const bf16x8*>(rows + off);
+        *reinterpret_cast<bf16x8*>(dst + off) = *reinterpret_cast<const bf16x8*>(src + in_kb);
     }
+    if (pass == 0) lds_barrier();   // the rows are read before the second pass overwrites the stages
   }
 }
 

@@ -572,11 +572,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_masked_kernel(BwdArgs a, PlanPtrs
 
   // sum the two query halves and store as the range-tiled kernel; global keys
   // are left to the global-key pass
-  char* stage = kb == 0 ? q_st0 : kb == 1 ? do_st0 : kb == 2 ? q_st1 : do_st1;
   const size_t row0 = (size_t)key_wg0 * (2 * D);
   const int b0 = min(2 * kt, p.nb - 1), b1 = min(2 * kt + 1, p.nb - 1);
   const unsigned long long gw0 = p.gbits[b0], gw1 = p.gbits[b1];
-  kv_store<D, F16>(st, stage, k_blk, reinterpret_cast<char*>(reinterpret_cast<bf16*>(a.dk) + kv_off) + row0,
+  kv_store<D, F16>(st, q_st0, do_st0, q_st1, do_st1, reinterpret_cast<char*>(reinterpret_cast<bf16*>(a.dk) + kv_off) + row0,
                    reinterpret_cast<char*>(reinterpret_cast<bf16*>(a.dv) + kv_off) + row0, a.scale, kb, qh, wave,
                    lane, [&](int r) {
                      const int key = key_wg0 + r;
