@@ -42,36 +42,51 @@ struct FwdCfg {
   static_assert(KT % 1024 == 0 && VT % 1024 == 0, "padded tiles must split into 1 KiB copies");
 };
 
-// Loop-invariant per-lane source offsets of this wave's share of a tile copy.
-// Copy n (0 <= n < COPIES) belongs to wave n % 4 and fills tile bytes
-// [1024n, 1024n + 1024).
-template <int D>
+// Loop-invariant per-lane source offsets of this wave's share of a tile copy,
+// for a work-group of NW waves.  Copy n (0 <= n < COPIES) belongs to wave
+// n % NW and fills tile bytes [1024n, 1024n + 1024).
+template <int D, int NW = 4>
 struct CopyPlan {
-  int koff[FwdCfg<D>::KPER];
-  int voff[FwdCfg<D>::VPER];
+  static constexpr int KPER = (FwdCfg<D>::KCOPIES + NW - 1) / NW;   // copies per wave (at most)
+  static constexpr int VPER = (FwdCfg<D>::VCOPIES + NW - 1) / NW;
+  int koff[KPER];
+  int voff[VPER];
 };
 
-template <int D>
-__device__ __forceinline__ void make_copy_plan(CopyPlan<D>& cp, int wave, int lane) {
-  using C = FwdCfg<D>;
+template <int D, int NW = 4>
+__device__ __forceinline__ void make_copy_plan(CopyPlan<D, NW>& cp, int wave, int lane) {
 #pragma unroll
-  for (int i = 0; i < C::KPER; ++i) cp.koff[i] = pad_slot_src<D, Pad<D>::KSTR>((wave + 4 * i) * 64 + lane);
+  for (int i = 0; i < CopyPlan<D, NW>::KPER; ++i) cp.koff[i] = pad_slot_src<D, Pad<D>::KSTR>((wave + NW * i) * 64 + lane);
 #pragma unroll
-  for (int i = 0; i < C::VPER; ++i) cp.voff[i] = pad_slot_src<D, Pad<D>::VSTR>((wave + 4 * i) * 64 + lane);
+  for (int i = 0; i < CopyPlan<D, NW>::VPER; ++i) cp.voff[i] = pad_slot_src<D, Pad<D>::VSTR>((wave + NW * i) * 64 + lane);
 }
 
-// Copy K and V rows [k0, k0 + 64) into one LDS stage (rows past L read zeros).
-template <int D>
-__device__ __forceinline__ void issue_kv(const CopyPlan<D>& cp, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
-                                         int k0, char* kbuf, char* vbuf, int wave) {
-  using C = FwdCfg<D>;
+// This wave's share of the copy of K rows [k0, k0 + 64) into one LDS stage
+// (rows past the end of the buffer resource read zeros); V likewise.
+template <int D, int NW = 4>
+__device__ __forceinline__ void issue_k(const CopyPlan<D, NW>& cp, __amdgpu_buffer_rsrc_t kr, int k0, char* kbuf, int wave) {
+  constexpr int COPIES = FwdCfg<D>::KCOPIES;
   const int soff = k0 * (2 * D);
 #pragma unroll
-  for (int i = 0; i < C::KPER; ++i)
-    if (owns_copy<4, C::KCOPIES>(wave, i)) buf2lds16(kr, cp.koff[i], soff, kbuf + (wave + 4 * i) * 1024);
+  for (int i = 0; i < CopyPlan<D, NW>::KPER; ++i)
+    if (owns_copy<NW, COPIES>(wave, i)) buf2lds16(kr, cp.koff[i], soff, kbuf + (wave + NW * i) * 1024);
+}
+
+template <int D, int NW = 4>
+__device__ __forceinline__ void issue_v(const CopyPlan<D, NW>& cp, __amdgpu_buffer_rsrc_t vr, int k0, char* vbuf, int wave) {
+  constexpr int COPIES = FwdCfg<D>::VCOPIES;
+  const int soff = k0 * (2 * D);
 #pragma unroll
-  for (int i = 0; i < C::VPER; ++i)
-    if (owns_copy<4, C::VCOPIES>(wave, i)) buf2lds16(vr, cp.voff[i], soff, vbuf + (wave + 4 * i) * 1024);
+  for (int i = 0; i < CopyPlan<D, NW>::VPER; ++i)
+    if (owns_copy<NW, COPIES>(wave, i)) buf2lds16(vr, cp.voff[i], soff, vbuf + (wave + NW * i) * 1024);
+}
+
+// Copy K and V rows [k0, k0 + 64) into one LDS stage.
+template <int D, int NW = 4>
+__device__ __forceinline__ void issue_kv(const CopyPlan<D, NW>& cp, __amdgpu_buffer_rsrc_t kr, __amdgpu_buffer_rsrc_t vr,
+                                         int k0, char* kbuf, char* vbuf, int wave) {
+  issue_k<D, NW>(cp, kr, k0, kbuf, wave);
+  issue_v<D, NW>(cp, vr, k0, vbuf, wave);
 }
 
 __device__ __forceinline__ void wait_copies_and_barrier() {
@@ -89,16 +104,12 @@ struct FwdState {
 
 __device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 
-// One key tile for one wave: S^T, mask, online softmax, O^T += V^T P^T.
-// need_mask (wave-uniform) says whether the tile straddles a mask boundary;
-// ok(j) then says whether key j is visible to the lane's query.
-template <int D, bool F16, class Mask>
-__device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, const char* vbuf, int k0,
-                                         bool need_mask, const Mask& ok, float c, int lane) {
+// 1. S^T (64 keys x 32 queries) for one key tile staged in LDS, as two 32x32
+// blocks: s0 keys 0..31, s1 keys 32..63 of the tile.
+template <int D, bool F16>
+__device__ __forceinline__ void tile_scores(const FwdState<D>& st, const char* kbuf, int lane, f32x16& s0, f32x16& s1) {
   using C = FwdCfg<D>;
   const int g = lane >> 5, ln = lane & 31;
-  // 1. S^T (64 keys x 32 queries) as two 32x32 blocks
-  f32x16 s0, s1;
   {
     const bf16x8 a0 = lds_load16(kbuf, row_offset_kpad<D>(ln, 0, g));
     const bf16x8 a1 = lds_load16(kbuf, row_offset_kpad<D>(32 + ln, 0, g));
@@ -112,8 +123,25 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
     s0 = mfma32x<F16>(a0, st.qr[k], s0);
     s1 = mfma32x<F16>(a1, st.qr[k], s1);
   }
+}
 
-  // 2. mask, only on tiles that straddle a boundary (wave-uniform decision)
+// 2.-3. Mask (only when need_mask, wave-uniform: the tile straddles a mask
+// boundary; ok(j) then says whether key j is visible to the lane's query) and
+// online-softmax update; the probabilities leave as the 16-bit B operand pb of
+// the P.V product.
+//
+// The two lanes holding one query share the tile maximum.  The running maximum
+// m is only raised when the tile's maximum exceeds it by more than
+// kRescaleSlack (log2 units); otherwise the tile is exponentiated against the
+// old m, so its terms are at most 2^kRescaleSlack.  O and l share that m, which
+// cancels in O / l and is folded into the log-sum-exp, so the result is the
+// same softmax; the rescale of O (and l) by exp2(m_old - m_new) then runs only
+// when some lane raised its maximum.
+template <int D, bool F16, class Mask>
+__device__ __forceinline__ void tile_softmax(FwdState<D>& st, f32x16& s0, f32x16& s1, int k0, bool need_mask,
+                                             const Mask& ok, float c, int lane, bf16x8 (&pb)[4]) {
+  using C = FwdCfg<D>;
+  const int g = lane >> 5;
   if (need_mask) {
     with_mask(ok, [&](const auto& m) __attribute__((always_inline)) {
 #pragma unroll
@@ -124,14 +152,6 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
       }
     });
   }
-
-  // 3. online softmax: the two lanes holding one query share the tile maximum.
-  // The running maximum m is only raised when the tile's maximum exceeds it by
-  // more than kRescaleSlack (log2 units); otherwise the tile is exponentiated
-  // against the old m, so its terms are at most 2^kRescaleSlack.  O and l share
-  // that m, which cancels in O / l and is folded into the log-sum-exp, so the
-  // result is the same softmax; the rescale of O (and l) by exp2(m_old - m_new)
-  // then runs only when some lane raised its maximum.
   float mA = max3(s0[0], s1[0], s0[1]), mB = max3(s1[1], s0[2], s1[2]);
 #pragma unroll
   for (int i = 3; i < 15; i += 2) {
@@ -159,15 +179,18 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
     rB += s1[i];
   }
   st.l_run += rA + rB;
-  bf16x8 pb[4];
   pb[0] = pack8<F16>(s0[0], s0[1], s0[2], s0[3], s0[4], s0[5], s0[6], s0[7]);
   pb[1] = pack8<F16>(s0[8], s0[9], s0[10], s0[11], s0[12], s0[13], s0[14], s0[15]);
   pb[2] = pack8<F16>(s1[0], s1[1], s1[2], s1[3], s1[4], s1[5], s1[6], s1[7]);
   pb[3] = pack8<F16>(s1[8], s1[9], s1[10], s1[11], s1[12], s1[13], s1[14], s1[15]);
+}
 
-  // 4. O^T += V^T P^T, 16 keys per MFMA step.  P^T's K slots (from the C
-  // layout of step 1) are keys 16t + 8*(slot/4) + 4g + slot%4; the transposing
-  // read gives V^T the same keys.
+// 4. O^T += V^T P^T, 16 keys per MFMA step.  P^T's K slots (from the C layout
+// of step 1) are keys 16t + 8*(slot/4) + 4g + slot%4; the transposing read
+// gives V^T the same keys.
+template <int D, bool F16>
+__device__ __forceinline__ void tile_pv(FwdState<D>& st, const char* vbuf, const bf16x8 (&pb)[4], int lane) {
+  using C = FwdCfg<D>;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
 #pragma unroll
@@ -177,6 +200,17 @@ __device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, cons
       st.o[db] = mfma32x<F16>(concat4(lo, hi), pb[t], st.o[db]);
     }
   }
+}
+
+// One key tile for one wave: S^T, mask, online softmax, O^T += V^T P^T.
+template <int D, bool F16, class Mask>
+__device__ __forceinline__ void fwd_tile(FwdState<D>& st, const char* kbuf, const char* vbuf, int k0,
+                                         bool need_mask, const Mask& ok, float c, int lane) {
+  f32x16 s0, s1;
+  tile_scores<D, F16>(st, kbuf, lane, s0, s1);
+  bf16x8 pb[4];
+  tile_softmax<D, F16>(st, s0, s1, k0, need_mask, ok, c, lane, pb);
+  tile_pv<D, F16>(st, vbuf, pb, lane);
 }
 
 }  // namespace fwdtile
