@@ -47,3 +47,20 @@ def test_allowed_pairs_counts_the_oracle_mask():
                                            (200, False, 300, (7,), None, 64), (64, True, 1, tuple(range(0, 64, 5)), None, 64)]:
         gl = tuple(p + L if p < 0 else p for p in glob)
         assert bench.allowed_pairs(L, causal, window, glob, bm, blk) == brute_pairs(L, causal, window, bm, blk, gl)
+
+
+def test_decode_cache_reads_counts_work_groups():
+    """The decode reads each K/V head once per work-group, and a work-group serves up to
+    four groups of 32 rows (query heads per K/V head x new tokens): 1 row group -> one
+    1-wave work-group, 2 -> one 2-wave work-group, more -> 4-wave work-groups."""
+    cases = [  # (Hq, Hkv, Lq) -> reads
+        ((32, 8, 1), 1),      # 4 rows
+        ((32, 8, 8), 1),      # 32 rows: one group
+        ((32, 8, 16), 1),     # 64 rows: two groups, one 2-wave work-group
+        ((32, 8, 32), 1),     # 128 rows: four groups
+        ((32, 8, 40), 2),     # 160 rows: five groups, two 4-wave work-groups
+        ((40, 2, 4), 1),      # 80 rows: three groups
+        ((8, 1, 100), 7),     # 800 rows: 25 groups
+    ]
+    for (hq, hkv, lq), reads in cases:
+        assert bench.decode_cache_reads(hq, hkv, lq) == reads, (hq, hkv, lq)
