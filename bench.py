@@ -626,7 +626,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(heads and batches would shard with no communication; see DESIGN.md).", file=sys.stderr)
+              "(heads and batches would shard with no communication).", file=sys.stderr)
         sys.exit(2)
 
     import torch
