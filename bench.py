@@ -625,7 +625,7 @@ def main():
                          "(FETCH_SIZE/WRITE_SIZE) can be scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(heads and batches would shard with no communication).", file=sys.stderr)
         sys.exit(2)
 
