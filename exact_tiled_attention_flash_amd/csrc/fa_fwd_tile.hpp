@@ -1,5 +1,6 @@
 // fa_fwd_tile.hpp -- the forward's per-tile machinery, shared by the
-// whole-sequence / chunk-pair forward kernel and the decode kernel.
+// whole-sequence / chunk-pair forward kernel, the decode kernel and the
+// mask-plan forward kernels.
 //
 // For one 64-key tile staged in LDS (padded rows, filled by direct
 // buffer->LDS copies) and one wave's 32 query columns:
@@ -35,8 +36,6 @@ struct FwdCfg {
   static constexpr int VT = BC * Pad<D>::VSTR;    // bytes of a padded V tile
   static constexpr int KCOPIES = KT / 1024;       // wave-wide 1 KiB copies per K tile
   static constexpr int VCOPIES = VT / 1024;
-  static constexpr int KPER = (KCOPIES + kWaves - 1) / kWaves;   // copies per wave (at most)
-  static constexpr int VPER = (VCOPIES + kWaves - 1) / kWaves;
   static constexpr int NSTEP = D / 16;            // MFMA K-steps over the head dim
   static constexpr int NDB = D / 32;              // 32-wide blocks of the head dim
   static_assert(KT % 1024 == 0 && VT % 1024 == 0, "padded tiles must split into 1 KiB copies");
