@@ -183,14 +183,21 @@ __device__ __forceinline__ void kv_store(KVState<D>& st, char* st0, char* st1, c
 }
 
 // Key-major element mask of the range-tiled kernels: the lane's key j is
-// fixed; query row q sits at key position q + shift (visibility as range_ok).
+// fixed; query row q (of L) sits at key position q + shift and sees j as
+// range_ok says, which for rows q >= 0 holds on one run of rows (fresh(): as
+// RangeMaskQ's).
 template <bool CAUSAL>
 struct RangeMaskK {
   int L, shift, window, j;
-  __device__ __forceinline__ bool operator()(int q) const {
-    // bitwise, not short-circuit, so that no divergent branch is formed
-    const int i = q + shift;
-    return (q < L) & (!CAUSAL | (j <= i)) & ((window <= 0) | ((i - j < window) & (CAUSAL | (j - i < window))));
+  __host__ __device__ __forceinline__ PosRun run() const {
+    const int p = j - shift;   // the row at the key's own position
+    return pos_run(CAUSAL ? max(0, p) : (window > 0 ? max(0, p - window + 1) : 0), window > 0 ? min(L, p + window) : L);
+  }
+  __host__ __device__ __forceinline__ bool operator()(int q) const { return run()(q); }
+  __device__ __forceinline__ PosRun fresh() const {
+    RangeMaskK m = *this;
+    asm volatile("" : "+v"(m.j));
+    return m.run();
   }
 };
 
@@ -288,9 +295,9 @@ __device__ __forceinline__ void kv_tile(KVState<D>& st, const Addr& ad_in, const
   // plain select writes new registers, and the join of the two versions of P
   // then costs 16 register copies on the unmasked path.
   if (need_mask) {
-    with_mask(ok, [&](const auto& m) __attribute__((always_inline)) {
+    with_mask(ok, qw0 + 4 * g, [&](const auto& m) __attribute__((always_inline)) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) p[i] = keep_or_zero(p[i], m(qw0 + 8 * (i >> 2) + 4 * g + (i & 3)));
+      for (int i = 0; i < 16; ++i) p[i] = keep_or_zero(p[i], m(8 * (i >> 2) + (i & 3)));
     });
   }
   // dV += P^T dO: A = P (lane = key, K slots = queries), B = dO via the transposing read
@@ -394,9 +401,9 @@ __device__ __forceinline__ void q_tile(QState<D>& st, const QAddr<D>& ad, const 
 #pragma unroll
     for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(p[i], c, -st.lse2));
     if (need_mask) {
-      with_mask(ok, [&](const auto& m) __attribute__((always_inline)) {
+      with_mask(ok, k0 + 32 * kb + 4 * g, [&](const auto& m) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) p[i] = keep_or_zero(p[i], m(k0 + 32 * kb + 8 * (i >> 2) + 4 * g + (i & 3)));
+        for (int i = 0; i < 16; ++i) p[i] = keep_or_zero(p[i], m(8 * (i >> 2) + (i & 3)));
       });
     }
     // dS^T = P^T * (dP^T - D)

@@ -362,12 +362,35 @@ struct EitherMask {
   B b;
 };
 
+// The tile steps evaluate a mask at base + c, base per lane and tile, c a
+// compile-time offset.  A mask with a fresh() member (one run of positions,
+// PosRun) is shifted by base once per tile, so that each element costs a
+// subtraction from an immediate, a compare and a select, with nothing held in
+// registers across tiles; fresh() forms the run from a copy of the lane's
+// position that the compiler must take as new on every tile (otherwise it
+// keeps the run, or per-element offsets, in registers for the whole kernel).
+// Other masks are called at base + c.
+template <class M>
+struct AtBase {
+  const M& m;
+  int base;
+  __device__ __forceinline__ bool operator()(int c) const { return m(base + c); }
+};
+template <class M>
+__device__ __forceinline__ auto mask_at(const M& m, int base, int) -> decltype(m.fresh()) {
+  auto r = m.fresh();
+  r.lo -= base;
+  return r;
+}
+template <class M>
+__device__ __forceinline__ AtBase<M> mask_at(const M& m, int base, long) { return AtBase<M>{m, base}; }
+
 template <class M, class F>
-__device__ __forceinline__ void with_mask(const M& m, const F& f) { f(m); }
+__device__ __forceinline__ void with_mask(const M& m, int base, const F& f) { f(mask_at(m, base, 0)); }
 template <class A, class B, class F>
-__device__ __forceinline__ void with_mask(const EitherMask<A, B>& m, const F& f) {
-  if (m.use_a) f(m.a);
-  else f(m.b);
+__device__ __forceinline__ void with_mask(const EitherMask<A, B>& m, int base, const F& f) {
+  if (m.use_a) f(mask_at(m.a, base, 0));
+  else f(mask_at(m.b, base, 0));
 }
 
 // x = keep ? x : y in place (a tied operand writes no new register, so the
@@ -390,16 +413,38 @@ __device__ __forceinline__ float keep_or_zero(float x, bool keep) {
 // window then reaches both ways, |i - j| < w (kler.cn "大模型高效注意力机制全
 // 解析" §3.2.1; book.anysome.cn "高效注意力" §4 for the one-sided form).
 template <bool CAUSAL>
-__device__ __forceinline__ bool range_ok(int j, int i, int Lk, int window) {
+__host__ __device__ __forceinline__ bool range_ok(int j, int i, int Lk, int window) {
   // bitwise, not short-circuit, so that no divergent branch is formed
   return (j < Lk) & (!CAUSAL | (j <= i)) & ((window <= 0) | ((j > i - window) & (CAUSAL | (j < i + window))));
 }
 
-// Query-major element mask: the lane's query position is fixed.
+// One run of positions, lo .. lo+span-1 (span 0: none): one subtraction and
+// one unsigned compare per position.
+struct PosRun {
+  int lo;
+  unsigned span;
+  __host__ __device__ __forceinline__ bool operator()(int x) const { return unsigned(x - lo) < span; }
+};
+__host__ __device__ __forceinline__ PosRun pos_run(int lo, int hi) { return PosRun{lo, hi > lo ? unsigned(hi - lo) : 0u}; }
+
+// Query-major element mask: the lane's query position i is fixed.  For keys
+// j >= 0, range_ok(j, i, ..) holds on one run of keys, which the tile steps
+// evaluate (fresh(): from a copy of i that the compiler must take as new on
+// every tile, so the run is formed per masked tile and not kept in registers
+// for the whole kernel).
 template <bool CAUSAL>
 struct RangeMaskQ {
   int Lk, window, i;
-  __device__ __forceinline__ bool operator()(int j) const { return range_ok<CAUSAL>(j, i, Lk, window); }
+  __host__ __device__ __forceinline__ PosRun run() const {
+    const int hi = CAUSAL ? min(Lk, i + 1) : (window > 0 ? min(Lk, i + window) : Lk);
+    return pos_run(window > 0 ? max(0, i - window + 1) : 0, hi);
+  }
+  __host__ __device__ __forceinline__ bool operator()(int j) const { return run()(j); }
+  __device__ __forceinline__ PosRun fresh() const {
+    RangeMaskQ m = *this;
+    asm volatile("" : "+v"(m.i));
+    return m.run();
+  }
 };
 
 // Do the keys [k0, k0 + BC) need the elementwise mask for queries [i_lo, i_hi]?

@@ -142,12 +142,12 @@ __device__ __forceinline__ void tile_softmax(FwdState<D>& st, f32x16& s0, f32x16
   using C = FwdCfg<D>;
   const int g = lane >> 5;
   if (need_mask) {
-    with_mask(ok, [&](const auto& m) __attribute__((always_inline)) {
+    with_mask(ok, k0 + 4 * g, [&](const auto& m) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int kk0 = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
-        s0[i] = keep_or(s0[i], m(kk0), -INFINITY);
-        s1[i] = keep_or(s1[i], m(kk0 + 32), -INFINITY);
+        const int c = 8 * (i >> 2) + (i & 3);
+        s0[i] = keep_or(s0[i], m(c), -INFINITY);
+        s1[i] = keep_or(s1[i], m(c + 32), -INFINITY);
       }
     });
   }
