@@ -25,7 +25,10 @@
 // 3. Global positions are whole rows and columns of the mask.  The row lists
 //    leave global query rows out and the column lists leave global keys out;
 //    split passes over the whole sequence compute those rows and keys
-//    (section 3 below), so no work-group has to walk a whole row.
+//    (section 3 below), so no work-group has to walk a whole row.  With few
+//    global positions the row kernels also take the global keys themselves,
+//    from LDS after their tiles, instead of visiting the tiles holding them
+//    (kFoldGlobals).
 #include "fa_bwd_tile.hpp"
 #include "fa_fwd_tile.hpp"
 
@@ -76,6 +79,20 @@ PlanPtrs plan_ptrs(const void* plan, int L) {
 namespace {
 
 // ------------------------------------------------------------ 1. plan
+
+// Global keys folded into the row kernels: with at most kFoldGlobals global
+// positions, the forward and dQ kernels take every row's global keys before
+// their first tile, straight from the keys' rows in HBM (fold_keys_fwd,
+// fold_keys_dq), instead of visiting the key tiles that hold them (a whole
+// tile for one key, on every work-group row).  The row lists then leave those
+// tiles out unless the window or the blocks reach them, and such tiles mask
+// the global keys out.  The count comes from the plan (meta[2], the distinct
+// global positions), so the plan and the kernels always agree.
+constexpr int kFoldGlobals = 8;
+__device__ __forceinline__ int fold_count(const int* meta, int L) {
+  const int n = min(max(meta[2], 0), L);
+  return n <= kFoldGlobals ? n : 0;
+}
 
 struct PlanBuild {
   MaskDesc m;
@@ -145,7 +162,10 @@ __global__ __launch_bounds__(1024) void plan_gpos_kernel(PlanBuild p) {
 // count only when use_gq (use_gk) is set: a global query row sees every key,
 // so the row lists leave it to the global-row pass instead of visiting every
 // tile; likewise the column lists leave global keys to the global-key pass.
-__device__ int block_class(const PlanBuild& p, int qb, int kb, bool use_gq, bool use_gk, int& block_ok) {
+// excl_gk: global keys are folded into the row kernels (fold_count), so a
+// block holding one is never full (the tile masks it out).
+__device__ int block_class(const PlanBuild& p, int qb, int kb, bool use_gq, bool use_gk, bool excl_gk,
+                           int& block_ok) {
   block_ok = 0;
   if (qb >= p.nb || kb >= p.nb) return 0;
   const int i0 = 64 * qb, i1 = min(i0 + 63, p.L - 1);
@@ -165,7 +185,7 @@ __device__ int block_class(const PlanBuild& p, int qb, int kb, bool use_gq, bool
   block_ok = bm ? 1 : 0;
   const bool glob = (use_gq && p.gbits[qb] != 0) || (use_gk && p.gbits[kb] != 0);
   if (c_none || ((w_none || !bm) && !glob)) return 0;
-  return (inside && c_all && w_all && bm) ? 2 : 1;
+  return (inside && c_all && w_all && bm && !(excl_gk && p.gbits[kb] != 0)) ? 2 : 1;
 }
 
 // One work-group per work-group row (blockIdx.y == 0: 128 queries against
@@ -177,6 +197,7 @@ __global__ __launch_bounds__(256) void plan_lists_kernel(PlanBuild p) {
   const bool cols = blockIdx.y == 1;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   unsigned* ent = (cols ? p.col_ent : p.row_ent) + (size_t)w * p.nb;
+  const bool fold = fold_count(p.meta, p.L) > 0;
   int base = 0;
   for (int x0 = 0; x0 < p.nb; x0 += 256) {
     const int x = x0 + tid;
@@ -184,11 +205,13 @@ __global__ __launch_bounds__(256) void plan_lists_kernel(PlanBuild p) {
     bool keep = false;
     if (x < p.nb) {
       int bm0, bm1;
-      const int c0 = cols ? block_class(p, x, 2 * w, true, false, bm0) : block_class(p, 2 * w, x, false, true, bm0);
-      const int c1 = cols ? block_class(p, x, 2 * w + 1, true, false, bm1)
-                          : block_class(p, 2 * w + 1, x, false, true, bm1);
+      const int c0 = cols ? block_class(p, x, 2 * w, true, false, false, bm0)
+                          : block_class(p, 2 * w, x, false, !fold, fold, bm0);
+      const int c1 = cols ? block_class(p, x, 2 * w + 1, true, false, false, bm1)
+                          : block_class(p, 2 * w + 1, x, false, !fold, fold, bm1);
       keep = (c0 | c1) != 0;
-      e = (unsigned)x | ((unsigned)c0 << 16) | ((unsigned)c1 << 18) | ((unsigned)bm0 << 20) | ((unsigned)bm1 << 21);
+      e = (unsigned)x | ((unsigned)c0 << 16) | ((unsigned)c1 << 18) | ((unsigned)bm0 << 20) | ((unsigned)bm1 << 21) |
+          ((unsigned)(p.gbits[x] != 0ull) << 22);
     }
     const unsigned long long bal = __ballot(keep);
     const int before = __popcll(bal & ((1ull << lane) - 1ull));
@@ -267,16 +290,20 @@ __device__ __forceinline__ void plan_wg(int r, int n_heads, int nw, int n_heavy_
 
 // Query-major element mask: the lane's query i is fixed; k0 is the tile's
 // first key, gk the global bits of its 64 keys, gq whether i is global, bm
-// the block-sparse bit of the lane's 64 x 64 block.
+// the block-sparse bit of the lane's 64 x 64 block.  excl: the global keys
+// are folded into the row's initial state (fold_keys_*), so the tile leaves
+// them out instead.
 template <bool CAUSAL>
 struct GeneralMaskQ {
   int L, window, i, k0;
   bool gq, bm;
   unsigned long long gk;
+  bool excl;
   // bitwise, not short-circuit, so that no divergent branch is formed
   __device__ __forceinline__ bool operator()(int j) const {
-    const bool local = bm & ((window <= 0) | ((j > i - window) & (j < i + window)));
-    const bool glob = gq | (((gk >> (j - k0)) & 1ull) != 0);
+    const bool gbit = ((gk >> (j - k0)) & 1ull) != 0;
+    const bool local = bm & ((window <= 0) | ((j > i - window) & (j < i + window))) & !(excl & gbit);
+    const bool glob = gq | (!excl & gbit);
     return (j < L) & (!CAUSAL | (j <= i)) & (local | glob);
   }
 };
@@ -299,10 +326,133 @@ __device__ __forceinline__ bool is_global(const unsigned long long* gbits, int p
   return pos < L && ((gbits[pos >> 6] >> (pos & 63)) & 1ull) != 0;
 }
 
+// ---- global keys folded into the row kernels (fold_count > 0)
+// With the work-group's first tile copies, its waves copy the n_g global
+// keys' K and V rows into an LDS area of their own (kGlobalRowsBytes) with
+// the direct buffer -> LDS copies, so the first tile's wait covers them: row
+// t of K at t * 2D bytes, row t of V at (kFoldGlobals + t) * 2D, 16 bytes per
+// lane, thread i = 64 wave + lane taking row i / (D/8), chunk i % (D/8); a
+// wave's rows are all K or all V, so its resource is uniform.  Rows past n_g
+// repeat the first global position (never read).  The global positions come
+// through the scalar path (plan memory is read-only here).
+template <int D>
+constexpr int kGlobalRowsBytes = 2 * kFoldGlobals * 2 * D;
+template <int D>
+__device__ __forceinline__ void stage_global_rows(char* lds, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs,
+                                                  const int* gpos, int n_g, int L, int wave, int lane) {
+  constexpr int CH = D / 8;                          // 16-byte chunks per row
+  constexpr int kWavesUsed = (2 * kFoldGlobals * CH) / 64;
+  static_assert((2 * kFoldGlobals * CH) % 64 == 0 && kWavesUsed <= 4, "rows of one wave must be all K or all V");
+  if (wave >= kWavesUsed) return;
+  typedef const __attribute__((address_space(4))) int* cptr;
+  const int t = wave * 64 + lane;
+  const int r = t / CH, chunk = t % CH;
+  const int row = r % kFoldGlobals;
+  int pos = ((cptr)gpos)[0];
+#pragma unroll
+  for (int i = 1; i < kFoldGlobals; ++i)
+    if (i < n_g) pos = row == i ? ((cptr)gpos)[i] : pos;
+  pos = min(max(pos, 0), L - 1);
+  const bool is_v = wave * 64 >= kFoldGlobals * CH;
+  buf2lds16(is_v ? vrs : krs, pos * (2 * D) + 16 * chunk, 0, lds + wave * 1024);
+}
+
+// The lane holds its query's head dims 16k + 8g .. +7 (the MFMA B-operand
+// layout of the Q and dO registers): half a dot product with an LDS row,
+// completed with the partner lane (lane ^ 32), which holds the other half.
+template <int D, bool F16>
+__device__ __forceinline__ float row_dot(const bf16x8 (&x)[D / 16], const char* row, int g) {
+  float acc = 0.f;
+#pragma unroll
+  for (int k = 0; k < D / 16; ++k) {
+    const bf16x8 y = lds_load16(row, 32 * k + 16 * g);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf(unpack1<F16>(x[k][e]), unpack1<F16>(y[e]), acc);
+  }
+  return pair_sum(acc);
+}
+
+// acc += f * an LDS row, over the lane's elements of an accumulator in the
+// MFMA C layout with lane = query (block db, register i: head dim 32db +
+// 8(i/4) + 4g + i%4).
+template <int D, bool F16>
+__device__ __forceinline__ void row_axpy(f32x16 (&acc)[D / 32], float f, const char* row, int g) {
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const bf16x4 y = *(const FA_LDS bf16x4*)((const FA_LDS char*)row + 64 * db + 16 * i4 + 8 * g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[db][4 * i4 + e] = fmaf(f, unpack1<F16>(y[e]), acc[db][4 * i4 + e]);
+    }
+}
+
+// Forward: the row's global keys (all n_g of them, or those at or before the
+// row when causal) taken into the online-softmax state after its tiles, one
+// key at a time like a tile of one key (the order does not change the
+// softmax); P stays in float32 here.  lds: the staged rows (read after the
+// tiles, when the tile loop's registers are free).
+template <int D, bool CAUSAL, bool F16>
+__device__ __forceinline__ void fold_keys_fwd(fwdtile::FwdState<D>& st, const char* lds, const int* gpos, int n_g,
+                                              int L, int my_q, float c, int g) {
+  typedef const __attribute__((address_space(4))) int* cptr;
+#pragma unroll 1
+  for (int t = 0; t < n_g; ++t) {
+    const int pg = ((cptr)gpos)[t];
+    const float x = row_dot<D, F16>(st.qr, lds + t * (2 * D), g) * c;
+    if (!CAUSAL || pg <= my_q) {
+      if (x > st.m_run) {
+        const float alpha = fast_exp2(st.m_run - x);
+        st.l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) st.o[db] *= alpha;
+        st.m_run = x;
+      }
+      const float pt = fast_exp2(x - st.m_run);
+      if (g == 0) st.l_run += pt;   // the row sum is the two lanes' sum
+      row_axpy<D, F16>(st.o, pt, lds + (kFoldGlobals + t) * (2 * D), g);
+    }
+  }
+}
+
+// dQ: the row's global keys' terms of dQ = sum_j dS_ij K_j (scaled at the
+// end like the rest), dS_ij = P_ij (dP_ij - D_i), P_ij = exp2(S_ij c - LSE_i
+// log2 e), dP_ij = dO_i . V_j (the chain from -D_i); dS stays in float32.
+// After the row's tiles, from the staged rows, as in the forward.
+template <int D, bool CAUSAL, bool F16>
+__device__ __forceinline__ void fold_keys_dq(bwdtile::QState<D>& st, const char* lds, const int* gpos, int n_g,
+                                             int L, int my_q, float c, int g) {
+  typedef const __attribute__((address_space(4))) int* cptr;
+#pragma unroll 1
+  for (int t = 0; t < n_g; ++t) {
+    const int pg = ((cptr)gpos)[t];
+    const char* krow = lds + t * (2 * D);
+    const float sc = row_dot<D, F16>(st.qr, krow, g);
+    const float dp = row_dot<D, F16>(st.dor, lds + (kFoldGlobals + t) * (2 * D), g) + st.negd[0];
+    const float pt = fast_exp2(fmaf(sc, c, -st.lse2));
+    const float ds = (!CAUSAL || pg <= my_q) ? pt * dp : 0.f;
+    row_axpy<D, F16>(st.dq, ds, krow, g);
+  }
+}
+
 // entry fields (the tile index is clamped by the caller's list length)
 __device__ __forceinline__ int ent_tile(unsigned e, int nb) { return min((int)(e & 0xffffu), nb - 1); }
 __device__ __forceinline__ int ent_class(unsigned e, int half) { return (int)((e >> (16 + 2 * half)) & 3u); }
 __device__ __forceinline__ bool ent_block(unsigned e, int half) { return ((e >> (20 + half)) & 1u) != 0; }
+// Does the listed tile hold a global position?  Only then do the kernels read
+// the tile's global bits (plan_word).
+__device__ __forceinline__ bool ent_glob(unsigned e) { return ((e >> 22) & 1u) != 0; }
+
+// A word of the plan at a wave-uniform index, read through the constant
+// address space (the attention kernels never write the plan), i.e. a scalar
+// load into scalar registers.  A vector load would be waited for with the
+// vector-memory counter, which also counts the next tile's copies issued just
+// before: where its register is reused after a branch, the wait is for all of
+// them, on every tile.
+__device__ __forceinline__ unsigned long long plan_word(const unsigned long long* a, int i) {
+  typedef const __attribute__((address_space(4))) unsigned long long* cptr;
+  return ((cptr)a)[i];
+}
 
 // A zero the compiler cannot see through.
 __device__ __forceinline__ int opaque_zero() {
@@ -334,6 +484,7 @@ __global__ __launch_bounds__(256, 2) void fwd_masked_kernel(FwdArgs a, PlanPtrs 
   __shared__ __attribute__((aligned(1024))) char v_st0[C::VT];
   __shared__ __attribute__((aligned(1024))) char k_st1[C::KT];
   __shared__ __attribute__((aligned(1024))) char v_st1[C::VT];
+  __shared__ __attribute__((aligned(1024))) char g_rows[kGlobalRowsBytes<D>];
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 5, ln = lane & 31;
@@ -362,6 +513,8 @@ __global__ __launch_bounds__(256, 2) void fwd_masked_kernel(FwdArgs a, PlanPtrs 
   CopyPlan<D> cp;
   make_copy_plan<D>(cp, wave, lane);
   if (n_ent > 0) issue_kv<D>(cp, krs, vrs, ent_tile(cur, p.nb) * C::BC, k_st0, v_st0, wave);
+  const int n_fold = fold_count(p.meta, L);
+  if (n_fold > 0) stage_global_rows<D>(g_rows, krs, vrs, p.gpos, n_fold, L, wave, lane);
 
   FwdState<D> st;
 #pragma unroll
@@ -379,14 +532,15 @@ __global__ __launch_bounds__(256, 2) void fwd_masked_kernel(FwdArgs a, PlanPtrs 
     const int cls = ent_class(ent, half);
     if (cls != 0 && q_w0 < L) {
       const int kt = ent_tile(ent, p.nb);
-      const unsigned long long gk = cls == 1 ? p.gbits[kt] : 0ull;
+      const bool tg = (cls == 1) & ent_glob(ent);
+      const unsigned long long gk = tg ? plan_word(p.gbits, kt) : 0ull;
       const bool bm = ent_block(ent, half);
       // without a global key in the tile and with the block allowed, the
       // window and causal range alone decide (a global row's own output is
       // not stored here): the range kernels' cheaper element test
       const EitherMask<RangeMaskQ<CAUSAL>, GeneralMaskQ<CAUSAL>> ok{
-          (bool)((gk == 0ull) & bm), RangeMaskQ<CAUSAL>{L, window, my_q},
-          GeneralMaskQ<CAUSAL>{L, window, my_q, kt * C::BC, gq, bm, gk}};
+          (bool)(!tg & bm), RangeMaskQ<CAUSAL>{L, window, my_q},
+          GeneralMaskQ<CAUSAL>{L, window, my_q, kt * C::BC, gq, bm, gk, n_fold > 0}};
       fwd_tile<D, F16>(st, kb, vb, kt * C::BC, cls == 1, ok, c, lane);
     }
   };
@@ -408,6 +562,8 @@ __global__ __launch_bounds__(256, 2) void fwd_masked_kernel(FwdArgs a, PlanPtrs 
     cur = nxt;
     nxt = uniform(far1);
   }
+
+  if (n_fold > 0 && q_w0 < L) fold_keys_fwd<D, CAUSAL, F16>(st, g_rows, p.gpos, n_fold, L, my_q, c, g);
 
   // epilogue: a row with no allowed key gets O = 0, LSE = -inf; a global row
   // is left to the global-row pass
@@ -533,13 +689,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_masked_kernel(BwdArgs a, PlanPtrs
     const int cls = ent_class(ent, half);
     const int q0 = ent_tile(ent, p.nb) * C::BQ;
     if (cls != 0 && key_w0 < L && q0 + 32 * qh < L) {
-      const unsigned long long gqb = cls == 1 ? p.gbits[ent_tile(ent, p.nb)] : 0ull;
+      const bool tg = (cls == 1) & ent_glob(ent);
+      const unsigned long long gqb = tg ? plan_word(p.gbits, ent_tile(ent, p.nb)) : 0ull;
       const bool bm = ent_block(ent, half);
       // without a global query in the tile and with the block allowed, the
       // window and causal range alone decide (a global key's own dK, dV are
       // not stored here)
       const EitherMask<RangeMaskK<CAUSAL>, GeneralMaskK<CAUSAL>> ok{
-          (bool)((gqb == 0ull) & bm), RangeMaskK<CAUSAL>{L, 0, window, my_key},
+          (bool)(!tg & bm), RangeMaskK<CAUSAL>{L, 0, window, my_key},
           GeneralMaskK<CAUSAL>{L, window, my_key, q0, gk, bm, gqb}};
       kv_tile<D, F16>(st, ad, k_blk, v_blk, qs, dos, ss, q0, cls == 1, ok, qh, c, lane);
     }
@@ -594,6 +751,7 @@ __global__ __launch_bounds__(256, 2) void dq_masked_kernel(BwdArgs a, PlanPtrs p
   __shared__ __attribute__((aligned(1024))) char v_st0[C::VT];
   __shared__ __attribute__((aligned(1024))) char k_st1[C::KT];
   __shared__ __attribute__((aligned(1024))) char v_st1[C::VT];
+  __shared__ __attribute__((aligned(1024))) char g_rows[kGlobalRowsBytes<D>];
 
   const int lane = threadIdx.x & 63, wave = wave_id();
   const int g = lane >> 5, ln = lane & 31;
@@ -641,6 +799,8 @@ __global__ __launch_bounds__(256, 2) void dq_masked_kernel(BwdArgs a, PlanPtrs p
   const EntryStream es{make_rsrc(ents, 4u * (unsigned)n_ent)};
   unsigned cur = n_ent > 0 ? ents[0] : 0u, nxt = n_ent > 1 ? ents[1] : 0u;
   if (n_ent > 0) issue(cur, k_st0, v_st0);
+  const int n_fold = fold_count(p.meta, L);
+  if (n_fold > 0) stage_global_rows<D>(g_rows, krs, vrs, p.gpos, n_fold, L, wave, lane);
 
   QState<D> st;
   {
@@ -658,6 +818,7 @@ __global__ __launch_bounds__(256, 2) void dq_masked_kernel(BwdArgs a, PlanPtrs p
     for (int db = 0; db < C::NDB; ++db) st.dq[db] = f32x16{};
   }
   const float c = a.scale_log2;
+  const bool excl_gk = n_fold > 0;
 
   auto step = [&](unsigned ent, const char* kb, const char* vb) {
     const int cls = ent_class(ent, half);
@@ -666,7 +827,7 @@ __global__ __launch_bounds__(256, 2) void dq_masked_kernel(BwdArgs a, PlanPtrs p
       // (the forward's choice of a cheaper element test costs this kernel
       // spills: it keeps the general one)
       const GeneralMaskQ<CAUSAL> ok{L, window, my_q, kt * C::BC, gq, ent_block(ent, half),
-                                    cls == 1 ? p.gbits[kt] : 0ull};
+                                    ((cls == 1) & ent_glob(ent)) ? plan_word(p.gbits, kt) : 0ull, excl_gk};
       q_tile<D, F16>(st, ad, kb, vb, kt * C::BC, cls == 1, ok, c, lane);
     }
   };
@@ -687,6 +848,8 @@ __global__ __launch_bounds__(256, 2) void dq_masked_kernel(BwdArgs a, PlanPtrs p
     cur = nxt;
     nxt = uniform(far1);
   }
+
+  if (n_fold > 0 && q_w0 < L) fold_keys_dq<D, CAUSAL, F16>(st, g_rows, p.gpos, n_fold, L, my_q, c, g);
 
   if (my_q < L && !gq) {         // global rows: the global-row pass
     bf16* dQr = reinterpret_cast<bf16*>(a.dq) + q_off + (size_t)my_q * D;

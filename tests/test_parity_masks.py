@@ -74,6 +74,14 @@ CASES = [
     ("globals only, many L700 fp16", 1, 2, 1, 700, 64, torch.float16, True, 1, tuple(range(0, 700, 37)), 64, None, 708),
     ("plain non-causal L300", 1, 2, 2, 300, 128, torch.bfloat16, False, 0, (), 64, None, 709),
     ("window 1 only L257", 1, 2, 2, 257, 128, torch.bfloat16, False, 1, (), 64, None, 710),
+    # global keys inside wide windows: their band tiles would be full, but the folded keys
+    # (at most 8 global positions) must be masked out of them and counted once
+    ("sym w300 globals in band L1000", 1, 2, 2, 1000, 128, torch.bfloat16, False, 300, (300, 301, 700), 64,
+     None, 711),
+    ("causal w400 globals in band L900 d64", 1, 2, 1, 900, 64, torch.bfloat16, True, 400, (100, 450, -1), 64,
+     None, 712),
+    ("nine globals, tile path L800", 1, 2, 2, 800, 128, torch.bfloat16, False, 100, tuple(range(40, 800, 90)), 64,
+     None, 713),
 ]
 
 
@@ -143,7 +151,7 @@ def plan_sections(L):
     return nb, nw, out
 
 
-def check_lists(cnt, ent, ordr, heavy, nb, nw, ok, L, cols):
+def check_lists(cnt, ent, ordr, heavy, nb, nw, ok, L, cols, no_full=None):
     assert sorted(ordr.tolist()) == list(range(nw))
     counts = cnt[ordr]
     assert np.all(counts[:-1] >= counts[1:]), "work-group order must be by descending count"
@@ -167,6 +175,8 @@ def check_lists(cnt, ent, ordr, heavy, nb, nw, ok, L, cols):
                     assert cls in (1, 2), (wg, t, half, "a block with an allowed pair must be listed")
                 if cls == 2:
                     assert inside and blk.all(), (wg, t, half, "a full block must hold only allowed pairs")
+                    if no_full is not None:
+                        assert not no_full[64 * t:64 * t + 64].any(), (wg, t, half, "a folded global key in a full block")
 
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
@@ -186,17 +196,22 @@ def test_plan_blocks_match_oracle_mask(case):
         assert bool((int(gbits[p // 64]) >> (p % 64)) & 1) == (p in gl)
     meta = arr("meta", np.int32)
     assert int(meta[2]) == len(gl) and arr("gpos", np.int32)[:len(gl)].tolist() == sorted(gl)
-    # the mask without global rows (for the row lists) and without global keys (column lists)
+    # the mask without global rows (for the row lists) and without global keys (column lists).
+    # With at most 8 global positions the row kernels fold the global keys into each row's
+    # initial state: the row lists then hold only the window / block pairs, and no full
+    # block of theirs may hold a global key (its tile must mask the key out).
     L = w.L
     i, j = np.arange(L)[:, None], np.arange(L)[None, :]
     causal_ok = (j <= i) if case[7] else np.ones((L, L), dtype=bool)
     base = oracle.general_mask(np.arange(L), np.arange(L), case[7], case[8], bm, case[10], ())
     isg = np.isin(np.arange(L), sorted(gl))
-    ok_rows = base | (isg[None, :] & causal_ok)
+    fold = 0 < len(gl) <= 8
+    ok_gk = isg[None, :] & causal_ok
+    ok_rows = base if fold else base | ok_gk
     ok_cols = base | (isg[:, None] & causal_ok)
-    assert np.array_equal(ok_rows | ok_cols, ok)
+    assert np.array_equal(ok_rows | ok_cols | ok_gk, ok)
     check_lists(arr("row_cnt", np.int32), arr("row_ent", np.uint32).reshape(nw, nb), arr("row_ord", np.int32),
-                int(meta[0]), nb, nw, ok_rows, w.L, cols=False)
+                int(meta[0]), nb, nw, ok_rows, w.L, cols=False, no_full=isg if fold else None)
     check_lists(arr("col_cnt", np.int32), arr("col_ent", np.uint32).reshape(nw, nb), arr("col_ord", np.int32),
                 int(meta[1]), nb, nw, ok_cols, w.L, cols=True)
 
