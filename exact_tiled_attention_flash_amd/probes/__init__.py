@@ -6,4 +6,5 @@ hipcc) and run them on an MI355X with::
 
     python -m exact_tiled_attention_flash_amd.probes --build
     python -m exact_tiled_attention_flash_amd.probes coissue
+    python -m exact_tiled_attention_flash_amd.probes ldsread
 """
