@@ -62,6 +62,11 @@ def bwd_flops(B, Hq, L, d, causal, window):
     return 2.5 * fwd_flops(B, Hq, L, d, causal, window)
 
 
+def score_matrix_bytes(B, H, L, elt=2):
+    """Bytes of the full L x L score matrix of one layer (what the tiled method never stores)."""
+    return elt * B * H * L * L
+
+
 def fwd_bytes(B, Hq, Hkv, L, d, elt=2):
     """Algorithmic HBM bytes of one forward: Q, K, V read once; O and LSE written."""
     return (B * Hq * L * d + 2 * B * Hkv * L * d) * elt + B * Hq * L * d * elt + B * Hq * L * 4
@@ -797,7 +802,7 @@ def main():
         out["sparse"] = measure_sparse()
         out["sparse_block"] = measure_sparse(block_band=True)
     ctx = dict(PAGES_CONTEXT)
-    ctx["this_layer"] = {"score_matrix_bytes_fp16": 2 * w.B * w.Hq * w.L * w.L,
+    ctx["this_layer"] = {"score_matrix_bytes_fp16": score_matrix_bytes(w.B, w.Hq, w.L),
                          "extra_bytes_fwd_lse": int(lse.numel() * 4),
                          "extra_bytes_bwd_workspace": int(ws.numel())}
     out["context"] = ctx
